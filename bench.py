@@ -1,0 +1,283 @@
+#!/usr/bin/env python3
+"""Benchmark of the libssd varlen SSD scan on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+A step is one call of ssd_chunk_scan_varlen_fwd_inplace (every kernel of the
+scan) over one batch of synthetic input already resident in HBM.  Each timed
+step first evicts the caches (a 512 MiB fill, outside the timed events), then
+the call is bracketed by HIP events; ms_per_step is the mean over the K steps
+and `value` = total tokens / that time.  Per-kernel durations come from the
+events the library records between its launches on the same stream.
+
+Prints ONE JSON line (the metric and workload of the 16-head x head_dim 64,
+dstate 256 benchmark), with a roofline object for the dominant kernel and a
+cpu_baseline object for the fp64 oracle timed on this host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SSD scan µs/call + tokens/s (16h×64, dstate 256); % of HBM/MFMA roofline"
+DEFAULT_WORKLOAD = "fixed_4x4096_h16_n256"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16/fp16 MFMA, TFLOP/s
+CHUNK = 256
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum CPU oracle time for the baseline sample")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ HIP events
+
+class Hip:
+    """hipEvent_* through ctypes, so events can be recorded by the library on
+    the very stream its kernels run on."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def elapsed_ms(self, a, b):
+        t = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(t), a, b) == 0
+        return t.value
+
+
+# ------------------------------------------------------- algorithmic figures
+
+def algorithmic(prob):
+    """Compulsory bytes and chunked-method MFMA flops of the whole call and of
+    each kernel (units and formulas as stated in the design doc)."""
+    T, H, P, G, N = prob["total_len"], prob["nheads"], prob["head_dim"], prob["ngroups"], prob["dstate"]
+    lens = prob["seqlens"]
+    hi = prob.get("has_initial_state")
+    n_init = int(sum(hi)) if hi is not None else 0
+    slot = H * P * N * 4
+    bytes_x = T * H * P * 2
+    bytes_bc = T * G * N * 2
+    bytes_dt = T * H * 4
+    pool_rw = n_init * slot + len(lens) * slot
+    whole_bytes = 2 * bytes_x + 2 * bytes_bc + bytes_dt + pool_rw
+    # flops per chunk of length l and head: state 2lNP, off-diagonal 2lNP,
+    # causal diagonal l(l+1)P, causal C.B^T shared by the H/G heads of a group
+    f_state = f_off = f_diag = f_cb = 0
+    for L in lens:
+        full, rem = divmod(L, CHUNK)
+        for l in [CHUNK] * full + ([rem] if rem else []):
+            f_state += 2 * l * N * P * H
+            f_off += 2 * l * N * P * H
+            f_diag += l * (l + 1) * P * H
+            f_cb += l * (l + 1) * N * G
+    return dict(
+        whole=dict(bytes=whole_bytes, flops=f_state + f_off + f_diag + f_cb),
+        ssd_chunk_scan=dict(bytes=2 * bytes_x + 2 * bytes_bc + bytes_dt, flops=f_off + f_diag + f_cb),
+        ssd_chunk_state=dict(bytes=bytes_x + bytes_bc + bytes_dt, flops=f_state),
+        ssd_state_passing=dict(bytes=pool_rw, flops=0),
+        ssd_prep=dict(bytes=bytes_dt + bytes_bc, flops=0),
+    )
+
+
+def roofline_entry(name, alg, t_us, traffic=None):
+    a = alg[name]
+    t_hbm = a["bytes"] / (HBM_PEAK_GBS * 1e9) * 1e6
+    t_mfma = a["flops"] / (MFMA_BF16_PEAK_TFS * 1e12) * 1e6
+    if t_mfma > t_hbm:
+        achieved = a["flops"] / (t_us * 1e-6) / 1e12
+        return dict(bound="mfma", achieved=round(achieved, 2), peak=MFMA_BF16_PEAK_TFS, unit="TFLOP/s",
+                    frac=round(achieved / MFMA_BF16_PEAK_TFS, 4), traffic=traffic, kernel=name)
+    achieved = a["bytes"] / (t_us * 1e-6) / 1e9
+    return dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic, kernel=name)
+
+
+def kernel_sources_hash():
+    csrc = os.path.join(ROOT, "mamba_ssd_chunked_chunk_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except ValueError:
+        return None
+    if d.get("sources_sha256_16") != kernel_sources_hash():
+        return None
+    return d.get(workload, {}).get(kernel)
+
+
+# ------------------------------------------------------------------ CPU leg
+
+def cpu_baseline(prob, min_seconds):
+    import oracle
+    T = prob["total_len"]
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        oracle.recurrence(prob, want_pool=False, want_final=False)
+        reps += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    el = time.perf_counter() - t0
+    return dict(value=round(reps * T / el, 1), unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"whole workload ({T} tokens, all heads), fp64 per-token recurrence, "
+                       f"{reps} run(s) in {el:.1f} s")
+
+
+# -------------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "libssd is a single-GPU library; this benchmark runs on exactly one "
+                                   "GPU (--gpus 1). Multi-GPU sharding is described in DESIGN.md, not run."}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from mamba_ssd_chunked_chunk_amd import binding, torch_io
+    from mamba_ssd_chunked_chunk_amd.workloads import make_workload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    prob = make_workload(args.workload)
+    T = prob["total_len"]
+    d = torch_io.upload(prob, dev)
+    ps = torch_io.problem_struct(d)
+    ws = torch.empty(binding.ssd_workspace_size(ps), dtype=torch.uint8, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    lib = binding.load_library()
+    hip = Hip()
+    nk = lib.ssd_kernel_count()
+    knames = [lib.ssd_kernel_name(i).decode() for i in range(nk)]
+    stream = torch.cuda.current_stream(dev)
+
+    def P(t):
+        return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+    args_ptrs = [P(d["y"]), P(d["x"]), P(d["dt"]), P(d["A"]), P(d["B"]), P(d["C"]), P(d["D"]),
+                 P(d["dt_bias"]), P(d["pool"]), P(d["query_start_loc"]), P(d["has_initial_state"]),
+                 P(d["cache_indices"]), P(ws), ctypes.c_size_t(ws.numel()), ctypes.c_void_p(stream.cuda_stream)]
+
+    ev_sets = [[hip.event() for _ in range(nk + 1)] for _ in range(args.steps)]
+
+    def call(events=None):
+        if events is None:
+            st = lib.ssd_chunk_scan_varlen_fwd_inplace(ctypes.byref(ps), *args_ptrs)
+        else:
+            arr = (ctypes.c_void_p * (nk + 1))(*[e.value for e in events])
+            st = lib.ssd_chunk_scan_varlen_fwd_inplace_profiled(ctypes.byref(ps), *args_ptrs, arr, nk + 1)
+        if st != 0:
+            raise RuntimeError(lib.ssd_status_string(st).decode())
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, each = cache eviction (untimed) + one call (events)
+    wall0 = time.perf_counter()
+    for k in range(args.steps):
+        flush.fill_(k & 0xFF)
+        call(ev_sets[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    per_call = []
+    per_kernel = {n: [] for n in knames}
+    for evs in ev_sets:
+        per_call.append(hip.elapsed_ms(evs[0], evs[nk]))
+        for i, n in enumerate(knames):
+            per_kernel[n].append(hip.elapsed_ms(evs[i], evs[i + 1]))
+    ms = statistics.fmean(per_call)
+
+    # warm (back-to-back, caches not evicted) for reference
+    w0, w1 = hip.event(), hip.event()
+    hip.lib.hipEventRecord(w0, ctypes.c_void_p(stream.cuda_stream))
+    for _ in range(args.steps):
+        call()
+    hip.lib.hipEventRecord(w1, ctypes.c_void_p(stream.cuda_stream))
+    hip.lib.hipEventSynchronize(w1)
+    warm_ms = hip.elapsed_ms(w0, w1) / args.steps
+
+    alg = algorithmic(prob)
+    kern_us = {n: statistics.fmean(v) * 1e3 for n, v in per_kernel.items()}
+    dom = max(kern_us, key=kern_us.get)
+    roof = roofline_entry(dom, alg, kern_us[dom], traffic_for(dom, args.workload))
+    whole = roofline_entry("whole", alg, ms * 1e3)
+    per_kernel_roof = {n: roofline_entry(n, alg, kern_us[n]) for n in knames if alg[n]["bytes"] or alg[n]["flops"]}
+
+    out = {
+        "metric": METRIC,
+        "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": prob["batch"], "seq_len": prob["seqlens"][0]
+                   if len(set(prob["seqlens"])) == 1 else None, "tokens": T, "nheads": prob["nheads"],
+                   "head_dim": prob["head_dim"], "ngroups": prob["ngroups"], "dstate": prob["dstate"],
+                   "chunk_size": CHUNK, "parallelism": "single-gpu"},
+        "us_per_call": {"mean": round(ms * 1e3, 2), "median": round(statistics.median(per_call) * 1e3, 2),
+                        "p10": round(float(np.percentile(per_call, 10)) * 1e3, 2),
+                        "p90": round(float(np.percentile(per_call, 90)) * 1e3, 2),
+                        "warm_back_to_back": round(warm_ms * 1e3, 2)},
+        "kernels_us": {n: round(v, 2) for n, v in kern_us.items()},
+        "roofline": roof,
+        "roofline_whole_call": whole,
+        "roofline_per_kernel": per_kernel_roof,
+        "wall_s_timed_region": round(wall, 3),
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(prob, args.cpu_seconds)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,178 @@
+/*
+ * libssd -- Mamba-2 SSD (state-space duality) varlen forward prefill scan
+ * for AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * The operation (what every entry point below computes) is defined by the
+ * per-token recurrence in "mamba2_ssd_scan" (Modular MAX kernels docs),
+ * section "Per-token recurrence": for each head h, head_dim channel p and
+ * group g = h / (nheads / ngroups),
+ *     dts   = softplus(dt[t,h] + dt_bias[h])       (or dt + dt_bias when
+ *                                                  dt_softplus is 0)
+ *     state = state * exp(A[h] * dts) + dts * B[t,g,:] * x[t,h,p]
+ *     y[t,h,p] = C[t,g,:] . state + D[h] * x[t,h,p]
+ * with the state reset at every query_start_loc boundary.  The in-place pool
+ * semantics (initial state read from ssm_pool[cache_indices[b]] when
+ * has_initial_state[b] is set; final state written to the same slot) and the
+ * tensor shapes follow "Mamba2SSDChunkScanVarlenFwdInplace" (Modular Mojo
+ * struct docs), struct description, "Tensor shapes" and "Parameters".  The
+ * GPU path evaluates it with the chunked segment-sum reformulation described
+ * on "Mamba chunk scan with segsum" (kernelindex.com, operation 043).
+ *
+ * Conventions shared by all entry points:
+ *   - All tensor pointers are DEVICE pointers to dense, row-major
+ *     (C-contiguous) buffers owned by the caller.  The library allocates no
+ *     device memory and keeps no pointer after a call returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Compute entry points are asynchronous and stream-ordered: they enqueue
+ *     kernels and return without synchronising the host.
+ *   - Host-side argument checks run before anything is enqueued; on any
+ *     error status nothing is launched and no buffer is modified.
+ *   - Device-side preconditions (query_start_loc[0] == 0, non-decreasing,
+ *     query_start_loc[batch] == total_len; cache_indices[b] < max_slots and
+ *     pairwise distinct) are NOT checked on the hot path (that would need a
+ *     host synchronisation); ssd_validate_inputs checks them on demand.
+ *     Violating them is undefined behaviour.
+ *   - y must not alias any input; ssm_pool is the only read-write buffer.
+ *   - A call that fails while kernels run (SSD_ERR_HIP from a later status
+ *     query) may leave the pool partially written.
+ */
+#ifndef LIBSSD_SSD_H
+#define LIBSSD_SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSD_ABI_VERSION 1
+#define SSD_MAX_DSTATE 256  /* largest dstate, as in "mamba2_ssd_scan", comptime MAX_DSTATE */
+
+typedef enum ssd_status {
+    SSD_OK = 0,
+    SSD_ERR_NULL_ARG = 1,     /* a required pointer is NULL                     */
+    SSD_ERR_BAD_SHAPE = 2,    /* negative/zero sizes, nheads % ngroups != 0 ...  */
+    SSD_ERR_UNSUPPORTED = 3,  /* a size this build has no kernel for            */
+    SSD_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than required         */
+    SSD_ERR_BAD_INPUT = 5,    /* ssd_validate_inputs found a violated precondition */
+    SSD_ERR_HIP = 6           /* a HIP runtime call or kernel launch failed       */
+} ssd_status;
+
+/* Problem sizes.  Dense row-major tensors:
+ *   y, x           [total_len, nheads, head_dim]   bf16
+ *   dt             [total_len, nheads]             fp32
+ *   A, D, dt_bias  [nheads]                        fp32 (D, dt_bias optional)
+ *   B, C           [total_len, ngroups, dstate]    bf16
+ *   ssm_pool       [max_slots, nheads, head_dim, dstate]  fp32
+ *   query_start_loc [batch + 1] int32, has_initial_state [batch] uint8
+ *   (optional), cache_indices [batch] uint32                                */
+typedef struct ssd_problem {
+    int64_t total_len;   /* T == query_start_loc[batch]; >= 0                */
+    int32_t batch;       /* number of sequences; >= 1                         */
+    int32_t nheads;      /* H; multiple of ngroups                            */
+    int32_t head_dim;    /* P; this build supports 64                         */
+    int32_t ngroups;     /* G                                                 */
+    int32_t dstate;      /* N; this build supports 64, 128, 256               */
+    int32_t max_slots;   /* leading dimension of ssm_pool; >= 1               */
+    int32_t chunk_size;  /* 0 selects 256; this build supports 256 only       */
+    int32_t dt_softplus; /* nonzero: dts = softplus(dt + dt_bias); zero: dt + dt_bias */
+} ssd_problem;
+
+/* Offsets (bytes from the workspace base) and sizes of the intermediates the
+ * compute entry point leaves in the workspace, so tests can compare each
+ * step with the oracle.  nchunks_max = floor(total_len / 256) + batch bounds
+ * the number of chunks; chunk c of the call occupies row c of each table.
+ *   meta      int32[4]                    {nchunks, 0, 0, 0}
+ *   chunk_off int32[batch + 1]            first chunk of each sequence
+ *   desc      int32[nchunks_max][4]       {sequence, first token, length, 0}
+ *   dts       fp32[nchunks_max][H][256]   dts per token, 0 past the chunk end
+ *   cs2       fp32[nchunks_max][H][256]   log2(e) * inclusive sum of A*dts
+ *   bexp      int32[nchunks_max][G]       power-of-two exponent applied to B
+ *   cexp      int32[nchunks_max][G]       power-of-two exponent applied to C
+ *   states    fp32[nchunks_max][H][P][N]  chunk's own state contribution
+ *   hin       fp16[nchunks_max][H][P][N]  state entering the chunk, row p
+ *                                         scaled by 2^hexp[c][h][p]
+ *   hexp      int32[nchunks_max][H][P]    exponent of each hin row           */
+typedef struct ssd_workspace_layout {
+    size_t total_bytes;
+    int64_t nchunks_max;
+    size_t meta, chunk_off, desc, dts, cs2, bexp, cexp, states, hin, hexp;
+} ssd_workspace_layout;
+
+/* ABI version of the loaded library (SSD_ABI_VERSION it was built with). */
+int ssd_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char *ssd_status_string(int status);
+
+/* Workspace size for a problem.  Returns SSD_OK and sets *bytes, or an error
+ * status when the problem is malformed or unsupported.  Host only.        */
+ssd_status ssd_workspace_size(const ssd_problem *prob, size_t *bytes);
+
+/* Full workspace layout (see ssd_workspace_layout).  Host only.           */
+ssd_status ssd_workspace_get_layout(const ssd_problem *prob, ssd_workspace_layout *layout);
+
+/* Varlen SSD forward prefill with in-place pool write-back
+ * ("Mamba2SSDChunkScanVarlenFwdInplace", execute; argument order as there).
+ *   y                 OUT  bf16 [T,H,P]
+ *   x                 IN   bf16 [T,H,P]
+ *   dt                IN   fp32 [T,H]   raw dt (before bias and softplus)
+ *   A                 IN   fp32 [H]     per-head scalar, normally negative
+ *   B, C              IN   bf16 [T,G,N]
+ *   D                 IN   fp32 [H] or NULL (treated as 0)
+ *   dt_bias           IN   fp32 [H] or NULL (treated as 0)
+ *   ssm_pool          IN/OUT fp32 [max_slots,H,P,N]: slot cache_indices[b] is
+ *                     read as sequence b's initial state when
+ *                     has_initial_state[b] != 0 (otherwise not read at all) and
+ *                     overwritten with its final state (also for zero-length
+ *                     sequences).  Every other slot is left bit-identical.
+ *   query_start_loc   IN   int32 [batch+1]
+ *   has_initial_state IN   uint8 [batch] or NULL (all false)
+ *   cache_indices     IN   uint32 [batch]
+ *   workspace         scratch of at least ssd_workspace_size() bytes, 256-byte
+ *                     aligned; its contents on return are the intermediates
+ *                     described by ssd_workspace_layout.
+ * Precision: y is rounded to bf16 (nearest even); the inter-chunk state chain
+ * and the pool are fp32.  Results are deterministic (bitwise run to run).  */
+ssd_status ssd_chunk_scan_varlen_fwd_inplace(
+    const ssd_problem *prob,
+    void *y, const void *x, const float *dt, const float *A,
+    const void *B, const void *C, const float *D, const float *dt_bias,
+    float *ssm_pool, const int32_t *query_start_loc,
+    const uint8_t *has_initial_state, const uint32_t *cache_indices,
+    void *workspace, size_t workspace_bytes, void *stream);
+
+/* Number of kernels one compute call enqueues, and the name of kernel i
+ * (0 <= i < ssd_kernel_count(), launch order; NULL otherwise).            */
+int ssd_kernel_count(void);
+const char *ssd_kernel_name(int i);
+
+/* Same computation as ssd_chunk_scan_varlen_fwd_inplace; additionally
+ * records events[i] (each a hipEvent_t created by the caller, passed as
+ * void*) on `stream` just before kernel i is enqueued and
+ * events[ssd_kernel_count()] after the last one, so a caller can time each
+ * step with hipEventElapsedTime.  n_events must equal ssd_kernel_count()+1
+ * (SSD_ERR_NULL_ARG / SSD_ERR_BAD_SHAPE otherwise, before any launch).     */
+ssd_status ssd_chunk_scan_varlen_fwd_inplace_profiled(
+    const ssd_problem *prob,
+    void *y, const void *x, const float *dt, const float *A,
+    const void *B, const void *C, const float *D, const float *dt_bias,
+    float *ssm_pool, const int32_t *query_start_loc,
+    const uint8_t *has_initial_state, const uint32_t *cache_indices,
+    void *workspace, size_t workspace_bytes, void *stream,
+    void *const *events, int n_events);
+
+/* Synchronous debug check of the device-side preconditions: copies
+ * query_start_loc and cache_indices to the host (after synchronising
+ * `stream`) and returns SSD_ERR_BAD_INPUT if query_start_loc does not run
+ * non-decreasing from 0 to total_len or a cache index is out of range or
+ * repeated; SSD_OK otherwise.                                              */
+ssd_status ssd_validate_inputs(const ssd_problem *prob, const int32_t *query_start_loc,
+                               const uint32_t *cache_indices, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBSSD_SSD_H */

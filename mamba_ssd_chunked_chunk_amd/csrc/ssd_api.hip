@@ -1,0 +1,219 @@
+// C ABI of libssd: argument checks, workspace carve and launch order.
+// The entry points and their conventions are declared in include/ssd.h.
+// The argument order of the compute entry point follows the execute method
+// of "Mamba2SSDChunkScanVarlenFwdInplace" (Modular Mojo struct docs); the
+// device context becomes a HIP stream.
+#include <string.h>
+
+#include <vector>
+
+#include "ssd.h"
+#include "ssd_common.hpp"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void *ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+ssd_status check_problem(const ssd_problem *p) {
+    if (p == nullptr) return SSD_ERR_NULL_ARG;
+    if (p->total_len < 0 || p->batch < 1 || p->nheads < 1 || p->head_dim < 1 ||
+        p->ngroups < 1 || p->dstate < 1 || p->max_slots < 1 || p->chunk_size < 0)
+        return SSD_ERR_BAD_SHAPE;
+    if (p->nheads % p->ngroups != 0) return SSD_ERR_BAD_SHAPE;
+    if (p->total_len > INT32_MAX) return SSD_ERR_BAD_SHAPE;  // query_start_loc is int32
+    if (p->dstate > SSD_MAX_DSTATE) return SSD_ERR_UNSUPPORTED;
+    if (p->dstate != 64 && p->dstate != 128 && p->dstate != 256) return SSD_ERR_UNSUPPORTED;
+    if (p->head_dim != ssd::kHeadDim) return SSD_ERR_UNSUPPORTED;
+    if (p->chunk_size != 0 && p->chunk_size != ssd::kChunk) return SSD_ERR_UNSUPPORTED;
+    if (p->nheads > 65535) return SSD_ERR_UNSUPPORTED;  // grid y limit
+    const int64_t ncm = p->total_len / ssd::kChunk + p->batch;
+    if (ncm > INT32_MAX) return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
+void layout_of(const ssd_problem *p, ssd_workspace_layout *L) {
+    const int64_t ncm = p->total_len / ssd::kChunk + p->batch;
+    const size_t H = (size_t)p->nheads, G = (size_t)p->ngroups;
+    const size_t PN = (size_t)p->head_dim * (size_t)p->dstate;
+    size_t off = 0;
+    memset(L, 0, sizeof *L);
+    L->nchunks_max = ncm;
+    L->meta = off;      off = align_up(off + 4 * sizeof(int32_t));
+    L->chunk_off = off; off = align_up(off + ((size_t)p->batch + 1) * sizeof(int32_t));
+    L->desc = off;      off = align_up(off + (size_t)ncm * 4 * sizeof(int32_t));
+    L->dts = off;       off = align_up(off + (size_t)ncm * H * ssd::kChunk * sizeof(float));
+    L->cs2 = off;       off = align_up(off + (size_t)ncm * H * ssd::kChunk * sizeof(float));
+    L->bexp = off;      off = align_up(off + (size_t)ncm * G * sizeof(int32_t));
+    L->cexp = off;      off = align_up(off + (size_t)ncm * G * sizeof(int32_t));
+    L->states = off;    off = align_up(off + (size_t)ncm * H * PN * sizeof(float));
+    L->hin = off;       off = align_up(off + (size_t)ncm * H * PN * sizeof(uint16_t));
+    L->hexp = off;      off = align_up(off + (size_t)ncm * H * (size_t)p->head_dim * sizeof(int32_t));
+    L->total_bytes = off;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssd_abi_version(void) { return SSD_ABI_VERSION; }
+
+const char *ssd_status_string(int s) {
+    switch (s) {
+    case SSD_OK: return "SSD_OK";
+    case SSD_ERR_NULL_ARG: return "SSD_ERR_NULL_ARG: a required pointer is NULL";
+    case SSD_ERR_BAD_SHAPE: return "SSD_ERR_BAD_SHAPE: malformed problem sizes";
+    case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED: sizes not supported by this build";
+    case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case SSD_ERR_BAD_INPUT: return "SSD_ERR_BAD_INPUT: query_start_loc or cache_indices violate a precondition";
+    case SSD_ERR_HIP: return "SSD_ERR_HIP: a HIP runtime call failed";
+    default: return "unknown ssd_status";
+    }
+}
+
+ssd_status ssd_workspace_size(const ssd_problem *prob, size_t *bytes) {
+    if (bytes == nullptr) return SSD_ERR_NULL_ARG;
+    const ssd_status st = check_problem(prob);
+    if (st != SSD_OK) return st;
+    ssd_workspace_layout L;
+    layout_of(prob, &L);
+    *bytes = L.total_bytes;
+    return SSD_OK;
+}
+
+ssd_status ssd_workspace_get_layout(const ssd_problem *prob, ssd_workspace_layout *layout) {
+    if (layout == nullptr) return SSD_ERR_NULL_ARG;
+    const ssd_status st = check_problem(prob);
+    if (st != SSD_OK) return st;
+    layout_of(prob, layout);
+    return SSD_OK;
+}
+
+static const char *const kKernelNames[] = {"ssd_prep", "ssd_chunk_state", "ssd_state_passing",
+                                           "ssd_chunk_scan"};
+static constexpr int kNumKernels = 4;
+
+int ssd_kernel_count(void) { return kNumKernels; }
+
+const char *ssd_kernel_name(int i) { return (i >= 0 && i < kNumKernels) ? kKernelNames[i] : nullptr; }
+
+static ssd_status run_scan(
+    const ssd_problem *prob, void *y, const void *x, const float *dt, const float *A,
+    const void *B, const void *C, const float *D, const float *dt_bias, float *ssm_pool,
+    const int32_t *query_start_loc, const uint8_t *has_initial_state,
+    const uint32_t *cache_indices, void *workspace, size_t workspace_bytes, void *stream,
+    void *const *events) {
+    ssd_status st = check_problem(prob);
+    if (st != SSD_OK) return st;
+    const bool has_tokens = prob->total_len > 0;
+    if (A == nullptr || ssm_pool == nullptr || query_start_loc == nullptr || cache_indices == nullptr)
+        return SSD_ERR_NULL_ARG;
+    if (has_tokens && (y == nullptr || x == nullptr || dt == nullptr || B == nullptr || C == nullptr))
+        return SSD_ERR_NULL_ARG;
+    if (!aligned(y, 16) || !aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) ||
+        !aligned(ssm_pool, 16) || !aligned(dt, 4) || !aligned(A, 4) || !aligned(D, 4) ||
+        !aligned(dt_bias, 4) || !aligned(query_start_loc, 4) || !aligned(cache_indices, 4))
+        return SSD_ERR_BAD_SHAPE;
+    ssd_workspace_layout L;
+    layout_of(prob, &L);
+    if (workspace == nullptr || workspace_bytes < L.total_bytes || !aligned(workspace, kAlign))
+        return SSD_ERR_WORKSPACE;
+
+    char *ws = static_cast<char *>(workspace);
+    ssd::Params p;
+    p.T = prob->total_len;
+    p.batch = prob->batch;
+    p.H = prob->nheads;
+    p.P = prob->head_dim;
+    p.G = prob->ngroups;
+    p.N = prob->dstate;
+    p.max_slots = prob->max_slots;
+    p.dt_softplus = prob->dt_softplus != 0;
+    p.nchunks_max = L.nchunks_max;
+    p.y = static_cast<uint16_t *>(y);
+    p.x = static_cast<const uint16_t *>(x);
+    p.dt = dt;
+    p.A = A;
+    p.B = static_cast<const uint16_t *>(B);
+    p.C = static_cast<const uint16_t *>(C);
+    p.D = D;
+    p.dt_bias = dt_bias;
+    p.pool = ssm_pool;
+    p.qsl = query_start_loc;
+    p.has_init = has_initial_state;
+    p.cache_idx = cache_indices;
+    p.meta = reinterpret_cast<int32_t *>(ws + L.meta);
+    p.chunk_off = reinterpret_cast<int32_t *>(ws + L.chunk_off);
+    p.desc = reinterpret_cast<int4 *>(ws + L.desc);
+    p.dts = reinterpret_cast<float *>(ws + L.dts);
+    p.cs2 = reinterpret_cast<float *>(ws + L.cs2);
+    p.bexp = reinterpret_cast<int32_t *>(ws + L.bexp);
+    p.cexp = reinterpret_cast<int32_t *>(ws + L.cexp);
+    p.hexp = reinterpret_cast<int32_t *>(ws + L.hexp);
+    p.states = reinterpret_cast<float *>(ws + L.states);
+    p.hin = reinterpret_cast<uint16_t *>(ws + L.hin);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t (*const launchers[kNumKernels])(const ssd::Params &, hipStream_t) = {
+        ssd::launch_prep, ssd::launch_chunk_state, ssd::launch_state_passing, ssd::launch_chunk_scan};
+    for (int k = 0; k < kNumKernels; ++k) {
+        if (events && hipEventRecord(static_cast<hipEvent_t>(events[k]), s) != hipSuccess)
+            return SSD_ERR_HIP;
+        if (launchers[k](p, s) != hipSuccess) return SSD_ERR_HIP;
+    }
+    if (events && hipEventRecord(static_cast<hipEvent_t>(events[kNumKernels]), s) != hipSuccess)
+        return SSD_ERR_HIP;
+    return SSD_OK;
+}
+
+ssd_status ssd_chunk_scan_varlen_fwd_inplace(
+    const ssd_problem *prob, void *y, const void *x, const float *dt, const float *A,
+    const void *B, const void *C, const float *D, const float *dt_bias, float *ssm_pool,
+    const int32_t *query_start_loc, const uint8_t *has_initial_state,
+    const uint32_t *cache_indices, void *workspace, size_t workspace_bytes, void *stream) {
+    return run_scan(prob, y, x, dt, A, B, C, D, dt_bias, ssm_pool, query_start_loc,
+                    has_initial_state, cache_indices, workspace, workspace_bytes, stream, nullptr);
+}
+
+ssd_status ssd_chunk_scan_varlen_fwd_inplace_profiled(
+    const ssd_problem *prob, void *y, const void *x, const float *dt, const float *A,
+    const void *B, const void *C, const float *D, const float *dt_bias, float *ssm_pool,
+    const int32_t *query_start_loc, const uint8_t *has_initial_state,
+    const uint32_t *cache_indices, void *workspace, size_t workspace_bytes, void *stream,
+    void *const *events, int n_events) {
+    if (events == nullptr) return SSD_ERR_NULL_ARG;
+    if (n_events != kNumKernels + 1) return SSD_ERR_BAD_SHAPE;
+    for (int k = 0; k <= kNumKernels; ++k)
+        if (events[k] == nullptr) return SSD_ERR_NULL_ARG;
+    return run_scan(prob, y, x, dt, A, B, C, D, dt_bias, ssm_pool, query_start_loc,
+                    has_initial_state, cache_indices, workspace, workspace_bytes, stream, events);
+}
+
+ssd_status ssd_validate_inputs(const ssd_problem *prob, const int32_t *query_start_loc,
+                               const uint32_t *cache_indices, void *stream) {
+    ssd_status st = check_problem(prob);
+    if (st != SSD_OK) return st;
+    if (query_start_loc == nullptr || cache_indices == nullptr) return SSD_ERR_NULL_ARG;
+    std::vector<int32_t> q((size_t)prob->batch + 1);
+    std::vector<uint32_t> ci((size_t)prob->batch);
+    if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return SSD_ERR_HIP;
+    if (hipMemcpy(q.data(), query_start_loc, q.size() * sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess)
+        return SSD_ERR_HIP;
+    if (hipMemcpy(ci.data(), cache_indices, ci.size() * sizeof(uint32_t), hipMemcpyDeviceToHost) != hipSuccess)
+        return SSD_ERR_HIP;
+    if (q[0] != 0 || (int64_t)q[(size_t)prob->batch] != prob->total_len) return SSD_ERR_BAD_INPUT;
+    for (int b = 0; b < prob->batch; ++b)
+        if (q[(size_t)b + 1] < q[(size_t)b]) return SSD_ERR_BAD_INPUT;
+    std::vector<uint8_t> seen((size_t)prob->max_slots, 0);
+    for (int b = 0; b < prob->batch; ++b) {
+        if (ci[(size_t)b] >= (uint32_t)prob->max_slots) return SSD_ERR_BAD_INPUT;
+        if (seen[ci[(size_t)b]]) return SSD_ERR_BAD_INPUT;
+        seen[ci[(size_t)b]] = 1;
+    }
+    return SSD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,152 @@
+// Shared definitions of the libssd HIP kernels (gfx950 / CDNA4).
+//
+// The operation is the Mamba-2 SSD varlen prefill scan ("mamba2_ssd_scan",
+// section "Per-token recurrence"), evaluated with the chunked segment-sum
+// reformulation of "Mamba chunk scan with segsum" (description): chunks of 256
+// tokens, an in-chunk causal block, an inter-chunk state recurrence with
+// exponential decay, and their sum.
+//
+// Base-2 exponentials: every decay exp(z) is computed as exp2(z * log2 e), the
+// constant being LOG2E of "mamba2_ssd_scan" (comptime values), so the kernels
+// keep the prefix sums in log2 units ("cs2") and call the hardware exp2.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+constexpr int kChunk = 256;      // chunk length (tokens)
+constexpr int kHeadDim = 64;     // P supported by this build
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Everything a launch needs, passed by value as the kernel argument.
+struct Params {
+    // sizes
+    int64_t T;
+    int batch, H, P, G, N, max_slots;
+    int dt_softplus;
+    int64_t nchunks_max;
+    // caller tensors (device)
+    uint16_t *y;
+    const uint16_t *x;
+    const float *dt, *A;
+    const uint16_t *B, *C;
+    const float *D, *dt_bias;
+    float *pool;
+    const int32_t *qsl;
+    const uint8_t *has_init;
+    const uint32_t *cache_idx;
+    // workspace carve (device)
+    int32_t *meta;       // [4]: nchunks
+    int32_t *chunk_off;  // [batch+1]
+    int4 *desc;          // [nchunks_max]: {seq, t0, len, 0}
+    float *dts;          // [nchunks_max][H][256]
+    float *cs2;          // [nchunks_max][H][256]
+    int32_t *bexp;       // [nchunks_max][G]   exponent applied to B before fp16
+    int32_t *cexp;       // [nchunks_max][G]   exponent applied to C before fp16
+    float *states;       // [nchunks_max][H][P][N]
+    uint16_t *hin;       // [nchunks_max][H][P][N] fp16, row p scaled by 2^hexp
+    int32_t *hexp;       // [nchunks_max][H][P]
+};
+
+// ---------------------------------------------------------------- helpers
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// float -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
+    __bf16 b = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)float_to_bf16_bits(lo) | ((uint32_t)float_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    _Float16 a = (_Float16)lo, b = (_Float16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ float f16_bits_to_float(uint32_t bits16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+// Exponent s that puts a positive maximum m in [2^14, 2^15) after scaling by
+// 2^s (0 when m is 0), so scaled values stay well inside fp16's range.
+__device__ __forceinline__ int f16_scale_exponent(float m) {
+    return m > 0.0f ? 14 - ((int)((__float_as_uint(m) >> 23) & 0xFF) - 127) : 0;
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_f16(const f16x8 &a, const f16x8 &b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Inclusive scan of one int over a 64-lane wavefront.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        int o = __shfl_up(v, d, 64);
+        if (lane >= d) v += o;
+    }
+    return v;
+}
+
+__device__ __forceinline__ float wave_incl_scan(float v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        float o = __shfl_up(v, d, 64);
+        if (lane >= d) v += o;
+    }
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+        uint32_t o = (uint32_t)__shfl_xor((int)v, d, 64);
+        v = v > o ? v : o;
+    }
+    return v;
+}
+
+// softplus(v) = log(1 + e^v), without overflow.
+__device__ __forceinline__ float softplus_f(float v) {
+    return fmaxf(v, 0.0f) + log1pf(expf(-fabsf(v)));
+}
+
+// Exponent e with 2^e <= |m| < 2^(e+1) for a finite positive float m.
+__device__ __forceinline__ int float_exponent(float m) {
+    return (int)((__float_as_uint(m) >> 23) & 0xFF) - 127;
+}
+
+}  // namespace ssd
+
+// Host-side launchers (one per kernel file).
+namespace ssd {
+hipError_t launch_prep(const Params &p, hipStream_t s);
+hipError_t launch_chunk_state(const Params &p, hipStream_t s);
+hipError_t launch_state_passing(const Params &p, hipStream_t s);
+hipError_t launch_chunk_scan(const Params &p, hipStream_t s);
+}  // namespace ssd

@@ -1,0 +1,86 @@
+// Steps 3 and 5 of the scan: the inter-chunk state recurrence ("state_passing")
+// and the in-place pool write-back.
+//
+// For sequence b, head h and every state element (p, n), walking the
+// sequence's chunks k in order:
+//   h_in[first]  = has_initial_state[b] ? ssm_pool[cache_indices[b]][h][p][n] : 0
+//   h_in[k + 1]  = exp(cs_last(k)) * h_in[k] + S[k]
+//   final        = exp(cs_last(K-1)) * h_in[K-1] + S[K-1]
+//   ssm_pool[cache_indices[b]][h][p][n] = final
+// This is the "inter-chunk state recurrence with exponential decay" of
+// "Mamba chunk scan with segsum" (description); the reset at each sequence
+// start and the final state at each sequence end come from "mamba2_ssd_scan"
+// ("Per-token recurrence"); reading the initial state from, and writing the
+// final state to, slot cache_indices[b] of the pool is
+// "Mamba2SSDChunkScanVarlenFwdInplace" (struct description).  A sequence with
+// no tokens writes its initial state (or zeros) back.
+//
+// The chain is fp32.  h_in only feeds the outputs y; it is stored as fp16
+// with one power-of-two scale per row p (11 significant bits: bf16's 8 would
+// put the off-diagonal part's rounding error near the tolerance of y).
+// Each thread owns four consecutive (p, n) elements of one (sequence, head),
+// reads its pool element before the sequence's loop and writes it after, so
+// the in-place read-then-write of a slot never races.
+#include "ssd_common.hpp"
+
+namespace ssd {
+
+__global__ __launch_bounds__(256) void ssd_state_passing_kernel(Params p) {
+    const int b = blockIdx.x;
+    const int h = blockIdx.y;
+    const int64_t head_elems = (int64_t)kHeadDim * p.N;
+    const int64_t e0 = ((int64_t)blockIdx.z * 256 + threadIdx.x) * 4;
+    if (e0 >= head_elems) return;
+
+    // clamped to the table so malformed query_start_loc cannot index past it
+    const int k1 = (int)min((int64_t)p.chunk_off[b + 1], p.nchunks_max);
+    const int k0 = min(p.chunk_off[b], k1);
+    const int64_t slot = p.cache_idx[b];
+    const bool init = p.has_init != nullptr && p.has_init[b] != 0;
+    float4 *pool4 = reinterpret_cast<float4 *>(p.pool + (slot * p.H + h) * head_elems + e0);
+
+    float4 st = init ? *pool4 : make_float4(0.f, 0.f, 0.f, 0.f);
+    const int64_t stride = (int64_t)p.H * head_elems;  // one chunk of states
+    const float4 *S4 = reinterpret_cast<const float4 *>(p.states + ((int64_t)k0 * p.H + h) * head_elems + e0);
+    uint16_t *hin = p.hin + ((int64_t)k0 * p.H + h) * head_elems + e0;
+
+    float4 s_next = make_float4(0.f, 0.f, 0.f, 0.f);
+    float d_next = 0.f;
+    if (k0 < k1) {
+        s_next = *S4;
+        d_next = p.cs2[((int64_t)k0 * p.H + h) * kChunk + kChunk - 1];
+    }
+    for (int k = k0; k < k1; ++k) {
+        const float4 s_cur = s_next;
+        const float d_cur = exp2f(d_next);
+        if (k + 1 < k1) {  // prefetch the next chunk's contribution
+            s_next = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(S4) + (int64_t)(k + 1 - k0) * stride);
+            d_next = p.cs2[((int64_t)(k + 1) * p.H + h) * kChunk + kChunk - 1];
+        }
+        // h_in row p as fp16, scaled by the power of two that puts the row's
+        // max |h| in [2^14, 2^15); the N/4 lanes of one row share it
+        float m = fmaxf(fmaxf(fabsf(st.x), fabsf(st.y)), fmaxf(fabsf(st.z), fabsf(st.w)));
+        for (int d = p.N / 8; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
+        const int sh = f16_scale_exponent(m);
+        uint2 hv;
+        hv.x = pack_f16x2(ldexpf(st.x, sh), ldexpf(st.y, sh));
+        hv.y = pack_f16x2(ldexpf(st.z, sh), ldexpf(st.w, sh));
+        *reinterpret_cast<uint2 *>(hin + (int64_t)(k - k0) * stride) = hv;
+        if (e0 % p.N == 0) p.hexp[((int64_t)k * p.H + h) * kHeadDim + e0 / p.N] = sh;
+        st.x = d_cur * st.x + s_cur.x;
+        st.y = d_cur * st.y + s_cur.y;
+        st.z = d_cur * st.z + s_cur.z;
+        st.w = d_cur * st.w + s_cur.w;
+    }
+    *pool4 = st;
+}
+
+hipError_t launch_state_passing(const Params &p, hipStream_t s) {
+    const int64_t head_elems = (int64_t)kHeadDim * p.N;
+    const unsigned zb = (unsigned)((head_elems / 4 + 255) / 256);
+    dim3 grid((unsigned)p.batch, (unsigned)p.H, zb);
+    hipLaunchKernelGGL(ssd_state_passing_kernel, grid, dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace ssd

@@ -1,0 +1,112 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/ssd.h declares, reports its version and status names,
+sizes its workspace, and rejects malformed calls before launching anything
+(only error paths that return before any HIP call are exercised here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from mamba_ssd_chunked_chunk_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return binding.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(binding.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert binding.ssd_abi_version() == 1
+    for code, name in binding.STATUS_NAMES.items():
+        assert lib.ssd_status_string(code).decode().startswith(name)
+    assert b"unknown" in lib.ssd_status_string(99)
+
+
+def _prob(**kw):
+    base = dict(total_len=1024, batch=4, nheads=16, head_dim=64, ngroups=1, dstate=256, max_slots=8)
+    base.update(kw)
+    return binding.make_problem(**base)
+
+
+def test_workspace_layout_arithmetic(lib):
+    p = _prob()
+    L = binding.ssd_workspace_get_layout(p)
+    ncm = 1024 // 256 + 4
+    assert L["nchunks_max"] == ncm
+    assert L["total_bytes"] == binding.ssd_workspace_size(p)
+    offs = [L[k] for k in ("meta", "chunk_off", "desc", "dts", "cs2", "bexp", "cexp", "states", "hin", "hexp")]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert L["hin"] - L["states"] >= ncm * 16 * 64 * 256 * 4
+    assert L["hexp"] - L["hin"] >= ncm * 16 * 64 * 256 * 2
+    assert L["total_bytes"] - L["hexp"] >= ncm * 16 * 64 * 4
+    assert L["cs2"] - L["dts"] >= ncm * 16 * 256 * 4
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), 2), (dict(nheads=6, ngroups=4), 2), (dict(total_len=-1), 2),
+    (dict(max_slots=0), 2), (dict(dstate=512), 3), (dict(dstate=96), 3),
+    (dict(head_dim=128), 3), (dict(chunk_size=128), 3),
+])
+def test_bad_problems_rejected(lib, kw, status):
+    n = ctypes.c_size_t(0)
+    assert lib.ssd_workspace_size(ctypes.byref(_prob(**kw)), ctypes.byref(n)) == status
+
+
+def test_null_and_workspace_errors_before_launch(lib):
+    p = _prob()
+    f = lib.ssd_chunk_scan_varlen_fwd_inplace
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails its host checks
+    args = [fake] * 13
+    need = binding.ssd_workspace_size(p)
+    # NULL problem
+    assert f(None, *args, need, None) == 1
+    # each required pointer NULL in turn (y, x, dt, A, B, C, pool, qsl, cache_indices)
+    for idx in (0, 1, 2, 3, 4, 5, 8, 9, 11):
+        a = list(args)
+        a[idx] = None
+        assert f(ctypes.byref(p), *a, need, None) == 1, idx
+    # workspace: NULL, too small, misaligned
+    a = list(args)
+    a[12] = None
+    assert f(ctypes.byref(p), *a, need, None) == 4
+    assert f(ctypes.byref(p), *args, need - 1, None) == 4
+    a = list(args)
+    a[12] = ctypes.c_void_p((1 << 20) + 16)
+    assert f(ctypes.byref(p), *a, need, None) == 4
+    # misaligned bf16 tensor
+    a = list(args)
+    a[1] = ctypes.c_void_p((1 << 20) + 2)
+    assert f(ctypes.byref(p), *a, need, None) == 2
+    # optional D / dt_bias / has_initial_state may be NULL: the call then only
+    # fails on the (deliberately too small) workspace
+    a = list(args)
+    a[6] = a[7] = a[10] = None
+    assert f(ctypes.byref(p), *a, need - 1, None) == 4
+
+
+def test_validate_inputs_host_errors(lib):
+    assert lib.ssd_validate_inputs(None, None, None, None) == 1
+    p = _prob()
+    assert lib.ssd_validate_inputs(ctypes.byref(p), None, None, None) == 1
+    assert lib.ssd_validate_inputs(ctypes.byref(_prob(batch=0)), None, None, None) == 2

@@ -1,0 +1,264 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bars (elementwise on y, per written slot on the final states):
+  |y_gpu - y_ref| <= 2e-2 * (1 + |y_ref|)          y_ref: fp64 recurrence
+  ||pool_gpu[slot] - final_ref||_F <= 1e-3 * ||final_ref||_F   (exact zeros when 0)
+  every slot outside cache_indices bit-identical to its value before the call.
+Intermediates left in the workspace are compared step by step with the
+chunked oracle (oracle.chunked) on small problems.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.chunked import chunked_scan
+from ssd_testlib import frob_rel, small_problem, sub_batch
+
+torch = pytest.importorskip("torch")
+from mamba_ssd_chunked_chunk_amd import binding, torch_io  # noqa: E402
+from mamba_ssd_chunked_chunk_amd.workloads import make_problem, make_workload  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+Y_RTOL = 2e-2
+FINAL_TOL = 1e-3
+
+
+def gpu_run(prob, **kw):
+    d = torch_io.upload(prob, "cuda")
+    ws = torch_io.run(d, **kw)
+    torch.cuda.synchronize()
+    return d, ws
+
+
+def y_host(d):
+    return d["y"].float().cpu().numpy().astype(np.float64)
+
+
+def assert_y(y_gpu, y_ref, what=""):
+    assert np.all(np.isfinite(y_gpu)), f"{what}: non-finite y"
+    err = np.abs(y_gpu - y_ref)
+    ratio = err / (Y_RTOL * (1.0 + np.abs(y_ref)))
+    worst = float(ratio.max()) if ratio.size else 0.0
+    assert worst <= 1.0, f"{what}: y error {worst:.3f} x the bound at {np.unravel_index(ratio.argmax(), ratio.shape)}"
+    return worst
+
+
+def assert_final(pool_slot, ref, what=""):
+    nref = np.linalg.norm(ref)
+    if nref == 0:
+        assert np.all(pool_slot == 0), f"{what}: expected zeros"
+        return 0.0
+    r = frob_rel(pool_slot, ref)
+    assert r <= FINAL_TOL, f"{what}: final-state rel err {r:.2e}"
+    return r
+
+
+def assert_untouched(pool_after, pool_before, written):
+    for s in range(pool_before.shape[0]):
+        if s not in written:
+            assert np.array_equal(pool_after[s].view(np.uint32), pool_before[s].view(np.uint32)), f"slot {s} modified"
+
+
+def full_check(prob, seqs=None):
+    """Run on GPU, compare with the oracle (optionally only sequences
+    seqs=(lo, hi)), check slot bookkeeping.  Returns (y worst ratio, final worst)."""
+    d = torch_io.upload(prob, "cuda")
+    before = d["pool"].clone()
+    torch_io.run(d)
+    torch.cuda.synchronize()
+    ref = oracle.recurrence(prob, seqs=seqs, want_pool=False)
+    qsl = prob["query_start_loc"]
+    lo, hi = (0, len(qsl) - 1) if seqs is None else seqs
+    s, e = int(qsl[lo]), int(qsl[hi])
+    yg = d["y"][s:e].float().cpu().numpy().astype(np.float64)
+    wy = assert_y(yg, ref["y"][s:e], prob.get("name", ""))
+    ci = prob["cache_indices"]
+    wf = 0.0
+    for b in range(lo, hi):
+        slot = int(ci[b])
+        wf = max(wf, assert_final(d["pool"][slot].cpu().numpy(), ref["final"][b], f"seq {b}"))
+    # slots outside cache_indices: bit-identical (compared on the device)
+    written = torch.zeros(prob["pool"].shape[0], dtype=torch.bool, device="cuda")
+    written[torch.from_numpy(ci.astype(np.int64)).cuda()] = True
+    keep = (~written).nonzero().flatten()
+    assert torch.equal(d["pool"].index_select(0, keep).view(torch.int32),
+                       before.index_select(0, keep).view(torch.int32)), "an untouched slot changed"
+    assert bool(torch.isfinite(d["y"]).all()), "non-finite y"
+    return wy, wf
+
+
+# ------------------------------------------------------------- small cases
+
+SMALL = {
+    "edges_g2_n64": dict(seqlens=[0, 1, 255, 256, 257, 511], H=4, P=64, G=2, N=64, init="bernoulli"),
+    "groups_eq_heads_n128": dict(seqlens=[300, 17, 600], H=4, P=64, G=4, N=128, init="all"),
+    "n256_two_heads": dict(seqlens=[1000, 5], H=2, P=64, G=1, N=256, init="half"),
+    "short_many_n128": dict(seqlens=list(np.random.default_rng(3).integers(1, 97, 48)), H=8, P=64, G=2,
+                            N=128, init="all"),
+    "single_token": dict(seqlens=[1], H=2, P=64, G=1, N=64, init="all"),
+    "all_empty": dict(seqlens=[0, 0, 0], H=2, P=64, G=1, N=64, init=[1, 0, 1]),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_cases(name):
+    spec = dict(SMALL[name])
+    lens = spec.pop("seqlens")
+    prob = small_problem(lens, seed=100 + len(name), **spec)
+    full_check(prob)
+
+
+@pytest.mark.parametrize("opt", ["no_D", "no_dt_bias", "no_has_init", "no_softplus"])
+def test_optional_inputs_and_flag(opt):
+    kw = dict(init="all")
+    if opt == "no_D":
+        kw["with_D"] = False
+    if opt == "no_dt_bias":
+        kw["with_dt_bias"] = False
+    if opt == "no_has_init":
+        kw["with_has_init"] = False
+    if opt == "no_softplus":
+        kw["dt_softplus"] = False
+    prob = small_problem([400, 130], H=4, P=64, G=1, N=128, seed=5, **kw)
+    if opt == "no_softplus":
+        prob["dt"] = (np.abs(prob["dt"]) * np.float32(0.1)).astype(np.float32)
+        prob["dt_bias"] = np.full_like(prob["dt_bias"], 0.01)
+    full_check(prob)
+
+
+def test_tiny_workload_full():
+    full_check(make_workload("tiny_1x512_h4_n64"))
+
+
+# ---------------------------------------------------- per-step intermediates
+
+def test_intermediates_match_chunked_oracle():
+    prob = small_problem([600, 0, 255, 129], H=4, P=64, G=2, N=128, seed=31, init="bernoulli")
+    d, ws = gpu_run(prob)
+    prob_s = binding.make_problem(prob["total_len"], 4, 4, 64, 2, 128, prob["pool"].shape[0])
+    L = binding.ssd_workspace_get_layout(prob_s)
+    w = ws.cpu().numpy()
+    ncm = L["nchunks_max"]
+    H, P, N = 4, 64, 128
+    nch = int(w[L["meta"]:L["meta"] + 4].view(np.int32)[0])
+    assert nch == 3 + 0 + 1 + 1
+    chunk_off = w[L["chunk_off"]:L["chunk_off"] + 5 * 4].view(np.int32)
+    assert list(chunk_off) == [0, 3, 3, 4, 5]
+    desc = w[L["desc"]:L["desc"] + ncm * 16].view(np.int32).reshape(ncm, 4)
+    dts = w[L["dts"]:L["dts"] + ncm * H * 256 * 4].view(np.float32).reshape(ncm, H, 256)
+    cs2 = w[L["cs2"]:L["cs2"] + ncm * H * 256 * 4].view(np.float32).reshape(ncm, H, 256)
+    S = w[L["states"]:L["states"] + ncm * H * P * N * 4].view(np.float32).reshape(ncm, H, P, N)
+    hin16 = w[L["hin"]:L["hin"] + ncm * H * P * N * 2].view(np.float16).reshape(ncm, H, P, N)
+    hexp = w[L["hexp"]:L["hexp"] + ncm * H * P * 4].view(np.int32).reshape(ncm, H, P)
+    hin = hin16.astype(np.float64) * np.exp2(-hexp.astype(np.float64))[..., None]
+    bexp = w[L["bexp"]:L["bexp"] + ncm * 2 * 4].view(np.int32).reshape(ncm, 2)
+    cexp = w[L["cexp"]:L["cexp"] + ncm * 2 * 4].view(np.int32).reshape(ncm, 2)
+    ref = chunked_scan(prob, 256, keep_intermediates=True)["chunks"]
+    qsl = prob["query_start_loc"]
+    for rec in ref:
+        b, h, t0, l = rec["b"], rec["h"], rec["t0"], rec["length"]
+        c = chunk_off[b] + (t0 - qsl[b]) // 256
+        assert tuple(desc[c][:3]) == (b, t0, l)
+        np.testing.assert_allclose(dts[c, h, :l], rec["dts"], rtol=1e-5, atol=1e-7)
+        assert np.all(dts[c, h, l:] == 0)
+        cs2_ref = rec["cs"] * math.log2(math.e)
+        tol = 3e-5 * (abs(cs2_ref[-1]) + 1.0)
+        assert np.max(np.abs(cs2[c, h, :l] - cs2_ref)) <= tol
+        assert frob_rel(S[c, h], rec["S"]) <= 1e-3
+        assert frob_rel(hin[c, h], rec["h_in"]) <= 1e-3
+        # the B / C exponents put the chunk's max magnitude in [2^14, 2^15)
+        T = prob["total_len"]
+        g = h // 2
+        for arr, ex in (("B", bexp), ("C", cexp)):
+            vals = prob[arr].reshape(T, 2, N)[t0:t0 + l, g]
+            mx = np.max((vals.astype(np.uint32) << 16).view(np.float32).__abs__())
+            assert 2.0 ** 14 <= mx * 2.0 ** ex[c, g] < 2.0 ** 15
+
+
+# --------------------------------------------------------------- invariants
+
+def test_concat_equals_separate_bitwise():
+    prob = small_problem([300, 45, 513], H=4, P=64, G=1, N=128, seed=41, init="all")
+    d, _ = gpu_run(prob)
+    yall = d["y"].cpu()
+    qsl = prob["query_start_loc"]
+    for b in range(3):
+        one = sub_batch(prob, [b])
+        d1, _ = gpu_run(one)
+        assert torch.equal(d1["y"].cpu(), yall[qsl[b]:qsl[b + 1]])
+        slot = int(prob["cache_indices"][b])
+        assert torch.equal(d1["pool"][slot].cpu(), d["pool"][slot].cpu())
+
+
+def test_deterministic_bitwise():
+    prob = small_problem([700, 90], H=4, P=64, G=2, N=256, seed=42, init="half")
+    d1, _ = gpu_run(prob)
+    d2, _ = gpu_run(prob)
+    assert torch.equal(d1["y"], d2["y"]) and torch.equal(d1["pool"], d2["pool"])
+
+
+def test_nan_sentinel_slots_not_read():
+    prob = small_problem([200, 0, 333], H=4, P=64, G=1, N=64, max_slots=6, seed=43, init=[0, 0, 1])
+    ci = prob["cache_indices"]
+    prob["pool"][ci[0]] = np.nan
+    prob["pool"][ci[1]] = np.nan
+    wy, wf = full_check(prob)
+    # the zero-length sequence without an initial state writes zeros
+    d, _ = gpu_run(prob)
+    assert torch.all(d["pool"][int(ci[1])] == 0)
+
+
+def test_split_carry_through_pool():
+    prob = small_problem([900], H=2, P=64, G=1, N=128, seed=44, init="all")
+    full = oracle.recurrence(prob, want_pool=False)
+    T, H, P, N = 900, 2, 64, 128
+    k = 333
+
+    def part(lo, hi, pool):
+        p = dict(prob)
+        for key, shape in (("x", (T, H, P)), ("dt", (T, H)), ("B", (T, 1, N)), ("C", (T, 1, N))):
+            p[key] = np.ascontiguousarray(prob[key].reshape(shape)[lo:hi])
+        p["query_start_loc"] = np.array([0, hi - lo], np.int32)
+        p["total_len"] = hi - lo
+        p["pool"] = pool
+        return p
+    d1, _ = gpu_run(part(0, k, prob["pool"]))
+    d2, _ = gpu_run(part(k, T, d1["pool"].cpu().numpy()))
+    y = np.concatenate([y_host(d1), y_host(d2)])
+    assert_y(y, full["y"], "split")
+    slot = int(prob["cache_indices"][0])
+    assert_final(d2["pool"][slot].cpu().numpy(), full["final"][0], "split final")
+
+
+def test_validate_inputs_on_device():
+    prob = small_problem([10, 20], H=2, P=64, G=1, N=64, max_slots=4, seed=45)
+    d = torch_io.upload(prob, "cuda")
+    ps = torch_io.problem_struct(d)
+    assert binding.ssd_validate_inputs(ps, d["query_start_loc"], d["cache_indices"]) == 0
+    bad = d["cache_indices"].clone()
+    bad[1] = bad[0]
+    assert binding.ssd_validate_inputs(ps, d["query_start_loc"], bad) == 5
+    bad[1] = 4
+    assert binding.ssd_validate_inputs(ps, d["query_start_loc"], bad) == 5
+    q = d["query_start_loc"].clone()
+    q[1] = 35  # beyond q[2] = 30: not non-decreasing
+    assert binding.ssd_validate_inputs(ps, q, d["cache_indices"]) == 5
+
+
+# ------------------------------------------------ workloads at full size
+
+@pytest.mark.parametrize("name,seqs", [
+    ("fixed_4x4096_h16_n256", (1, 2)),
+    ("long_8x16384_h16_n256", (2, 4)),
+    ("ragged_32_h128_g8_n128", (0, 6)),
+    ("short_512_h128_g8_n128", (100, 164)),
+])
+def test_workloads_full_size_sampled(name, seqs):
+    prob = make_workload(name)
+    print(f"\n{name}: T={prob['total_len']} batch={prob['batch']} checking sequences {seqs}", flush=True)
+    wy, wf = full_check(prob, seqs=seqs)
+    print(f"{name}: y worst/bound {wy:.3f}  final rel {wf:.2e}", flush=True)
