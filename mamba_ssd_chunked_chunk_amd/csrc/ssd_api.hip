@@ -133,6 +133,13 @@ static ssd_status run_scan(
     p.max_slots = prob->max_slots;
     p.dt_softplus = prob->dt_softplus != 0;
     p.nchunks_max = L.nchunks_max;
+    {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return SSD_ERR_HIP;
+        p.num_cus = cus > 0 ? cus : 256;
+    }
     p.y = static_cast<uint16_t *>(y);
     p.x = static_cast<const uint16_t *>(x);
     p.dt = dt;

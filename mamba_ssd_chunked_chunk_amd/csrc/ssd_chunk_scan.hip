@@ -12,272 +12,367 @@
 // their sum); D*x is the skip term of "mamba2_ssd_scan" ("Per-token
 // recurrence").  y is rounded to bf16.
 //
-// Precision: all three products run on v_mfma_f32_16x16x32_f16 (fp32
-// accumulate).  B, C and x are bf16 inputs and convert to fp16 exactly after
-// a power-of-two scaling (per chunk and group for B and C, per chunk and head
-// for x) that keeps them inside fp16's range; G is then exact up to fp32
-// summation.  M and h_in are rounded to fp16 (11-bit significand) with their
-// own power-of-two scales (per 16-row block of M, per row p of h_in).  With
-// bf16 (8 bits) for M or h_in the rounding error, which scales with the
-// typical size of y rather than with each y, would approach the tolerance on
-// y wherever y is near zero.
+// Work split.  G depends only on (chunk, group), so one workgroup takes a
+// chunk and HW heads of one group.  A single pass over n (32 at a time, the
+// next slice prefetched into registers) forms G and, with the same C
+// fragments, the off-diagonal products C * h_in^T of all HW heads.  A second
+// phase then runs the diagonal block of each head from G kept in registers.
+// Eight wavefronts, one 32-row block each; the two wavefronts that share a
+// SIMD own row blocks k and 7-k, so each SIMD multiplies 9 of the 36
+// lower-triangular 32x32 tiles.  Workgroups are numbered so that all head groups of a chunk land on
+// one XCD (dispatch is round-robin over the 8 XCDs) and share B and C in its
+// L2.
 //
-// Workgroup = one (chunk, head), 8 wavefronts.  Wavefront w owns the 16-row
-// blocks w and 15-w, which balances the causal triangle (17 of the 136
-// lower-triangular 16x16 tiles each).
-//   * G is formed transposed (rows j, columns i) over n, so the accumulator
-//     layout of a G tile (4 consecutive j per lane at one i) is directly the
-//     A-operand layout of M for the next product, with the 32 j of a K-step
-//     ordered {4q..4q+3, 16+4q..16+4q+3}; x is read from LDS in that order.
-//   * The C fragment of a K-step serves both G^T (as B operand) and the
-//     off-diagonal product (as A operand).
-// B, C and h_in are staged 32 n at a time; x is staged once, transposed to
-// [p][token].
+// MFMA layout (v_mfma_f32_32x32x16_f16).  G is formed transposed (rows j,
+// columns i) over n, so the accumulator layout of a G tile (16 values per
+// lane, all at one i, at j = 8a + 4(l/32) + b) is directly the A-operand
+// layout of M for M*x: the 16 j of the first K-step are {0..3, 8..11} for
+// lanes 0-31 and {4..7, 12..15} for lanes 32-63 (a permutation of 0..15),
+// likewise 16..31 for the second; x is read from LDS in the same order.  The
+// C fragment of a K-step is the B operand of G^T and the A operand of C*h^T.
+//
+// Decay without one exp2 per element.  For a tile strictly below the
+// diagonal block (all j < 32*rb <= i), exp2(cs2_i - cs2_j) =
+// exp2(cs2_i - cs2_r) * exp2(cs2_r - cs2_j) with r = 32*rb; both factors are
+// at most 1 for A <= 0.  The second factor (times dts_j and the x row scale)
+// is tabulated once per head in LDS; only the diagonal blocks use exp2 per
+// element.
+//
+// Precision.  Products run on v_mfma_f32_16x16x32_f16 with fp32 accumulate.
+// B and C convert exactly to fp16 after a power-of-two scaling per (chunk,
+// group); each x row converts exactly after its own power-of-two scaling,
+// compensated inside M.  M and h_in are rounded to fp16 (11-bit significand)
+// under power-of-two scales that keep them far from overflow (one per
+// workgroup and head for M, one per row for h_in); bf16 (8 bits)
+// there would put the rounding error, which scales with the typical size of
+// y rather than with each y, close to the tolerance wherever y is near zero.
 #include "ssd_common.hpp"
 
 namespace ssd {
 
-template <int N>
-__global__ __launch_bounds__(512) void ssd_chunk_scan_kernel(Params p) {
-    constexpr int KS = N / 32;
-    constexpr int XT_STRIDE = 130;  // dwords per x^T row: 128 token pairs + pad (8-byte rows)
-    constexpr int R_STRIDE = 20;    // dwords per staged row of 32 fp16 + pad
+namespace {
+constexpr int kThreads = 512;
+constexpr int XT_STRIDE = 130;  // dwords per x^T row: 128 token pairs + pad (8-byte aligned rows)
+constexpr int R_STRIDE = 20;    // dwords per staged row of 32 fp16 + pad
 
-    const int c = blockIdx.x;
-    const int h = blockIdx.y;
+template <int HW>
+struct ScanSmem {
+    union {
+        struct {  // phase 1: one n-slice of B, C and the heads' h_in
+            uint32_t b[kChunk * R_STRIDE];
+            uint32_t c[kChunk * R_STRIDE];
+            uint32_t h[HW * kHeadDim * R_STRIDE];
+        } g;
+        struct {  // phase 2: one head
+            uint32_t xt[kHeadDim * XT_STRIDE];
+            float v[8 * kChunk];  // row block r: exp2(cs2[32r]-cs2[j]) * dts_j * 2^-xe_j, j < 32r
+            float ei[kChunk];     // exp2(cs2_i)
+        } hd;
+    } u;
+    float cs2[HW][kChunk];
+    float dts[HW][kChunk];
+    int hexp[HW][kHeadDim];
+    int xexp[kChunk];
+    float red[8];
+};
+
+// Raw (bf16 / fp16 bits) contents of one n-slice held in registers while the
+// previous slice is being multiplied.
+template <int HW>
+struct SliceRegs {
+    u32x4 b[2], c[2];
+    u32x4 h[(HW * kHeadDim * 4 + kThreads - 1) / kThreads];
+};
+
+__device__ __forceinline__ f16x8 lds_f16x8(const uint32_t *p) {
+    return __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4 *>(p));
+}
+}  // namespace
+
+template <int N, int HW>
+__global__ __launch_bounds__(kThreads, 1) void ssd_chunk_scan_kernel(Params p) {
+    constexpr int KS = N / 32;
+    constexpr int HV = (HW * kHeadDim * 4 + kThreads - 1) / kThreads;  // h_in vectors per thread per slice
+    __shared__ ScanSmem<HW> sm;
+
+    // ---- XCD-aware decode: all head groups of chunk c share one XCD
+    const int nhg = p.H / HW;
+    const int id = blockIdx.x;
+    const int xcd = id & 7;
+    const int slot = id >> 3;
+    const int c = (slot / nhg) * 8 + xcd;
+    const int hg = slot - (slot / nhg) * nhg;
     if (c >= p.meta[0]) return;
     const int4 dsc = p.desc[c];
     const int64_t t0 = dsc.y;
     const int len = dsc.z;
-    const int g = h / (p.H / p.G);
+    const int h_first = hg * HW;
+    const int g = h_first / (p.H / p.G);
+
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int lc = lane & 15;
-    const int q = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31;
+    const int hl = lane >> 5;
+    // row block of this wavefront: SIMD k (= wave & 3) runs blocks k and 7-k
+    const int rb = (wave >> 2) ? 7 - (wave & 3) : (wave & 3);
 
-    __shared__ float s_cs2[kChunk];
-    __shared__ float s_dts[kChunk];
-    __shared__ int s_hexp[kHeadDim];
-    __shared__ uint32_t s_red[8];
-    __shared__ uint32_t s_xt[kHeadDim * XT_STRIDE];
-    __shared__ uint32_t s_b[kChunk * R_STRIDE];
-    __shared__ uint32_t s_c[kChunk * R_STRIDE];
-    __shared__ uint32_t s_h[kHeadDim * R_STRIDE];
-
-    const int64_t crow = ((int64_t)c * p.H + h) * kChunk;
-    if (tid < kChunk) {
-        s_cs2[tid] = p.cs2[crow + tid];
-        s_dts[tid] = p.dts[crow + tid];
-    } else if (tid < kChunk + kHeadDim) {
-        s_hexp[tid - kChunk] = p.hexp[((int64_t)c * p.H + h) * kHeadDim + (tid - kChunk)];
-    }
     const int sb = p.bexp[(int64_t)c * p.G + g];
     const int sc = p.cexp[(int64_t)c * p.G + g];
 
-    // x^T[p][token] as scaled fp16 pairs; thread = (token pair, quarter of p)
-    int sx;
-    {
-        const int pair = tid & 127;
-        const int pq = tid >> 7;
-        u32x4 v[2][2];
-        uint32_t mloc = 0;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int j = pair * 2 + e;
-            if (j < len) {
-                const u32x4 *src = reinterpret_cast<const u32x4 *>(
-                    p.x + ((t0 + j) * p.H + h) * kHeadDim + pq * 16);
-                v[e][0] = src[0];
-                v[e][1] = src[1];
-            } else {
-                v[e][0] = u32x4{0u, 0u, 0u, 0u};
-                v[e][1] = u32x4{0u, 0u, 0u, 0u};
-            }
-#pragma unroll
-            for (int a = 0; a < 2; ++a)
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const uint32_t lo = v[e][a][k] & 0x7FFFu, hi = (v[e][a][k] >> 16) & 0x7FFFu;
-                    mloc = mloc > lo ? mloc : lo;
-                    mloc = mloc > hi ? mloc : hi;
-                }
-        }
-        mloc = wave_max_u32(mloc);
-        if (lane == 0) s_red[wave] = mloc;
-        __syncthreads();
-        uint32_t mm = s_red[0];
-#pragma unroll
-        for (int w = 1; w < 8; ++w) mm = mm > s_red[w] ? mm : s_red[w];
-        sx = mm == 0 ? 0 : 14 - ((int)(mm >> 7) - 127);
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const uint32_t a = v[0][k >> 3][(k >> 1) & 3];
-            const uint32_t b = v[1][k >> 3][(k >> 1) & 3];
-            const float lo = bf16_bits_to_float((k & 1) ? (a >> 16) : (a & 0xFFFFu));
-            const float hi = bf16_bits_to_float((k & 1) ? (b >> 16) : (b & 0xFFFFu));
-            s_xt[(pq * 16 + k) * XT_STRIDE + pair] = pack_f16x2(ldexpf(lo, sx), ldexpf(hi, sx));
-        }
+    for (int e = tid; e < HW * kChunk; e += kThreads) {
+        const int hh = e >> 8, j = e & 255;
+        const int64_t crow = ((int64_t)c * p.H + h_first + hh) * kChunk;
+        sm.cs2[hh][j] = p.cs2[crow + j];
+        sm.dts[hh][j] = p.dts[crow + j];
+    }
+    for (int e = tid; e < HW * kHeadDim; e += kThreads) {
+        const int hh = e >> 6, pp = e & 63;
+        sm.hexp[hh][pp] = p.hexp[((int64_t)c * p.H + h_first + hh) * kHeadDim + pp];
     }
 
-    // tile bookkeeping: 9 K-pairs of two 16-column j-blocks
-    const int rb0 = wave, rb1 = 15 - wave;
-    const int P0 = (wave + 2) >> 1;  // pairs for row block rb0
-
-    f32x4 accg[18];
-    f32x4 accy[2][4];
-#pragma unroll
-    for (int s = 0; s < 18; ++s) accg[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt) accy[r][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const uint16_t *hin_head = p.hin + ((int64_t)c * p.H + h) * kHeadDim * N;
-
-    for (int ks = 0; ks < KS; ++ks) {
-        __syncthreads();
-        // stage B and C rows (all 256 tokens, scaled fp16) and h_in rows (64 p)
-        // for n in [32ks, 32ks+32)
+    // ================= phase 1: G^T[j][i] and C * h_in^T for all HW heads
+    auto load_slice = [&](int ks, SliceRegs<HW> &r) {
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
-            const int idx = tid + it * 512;
-            const int j = idx >> 2;
-            const int v = idx & 3;
-            u32x4 bv = u32x4{0u, 0u, 0u, 0u}, cv = u32x4{0u, 0u, 0u, 0u};
+            const int j = (tid + it * kThreads) >> 2;
+            const int v = tid & 3;
+            r.b[it] = u32x4{0u, 0u, 0u, 0u};
+            r.c[it] = u32x4{0u, 0u, 0u, 0u};
             if (j < len) {
                 const int64_t off = ((t0 + j) * p.G + g) * N + ks * 32 + v * 8;
-                const u32x4 braw = *reinterpret_cast<const u32x4 *>(p.B + off);
-                const u32x4 craw = *reinterpret_cast<const u32x4 *>(p.C + off);
+                r.b[it] = *reinterpret_cast<const u32x4 *>(p.B + off);
+                r.c[it] = *reinterpret_cast<const u32x4 *>(p.C + off);
+            }
+        }
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    bv[k] = pack_f16x2(ldexpf(bf16_bits_to_float(braw[k] & 0xFFFFu), sb),
-                                       ldexpf(bf16_bits_to_float(braw[k] >> 16), sb));
-                    cv[k] = pack_f16x2(ldexpf(bf16_bits_to_float(craw[k] & 0xFFFFu), sc),
-                                       ldexpf(bf16_bits_to_float(craw[k] >> 16), sc));
+        for (int it = 0; it < HV; ++it) {
+            const int idx = tid + it * kThreads;
+            if (idx < HW * kHeadDim * 4) {
+                const int row = idx >> 2;  // hh * 64 + p
+                const int v = idx & 3;
+                r.h[it] = *reinterpret_cast<const u32x4 *>(
+                    p.hin + (((int64_t)c * p.H + h_first + (row >> 6)) * kHeadDim + (row & 63)) * N +
+                    ks * 32 + v * 8);
+            }
+        }
+    };
+    auto store_slice = [&](const SliceRegs<HW> &r) {
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int j = (tid + it * kThreads) >> 2;
+            const int v = tid & 3;
+            u32x4 bv, cv;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                bv[k] = pack_f16x2(ldexpf(bf16_bits_to_float(r.b[it][k] & 0xFFFFu), sb),
+                                   ldexpf(bf16_bits_to_float(r.b[it][k] >> 16), sb));
+                cv[k] = pack_f16x2(ldexpf(bf16_bits_to_float(r.c[it][k] & 0xFFFFu), sc),
+                                   ldexpf(bf16_bits_to_float(r.c[it][k] >> 16), sc));
+            }
+            *reinterpret_cast<u32x4 *>(sm.u.g.b + j * R_STRIDE + v * 4) = bv;
+            *reinterpret_cast<u32x4 *>(sm.u.g.c + j * R_STRIDE + v * 4) = cv;
+        }
+#pragma unroll
+        for (int it = 0; it < HV; ++it) {
+            const int idx = tid + it * kThreads;
+            if (idx < HW * kHeadDim * 4)
+                *reinterpret_cast<u32x4 *>(sm.u.g.h + (idx >> 2) * R_STRIDE + (idx & 3) * 4) = r.h[it];
+        }
+    };
+
+    f32x16 accg[8];
+    f32x16 accy[HW][2];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) accg[t] = f32x16{};
+#pragma unroll
+    for (int hh = 0; hh < HW; ++hh) accy[hh][0] = accy[hh][1] = f32x16{};
+
+    SliceRegs<HW> sr;
+    load_slice(0, sr);
+    for (int ks = 0; ks < KS; ++ks) {
+        __syncthreads();  // previous slice consumed
+        store_slice(sr);
+        if (ks + 1 < KS) load_slice(ks + 1, sr);  // in flight during this slice's MFMAs
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const f16x8 cf = lds_f16x8(sm.u.g.c + (32 * rb + l32) * R_STRIDE + 8 * kk + 4 * hl);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                if (t <= rb) {
+                    const f16x8 bf = lds_f16x8(sm.u.g.b + (32 * t + l32) * R_STRIDE + 8 * kk + 4 * hl);
+                    accg[t] = mfma32_f16(bf, cf, accg[t]);
                 }
             }
-            *reinterpret_cast<u32x4 *>(s_b + j * R_STRIDE + v * 4) = bv;
-            *reinterpret_cast<u32x4 *>(s_c + j * R_STRIDE + v * 4) = cv;
-        }
-        if (tid < 256) {
-            const int pp = tid >> 2;
-            const int v = tid & 3;
-            *reinterpret_cast<u32x4 *>(s_h + pp * R_STRIDE + v * 4) =
-                *reinterpret_cast<const u32x4 *>(hin_head + pp * N + ks * 32 + v * 8);
-        }
-        __syncthreads();
-
-        const f16x8 cf0 = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4 *>(
-            s_c + (rb0 * 16 + lc) * R_STRIDE + q * 4));
-        const f16x8 cf1 = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4 *>(
-            s_c + (rb1 * 16 + lc) * R_STRIDE + q * 4));
 #pragma unroll
-        for (int s = 0; s < 18; ++s) {
-            const int k = s >> 1;
-            const bool first = k < P0;
-            const int rb = first ? rb0 : rb1;
-            const int jb = 2 * (first ? k : k - P0) + (s & 1);
-            if (jb <= rb) {
-                const f16x8 bfr = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4 *>(
-                    s_b + (jb * 16 + lc) * R_STRIDE + q * 4));
-                accg[s] = mfma_f16(bfr, first ? cf0 : cf1, accg[s]);
+            for (int hh = 0; hh < HW; ++hh)
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt) {
+                    const f16x8 hf = lds_f16x8(sm.u.g.h + (hh * kHeadDim + 32 * pt + l32) * R_STRIDE + 8 * kk + 4 * hl);
+                    accy[hh][pt] = mfma32_f16(cf, hf, accy[hh][pt]);
+                }
+        }
+    }
+    // G in fp32 (undo the B and C scalings); max |G| over this wavefront's tiles
+    float gmax = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            accg[t][e] = ldexpf(accg[t][e], -(sb + sc));
+            gmax = fmaxf(gmax, fabsf(accg[t][e]));
+        }
+    gmax = wave_max(gmax);
+
+    // ================= phase 2: the diagonal block of each head
+#pragma unroll
+    for (int hh = 0; hh < HW; ++hh) {
+        const int h = h_first + hh;
+        const float *cs2 = sm.cs2[hh];
+        const float *dts = sm.dts[hh];
+        __syncthreads();  // phase 1 / previous head done with the shared buffers
+        // x^T: thread = (quarter of p, token pair); each x row scaled by its own 2^xe
+        {
+            const int pq = tid & 3;
+            const int pair = tid >> 2;
+            u32x4 v[2][2];
+            uint32_t mrow[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int j = pair * 2 + e;
+                if (j < len) {
+                    const u32x4 *src = reinterpret_cast<const u32x4 *>(
+                        p.x + ((t0 + j) * p.H + h) * kHeadDim + pq * 16);
+                    v[e][0] = src[0];
+                    v[e][1] = src[1];
+                } else {
+                    v[e][0] = u32x4{0u, 0u, 0u, 0u};
+                    v[e][1] = u32x4{0u, 0u, 0u, 0u};
+                }
+                uint32_t m = 0;
+#pragma unroll
+                for (int a = 0; a < 2; ++a)
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const uint32_t lo = v[e][a][k] & 0x7FFFu, hi = (v[e][a][k] >> 16) & 0x7FFFu;
+                        m = m > lo ? m : lo;
+                        m = m > hi ? m : hi;
+                    }
+                // row max over the 4 lanes holding this token
+                uint32_t o = (uint32_t)__shfl_xor((int)m, 1, 64);
+                m = m > o ? m : o;
+                o = (uint32_t)__shfl_xor((int)m, 2, 64);
+                mrow[e] = m > o ? m : o;
+            }
+            const int xe0 = mrow[0] == 0 ? 0 : 14 - ((int)(mrow[0] >> 7) - 127);
+            const int xe1 = mrow[1] == 0 ? 0 : 14 - ((int)(mrow[1] >> 7) - 127);
+            if (pq == 0) {
+                sm.xexp[pair * 2] = xe0;
+                sm.xexp[pair * 2 + 1] = xe1;
+            }
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const uint32_t a = v[0][k >> 3][(k >> 1) & 3];
+                const uint32_t b = v[1][k >> 3][(k >> 1) & 3];
+                const float lo = bf16_bits_to_float((k & 1) ? (a >> 16) : (a & 0xFFFFu));
+                const float hi = bf16_bits_to_float((k & 1) ? (b >> 16) : (b & 0xFFFFu));
+                sm.u.hd.xt[(pq * 16 + k) * XT_STRIDE + pair] = pack_f16x2(ldexpf(lo, xe0), ldexpf(hi, xe1));
             }
         }
+        __syncthreads();
+        // decay tables and the bound on |M|
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-            const f16x8 hf = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4 *>(
-                s_h + (pt * 16 + lc) * R_STRIDE + q * 4));
-            accy[0][pt] = mfma_f16(cf0, hf, accy[0][pt]);
-            accy[1][pt] = mfma_f16(cf1, hf, accy[1][pt]);
+        for (int it = 0; it < 8 * kChunk / kThreads; ++it) {
+            const int e = tid + it * kThreads;
+            const int r = e >> 8;
+            const int j = e & 255;
+            float val = 0.f;
+            if (j < 32 * r) val = exp2f(cs2[32 * r] - cs2[j]) * dts[j] * ldexpf(1.0f, -sm.xexp[j]);
+            sm.u.hd.v[e] = val;
         }
-    }
+        float wmax = 0.f;
+        if (tid < kChunk) {
+            sm.u.hd.ei[tid] = exp2f(cs2[tid]);
+            wmax = fabsf(dts[tid]) * ldexpf(1.0f, -sm.xexp[tid]);
+        }
+        wmax = wave_max(wmax);
+        if (lane == 0) sm.red[wave] = wmax;
+        __syncthreads();
+        wmax = fmaxf(fmaxf(sm.red[0], sm.red[1]), fmaxf(sm.red[2], sm.red[3]));
+        // decays exceed 1 only when A > 0: bound them by the chunk's total growth
+        const float dgrow = exp2f(fmaxf(0.f, cs2[kChunk - 1] - cs2[0]));
+        const int smx = f16_scale_exponent(gmax * wmax * dgrow);
 
-    // off-diagonal part: undo the C and h_in scalings, scale row i by exp2(cs2_i)
+        // off-diagonal part: undo the C and h_in scalings, decay row i by
+        // exp2(cs2_i), move to the M scale
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int rb = r ? rb1 : rb0;
+        for (int pt = 0; pt < 2; ++pt) {
+            const int cs = smx - (sc + sm.hexp[hh][32 * pt + l32]);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const float dec = exp2f(s_cs2[rb * 16 + q * 4 + t]);
-#pragma unroll
-            for (int pt = 0; pt < 4; ++pt)
-                accy[r][pt][t] = ldexpf(accy[r][pt][t], -(sc + s_hexp[pt * 16 + lc])) * dec;
+            for (int a = 0; a < 4; ++a) {
+                const float4 d4 = *reinterpret_cast<const float4 *>(sm.u.hd.ei + 32 * rb + 8 * a + 4 * hl);
+                accy[hh][pt][4 * a + 0] = ldexpf(accy[hh][pt][4 * a + 0], cs) * d4.x;
+                accy[hh][pt][4 * a + 1] = ldexpf(accy[hh][pt][4 * a + 1], cs) * d4.y;
+                accy[hh][pt][4 * a + 2] = ldexpf(accy[hh][pt][4 * a + 2], cs) * d4.z;
+                accy[hh][pt][4 * a + 3] = ldexpf(accy[hh][pt][4 * a + 3], cs) * d4.w;
+            }
         }
-    }
 
-    // M = G * decay * dts (masked), in place of the G^T accumulators;
-    // track max |M| per owned row block
-    float mx0 = 0.0f, mx1 = 0.0f;
+        // diagonal block: (2^smx M 2^-xe) (2^xe x)
+        const int i_a = 32 * rb + l32;  // this lane's row in the A layout
+        const float cs_i = cs2[i_a];
+        const float u = ldexpf(exp2f(cs_i - cs2[32 * rb]), smx);
 #pragma unroll
-    for (int s = 0; s < 18; ++s) {
-        const int k = s >> 1;
-        const bool first = k < P0;
-        const int rb = first ? rb0 : rb1;
-        const int jb = 2 * (first ? k : k - P0) + (s & 1);
-        const int i = rb * 16 + lc;
-        const float cs_i = s_cs2[i];
-        float m = 0.0f;
+        for (int t = 0; t < 8; ++t) {
+            if (t <= rb) {
+                float mv[16];
+                if (t < rb) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int j = jb * 16 + q * 4 + t;
-            float val = 0.0f;
-            if (j <= i) val = ldexpf(accg[s][t], -(sb + sc)) * exp2f(cs_i - s_cs2[j]) * s_dts[j];
-            accg[s][t] = val;
-            m = fmaxf(m, fabsf(val));
+                    for (int a = 0; a < 4; ++a) {
+                        const float4 v4 = *reinterpret_cast<const float4 *>(
+                            sm.u.hd.v + rb * kChunk + 32 * t + 8 * a + 4 * hl);
+                        mv[4 * a + 0] = accg[t][4 * a + 0] * v4.x * u;
+                        mv[4 * a + 1] = accg[t][4 * a + 1] * v4.y * u;
+                        mv[4 * a + 2] = accg[t][4 * a + 2] * v4.z * u;
+                        mv[4 * a + 3] = accg[t][4 * a + 3] * v4.w * u;
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int j = 32 * t + 8 * (e >> 2) + 4 * hl + (e & 3);
+                        mv[e] = j <= i_a ? ldexpf(accg[t][e] * exp2f(cs_i - cs2[j]) * dts[j], smx - sm.xexp[j])
+                                         : 0.f;
+                    }
+                }
+                const f16x8 mf0 = __builtin_bit_cast(f16x8, u32x4{pack_f16x2(mv[0], mv[1]), pack_f16x2(mv[2], mv[3]),
+                                                                  pack_f16x2(mv[4], mv[5]), pack_f16x2(mv[6], mv[7])});
+                const f16x8 mf1 = __builtin_bit_cast(f16x8, u32x4{pack_f16x2(mv[8], mv[9]), pack_f16x2(mv[10], mv[11]),
+                                                                  pack_f16x2(mv[12], mv[13]), pack_f16x2(mv[14], mv[15])});
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt) {
+                    const uint32_t *row = sm.u.hd.xt + (32 * pt + l32) * XT_STRIDE + 16 * t + 2 * hl;
+                    const f16x8 x0 = __builtin_bit_cast(f16x8, u32x4{row[0], row[1], row[4], row[5]});
+                    const f16x8 x1 = __builtin_bit_cast(f16x8, u32x4{row[8], row[9], row[12], row[13]});
+                    accy[hh][pt] = mfma32_f16(mf0, x0, accy[hh][pt]);
+                    accy[hh][pt] = mfma32_f16(mf1, x1, accy[hh][pt]);
+                }
+            }
         }
-        if (first) mx0 = fmaxf(mx0, m);
-        else mx1 = fmaxf(mx1, m);
-    }
-    const int sm0 = f16_scale_exponent(wave_max(mx0));
-    const int sm1 = f16_scale_exponent(wave_max(mx1));
 
-    // diagonal block: (2^sm M) (2^sx x), accumulated on top of the
-    // off-diagonal part brought to the same scale
+        // back to unit scale, add D * x, store bf16
+        const float dh = p.D ? p.D[h] : 0.0f;
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            accy[0][pt][t] = ldexpf(accy[0][pt][t], sm0 + sx);
-            accy[1][pt][t] = ldexpf(accy[1][pt][t], sm1 + sx);
-        }
-#pragma unroll
-    for (int k = 0; k < 9; ++k) {
-        const bool first = k < P0;
-        const int m = first ? k : k - P0;
-        const int sm = first ? sm0 : sm1;
-        const u32x4 mp = u32x4{
-            pack_f16x2(ldexpf(accg[2 * k][0], sm), ldexpf(accg[2 * k][1], sm)),
-            pack_f16x2(ldexpf(accg[2 * k][2], sm), ldexpf(accg[2 * k][3], sm)),
-            pack_f16x2(ldexpf(accg[2 * k + 1][0], sm), ldexpf(accg[2 * k + 1][1], sm)),
-            pack_f16x2(ldexpf(accg[2 * k + 1][2], sm), ldexpf(accg[2 * k + 1][3], sm))};
-        const f16x8 mf = __builtin_bit_cast(f16x8, mp);
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-            const uint32_t *row = s_xt + (pt * 16 + lc) * XT_STRIDE + m * 16 + q * 2;
-            const u32x4 xv = u32x4{row[0], row[1], row[8], row[9]};
-            const f16x8 xf = __builtin_bit_cast(f16x8, xv);
-            if (first) accy[0][pt] = mfma_f16(mf, xf, accy[0][pt]);
-            else accy[1][pt] = mfma_f16(mf, xf, accy[1][pt]);
-        }
-    }
-
-    // back to unit scale, add D * x, store bf16
-    const float dh = p.D ? p.D[h] : 0.0f;
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int rb = r ? rb1 : rb0;
-        const int sh = -((r ? sm1 : sm0) + sx);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int i = rb * 16 + q * 4 + t;
+        for (int e = 0; e < 16; ++e) {
+            const int i = 32 * rb + 8 * (e >> 2) + 4 * hl + (e & 3);
             if (i < len) {
+                const int xe = sm.xexp[i];
 #pragma unroll
-                for (int pt = 0; pt < 4; ++pt) {
-                    const int pc = pt * 16 + lc;
-                    const uint32_t w2 = s_xt[pc * XT_STRIDE + (i >> 1)];
-                    const float xvv = ldexpf(f16_bits_to_float((i & 1) ? (w2 >> 16) : (w2 & 0xFFFFu)), -sx);
-                    const float yv = ldexpf(accy[r][pt][t], sh) + dh * xvv;
+                for (int pt = 0; pt < 2; ++pt) {
+                    const int pc = 32 * pt + l32;
+                    const uint32_t w2 = sm.u.hd.xt[pc * XT_STRIDE + (i >> 1)];
+                    const float xvv = ldexpf(f16_bits_to_float((i & 1) ? (w2 >> 16) : (w2 & 0xFFFFu)), -xe);
+                    const float yv = ldexpf(accy[hh][pt][e], -smx) + dh * xvv;
                     p.y[((t0 + i) * p.H + h) * kHeadDim + pc] = float_to_bf16_bits(yv);
                 }
             }
@@ -285,15 +380,43 @@ __global__ __launch_bounds__(512) void ssd_chunk_scan_kernel(Params p) {
     }
 }
 
+// Heads per workgroup (1 or 2, dividing H/G; more would not fit the
+// accumulators of all heads in the register file).  One workgroup runs per CU;
+// a workgroup costs about one unit for G plus one unit per head, and the grid
+// runs in ceil(workgroups / CUs) rounds.  Pick the smallest
+// rounds * (G + heads) estimate.
+int chunk_scan_heads_per_wg(const Params &p) {
+    const int hpg = p.H / p.G;
+    const double g_cost = 1.4;  // G^T relative to one head, from their MFMA counts
+    int best = 1;
+    double best_cost = 1e300;
+    for (int hw = 1; hw <= 2 && hw <= hpg; hw *= 2) {
+        if (hpg % hw) continue;
+        const int64_t wgs = p.nchunks_max * (p.H / hw);
+        const double rounds = (double)((wgs + p.num_cus - 1) / p.num_cus);
+        const double cost = rounds * (g_cost + hw);
+        if (cost < best_cost) { best_cost = cost; best = hw; }
+    }
+    return best;
+}
+
+template <int N>
+static hipError_t launch_n(const Params &p, hipStream_t s) {
+    const int hw = chunk_scan_heads_per_wg(p);
+    const int64_t slots = (p.nchunks_max + 7) / 8 * (p.H / hw);
+    const dim3 grid((unsigned)(slots * 8));
+    if (hw == 2) hipLaunchKernelGGL((ssd_chunk_scan_kernel<N, 2>), grid, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((ssd_chunk_scan_kernel<N, 1>), grid, dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
 hipError_t launch_chunk_scan(const Params &p, hipStream_t s) {
-    dim3 grid((unsigned)p.nchunks_max, (unsigned)p.H);
     switch (p.N) {
-    case 64: hipLaunchKernelGGL(ssd_chunk_scan_kernel<64>, grid, dim3(512), 0, s, p); break;
-    case 128: hipLaunchKernelGGL(ssd_chunk_scan_kernel<128>, grid, dim3(512), 0, s, p); break;
-    case 256: hipLaunchKernelGGL(ssd_chunk_scan_kernel<256>, grid, dim3(512), 0, s, p); break;
+    case 64: return launch_n<64>(p, s);
+    case 128: return launch_n<128>(p, s);
+    case 256: return launch_n<256>(p, s);
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace ssd

@@ -33,6 +33,7 @@ struct Params {
     int batch, H, P, G, N, max_slots;
     int dt_softplus;
     int64_t nchunks_max;
+    int num_cus;  // compute units of the device the call runs on
     // caller tensors (device)
     uint16_t *y;
     const uint16_t *x;
@@ -72,9 +73,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return (uint32_t)float_to_bf16_bits(lo) | ((uint32_t)float_to_bf16_bits(hi) << 16);
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// two floats -> two fp16 (nearest even) in one dword: v_cvt_pk_f16_f32 on gfx950
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
-    _Float16 a = (_Float16)lo, b = (_Float16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    const f16x2 h = __builtin_convertvector((f32x2){lo, hi}, f16x2);
+    return __builtin_bit_cast(uint32_t, h);
 }
 
 __device__ __forceinline__ float f16_bits_to_float(uint32_t bits16) {
@@ -93,6 +98,14 @@ __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8 &a, const bf16x8 &b, con
 
 __device__ __forceinline__ f32x4 mfma_f16(const f16x8 &a, const f16x8 &b, const f32x4 &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// 32x32 output tile, K = 16.  Lane l: A row l%32, k = (l/32)*8 + e; B column
+// l%32, same k; D element t at row 8*(t/4) + 4*(l/32) + t%4, column l%32.
+__device__ __forceinline__ f32x16 mfma32_f16(const f16x8 &a, const f16x8 &b, const f32x16 &c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 // Inclusive scan of one int over a 64-lane wavefront.
