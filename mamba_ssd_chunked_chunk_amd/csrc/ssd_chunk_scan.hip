@@ -19,33 +19,33 @@
 // phase then runs the diagonal block of each head from G kept in registers.
 // Eight wavefronts, one 32-row block each; the two wavefronts that share a
 // SIMD own row blocks k and 7-k, so each SIMD multiplies 9 of the 36
-// lower-triangular 32x32 tiles.  Workgroups are numbered so that all head groups of a chunk land on
-// one XCD (dispatch is round-robin over the 8 XCDs) and share B and C in its
-// L2.
+// lower-triangular 32x32 tiles.  Workgroups are numbered so that all head
+// groups of a chunk land on one XCD (dispatch is round-robin over the 8 XCDs)
+// and share B and C in its L2.
 //
-// MFMA layout (v_mfma_f32_32x32x16_f16).  G is formed transposed (rows j,
-// columns i) over n, so the accumulator layout of a G tile (16 values per
-// lane, all at one i, at j = 8a + 4(l/32) + b) is directly the A-operand
-// layout of M for M*x: the 16 j of the first K-step are {0..3, 8..11} for
-// lanes 0-31 and {4..7, 12..15} for lanes 32-63 (a permutation of 0..15),
-// likewise 16..31 for the second; x is read from LDS in the same order.  The
-// C fragment of a K-step is the B operand of G^T and the A operand of C*h^T.
+// MFMA layout (32x32x16).  G is formed transposed (rows j, columns i) over n,
+// so the accumulator layout of a G tile (16 values per lane, all at one i, at
+// j = 8a + 4(l/32) + b) is directly the A-operand layout of M for M*x: the 16
+// j of the first K-step are {0..3, 8..11} for lanes 0-31 and {4..7, 12..15}
+// for lanes 32-63 (a permutation of 0..15), likewise 16..31 for the second;
+// x is read from LDS in the same order.  The C fragment of a K-step is the B
+// operand of G^T and, converted to fp16, the A operand of C*h^T.
 //
 // Decay without one exp2 per element.  For a tile strictly below the
 // diagonal block (all j < 32*rb <= i), exp2(cs2_i - cs2_j) =
 // exp2(cs2_i - cs2_r) * exp2(cs2_r - cs2_j) with r = 32*rb; both factors are
 // at most 1 for A <= 0.  The second factor (times dts_j and the x row scale)
 // is tabulated once per head in LDS; only the diagonal blocks use exp2 per
-// element.
+// element.  The skip term D*x is folded into the diagonal of M.
 //
-// Precision.  Products run on v_mfma_f32_16x16x32_f16 with fp32 accumulate.
-// B and C convert exactly to fp16 after a power-of-two scaling per (chunk,
-// group); each x row converts exactly after its own power-of-two scaling,
-// compensated inside M.  M and h_in are rounded to fp16 (11-bit significand)
-// under power-of-two scales that keep them far from overflow (one per
-// workgroup and head for M, one per row for h_in); bf16 (8 bits)
-// there would put the rounding error, which scales with the typical size of
-// y rather than with each y, close to the tolerance wherever y is near zero.
+// Precision.  G comes from bf16 MFMA on the exact bf16 inputs (fp32
+// accumulate).  M and h_in are rounded to fp16 (11-bit significand) under
+// power-of-two scales that keep them far from overflow (one per workgroup and
+// head for M, one per row for h_in); C is converted to fp16 exactly after a
+// power-of-two scaling per (chunk, group), and each x row after its own
+// power-of-two scaling compensated inside M.  bf16 (8 bits) for M or h_in
+// would put the rounding error, which scales with the typical size of y
+// rather than with each y, close to the tolerance wherever y is near zero.
 #include "ssd_common.hpp"
 
 namespace ssd {
@@ -53,12 +53,12 @@ namespace ssd {
 namespace {
 constexpr int kThreads = 512;
 constexpr int XT_STRIDE = 130;  // dwords per x^T row: 128 token pairs + pad (8-byte aligned rows)
-constexpr int R_STRIDE = 20;    // dwords per staged row of 32 fp16 + pad
+constexpr int R_STRIDE = 20;    // dwords per staged row of 32 16-bit values + pad
 
 template <int HW>
 struct ScanSmem {
     union {
-        struct {  // phase 1: one n-slice of B, C and the heads' h_in
+        struct {  // phase 1: one n-slice of B, C (bf16) and the heads' h_in (fp16)
             uint32_t b[kChunk * R_STRIDE];
             uint32_t c[kChunk * R_STRIDE];
             uint32_t h[HW * kHeadDim * R_STRIDE];
@@ -73,19 +73,26 @@ struct ScanSmem {
     float dts[HW][kChunk];
     int hexp[HW][kHeadDim];
     int xexp[kChunk];
-    float red[8];
+    float red[8][2];
 };
 
-// Raw (bf16 / fp16 bits) contents of one n-slice held in registers while the
-// previous slice is being multiplied.
+// Contents of one n-slice held in registers while the previous slice is
+// being multiplied.
 template <int HW>
 struct SliceRegs {
     u32x4 b[2], c[2];
     u32x4 h[(HW * kHeadDim * 4 + kThreads - 1) / kThreads];
 };
 
-__device__ __forceinline__ f16x8 lds_f16x8(const uint32_t *p) {
-    return __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4 *>(p));
+__device__ __forceinline__ u32x4 lds_u32x4(const uint32_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
+
+// 8 bf16 (as 4 dwords) -> 8 fp16 scaled by `scale` (a power of two)
+__device__ __forceinline__ f16x8 bf16x8_to_f16x8(const u32x4 v, float scale) {
+    u32x4 r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        r[k] = pack_f16x2(__uint_as_float(v[k] << 16) * scale, __uint_as_float(v[k] & 0xFFFF0000u) * scale);
+    return __builtin_bit_cast(f16x8, r);
 }
 }  // namespace
 
@@ -119,6 +126,7 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_chunk_scan_kernel(Params p) {
 
     const int sb = p.bexp[(int64_t)c * p.G + g];
     const int sc = p.cexp[(int64_t)c * p.G + g];
+    const float c_scale = ldexpf(1.0f, sc);
 
     for (int e = tid; e < HW * kChunk; e += kThreads) {
         const int hh = e >> 8, j = e & 255;
@@ -162,16 +170,8 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_chunk_scan_kernel(Params p) {
         for (int it = 0; it < 2; ++it) {
             const int j = (tid + it * kThreads) >> 2;
             const int v = tid & 3;
-            u32x4 bv, cv;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                bv[k] = pack_f16x2(ldexpf(bf16_bits_to_float(r.b[it][k] & 0xFFFFu), sb),
-                                   ldexpf(bf16_bits_to_float(r.b[it][k] >> 16), sb));
-                cv[k] = pack_f16x2(ldexpf(bf16_bits_to_float(r.c[it][k] & 0xFFFFu), sc),
-                                   ldexpf(bf16_bits_to_float(r.c[it][k] >> 16), sc));
-            }
-            *reinterpret_cast<u32x4 *>(sm.u.g.b + j * R_STRIDE + v * 4) = bv;
-            *reinterpret_cast<u32x4 *>(sm.u.g.c + j * R_STRIDE + v * 4) = cv;
+            *reinterpret_cast<u32x4 *>(sm.u.g.b + j * R_STRIDE + v * 4) = r.b[it];
+            *reinterpret_cast<u32x4 *>(sm.u.g.c + j * R_STRIDE + v * 4) = r.c[it];
         }
 #pragma unroll
         for (int it = 0; it < HV; ++it) {
@@ -197,33 +197,30 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_chunk_scan_kernel(Params p) {
         __syncthreads();
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            const f16x8 cf = lds_f16x8(sm.u.g.c + (32 * rb + l32) * R_STRIDE + 8 * kk + 4 * hl);
+            const u32x4 craw = lds_u32x4(sm.u.g.c + (32 * rb + l32) * R_STRIDE + 8 * kk + 4 * hl);
+            const bf16x8 cb = __builtin_bit_cast(bf16x8, craw);
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 if (t <= rb) {
-                    const f16x8 bf = lds_f16x8(sm.u.g.b + (32 * t + l32) * R_STRIDE + 8 * kk + 4 * hl);
-                    accg[t] = mfma32_f16(bf, cf, accg[t]);
+                    const bf16x8 bb = __builtin_bit_cast(
+                        bf16x8, lds_u32x4(sm.u.g.b + (32 * t + l32) * R_STRIDE + 8 * kk + 4 * hl));
+                    accg[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bb, cb, accg[t], 0, 0, 0);
                 }
             }
+            const f16x8 cf = bf16x8_to_f16x8(craw, c_scale);
 #pragma unroll
             for (int hh = 0; hh < HW; ++hh)
 #pragma unroll
                 for (int pt = 0; pt < 2; ++pt) {
-                    const f16x8 hf = lds_f16x8(sm.u.g.h + (hh * kHeadDim + 32 * pt + l32) * R_STRIDE + 8 * kk + 4 * hl);
+                    const f16x8 hf = __builtin_bit_cast(
+                        f16x8, lds_u32x4(sm.u.g.h + (hh * kHeadDim + 32 * pt + l32) * R_STRIDE + 8 * kk + 4 * hl));
                     accy[hh][pt] = mfma32_f16(cf, hf, accy[hh][pt]);
                 }
         }
     }
-    // G in fp32 (undo the B and C scalings); max |G| over this wavefront's tiles
-    float gmax = 0.f;
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            accg[t][e] = ldexpf(accg[t][e], -(sb + sc));
-            gmax = fmaxf(gmax, fabsf(accg[t][e]));
-        }
-    gmax = wave_max(gmax);
+
+    // bound on |G|: |C_i . B_j| <= N max|B| max|C| < N 2^(15-sb) 2^(15-sc)
+    const float gbound = ldexpf((float)N, 30 - sb - sc);
 
     // ================= phase 2: the diagonal block of each head
 #pragma unroll
@@ -271,13 +268,14 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_chunk_scan_kernel(Params p) {
                 sm.xexp[pair * 2] = xe0;
                 sm.xexp[pair * 2 + 1] = xe1;
             }
+            const float s0 = ldexpf(1.0f, xe0), s1 = ldexpf(1.0f, xe1);
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
                 const uint32_t a = v[0][k >> 3][(k >> 1) & 3];
                 const uint32_t b = v[1][k >> 3][(k >> 1) & 3];
-                const float lo = bf16_bits_to_float((k & 1) ? (a >> 16) : (a & 0xFFFFu));
-                const float hi = bf16_bits_to_float((k & 1) ? (b >> 16) : (b & 0xFFFFu));
-                sm.u.hd.xt[(pq * 16 + k) * XT_STRIDE + pair] = pack_f16x2(ldexpf(lo, xe0), ldexpf(hi, xe1));
+                const float lo = __uint_as_float((k & 1) ? (a & 0xFFFF0000u) : (a << 16));
+                const float hi = __uint_as_float((k & 1) ? (b & 0xFFFF0000u) : (b << 16));
+                sm.u.hd.xt[(pq * 16 + k) * XT_STRIDE + pair] = pack_f16x2(lo * s0, hi * s1);
             }
         }
         __syncthreads();
@@ -288,41 +286,47 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_chunk_scan_kernel(Params p) {
             const int r = e >> 8;
             const int j = e & 255;
             float val = 0.f;
-            if (j < 32 * r) val = exp2f(cs2[32 * r] - cs2[j]) * dts[j] * ldexpf(1.0f, -sm.xexp[j]);
+            if (j < 32 * r) val = ldexpf(fast_exp2(cs2[32 * r] - cs2[j]) * dts[j], -sm.xexp[j]);
             sm.u.hd.v[e] = val;
         }
-        float wmax = 0.f;
+        float wmax = 0.f, emax = 0.f;
         if (tid < kChunk) {
-            sm.u.hd.ei[tid] = exp2f(cs2[tid]);
-            wmax = fabsf(dts[tid]) * ldexpf(1.0f, -sm.xexp[tid]);
+            sm.u.hd.ei[tid] = fast_exp2(cs2[tid]);
+            emax = ldexpf(1.0f, -sm.xexp[tid]);
+            wmax = fabsf(dts[tid]) * emax;
         }
         wmax = wave_max(wmax);
-        if (lane == 0) sm.red[wave] = wmax;
+        emax = wave_max(emax);
+        if (lane == 0) { sm.red[wave][0] = wmax; sm.red[wave][1] = emax; }
         __syncthreads();
-        wmax = fmaxf(fmaxf(sm.red[0], sm.red[1]), fmaxf(sm.red[2], sm.red[3]));
-        // decays exceed 1 only when A > 0: bound them by the chunk's total growth
-        const float dgrow = exp2f(fmaxf(0.f, cs2[kChunk - 1] - cs2[0]));
-        const int smx = f16_scale_exponent(gmax * wmax * dgrow);
+        wmax = fmaxf(fmaxf(sm.red[0][0], sm.red[1][0]), fmaxf(sm.red[2][0], sm.red[3][0]));
+        emax = fmaxf(fmaxf(sm.red[0][1], sm.red[1][1]), fmaxf(sm.red[2][1], sm.red[3][1]));
+        const float dh = p.D ? p.D[h] : 0.0f;
+        // |2^-xe M| <= |G| * max(dts 2^-xe) * (decay <= 1, or the chunk's total
+        // growth when A > 0) + |D| max(2^-xe) on the diagonal
+        const float dgrow = fast_exp2(fmaxf(0.f, cs2[kChunk - 1] - cs2[0]));
+        const int smx = f16_scale_exponent(gbound * wmax * dgrow + fabsf(dh) * emax);
+        const float m_scale = ldexpf(1.0f, smx);
 
         // off-diagonal part: undo the C and h_in scalings, decay row i by
         // exp2(cs2_i), move to the M scale
 #pragma unroll
         for (int pt = 0; pt < 2; ++pt) {
-            const int cs = smx - (sc + sm.hexp[hh][32 * pt + l32]);
+            const float f = ldexpf(1.0f, smx - (sc + sm.hexp[hh][32 * pt + l32]));
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
                 const float4 d4 = *reinterpret_cast<const float4 *>(sm.u.hd.ei + 32 * rb + 8 * a + 4 * hl);
-                accy[hh][pt][4 * a + 0] = ldexpf(accy[hh][pt][4 * a + 0], cs) * d4.x;
-                accy[hh][pt][4 * a + 1] = ldexpf(accy[hh][pt][4 * a + 1], cs) * d4.y;
-                accy[hh][pt][4 * a + 2] = ldexpf(accy[hh][pt][4 * a + 2], cs) * d4.z;
-                accy[hh][pt][4 * a + 3] = ldexpf(accy[hh][pt][4 * a + 3], cs) * d4.w;
+                accy[hh][pt][4 * a + 0] *= f * d4.x;
+                accy[hh][pt][4 * a + 1] *= f * d4.y;
+                accy[hh][pt][4 * a + 2] *= f * d4.z;
+                accy[hh][pt][4 * a + 3] *= f * d4.w;
             }
         }
 
         // diagonal block: (2^smx M 2^-xe) (2^xe x)
         const int i_a = 32 * rb + l32;  // this lane's row in the A layout
         const float cs_i = cs2[i_a];
-        const float u = ldexpf(exp2f(cs_i - cs2[32 * rb]), smx);
+        const float u = fast_exp2(cs_i - cs2[32 * rb]) * m_scale;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             if (t <= rb) {
@@ -332,17 +336,18 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_chunk_scan_kernel(Params p) {
                     for (int a = 0; a < 4; ++a) {
                         const float4 v4 = *reinterpret_cast<const float4 *>(
                             sm.u.hd.v + rb * kChunk + 32 * t + 8 * a + 4 * hl);
-                        mv[4 * a + 0] = accg[t][4 * a + 0] * v4.x * u;
-                        mv[4 * a + 1] = accg[t][4 * a + 1] * v4.y * u;
-                        mv[4 * a + 2] = accg[t][4 * a + 2] * v4.z * u;
-                        mv[4 * a + 3] = accg[t][4 * a + 3] * v4.w * u;
+                        mv[4 * a + 0] = accg[t][4 * a + 0] * (v4.x * u);
+                        mv[4 * a + 1] = accg[t][4 * a + 1] * (v4.y * u);
+                        mv[4 * a + 2] = accg[t][4 * a + 2] * (v4.z * u);
+                        mv[4 * a + 3] = accg[t][4 * a + 3] * (v4.w * u);
                     }
                 } else {
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
                         const int j = 32 * t + 8 * (e >> 2) + 4 * hl + (e & 3);
-                        mv[e] = j <= i_a ? ldexpf(accg[t][e] * exp2f(cs_i - cs2[j]) * dts[j], smx - sm.xexp[j])
-                                         : 0.f;
+                        float val = accg[t][e] * fast_exp2(cs_i - cs2[j]) * dts[j];
+                        if (j == i_a) val += dh;
+                        mv[e] = j <= i_a ? ldexpf(val, smx - sm.xexp[j]) : 0.f;
                     }
                 }
                 const f16x8 mf0 = __builtin_bit_cast(f16x8, u32x4{pack_f16x2(mv[0], mv[1]), pack_f16x2(mv[2], mv[3]),
@@ -360,21 +365,15 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_chunk_scan_kernel(Params p) {
             }
         }
 
-        // back to unit scale, add D * x, store bf16
-        const float dh = p.D ? p.D[h] : 0.0f;
+        // back to unit scale, store bf16
+        const float inv = ldexpf(1.0f, -smx);
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int i = 32 * rb + 8 * (e >> 2) + 4 * hl + (e & 3);
             if (i < len) {
-                const int xe = sm.xexp[i];
-#pragma unroll
-                for (int pt = 0; pt < 2; ++pt) {
-                    const int pc = 32 * pt + l32;
-                    const uint32_t w2 = sm.u.hd.xt[pc * XT_STRIDE + (i >> 1)];
-                    const float xvv = ldexpf(f16_bits_to_float((i & 1) ? (w2 >> 16) : (w2 & 0xFFFFu)), -xe);
-                    const float yv = ldexpf(accy[hh][pt][e], -smx) + dh * xvv;
-                    p.y[((t0 + i) * p.H + h) * kHeadDim + pc] = float_to_bf16_bits(yv);
-                }
+                uint16_t *dst = p.y + ((t0 + i) * p.H + h) * kHeadDim + l32;
+                dst[0] = float_to_bf16_bits(accy[hh][0][e] * inv);
+                dst[32] = float_to_bf16_bits(accy[hh][1][e] * inv);
             }
         }
     }

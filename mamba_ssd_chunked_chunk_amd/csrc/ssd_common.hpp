@@ -144,6 +144,18 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return v;
 }
 
+// 2^x with the hardware instruction (v_exp_f32).  Used for decays, whose
+// arguments are <= 0 for A <= 0: results below the smallest normal float are
+// flushed toward zero, which is harmless for a decay factor.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 2^k as a float for |k| < 127 (exact), for scaling by powers of two with a
+// multiply.
+__device__ __forceinline__ float pow2i(int k) {
+    k = k < -126 ? -126 : (k > 127 ? 127 : k);
+    return __uint_as_float((uint32_t)(k + 127) << 23);
+}
+
 // softplus(v) = log(1 + e^v), without overflow.
 __device__ __forceinline__ float softplus_f(float v) {
     return fmaxf(v, 0.0f) + log1pf(expf(-fabsf(v)));

@@ -20,10 +20,16 @@
 // put the off-diagonal part's rounding error near the tolerance of y).
 // Each thread owns four consecutive (p, n) elements of one (sequence, head),
 // reads its pool element before the sequence's loop and writes it after, so
-// the in-place read-then-write of a slot never races.
+// the in-place read-then-write of a slot never races.  The chunk
+// contributions are loaded kDepth chunks ahead of their use, so that many
+// loads per thread are in flight while the chain advances.
 #include "ssd_common.hpp"
 
 namespace ssd {
+
+namespace {
+constexpr int kDepth = 4;
+}
 
 __global__ __launch_bounds__(256) void ssd_state_passing_kernel(Params p) {
     const int b = blockIdx.x;
@@ -41,36 +47,51 @@ __global__ __launch_bounds__(256) void ssd_state_passing_kernel(Params p) {
 
     float4 st = init ? *pool4 : make_float4(0.f, 0.f, 0.f, 0.f);
     const int64_t stride = (int64_t)p.H * head_elems;  // one chunk of states
-    const float4 *S4 = reinterpret_cast<const float4 *>(p.states + ((int64_t)k0 * p.H + h) * head_elems + e0);
+    const float *S = p.states + ((int64_t)k0 * p.H + h) * head_elems + e0;
+    const float *cs_last = p.cs2 + ((int64_t)k0 * p.H + h) * kChunk + kChunk - 1;
+    const int64_t cs_stride = (int64_t)p.H * kChunk;
     uint16_t *hin = p.hin + ((int64_t)k0 * p.H + h) * head_elems + e0;
+    int32_t *hexp = p.hexp + ((int64_t)k0 * p.H + h) * kHeadDim + e0 / p.N;
+    const int nk = k1 - k0;
 
-    float4 s_next = make_float4(0.f, 0.f, 0.f, 0.f);
-    float d_next = 0.f;
-    if (k0 < k1) {
-        s_next = *S4;
-        d_next = p.cs2[((int64_t)k0 * p.H + h) * kChunk + kChunk - 1];
-    }
-    for (int k = k0; k < k1; ++k) {
-        const float4 s_cur = s_next;
-        const float d_cur = exp2f(d_next);
-        if (k + 1 < k1) {  // prefetch the next chunk's contribution
-            s_next = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(S4) + (int64_t)(k + 1 - k0) * stride);
-            d_next = p.cs2[((int64_t)(k + 1) * p.H + h) * kChunk + kChunk - 1];
+    float4 s[kDepth];
+    float d[kDepth];
+#pragma unroll
+    for (int q = 0; q < kDepth; ++q) {
+        s[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+        d[q] = 0.f;
+        if (q < nk) {
+            s[q] = *reinterpret_cast<const float4 *>(S + q * stride);
+            d[q] = cs_last[q * cs_stride];
         }
-        // h_in row p as fp16, scaled by the power of two that puts the row's
-        // max |h| in [2^14, 2^15); the N/4 lanes of one row share it
-        float m = fmaxf(fmaxf(fabsf(st.x), fabsf(st.y)), fmaxf(fabsf(st.z), fabsf(st.w)));
-        for (int d = p.N / 8; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
-        const int sh = f16_scale_exponent(m);
-        uint2 hv;
-        hv.x = pack_f16x2(ldexpf(st.x, sh), ldexpf(st.y, sh));
-        hv.y = pack_f16x2(ldexpf(st.z, sh), ldexpf(st.w, sh));
-        *reinterpret_cast<uint2 *>(hin + (int64_t)(k - k0) * stride) = hv;
-        if (e0 % p.N == 0) p.hexp[((int64_t)k * p.H + h) * kHeadDim + e0 / p.N] = sh;
-        st.x = d_cur * st.x + s_cur.x;
-        st.y = d_cur * st.y + s_cur.y;
-        st.z = d_cur * st.z + s_cur.z;
-        st.w = d_cur * st.w + s_cur.w;
+    }
+    for (int kb = 0; kb < nk; kb += kDepth) {
+#pragma unroll
+        for (int q = 0; q < kDepth; ++q) {
+            const int k = kb + q;
+            if (k < nk) {
+                // h_in row p as fp16, scaled by the power of two that puts the
+                // row's max |h| in [2^14, 2^15); the N/4 lanes of one row share it
+                float m = fmaxf(fmaxf(fabsf(st.x), fabsf(st.y)), fmaxf(fabsf(st.z), fabsf(st.w)));
+                for (int dd = p.N / 8; dd >= 1; dd >>= 1) m = fmaxf(m, __shfl_xor(m, dd, 64));
+                const int sh = f16_scale_exponent(m);
+                const float sc = ldexpf(1.0f, sh);
+                uint2 hv;
+                hv.x = pack_f16x2(st.x * sc, st.y * sc);
+                hv.y = pack_f16x2(st.z * sc, st.w * sc);
+                *reinterpret_cast<uint2 *>(hin + (int64_t)k * stride) = hv;
+                if (e0 % p.N == 0) hexp[(int64_t)k * p.H * kHeadDim] = sh;
+                const float dec = exp2f(d[q]);
+                st.x = dec * st.x + s[q].x;
+                st.y = dec * st.y + s[q].y;
+                st.z = dec * st.z + s[q].z;
+                st.w = dec * st.w + s[q].w;
+                if (k + kDepth < nk) {  // refill this ring slot kDepth chunks ahead
+                    s[q] = *reinterpret_cast<const float4 *>(S + (int64_t)(k + kDepth) * stride);
+                    d[q] = cs_last[(int64_t)(k + kDepth) * cs_stride];
+                }
+            }
+        }
     }
     *pool4 = st;
 }
