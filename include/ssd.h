@@ -90,14 +90,23 @@ typedef struct ssd_problem {
  *   cs2       fp32[nchunks_max][H][256]   log2(e) * inclusive sum of A*dts
  *   bexp      int32[nchunks_max][G]       power-of-two exponent applied to B
  *   cexp      int32[nchunks_max][G]       power-of-two exponent applied to C
- *   states    fp32[nchunks_max][H][P][N]  chunk's own state contribution
+ *   cbt       fp32[nchunks_max][G][36][64][16]  G^T[j][i] = C_i . B_j of the
+ *                                         chunk, as the 36 lower-triangular
+ *                                         32x32 tiles (row block rb, column
+ *                                         block t <= rb, tile rb(rb+1)/2 + t),
+ *                                         each in MFMA accumulator order: lane
+ *                                         l, element e holds j = 32t + 8(e/4)
+ *                                         + 4(l/32) + e%4, i = 32rb + l%32
+ *   states    fp16[nchunks_max][H][P][N]  chunk's own state contribution,
+ *                                         scaled by 2^sexp[c][h]
+ *   sexp      int32[nchunks_max][H]       exponent of each states block
  *   hin       fp16[nchunks_max][H][P][N]  state entering the chunk, row p
  *                                         scaled by 2^hexp[c][h][p]
  *   hexp      int32[nchunks_max][H][P]    exponent of each hin row           */
 typedef struct ssd_workspace_layout {
     size_t total_bytes;
     int64_t nchunks_max;
-    size_t meta, chunk_off, desc, dts, cs2, bexp, cexp, states, hin, hexp;
+    size_t meta, chunk_off, desc, dts, cs2, bexp, cexp, cbt, states, sexp, hin, hexp;
 } ssd_workspace_layout;
 
 /* ABI version of the loaded library (SSD_ABI_VERSION it was built with). */

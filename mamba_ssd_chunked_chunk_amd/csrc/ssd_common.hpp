@@ -52,7 +52,9 @@ struct Params {
     float *cs2;          // [nchunks_max][H][256]
     int32_t *bexp;       // [nchunks_max][G]   exponent applied to B before fp16
     int32_t *cexp;       // [nchunks_max][G]   exponent applied to C before fp16
-    float *states;       // [nchunks_max][H][P][N]
+    float *cbt;          // [nchunks_max][G][36][64][16] C.B^T tiles, accumulator order
+    uint16_t *states;    // [nchunks_max][H][P][N] fp16, scaled by 2^sexp
+    int32_t *sexp;       // [nchunks_max][H]
     uint16_t *hin;       // [nchunks_max][H][P][N] fp16, row p scaled by 2^hexp
     int32_t *hexp;       // [nchunks_max][H][P]
 };

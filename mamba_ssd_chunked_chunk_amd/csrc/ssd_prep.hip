@@ -1,5 +1,6 @@
 // Step 0 + step 1 of the scan: the chunk table and the per-chunk cumulative
-// decay ("chunk_cumsum"), plus the power-of-two exponents of B and C.
+// decay ("chunk_cumsum"), plus the per-(chunk, group) products that do not
+// depend on the head: C.B^T and the power-of-two exponents of B and C.
 //
 // Chunk table: sequence b owns ceil(len_b / 256) chunks (none when empty);
 // chunk c of the call is found from the exclusive prefix sum of those counts,
@@ -15,32 +16,45 @@
 // ("mamba2_ssd_scan", "Per-token recurrence": dA = exp(A * dts); the segment
 // sums of "Mamba chunk scan with segsum", description).  Past the chunk end,
 // dts = 0 and cs2 stays at its last value, so cs2[255] is the chunk's total.
-// One thread per token; 16 heads at a time are scanned across the 256 threads.
+// One thread per token; 16 heads at a time are scanned across the workgroup.
 //
-// B and C exponents (blockIdx.y == 1 + array * G + g): the contractions feed
-// B and C to fp16 MFMA after an exact power-of-two scaling; the exponent that
-// puts max|B| (or max|C|) of the chunk's rows of group g in [2^14, 2^15) is
-// computed here, once per (chunk, group).
+// Per group (blockIdx.y == 1 + g):
+//   G^T[j][i] = sum_n B[t0+j,g,n] C[t0+i,g,n] for the causal tiles (j <= i
+//   blockwise), the "attention-like" intra-chunk scores of "Mamba chunk scan
+//   with segsum" (description) before decay.  They are shared by every head
+//   of the group, so they are formed once here (bf16 MFMA on the exact bf16
+//   inputs, fp32 accumulate) and stored in MFMA accumulator order, so the
+//   chunk-scan step reads each lane's 16 values as one 64-byte run.
+//   Eight wavefronts, one 32-row block (of i) each; the two wavefronts that
+//   share a SIMD own row blocks k and 7-k, so each SIMD forms 9 of the 36
+//   lower-triangular 32x32 tiles.
+//   The same pass records max|B| and max|C|; the exponents that put them in
+//   [2^14, 2^15) let the later fp16 products convert B and C exactly.
 #include "ssd_common.hpp"
 
 namespace ssd {
 
 namespace {
-constexpr int kPrepThreads = 256;
+constexpr int kPrepThreads = 512;
 constexpr int kHeadBlock = 16;
+constexpr int R_STRIDE = 20;  // dwords per staged row of 32 bf16 + pad
 }  // namespace
 
+template <int N>
 __global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(Params p) {
+    constexpr int KS = N / 32;
     const int c = blockIdx.x;
     const int job = blockIdx.y;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
 
-    __shared__ int s_wtot[4];
+    __shared__ int s_wtot[8];
     __shared__ int s_loc[2];
-    __shared__ float s_hsum[4][kHeadBlock];
-    __shared__ uint32_t s_umax[4];
+    __shared__ float s_hsum[8][kHeadBlock];
+    __shared__ uint32_t s_umax[8][2];
+    __shared__ __attribute__((aligned(16))) uint32_t s_b[kChunk * R_STRIDE];
+    __shared__ __attribute__((aligned(16))) uint32_t s_c[kChunk * R_STRIDE];
 
     // ---- locate chunk c: exclusive prefix of per-sequence chunk counts
     if (tid == 0) { s_loc[0] = -1; s_loc[1] = 0; }
@@ -56,9 +70,11 @@ __global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(Params p) {
         __syncthreads();  // protects s_wtot from the previous round
         if (lane == 63) s_wtot[wave] = wincl;
         __syncthreads();
-        int before = 0;
-        for (int w = 0; w < wave; ++w) before += s_wtot[w];
-        const int total = s_wtot[0] + s_wtot[1] + s_wtot[2] + s_wtot[3];
+        int before = 0, total = 0;
+        for (int w = 0; w < 8; ++w) {
+            if (w < wave) before += s_wtot[w];
+            total += s_wtot[w];
+        }
         const int excl = carry + before + wincl - n;
         if (b < p.batch) {
             if (c >= excl && c < excl + n) { s_loc[0] = b; s_loc[1] = c - excl; }
@@ -82,7 +98,7 @@ __global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(Params p) {
 
     if (job == 0) {
         if (tid == 0) p.desc[c] = make_int4(b, (int)t0, len, 0);
-        // ---- dts and cs2: thread = token, 16 heads at a time
+        // ---- dts and cs2: thread = token (threads past 255 hold zeros), 16 heads at a time
         const int j = tid;
         const bool valid = j < len;
         for (int hb = 0; hb < p.H; hb += kHeadBlock) {
@@ -98,7 +114,7 @@ __global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(Params p) {
                 d[k] = ds;
                 a[k] = h < p.H ? p.A[h] * ds : 0.0f;
             }
-            // inclusive scan over the 256 tokens, per head
+            // inclusive scan over the tokens, per head
 #pragma unroll
             for (int k = 0; k < kHeadBlock; ++k) a[k] = wave_incl_scan(a[k]);
             __syncthreads();  // s_hsum free from the previous head block
@@ -107,65 +123,114 @@ __global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(Params p) {
                 for (int k = 0; k < kHeadBlock; ++k) s_hsum[wave][k] = a[k];
             }
             __syncthreads();
+            if (j < kChunk) {
 #pragma unroll
-            for (int k = 0; k < kHeadBlock; ++k) {
-                float off = 0.0f;
-                for (int w = 0; w < wave; ++w) off += s_hsum[w][k];
-                const int h = hb + k;
-                if (h < p.H) {
-                    const int64_t row = ((int64_t)c * p.H + h) * kChunk + j;
-                    p.dts[row] = d[k];
-                    p.cs2[row] = (off + a[k]) * kLog2e;
+                for (int k = 0; k < kHeadBlock; ++k) {
+                    float off = 0.0f;
+                    for (int w = 0; w < wave; ++w) off += s_hsum[w][k];
+                    const int h = hb + k;
+                    if (h < p.H) {
+                        const int64_t row = ((int64_t)c * p.H + h) * kChunk + j;
+                        p.dts[row] = d[k];
+                        p.cs2[row] = (off + a[k]) * kLog2e;
+                    }
                 }
             }
         }
         return;
     }
 
-    // ---- B or C exponent for one group: max |value| over the chunk's rows
-    const int which = (job - 1) / p.G;
-    const int g = (job - 1) - which * p.G;
-    const uint16_t *src = which ? p.C : p.B;
-    const int nvec = p.N / 8;  // 16-byte vectors per token row
-    const int total = len * nvec;
-    uint32_t m = 0;
-    for (int base = tid; base < total; base += kPrepThreads * 8) {
-        u32x4 v[8];
+    // ---- group g: C.B^T tiles and the B / C exponents
+    const int g = job - 1;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int rb = (wv >> 2) ? 7 - (wv & 3) : (wv & 3);
+    const int l32 = lane & 31;
+    const int hl = lane >> 5;
+
+    u32x4 rbv[2], rcv[2];
+    auto load_slice = [&](int ks) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int i = base + u * kPrepThreads;
-            v[u] = u32x4{0u, 0u, 0u, 0u};
-            if (i < total) {
-                const int jj = i / nvec;
-                const int vv = i - jj * nvec;
-                v[u] = *reinterpret_cast<const u32x4 *>(src + ((t0 + jj) * p.G + g) * p.N + vv * 8);
+        for (int it = 0; it < 2; ++it) {
+            const int j = (tid + it * kPrepThreads) >> 2;
+            const int v = tid & 3;
+            rbv[it] = rcv[it] = u32x4{0u, 0u, 0u, 0u};
+            if (j < len) {
+                const int64_t off = ((t0 + j) * p.G + g) * N + ks * 32 + v * 8;
+                rbv[it] = *reinterpret_cast<const u32x4 *>(p.B + off);
+                rcv[it] = *reinterpret_cast<const u32x4 *>(p.C + off);
             }
         }
+    };
+    uint32_t bmax = 0, cmax = 0;
+    f32x16 accg[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+    for (int t = 0; t < 8; ++t) accg[t] = f32x16{};
+
+    load_slice(0);
+    for (int ks = 0; ks < KS; ++ks) {
+        __syncthreads();  // previous slice consumed
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int j = (tid + it * kPrepThreads) >> 2;
+            const int v = tid & 3;
+            *reinterpret_cast<u32x4 *>(s_b + j * R_STRIDE + v * 4) = rbv[it];
+            *reinterpret_cast<u32x4 *>(s_c + j * R_STRIDE + v * 4) = rcv[it];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const uint32_t lo = v[u][k] & 0x7FFFu, hi = (v[u][k] >> 16) & 0x7FFFu;
-                m = m > lo ? m : lo;
-                m = m > hi ? m : hi;
+                const uint32_t b0 = rbv[it][k] & 0x7FFFu, b1 = (rbv[it][k] >> 16) & 0x7FFFu;
+                const uint32_t c0 = rcv[it][k] & 0x7FFFu, c1 = (rcv[it][k] >> 16) & 0x7FFFu;
+                bmax = max(bmax, max(b0, b1));
+                cmax = max(cmax, max(c0, c1));
             }
+        }
+        if (ks + 1 < KS) load_slice(ks + 1);  // in flight during this slice's MFMAs
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const bf16x8 cb = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4 *>(s_c + (32 * rb + l32) * R_STRIDE + 8 * kk + 4 * hl));
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                if (t <= rb) {
+                    const bf16x8 bb = __builtin_bit_cast(
+                        bf16x8, *reinterpret_cast<const u32x4 *>(s_b + (32 * t + l32) * R_STRIDE + 8 * kk + 4 * hl));
+                    accg[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bb, cb, accg[t], 0, 0, 0);
+                }
+            }
+        }
     }
-    m = wave_max_u32(m);
-    if (lane == 0) s_umax[wave] = m;
+    // tiles in accumulator order: tile rb(rb+1)/2 + t, 64 lanes x 16 floats
+    float *dst = p.cbt + ((int64_t)c * p.G + g) * 36 * 1024;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        if (t <= rb) {
+            float4 *o = reinterpret_cast<float4 *>(dst + (rb * (rb + 1) / 2 + t) * 1024 + lane * 16);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                o[q] = make_float4(accg[t][4 * q], accg[t][4 * q + 1], accg[t][4 * q + 2], accg[t][4 * q + 3]);
+        }
+    }
+    bmax = wave_max_u32(bmax);
+    cmax = wave_max_u32(cmax);
+    if (lane == 0) { s_umax[wave][0] = bmax; s_umax[wave][1] = cmax; }
     __syncthreads();
-    if (tid == 0) {
-        uint32_t mm = s_umax[0];
-        for (int w = 1; w < 4; ++w) mm = mm > s_umax[w] ? mm : s_umax[w];
+    if (tid < 2) {
+        uint32_t mm = 0;
+        for (int w = 0; w < 8; ++w) mm = max(mm, s_umax[w][tid]);
         // bf16 magnitude bits: exponent field in bits 7..14
         const int e = (int)(mm >> 7) - 127;
-        int32_t *dst = which ? p.cexp : p.bexp;
-        dst[(int64_t)c * p.G + g] = mm == 0 ? 0 : 14 - e;
+        (tid ? p.cexp : p.bexp)[(int64_t)c * p.G + g] = mm == 0 ? 0 : 14 - e;
     }
 }
 
 hipError_t launch_prep(const Params &p, hipStream_t s) {
-    hipLaunchKernelGGL(ssd_prep_kernel, dim3((unsigned)p.nchunks_max, (unsigned)(1 + 2 * p.G)),
-                       dim3(kPrepThreads), 0, s, p);
+    const dim3 grid((unsigned)p.nchunks_max, (unsigned)(1 + p.G));
+    switch (p.N) {
+    case 64: hipLaunchKernelGGL(ssd_prep_kernel<64>, grid, dim3(kPrepThreads), 0, s, p); break;
+    case 128: hipLaunchKernelGGL(ssd_prep_kernel<128>, grid, dim3(kPrepThreads), 0, s, p); break;
+    case 256: hipLaunchKernelGGL(ssd_prep_kernel<256>, grid, dim3(kPrepThreads), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

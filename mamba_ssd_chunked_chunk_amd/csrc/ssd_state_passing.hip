@@ -15,7 +15,8 @@
 // "Mamba2SSDChunkScanVarlenFwdInplace" (struct description).  A sequence with
 // no tokens writes its initial state (or zeros) back.
 //
-// The chain is fp32.  h_in only feeds the outputs y; it is stored as fp16
+// Chunk contributions arrive as fp16 under one power-of-two exponent per
+// (chunk, head).  The chain is fp32.  h_in only feeds the outputs y; it is stored as fp16
 // with one power-of-two scale per row p (11 significant bits: bf16's 8 would
 // put the off-diagonal part's rounding error near the tolerance of y).
 // Each thread owns four consecutive (p, n) elements of one (sequence, head),
@@ -47,21 +48,26 @@ __global__ __launch_bounds__(256) void ssd_state_passing_kernel(Params p) {
 
     float4 st = init ? *pool4 : make_float4(0.f, 0.f, 0.f, 0.f);
     const int64_t stride = (int64_t)p.H * head_elems;  // one chunk of states
-    const float *S = p.states + ((int64_t)k0 * p.H + h) * head_elems + e0;
+    const uint16_t *S = p.states + ((int64_t)k0 * p.H + h) * head_elems + e0;
+    const int32_t *sexp = p.sexp + (int64_t)k0 * p.H + h;
     const float *cs_last = p.cs2 + ((int64_t)k0 * p.H + h) * kChunk + kChunk - 1;
     const int64_t cs_stride = (int64_t)p.H * kChunk;
     uint16_t *hin = p.hin + ((int64_t)k0 * p.H + h) * head_elems + e0;
     int32_t *hexp = p.hexp + ((int64_t)k0 * p.H + h) * kHeadDim + e0 / p.N;
     const int nk = k1 - k0;
 
-    float4 s[kDepth];
+    // ring of the next kDepth chunk contributions: fp16 values, their exponent, cs2_last
+    uint2 s[kDepth];
+    int se[kDepth];
     float d[kDepth];
 #pragma unroll
     for (int q = 0; q < kDepth; ++q) {
-        s[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+        s[q] = make_uint2(0u, 0u);
+        se[q] = 0;
         d[q] = 0.f;
         if (q < nk) {
-            s[q] = *reinterpret_cast<const float4 *>(S + q * stride);
+            s[q] = *reinterpret_cast<const uint2 *>(S + q * stride);
+            se[q] = sexp[q * p.H];
             d[q] = cs_last[q * cs_stride];
         }
     }
@@ -82,12 +88,14 @@ __global__ __launch_bounds__(256) void ssd_state_passing_kernel(Params p) {
                 *reinterpret_cast<uint2 *>(hin + (int64_t)k * stride) = hv;
                 if (e0 % p.N == 0) hexp[(int64_t)k * p.H * kHeadDim] = sh;
                 const float dec = exp2f(d[q]);
-                st.x = dec * st.x + s[q].x;
-                st.y = dec * st.y + s[q].y;
-                st.z = dec * st.z + s[q].z;
-                st.w = dec * st.w + s[q].w;
+                const float us = ldexpf(1.0f, -se[q]);
+                st.x = dec * st.x + f16_bits_to_float(s[q].x & 0xFFFFu) * us;
+                st.y = dec * st.y + f16_bits_to_float(s[q].x >> 16) * us;
+                st.z = dec * st.z + f16_bits_to_float(s[q].y & 0xFFFFu) * us;
+                st.w = dec * st.w + f16_bits_to_float(s[q].y >> 16) * us;
                 if (k + kDepth < nk) {  // refill this ring slot kDepth chunks ahead
-                    s[q] = *reinterpret_cast<const float4 *>(S + (int64_t)(k + kDepth) * stride);
+                    s[q] = *reinterpret_cast<const uint2 *>(S + (int64_t)(k + kDepth) * stride);
+                    se[q] = sexp[(int64_t)(k + kDepth) * p.H];
                     d[q] = cs_last[(int64_t)(k + kDepth) * cs_stride];
                 }
             }

@@ -55,9 +55,12 @@ def test_workspace_layout_arithmetic(lib):
     ncm = 1024 // 256 + 4
     assert L["nchunks_max"] == ncm
     assert L["total_bytes"] == binding.ssd_workspace_size(p)
-    offs = [L[k] for k in ("meta", "chunk_off", "desc", "dts", "cs2", "bexp", "cexp", "states", "hin", "hexp")]
+    offs = [L[k] for k in ("meta", "chunk_off", "desc", "dts", "cs2", "bexp", "cexp", "cbt", "states", "sexp",
+                           "hin", "hexp")]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
-    assert L["hin"] - L["states"] >= ncm * 16 * 64 * 256 * 4
+    assert L["states"] - L["cbt"] >= ncm * 1 * 36 * 64 * 16 * 4
+    assert L["sexp"] - L["states"] >= ncm * 16 * 64 * 256 * 2
+    assert L["hin"] - L["sexp"] >= ncm * 16 * 4
     assert L["hexp"] - L["hin"] >= ncm * 16 * 64 * 256 * 2
     assert L["total_bytes"] - L["hexp"] >= ncm * 16 * 64 * 4
     assert L["cs2"] - L["dts"] >= ncm * 16 * 256 * 4

@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 from oracle.chunked import chunked_scan
-from ssd_testlib import frob_rel, small_problem, sub_batch
+from ssd_testlib import bf16_to_f64, frob_rel, small_problem, sub_batch
 
 torch = pytest.importorskip("torch")
 from mamba_ssd_chunked_chunk_amd import binding, torch_io  # noqa: E402
@@ -151,7 +151,10 @@ def test_intermediates_match_chunked_oracle():
     desc = w[L["desc"]:L["desc"] + ncm * 16].view(np.int32).reshape(ncm, 4)
     dts = w[L["dts"]:L["dts"] + ncm * H * 256 * 4].view(np.float32).reshape(ncm, H, 256)
     cs2 = w[L["cs2"]:L["cs2"] + ncm * H * 256 * 4].view(np.float32).reshape(ncm, H, 256)
-    S = w[L["states"]:L["states"] + ncm * H * P * N * 4].view(np.float32).reshape(ncm, H, P, N)
+    S16 = w[L["states"]:L["states"] + ncm * H * P * N * 2].view(np.float16).reshape(ncm, H, P, N)
+    sexp = w[L["sexp"]:L["sexp"] + ncm * H * 4].view(np.int32).reshape(ncm, H)
+    S = S16.astype(np.float64) * np.exp2(-sexp.astype(np.float64))[..., None, None]
+    cbt = w[L["cbt"]:L["cbt"] + ncm * 2 * 36 * 1024 * 4].view(np.float32).reshape(ncm, 2, 36, 64, 16)
     hin16 = w[L["hin"]:L["hin"] + ncm * H * P * N * 2].view(np.float16).reshape(ncm, H, P, N)
     hexp = w[L["hexp"]:L["hexp"] + ncm * H * P * 4].view(np.int32).reshape(ncm, H, P)
     hin = hin16.astype(np.float64) * np.exp2(-hexp.astype(np.float64))[..., None]
@@ -173,6 +176,18 @@ def test_intermediates_match_chunked_oracle():
         # the B / C exponents put the chunk's max magnitude in [2^14, 2^15)
         T = prob["total_len"]
         g = h // 2
+        # C.B^T tiles (stored transposed, in MFMA accumulator order) against the plain product
+        Bc = bf16_to_f64(prob["B"]).reshape(T, 2, N)[t0:t0 + l, g]
+        Cc = bf16_to_f64(prob["C"]).reshape(T, 2, N)[t0:t0 + l, g]
+        GT = np.zeros((256, 256))
+        GT[:l, :l] = Bc @ Cc.T  # G^T[j][i] = B_j . C_i
+        lane = np.arange(64)[:, None]
+        e = np.arange(16)[None, :]
+        for rb in range(8):
+            for t in range(rb + 1):
+                jj = 32 * t + 8 * (e // 4) + 4 * (lane // 32) + e % 4
+                ii = 32 * rb + lane % 32
+                np.testing.assert_allclose(cbt[c, g, rb * (rb + 1) // 2 + t], GT[jj, ii], rtol=1e-5, atol=1e-3)
         for arr, ex in (("B", bexp), ("C", cexp)):
             vals = prob[arr].reshape(T, 2, N)[t0:t0 + l, g]
             mx = np.max((vals.astype(np.uint32) << 16).view(np.float32).__abs__())
