@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU oracle time for the baseline sample")
+    ap.add_argument("--summarize-profile", metavar="DIR",
+                    help="no GPU run: summarise the rocprofv3 output under DIR (kt/, fetch/, write/) "
+                         "for --workload, print it as markdown and write profiles/traffic.json")
     return ap.parse_args()
 
 
@@ -61,6 +64,7 @@ class Hip:
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
 
     def event(self):
@@ -145,6 +149,99 @@ def traffic_for(kernel, workload):
     return d.get(workload, {}).get(kernel)
 
 
+# ------------------------------------------------------- copy probe + counters
+
+COPY_MIB = 256
+
+
+def copy_probe(torch, dev, hip, stream, reps=5):
+    """A plain streaming copy of COPY_MIB MiB (fp32 dst = src * 1) timed with
+    HIP events: the achievable HBM rate beside the 8 TB/s peak, and the kernel
+    of known size whose FETCH_SIZE / WRITE_SIZE readings calibrate the
+    counters."""
+    n = (COPY_MIB << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.mul(src, 1.0, out=dst)
+    e0, e1 = hip.event(), hip.event()
+    hip.lib.hipEventRecord(e0, ctypes.c_void_p(stream.cuda_stream))
+    for _ in range(reps):
+        torch.mul(src, 1.0, out=dst)
+    hip.lib.hipEventRecord(e1, ctypes.c_void_p(stream.cuda_stream))
+    hip.lib.hipEventSynchronize(e1)
+    ms = hip.elapsed_ms(e0, e1) / reps
+    return round(2 * (COPY_MIB << 20) / (ms * 1e-3) / 1e9, 1)
+
+
+def _per_dispatch(csv_path):
+    """{dispatch id: (kernel name, grid size, summed counter value)} of one
+    rocprofv3 counter-collection CSV (values summed over the instances)."""
+    import csv
+    out = {}
+    for r in csv.DictReader(open(csv_path)):
+        d = int(r["Dispatch_Id"])
+        name, grid, v = out.get(d, (r["Kernel_Name"], int(r["Grid_Size"]), 0.0))
+        out[d] = (name, grid, v + float(r["Counter_Value"]))
+    return out
+
+
+def _short(name):
+    k = name.split("(")[0].replace("void ", "").split("<")[0].split("::")[-1]
+    return k[:-len("_kernel")] if k.startswith("ssd_") and k.endswith("_kernel") else k
+
+
+def summarize_profile(root, workload):
+    """Markdown summary of a kernel-trace run and two counter runs (FETCH_SIZE,
+    WRITE_SIZE) of `bench.py --workload <workload> --no-cpu`, and the
+    calibrated HBM bytes per launch of each libssd kernel -> traffic.json."""
+    import csv
+    from mamba_ssd_chunked_chunk_amd.workloads import make_workload
+    prob = make_workload(workload)
+    alg = algorithmic(prob)
+    copy_kib = (COPY_MIB << 20) / 1024.0
+    per = {}
+    for which in ("fetch", "write"):
+        disp = _per_dispatch(os.path.join(root, which, "run_counter_collection.csv"))
+        copies = [v for (n, g, v) in disp.values() if "Mul" in n]
+        cal = copy_kib / statistics.median(copies)
+        per[which] = dict(cal=cal, raw={})
+        for n, g, v in disp.values():
+            k = _short(n)
+            if k.startswith("ssd_"):
+                per[which]["raw"].setdefault(k, []).append(v)
+    stats = list(csv.DictReader(open(os.path.join(root, "kt", "run_kernel_stats.csv"))))
+    lines = ["| kernel | calls | avg µs | min µs | max µs | FETCH KiB/launch | WRITE KiB/launch "
+             "| HBM MB/launch (calibrated) | algorithmic MB/launch |", "|---|---|---|---|---|---|---|---|---|"]
+    traffic = {}
+    for r in stats:
+        k = _short(r["Name"])
+        f = w = None
+        if k in per["fetch"]["raw"]:
+            f = statistics.median(per["fetch"]["raw"][k])
+            w = statistics.median(per["write"]["raw"][k])
+            traffic[k] = round((f * per["fetch"]["cal"] + w * per["write"]["cal"]) * 1024)
+        a = alg.get(k, {}).get("bytes")
+        lines.append(f"| {k} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} "
+                     f"| {float(r['MaxNs']) / 1e3:.2f} | {'' if f is None else f'{f:.0f}'} "
+                     f"| {'' if w is None else f'{w:.0f}'} "
+                     f"| {'' if k not in traffic else f'{traffic[k] / 1e6:.1f}'} "
+                     f"| {'' if a is None else f'{a / 1e6:.1f}'} |")
+    lines.append("")
+    lines.append(f"Counter calibration on a {COPY_MIB} MiB fp32 copy kernel (dst = src * 1): "
+                 f"FETCH_SIZE x {per['fetch']['cal']:.4f}, WRITE_SIZE x {per['write']['cal']:.4f}.")
+    print("\n".join(lines))
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    d = json.load(open(path)) if os.path.exists(path) else {}
+    if d.get("sources_sha256_16") != kernel_sources_hash():
+        d = {"sources_sha256_16": kernel_sources_hash()}
+    d["calibration"] = {"copy_mib": COPY_MIB, "fetch": round(per["fetch"]["cal"], 5),
+                        "write": round(per["write"]["cal"], 5)}
+    d[workload] = traffic
+    with open(path, "w") as fh:
+        json.dump(d, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+
+
 # ------------------------------------------------------------------ CPU leg
 
 def cpu_baseline(prob, min_seconds):
@@ -167,6 +264,9 @@ def cpu_baseline(prob, min_seconds):
 
 def main():
     args = parse()
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile, args.workload)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "libssd is a single-GPU library; this benchmark runs on exactly one "
                                    "GPU (--gpus 1). Multi-GPU sharding is described in DESIGN.md, not run."}))
@@ -240,6 +340,8 @@ def main():
     hip.lib.hipEventSynchronize(w1)
     warm_ms = hip.elapsed_ms(w0, w1) / args.steps
 
+    copy_gbs = copy_probe(torch, dev, hip, stream)
+
     alg = algorithmic(prob)
     kern_us = {n: statistics.fmean(v) * 1e3 for n, v in per_kernel.items()}
     dom = max(kern_us, key=kern_us.get)
@@ -272,6 +374,7 @@ def main():
         "roofline": roof,
         "roofline_whole_call": whole,
         "roofline_per_kernel": per_kernel_roof,
+        "achievable_copy_GBps": copy_gbs,
         "wall_s_timed_region": round(wall, 3),
     }
     if not args.no_cpu:
