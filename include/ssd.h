@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 1
+#define SSD_ABI_VERSION 3
 #define SSD_MAX_DSTATE 256  /* largest dstate, as in "mamba2_ssd_scan", comptime MAX_DSTATE */
 
 typedef enum ssd_status {
@@ -90,23 +90,30 @@ typedef struct ssd_problem {
  *   cs2       fp32[nchunks_max][H][256]   log2(e) * inclusive sum of A*dts
  *   bexp      int32[nchunks_max][G]       power-of-two exponent applied to B
  *   cexp      int32[nchunks_max][G]       power-of-two exponent applied to C
- *   cbt       fp32[nchunks_max][G][36][64][16]  G^T[j][i] = C_i . B_j of the
+ *   cbt       fp16[nchunks_max][G][36][64][16]  G^T[j][i] = C_i . B_j of the
  *                                         chunk, as the 36 lower-triangular
  *                                         32x32 tiles (row block rb, column
  *                                         block t <= rb, tile rb(rb+1)/2 + t),
  *                                         each in MFMA accumulator order: lane
  *                                         l, element e holds j = 32t + 8(e/4)
- *                                         + 4(l/32) + e%4, i = 32rb + l%32
+ *                                         + 4(l/32) + e%4, i = 32rb + l%32;
+ *                                         scaled by 2^gexp[c][g]
+ *   gexp      int32[nchunks_max][G]       exponent of each cbt block
+ *   cf16      fp16[nchunks_max][G][256][N] C * 2^cexp of the chunk's tokens,
+ *                                         rows past the chunk end zero
+ *   bt16      fp16[nchunks_max][G][N][256] B^T * 2^bexp (token index
+ *                                         contiguous), zero past the chunk end
  *   states    fp16[nchunks_max][H][P][N]  chunk's own state contribution,
- *                                         scaled by 2^sexp[c][h]
- *   sexp      int32[nchunks_max][H]       exponent of each states block
+ *                                         element (p, n) scaled by
+ *                                         2^sexp[c][h][p/32][n/32]
+ *   sexp      int32[nchunks_max][H][2][N/32]  exponent of each 32x32 tile
  *   hin       fp16[nchunks_max][H][P][N]  state entering the chunk, row p
  *                                         scaled by 2^hexp[c][h][p]
  *   hexp      int32[nchunks_max][H][P]    exponent of each hin row           */
 typedef struct ssd_workspace_layout {
     size_t total_bytes;
     int64_t nchunks_max;
-    size_t meta, chunk_off, desc, dts, cs2, bexp, cexp, cbt, states, sexp, hin, hexp;
+    size_t meta, chunk_off, desc, dts, cs2, bexp, cexp, cbt, gexp, cf16, bt16, states, sexp, hin, hexp;
 } ssd_workspace_layout;
 
 /* ABI version of the loaded library (SSD_ABI_VERSION it was built with). */

@@ -45,13 +45,17 @@ class ssd_workspace_layout(ctypes.Structure):
     _fields_ = [("total_bytes", ctypes.c_size_t), ("nchunks_max", ctypes.c_int64),
                 ("meta", ctypes.c_size_t), ("chunk_off", ctypes.c_size_t),
                 ("desc", ctypes.c_size_t), ("dts", ctypes.c_size_t), ("cs2", ctypes.c_size_t),
-                ("bexp", ctypes.c_size_t), ("cexp", ctypes.c_size_t), ("cbt", ctypes.c_size_t),
+                ("bexp", ctypes.c_size_t), ("cexp", ctypes.c_size_t), ("cbt", ctypes.c_size_t), ("gexp", ctypes.c_size_t),
+                ("cf16", ctypes.c_size_t), ("bt16", ctypes.c_size_t),
                 ("states", ctypes.c_size_t), ("sexp", ctypes.c_size_t),
                 ("hin", ctypes.c_size_t), ("hexp", ctypes.c_size_t)]
 
 
 _lock = threading.Lock()
 _lib = None
+
+# SSD_ABI_VERSION of include/ssd.h that the ctypes structures below mirror
+ABI_VERSION = 3
 
 
 def load_library():
@@ -68,6 +72,9 @@ def load_library():
             PP = ctypes.POINTER(ssd_problem)
             lib.ssd_abi_version.restype = ctypes.c_int
             lib.ssd_abi_version.argtypes = []
+            if lib.ssd_abi_version() != ABI_VERSION:
+                raise RuntimeError(f"{LIB_PATH} has ABI version {lib.ssd_abi_version()}, the binding "
+                                   f"expects {ABI_VERSION}: rebuild it")
             lib.ssd_status_string.restype = ctypes.c_char_p
             lib.ssd_status_string.argtypes = [ctypes.c_int]
             lib.ssd_workspace_size.restype = ctypes.c_int

@@ -12,34 +12,40 @@
 // their sum); D*x is the skip term of "mamba2_ssd_scan" ("Per-token
 // recurrence").  y is rounded to bf16.
 //
-// Work split.  One workgroup per (chunk, head), eight wavefronts, one 32-row
-// block each; the two wavefronts that share a SIMD own row blocks k and 7-k,
-// so each SIMD handles 9 of the 36 lower-triangular 32x32 tiles.  Workgroups
-// are numbered so that all heads of a chunk land on one XCD (dispatch is
-// round-robin over the 8 XCDs) and share C and the C.B^T tiles in its L2.
-// Every global load a wavefront needs (its C rows, the head's h_in and x, its
-// first C.B^T tiles) is issued at the start, so they are all in flight
-// together while the workgroup stages x and builds its decay tables.
+// Work split.  One workgroup per (chunk, block of HB heads of one group),
+// eight wavefronts, one 32-row block each; the two wavefronts that share a
+// SIMD own row blocks k and 7-k, so each SIMD handles 9 of the 36
+// lower-triangular 32x32 tiles.  The operands the heads of a group share,
+// the wavefront's C rows (registers) and its C.B^T tiles (LDS), are loaded
+// once and stay on chip while the workgroup walks its heads; each head's x
+// and h_in are loaded into registers during the previous head's products.  Workgroups
+// are numbered so that all head blocks of a chunk land on one XCD (dispatch
+// is round-robin over the 8 XCDs) and share C and the tiles in its L2.
+// Row blocks that start past the chunk end skip their products.
 //
-// MFMA layout (v_mfma_f32_32x32x16).  C.B^T is stored transposed (rows j,
-// columns i) in accumulator order, so a tile's 16 values per lane (all at one
-// i, at j = 8a + 4(l/32) + b) are directly the A-operand layout of M for
-// M*x: the 16 j of the first K-step are {0..3, 8..11} for lanes 0-31 and
-// {4..7, 12..15} for lanes 32-63 (a permutation of 0..15), likewise 16..31
-// for the second; x is read from LDS in the same order.
+// MFMA layout (v_mfma_f32_32x32x16).  Every product is formed transposed,
+// y^T[p][i], so each lane ends up with 4 consecutive p of one token i (one
+// 8-byte store of 4 bf16) and the per-token factors are per-lane scalars.
+// C.B^T is stored transposed (rows j, columns i) in accumulator order, so a
+// tile's 16 values per lane (all at one i, at j = 8a + 4(l/32) + b) are
+// directly the B-operand layout of M^T for x^T*M^T: the 16 j of the first
+// K-step are {0..3, 8..11} for lanes 0-31 and {4..7, 12..15} for lanes 32-63
+// (a permutation of 0..15), likewise 16..31 for the second; x^T is read from
+// LDS in the same order.  C comes as the prep step's fp16 copy (scaled,
+// zero past the chunk end), one 16-byte load per lane and K-step.
 //
 // Decay without one exp2 per element.  For a tile strictly below the
 // diagonal block (all j < 32*rb <= i), exp2(cs2_i - cs2_j) =
 // exp2(cs2_i - cs2_r) * exp2(cs2_r - cs2_j) with r = 32*rb; both factors are
 // at most 1 for A <= 0.  The second factor (times dts_j and the x row scale)
-// is tabulated once in LDS; only the diagonal tile evaluates exp2 per
-// element.  The skip term D*x is folded into the diagonal of M.
+// is tabulated once per head in LDS; only the diagonal tile evaluates exp2
+// per element.  The skip term D*x is folded into the diagonal of M.
 //
 // Precision.  M and h_in are rounded to fp16 (11-bit significand) under
-// power-of-two scales that keep them far from overflow (one per workgroup for
-// M, one per row for h_in); C is converted to fp16 exactly after a
-// power-of-two scaling per (chunk, group), and each x row after its own
-// power-of-two scaling compensated inside M.  All products accumulate in
+// power-of-two scales that keep them far from overflow (one per head for M,
+// one per row for h_in); C and C.B^T were rounded to fp16 after power-of-two
+// scalings per (chunk, group), and each x row is converted after its own
+// power-of-two scaling, compensated inside M.  All products accumulate in
 // fp32.  bf16 (8 bits) for M or h_in would put the rounding error, which
 // scales with the typical size of y rather than with each y, close to the
 // tolerance wherever y is near zero.
@@ -54,56 +60,43 @@ constexpr int XT_STRIDE = 130;  // dwords per x^T row: 128 token pairs + pad (8-
 template <int N>
 struct __attribute__((aligned(16))) ScanSmem {
     static constexpr int H_STRIDE = N / 2 + 4;  // dwords per h_in row + pad
+    uint32_t g[36 * 2 * 64 * 4];  // the chunk's fp16 C.B^T tiles: [tile][half][lane] 16-byte runs
     uint32_t h[kHeadDim * H_STRIDE];
     uint32_t xt[kHeadDim * XT_STRIDE];
     float v[8 * kChunk];  // row block r: exp2(cs2[32r]-cs2[j]) * dts_j * 2^-xe_j, j < 32r
-    float ei[kChunk];     // exp2(cs2_i)
     float cs2[kChunk];
     float dts[kChunk];
+    float wx[kChunk];     // dts_j * 2^-xe_j
     int xexp[kChunk];
-    int hexp[kHeadDim];
+    float hs[kHeadDim];   // 2^-hexp[p]
     float red[8][2];
 };
 
-// 8 bf16 (as 4 dwords) -> 8 fp16 scaled by `scale` (a power of two)
-__device__ __forceinline__ f16x8 bf16x8_to_f16x8(const u32x4 v, float scale) {
-    u32x4 r;
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-        r[k] = pack_f16x2(__uint_as_float(v[k] << 16) * scale, __uint_as_float(v[k] & 0xFFFF0000u) * scale);
-    return __builtin_bit_cast(f16x8, r);
-}
-
-__device__ __forceinline__ f32x16 load_tile(const float *src) {
-    const float4 *s4 = reinterpret_cast<const float4 *>(src);
-    f32x16 r;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const float4 v = s4[q];
-        r[4 * q] = v.x; r[4 * q + 1] = v.y; r[4 * q + 2] = v.z; r[4 * q + 3] = v.w;
-    }
-    return r;
+__device__ __forceinline__ float h2f(uint32_t w, int hi) {
+    return f16_bits_to_float(hi ? (w >> 16) : (w & 0xFFFFu));
 }
 }  // namespace
 
-template <int N>
-__global__ __launch_bounds__(kThreads, 1) void ssd_chunk_scan_kernel(Params p) {
+template <int N, int HB>
+__global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
     constexpr int KS = N / 16;  // K-steps of the off-diagonal product
     constexpr int H_STRIDE = ScanSmem<N>::H_STRIDE;
     constexpr int HVEC = kHeadDim * (N / 8) / kThreads;  // h_in 16-byte vectors per thread
     __shared__ ScanSmem<N> sm;
 
-    // ---- XCD-aware decode: all heads of chunk c share one XCD
+    // ---- XCD-aware decode: all head blocks of chunk c share one XCD
+    const int nhb = p.H / HB;
     const int id = blockIdx.x;
     const int xcd = id & 7;
     const int slot = id >> 3;
-    const int c = (slot / p.H) * 8 + xcd;
-    const int h = slot - (slot / p.H) * p.H;
+    const int c = (slot / nhb) * 8 + xcd;
+    const int hb = slot - (slot / nhb) * nhb;
     if (c >= p.meta[0]) return;
     const int4 dsc = p.desc[c];
     const int64_t t0 = dsc.y;
     const int len = dsc.z;
-    const int g = h / (p.H / p.G);
+    const int h_first = hb * HB;
+    const int g = h_first / (p.H / p.G);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -112,213 +105,287 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_chunk_scan_kernel(Params p) {
     const int hl = lane >> 5;
     // row block of this wavefront: SIMD k (= wave & 3) runs blocks k and 7-k
     const int rb = (wave >> 2) ? 7 - (wave & 3) : (wave & 3);
+    const bool active = 32 * rb < len;  // wavefront-uniform
+    const int i_l = 32 * rb + l32;      // this lane's token (column of y^T)
 
-    // ---- issue every early global load
-    // C rows of this wavefront's row block, in the A-operand layout (zero past the chunk end)
-    u32x4 cfr[KS];
+    // ---- per-group operands, kept in registers for all heads
+    // fp16 C row i_l (zero past the chunk end), 8 values per K-step
+    u32x4 cq[KS];
     {
-        const int i = 32 * rb + l32;
-        const uint16_t *crow = p.C + ((t0 + min(i, len - 1)) * p.G + g) * N + 8 * hl;
+        const uint16_t *crow = p.cf16 + (((int64_t)c * p.G + g) * kChunk + i_l) * N + 8 * hl;
+        const uint16_t *cbt = p.cbt + (((int64_t)c * p.G + g) * 36 + rb * (rb + 1) / 2) * 1024 + lane * 16;
 #pragma unroll
-        for (int k = 0; k < KS; ++k) cfr[k] = i < len ? *reinterpret_cast<const u32x4 *>(crow + 16 * k) : u32x4{};
-    }
-    // the head's h_in rows
-    u32x4 hreg[HVEC];
-    const uint16_t *hin_head = p.hin + ((int64_t)c * p.H + h) * kHeadDim * N;
+        for (int k = 0; k < KS; ++k) cq[k] = *reinterpret_cast<const u32x4 *>(crow + 16 * k);
+        // this row block's tiles into LDS, each lane its own 32 bytes (read
+        // back only by the same lane, so no barrier is needed)
 #pragma unroll
-    for (int it = 0; it < HVEC; ++it) hreg[it] = *reinterpret_cast<const u32x4 *>(hin_head + (tid + it * kThreads) * 8);
-    // x: thread = (quarter of p, token pair)
-    const int pq = tid & 3;
-    const int pair = tid >> 2;
-    u32x4 xr[2][2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        const int j = pair * 2 + e;
-        if (j < len) {
-            const u32x4 *src = reinterpret_cast<const u32x4 *>(p.x + ((t0 + j) * p.H + h) * kHeadDim + pq * 16);
-            xr[e][0] = src[0];
-            xr[e][1] = src[1];
-        } else {
-            xr[e][0] = xr[e][1] = u32x4{};
+        for (int t = 0; t < 8; ++t) {
+            if (t <= rb) {
+                const u32x4 a = *reinterpret_cast<const u32x4 *>(cbt + t * 1024);
+                const u32x4 b = *reinterpret_cast<const u32x4 *>(cbt + t * 1024 + 8);
+                u32x4 *d = reinterpret_cast<u32x4 *>(sm.g) + (rb * (rb + 1) / 2 + t) * 128 + lane;
+                d[0] = a;
+                d[64] = b;
+            }
         }
-    }
-    // the first two C.B^T tiles of this row block
-    const float *cbt = p.cbt + (((int64_t)c * p.G + g) * 36 + rb * (rb + 1) / 2) * 1024 + lane * 16;
-    f32x16 gt[2];
-    gt[0] = load_tile(cbt);
-    gt[1] = rb >= 1 ? load_tile(cbt + 1024) : f32x16{};
-    const int64_t crow = ((int64_t)c * p.H + h) * kChunk;
-    if (tid < kChunk) {
-        sm.cs2[tid] = p.cs2[crow + tid];
-        sm.dts[tid] = p.dts[crow + tid];
-    } else if (tid < kChunk + kHeadDim) {
-        sm.hexp[tid - kChunk] = p.hexp[((int64_t)c * p.H + h) * kHeadDim + (tid - kChunk)];
     }
     const int sc = p.cexp[(int64_t)c * p.G + g];
-    const float c_scale = ldexpf(1.0f, sc);
-    const float dh = p.D ? p.D[h] : 0.0f;
+    const int sg = p.gexp[(int64_t)c * p.G + g];
 
-    // ---- stage h_in and x^T (each x row scaled by its own 2^xe)
+    // ---- per-head inputs: thread = (quarter of p, token pair) for x, 16-byte vectors of h_in
+    const int pq = tid & 3;
+    const int pair = tid >> 2;
+    u32x4 hreg[HVEC];
+    u32x4 xr[2][2];
+    auto load_head = [&](int h) {
+        const uint16_t *hin_head = p.hin + ((int64_t)c * p.H + h) * kHeadDim * N;
 #pragma unroll
-    for (int it = 0; it < HVEC; ++it) {
-        const int idx = tid + it * kThreads;
-        const int row = idx / (N / 8), v = idx - row * (N / 8);
-        *reinterpret_cast<u32x4 *>(sm.h + row * H_STRIDE + v * 4) = hreg[it];
-    }
-    {
-        uint32_t mrow[2];
+        for (int it = 0; it < HVEC; ++it)
+            hreg[it] = *reinterpret_cast<const u32x4 *>(hin_head + (tid + it * kThreads) * 8);
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-            uint32_t m = 0;
-#pragma unroll
-            for (int a = 0; a < 2; ++a)
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const uint32_t lo = xr[e][a][k] & 0x7FFFu, hi = (xr[e][a][k] >> 16) & 0x7FFFu;
-                    m = max(m, max(lo, hi));
-                }
-            // row max over the 4 lanes holding this token
-            m = max(m, (uint32_t)__shfl_xor((int)m, 1, 64));
-            mrow[e] = max(m, (uint32_t)__shfl_xor((int)m, 2, 64));
+            const int j = pair * 2 + e;
+            // rows past the chunk end read the last row and are zeroed (len >= 1)
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(
+                p.x + ((t0 + min(j, len - 1)) * p.H + h) * kHeadDim + pq * 16);
+            const u32x4 a = src[0], b = src[1];
+            const bool ok = j < len;
+            xr[e][0] = ok ? a : u32x4{};
+            xr[e][1] = ok ? b : u32x4{};
         }
-        const int xe0 = mrow[0] == 0 ? 0 : 14 - ((int)(mrow[0] >> 7) - 127);
-        const int xe1 = mrow[1] == 0 ? 0 : 14 - ((int)(mrow[1] >> 7) - 127);
-        if (pq == 0) {
-            sm.xexp[pair * 2] = xe0;
-            sm.xexp[pair * 2 + 1] = xe1;
-        }
-        const float s0 = ldexpf(1.0f, xe0), s1 = ldexpf(1.0f, xe1);
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const uint32_t a = xr[0][k >> 3][(k >> 1) & 3];
-            const uint32_t b = xr[1][k >> 3][(k >> 1) & 3];
-            const float lo = __uint_as_float((k & 1) ? (a & 0xFFFF0000u) : (a << 16));
-            const float hi = __uint_as_float((k & 1) ? (b & 0xFFFF0000u) : (b << 16));
-            sm.xt[(pq * 16 + k) * XT_STRIDE + pair] = pack_f16x2(lo * s0, hi * s1);
-        }
-    }
-    __syncthreads();
+    };
+    load_head(h_first);
 
-    // ---- decay tables and the bound on |M|
+    for (int hh = 0; hh < HB; ++hh) {
+        const int h = h_first + hh;
+        // keep the per-group operands opaque across heads, so values derived
+        // from them (fp32 copies of the tiles) are not hoisted out of the loop
+        // and held in registers for all heads
 #pragma unroll
-    for (int it = 0; it < 8 * kChunk / kThreads; ++it) {
-        const int e = tid + it * kThreads;
-        const int r = e >> 8;
-        const int j = e & 255;
-        float val = 0.f;
-        if (j < 32 * r) val = ldexpf(fast_exp2(sm.cs2[32 * r] - sm.cs2[j]) * sm.dts[j], -sm.xexp[j]);
-        sm.v[e] = val;
-    }
-    float wmax = 0.f, emax = 0.f;
-    if (tid < kChunk) {
-        sm.ei[tid] = fast_exp2(sm.cs2[tid]);
-        emax = ldexpf(1.0f, -sm.xexp[tid]);
-        wmax = fabsf(sm.dts[tid]) * emax;
-    }
-    wmax = wave_max(wmax);
-    emax = wave_max(emax);
-    if (lane == 0) { sm.red[wave][0] = wmax; sm.red[wave][1] = emax; }
-
-    // ---- off-diagonal part: C (registers, converted to fp16) x h_in^T (LDS)
-    f32x16 accy[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int k = 0; k < KS; ++k) {
-        const f16x8 cf = bf16x8_to_f16x8(cfr[k], c_scale);
-#pragma unroll
-        for (int pt = 0; pt < 2; ++pt) {
-            const f16x8 hf = __builtin_bit_cast(
-                f16x8, *reinterpret_cast<const u32x4 *>(sm.h + (32 * pt + l32) * H_STRIDE + 8 * k + 4 * hl));
-            accy[pt] = mfma32_f16(cf, hf, accy[pt]);
+        for (int k = 0; k < KS; ++k) asm volatile("" : "+v"(cq[k]));
+        // likewise the lane-derived indices, so masks and addresses are
+        // recomputed per head instead of being held in registers
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63;
+        const int l32 = lane & 31;
+        const int hl = lane >> 5;
+        const int i_l = 32 * rb + l32;
+        const int pq = tid & 3;
+        const int pair = tid >> 2;
+        const int64_t crow2 = ((int64_t)c * p.H + h) * kChunk;
+        __syncthreads();  // the previous head's LDS reads are done
+        if (tid < kChunk) {
+            sm.cs2[tid] = p.cs2[crow2 + tid];
+            sm.dts[tid] = p.dts[crow2 + tid];
+        } else if (tid < kChunk + kHeadDim) {
+            sm.hs[tid - kChunk] = ldexpf(1.0f, -p.hexp[((int64_t)c * p.H + h) * kHeadDim + (tid - kChunk)]);
         }
-    }
-    __syncthreads();  // tables and red[] complete
-    wmax = fmaxf(fmaxf(sm.red[0][0], sm.red[1][0]), fmaxf(sm.red[2][0], sm.red[3][0]));
-    emax = fmaxf(fmaxf(sm.red[0][1], sm.red[1][1]), fmaxf(sm.red[2][1], sm.red[3][1]));
-    // |2^-xe M| <= |G| * max(dts 2^-xe) * (decay <= 1, or the chunk's total
-    // growth when A > 0) + |D| max(2^-xe) on the diagonal, with
-    // |G| = |C_i . B_j| <= N max|B| max|C| < N 2^(15-sb) 2^(15-sc)
-    const int sb = p.bexp[(int64_t)c * p.G + g];
-    const float gbound = ldexpf((float)N, 30 - sb - sc);
-    const float dgrow = fast_exp2(fmaxf(0.f, sm.cs2[kChunk - 1] - sm.cs2[0]));
-    const int smx = f16_scale_exponent(gbound * wmax * dgrow + fabsf(dh) * emax);
-    const float m_scale = ldexpf(1.0f, smx);
+        const float dh = p.D ? p.D[h] : 0.0f;
 
-    // undo the C and h_in scalings, decay row i by exp2(cs2_i), move to the M scale
+        // ---- stage h_in and x^T (each x row scaled by its own 2^xe)
 #pragma unroll
-    for (int pt = 0; pt < 2; ++pt) {
-        const float f = ldexpf(1.0f, smx - (sc + sm.hexp[32 * pt + l32]));
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            const float4 d4 = *reinterpret_cast<const float4 *>(sm.ei + 32 * rb + 8 * a + 4 * hl);
-            accy[pt][4 * a + 0] *= f * d4.x;
-            accy[pt][4 * a + 1] *= f * d4.y;
-            accy[pt][4 * a + 2] *= f * d4.z;
-            accy[pt][4 * a + 3] *= f * d4.w;
+        for (int it = 0; it < HVEC; ++it) {
+            const int idx = tid + it * kThreads;
+            const int row = idx / (N / 8), v = idx - row * (N / 8);
+            *reinterpret_cast<u32x4 *>(sm.h + row * H_STRIDE + v * 4) = hreg[it];
         }
-    }
+        {
+            uint32_t mrow[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                uint32_t m = 0;
+#pragma unroll
+                for (int a = 0; a < 2; ++a)
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const uint32_t lo = xr[e][a][k] & 0x7FFFu, hi = (xr[e][a][k] >> 16) & 0x7FFFu;
+                        m = max(m, max(lo, hi));
+                    }
+                // row max over the 4 lanes holding this token
+                m = max(m, (uint32_t)__shfl_xor((int)m, 1, 64));
+                mrow[e] = max(m, (uint32_t)__shfl_xor((int)m, 2, 64));
+            }
+            const int xe0 = mrow[0] == 0 ? 0 : 14 - ((int)(mrow[0] >> 7) - 127);
+            const int xe1 = mrow[1] == 0 ? 0 : 14 - ((int)(mrow[1] >> 7) - 127);
+            if (pq == 0) {
+                sm.xexp[pair * 2] = xe0;
+                sm.xexp[pair * 2 + 1] = xe1;
+            }
+            const float s0 = ldexpf(1.0f, xe0), s1 = ldexpf(1.0f, xe1);
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const uint32_t a = xr[0][k >> 3][(k >> 1) & 3];
+                const uint32_t b = xr[1][k >> 3][(k >> 1) & 3];
+                const float lo = __uint_as_float((k & 1) ? (a & 0xFFFF0000u) : (a << 16));
+                const float hi = __uint_as_float((k & 1) ? (b & 0xFFFF0000u) : (b << 16));
+                sm.xt[(pq * 16 + k) * XT_STRIDE + pair] = pack_f16x2(lo * s0, hi * s1);
+            }
+        }
+        __syncthreads();
+        if (hh + 1 < HB) load_head(h + 1);  // next head's inputs in flight during this head's products
 
-    // ---- diagonal block: (2^smx M 2^-xe) (2^xe x), M from the C.B^T tiles
-    const int i_a = 32 * rb + l32;  // this lane's row in the A layout
-    const float cs_i = sm.cs2[i_a];
-    const float u = fast_exp2(cs_i - sm.cs2[32 * rb]) * m_scale;
+        // ---- decay tables and the bound on |M|
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        if (t <= rb) {
-            const f32x16 gv = gt[t & 1];
-            if (t + 2 <= rb) gt[t & 1] = load_tile(cbt + (t + 2) * 1024);
-            float mv[16];
-            if (t < rb) {
+        for (int it = 0; it < 8 * kChunk / kThreads; ++it) {
+            const int e = tid + it * kThreads;
+            const int r = e >> 8;
+            const int j = e & 255;
+            float val = 0.f;
+            if (j < 32 * r) val = ldexpf(fast_exp2(sm.cs2[32 * r] - sm.cs2[j]) * sm.dts[j], -sm.xexp[j]);
+            sm.v[e] = val;
+        }
+        float wmax = 0.f, emax = 0.f;
+        if (tid < kChunk) {
+            emax = ldexpf(1.0f, -sm.xexp[tid]);
+            wmax = sm.dts[tid] * emax;
+            sm.wx[tid] = wmax;
+            wmax = fabsf(wmax);
+        }
+        wmax = wave_max(wmax);
+        emax = wave_max(emax);
+        if (lane == 0) { sm.red[wave][0] = wmax; sm.red[wave][1] = emax; }
+
+        // ---- off-diagonal part: y^T_off = h_in (LDS) x C^T (registers)
+        f32x16 acc[2] = {f32x16{}, f32x16{}};
+        if (active) {
 #pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    const float4 v4 = *reinterpret_cast<const float4 *>(sm.v + rb * kChunk + 32 * t + 8 * a + 4 * hl);
-                    mv[4 * a + 0] = gv[4 * a + 0] * (v4.x * u);
-                    mv[4 * a + 1] = gv[4 * a + 1] * (v4.y * u);
-                    mv[4 * a + 2] = gv[4 * a + 2] * (v4.z * u);
-                    mv[4 * a + 3] = gv[4 * a + 3] * (v4.w * u);
-                }
-            } else {
+            for (int k = 0; k < KS; ++k) {
+                const f16x8 cf = __builtin_bit_cast(f16x8, cq[k]);
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int j = 32 * t + 8 * (e >> 2) + 4 * hl + (e & 3);
-                    float val = gv[e] * fast_exp2(cs_i - sm.cs2[j]) * sm.dts[j];
-                    if (j == i_a) val += dh;
-                    mv[e] = j <= i_a ? ldexpf(val, smx - sm.xexp[j]) : 0.f;
+                for (int pt = 0; pt < 2; ++pt) {
+                    const f16x8 hf = __builtin_bit_cast(
+                        f16x8, *reinterpret_cast<const u32x4 *>(sm.h + (32 * pt + l32) * H_STRIDE + 8 * k + 4 * hl));
+                    acc[pt] = mfma32_f16(hf, cf, acc[pt]);
                 }
             }
-            const f16x8 mf0 = __builtin_bit_cast(f16x8, u32x4{pack_f16x2(mv[0], mv[1]), pack_f16x2(mv[2], mv[3]),
-                                                              pack_f16x2(mv[4], mv[5]), pack_f16x2(mv[6], mv[7])});
-            const f16x8 mf1 = __builtin_bit_cast(f16x8, u32x4{pack_f16x2(mv[8], mv[9]), pack_f16x2(mv[10], mv[11]),
-                                                              pack_f16x2(mv[12], mv[13]), pack_f16x2(mv[14], mv[15])});
+        }
+        __syncthreads();  // tables and red[] complete
+        wmax = fmaxf(fmaxf(sm.red[0][0], sm.red[1][0]), fmaxf(sm.red[2][0], sm.red[3][0]));
+        emax = fmaxf(fmaxf(sm.red[0][1], sm.red[1][1]), fmaxf(sm.red[2][1], sm.red[3][1]));
+        if (!active) continue;  // wavefront-uniform; no barrier before the next head's
+        // |2^-xe M| <= |G| * max(dts 2^-xe) * (decay <= 1, or the chunk's total
+        // growth when A > 0) + |D| max(2^-xe) on the diagonal, with
+        // |G| < 2^(15 - sg) from the tiles' scaling
+        const float gbound = ldexpf(1.0f, 15 - sg);
+        const float dgrow = fast_exp2(fmaxf(0.f, sm.cs2[kChunk - 1] - sm.cs2[0]));
+        const int smx = f16_scale_exponent(gbound * wmax * dgrow + fabsf(dh) * emax);
+        const float m_scale = ldexpf(1.0f, smx);
+        const float mg = ldexpf(1.0f, smx - sg);  // takes the fp16 tiles to the M scale
+        const float cs_i = sm.cs2[i_l];
+
+        // undo the C and h_in scalings, decay column i by exp2(cs2_i), move to the M scale
+        {
+            const float f = ldexpf(fast_exp2(cs_i), smx - sc);
 #pragma unroll
             for (int pt = 0; pt < 2; ++pt) {
-                const uint2 *row = reinterpret_cast<const uint2 *>(sm.xt + (32 * pt + l32) * XT_STRIDE + 16 * t + 2 * hl);
-                const uint2 xa = row[0], xb = row[2], xc = row[4], xd = row[6];
-                const f16x8 x0 = __builtin_bit_cast(f16x8, u32x4{xa.x, xa.y, xb.x, xb.y});
-                const f16x8 x1 = __builtin_bit_cast(f16x8, u32x4{xc.x, xc.y, xd.x, xd.y});
-                accy[pt] = mfma32_f16(mf0, x0, accy[pt]);
-                accy[pt] = mfma32_f16(mf1, x1, accy[pt]);
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const float4 s4 = *reinterpret_cast<const float4 *>(sm.hs + 32 * pt + 8 * a + 4 * hl);
+                    acc[pt][4 * a + 0] *= f * s4.x;
+                    acc[pt][4 * a + 1] *= f * s4.y;
+                    acc[pt][4 * a + 2] *= f * s4.z;
+                    acc[pt][4 * a + 3] *= f * s4.w;
+                }
             }
         }
-    }
 
-    // ---- back to unit scale, store bf16
-    const float inv = ldexpf(1.0f, -smx);
+        // ---- diagonal block: (2^xe x)^T (2^smx M 2^-xe)^T, M from the C.B^T tiles
+        const float u = fast_exp2(cs_i - sm.cs2[32 * rb]) * mg;
+        const float dx = dh * ldexpf(1.0f, -sm.xexp[i_l]) * m_scale;  // D on the diagonal
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const int i = 32 * rb + 8 * (e >> 2) + 4 * hl + (e & 3);
-        if (i < len) {
-            uint16_t *dst = p.y + ((t0 + i) * p.H + h) * kHeadDim + l32;
-            dst[0] = float_to_bf16_bits(accy[0][e] * inv);
-            dst[32] = float_to_bf16_bits(accy[1][e] * inv);
+        for (int t = 0; t < 8; ++t) {
+            if (t <= rb && 32 * t < len) {
+                const u32x4 *gp = reinterpret_cast<const u32x4 *>(sm.g) + (rb * (rb + 1) / 2 + t) * 128 + lane;
+                const u32x4 gt[2] = {gp[0], gp[64]};
+                float mv[16];
+                if (t < rb) {
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) {
+                        const float4 v4 = *reinterpret_cast<const float4 *>(sm.v + rb * kChunk + 32 * t + 8 * a + 4 * hl);
+                        const uint32_t w0 = gt[a >> 1][2 * (a & 1)], w1 = gt[a >> 1][2 * (a & 1) + 1];
+                        mv[4 * a + 0] = h2f(w0, 0) * (v4.x * u);
+                        mv[4 * a + 1] = h2f(w0, 1) * (v4.y * u);
+                        mv[4 * a + 2] = h2f(w1, 0) * (v4.z * u);
+                        mv[4 * a + 3] = h2f(w1, 1) * (v4.w * u);
+                    }
+                } else {
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) {
+                        const int j0 = 32 * t + 8 * a + 4 * hl;
+                        const float4 c4 = *reinterpret_cast<const float4 *>(sm.cs2 + j0);
+                        const float4 w4 = *reinterpret_cast<const float4 *>(sm.wx + j0);
+                        const float cj[4] = {c4.x, c4.y, c4.z, c4.w};
+                        const float wj[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) {
+                            const int j = j0 + b;
+                            const uint32_t w = gt[a >> 1][2 * (a & 1) + (b >> 1)];
+                            float val = h2f(w, b & 1) * fast_exp2(cs_i - cj[b]) * wj[b] * mg;
+                            if (j == i_l) val += dx;
+                            mv[4 * a + b] = j <= i_l ? val : 0.f;
+                        }
+                    }
+                }
+                const f16x8 mf0 = __builtin_bit_cast(f16x8, u32x4{pack_f16x2(mv[0], mv[1]), pack_f16x2(mv[2], mv[3]),
+                                                                  pack_f16x2(mv[4], mv[5]), pack_f16x2(mv[6], mv[7])});
+                const f16x8 mf1 = __builtin_bit_cast(f16x8, u32x4{pack_f16x2(mv[8], mv[9]), pack_f16x2(mv[10], mv[11]),
+                                                                  pack_f16x2(mv[12], mv[13]), pack_f16x2(mv[14], mv[15])});
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt) {
+                    const uint2 *row = reinterpret_cast<const uint2 *>(sm.xt + (32 * pt + l32) * XT_STRIDE + 16 * t + 2 * hl);
+                    const uint2 xa = row[0], xb = row[2], xc = row[4], xd = row[6];
+                    const f16x8 x0 = __builtin_bit_cast(f16x8, u32x4{xa.x, xa.y, xb.x, xb.y});
+                    const f16x8 x1 = __builtin_bit_cast(f16x8, u32x4{xc.x, xc.y, xd.x, xd.y});
+                    acc[pt] = mfma32_f16(x0, mf0, acc[pt]);
+                    acc[pt] = mfma32_f16(x1, mf1, acc[pt]);
+                }
+            }
+        }
+
+        // ---- back to unit scale, store bf16: 4 consecutive p of token i_l per 8-byte write
+        if (i_l < len) {
+            const float inv = ldexpf(1.0f, -smx);
+            uint16_t *dst = p.y + ((t0 + i_l) * p.H + h) * kHeadDim + 4 * hl;
+#pragma unroll
+            for (int pt = 0; pt < 2; ++pt) {
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    uint2 v;
+                    v.x = pack_bf16x2(acc[pt][4 * a] * inv, acc[pt][4 * a + 1] * inv);
+                    v.y = pack_bf16x2(acc[pt][4 * a + 2] * inv, acc[pt][4 * a + 3] * inv);
+                    *reinterpret_cast<uint2 *>(dst + 32 * pt + 8 * a) = v;
+                }
+            }
         }
     }
 }
 
+// Heads per workgroup: the largest of 8, 4, 2, 1 that divides the heads of a
+// group and still gives at least two workgroups per compute unit.
+static int heads_per_block(const Params &p) {
+    const int hg = p.H / p.G;
+    const int64_t chunks = (p.nchunks_max + 7) / 8 * 8;
+    for (int hb = 8; hb > 1; hb /= 2)
+        if (hg % hb == 0 && chunks * (p.H / hb) >= 2 * (int64_t)p.num_cus) return hb;
+    return 1;
+}
+
+template <int N, int HB>
+static hipError_t launch_nh(const Params &p, hipStream_t s) {
+    const int64_t slots = (p.nchunks_max + 7) / 8 * (p.H / HB);
+    hipLaunchKernelGGL((ssd_chunk_scan_kernel<N, HB>), dim3((unsigned)(slots * 8)), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
 template <int N>
 static hipError_t launch_n(const Params &p, hipStream_t s) {
-    const int64_t slots = (p.nchunks_max + 7) / 8 * p.H;
-    hipLaunchKernelGGL(ssd_chunk_scan_kernel<N>, dim3((unsigned)(slots * 8)), dim3(kThreads), 0, s, p);
-    return hipGetLastError();
+    switch (heads_per_block(p)) {
+    case 8: return launch_nh<N, 8>(p, s);
+    case 4: return launch_nh<N, 4>(p, s);
+    case 2: return launch_nh<N, 2>(p, s);
+    default: return launch_nh<N, 1>(p, s);
+    }
 }
 
 hipError_t launch_chunk_scan(const Params &p, hipStream_t s) {

@@ -11,55 +11,69 @@
 // v_mfma_f32_32x32x16_f16 (fp32 accumulate).  Precision: the weighted operand
 // w_j * x is not exact in 16 bits; fp16 (11-bit significand) keeps the
 // final-state error near 2e-4 where bf16 (8 bits) would give about 1.6e-3.
-// Both operands are first scaled by exact powers of two (per chunk and head
-// for w*x, per chunk and group for B, from the prep step) so their maxima sit
-// in [2^14, 2^15), far from fp16 overflow.  S itself is stored as fp16 under
-// one power-of-two exponent per (chunk, head) (the net exponent of all
-// scalings, so the reader undoes them exactly); its rounding adds about 3e-4
-// relative error to the final states and halves the states traffic.
+// w*x is scaled by the power of two that puts its maximum (per chunk and
+// head) in [2^14, 2^15); B arrives from the prep step already converted under
+// its own power of two per chunk and group.  S itself is stored as fp16
+// under one power-of-two exponent per 32x32 tile of (chunk, head), the net
+// exponent of all scalings, so the reader undoes them exactly; its rounding
+// adds about 3e-4 relative error to the final states and halves the states
+// traffic.
 //
-// Work split: one workgroup = one chunk and HW heads of one group (B is
-// staged once for all of them), four wavefronts per head.  The weighted x of
-// each head is staged once in LDS, transposed to [p][token]; B is staged 32
-// tokens at a time, transposed to [n][token] (fp16 pairs of tokens per
-// dword), the next slice prefetched into registers.  16-byte LDS chunks of
-// rows 16..31 of every 32-row block are swapped pairwise so the 32 rows an
-// MFMA operand reads fall on distinct banks.
+// Work split: one workgroup = one chunk and a block of HB heads of one group.
+// The products are formed transposed, S^T[n][p] = sum_j B^T[n][j] (w_j
+// x_j[p]); each wavefront owns one n tile and one or both p tiles, and keeps
+// the B^T fragments of its n tile (16 K-steps of 16 tokens, from the prep
+// step's token-contiguous fp16 copy) in registers while the workgroup walks
+// its heads, so B is read once per block of heads.  Each head's weighted x is
+// staged in LDS, transposed to [p][token] (fp16 pairs of tokens per dword;
+// 16-byte chunks of rows 16..31 of every 32-row block swapped pairwise so the
+// 32 rows an MFMA operand reads fall on distinct banks); the next head's x,
+// dts and cs2 are loaded into registers during the current head's products.
+// Each lane ends up with 4 consecutive n of one p, stored as one 8-byte write.
 #include "ssd_common.hpp"
 
 namespace ssd {
 
 namespace {
 constexpr int XT_STRIDE = 132;  // dwords per x^T row: 128 token pairs + pad
-constexpr int BT_STRIDE = 20;   // dwords per B^T row: 16 token pairs + pad
 
 // dword index of 16-byte chunk `q4` (in dwords, a multiple of 4) of row r
 __device__ __forceinline__ int swz(int r, int q4) { return q4 ^ (((r >> 4) & 1) << 2); }
+
+template <int N>
+struct StateShape {
+    static constexpr int NT = N / 32;                      // n tiles
+    static constexpr int WAVES = 2 * NT < 8 ? 2 * NT : 8;  // 4 for dstate 64, else 8
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int PTW = WAVES == NT ? 2 : 1;        // p tiles per wavefront
+    static constexpr int PQ = THREADS / 128;               // threads per token pair (p parts)
+    static constexpr int PPT = kHeadDim / PQ;              // p values per thread in staging
+};
 }  // namespace
 
-template <int N, int HW>
-__global__ __launch_bounds__(256 * HW) void ssd_chunk_state_kernel(Params p) {
-    constexpr int kThreads = 256 * HW;
-    constexpr int NT = N / 32;      // 32-wide n tiles
-    constexpr int TPW = NT / 2;     // n tiles per wavefront (two p tiles x NT n tiles over 4 waves)
-    constexpr int ITEMS = 16 * (N / 8);  // (token pair, 8-wide n chunk) items per B slice
+template <int N, int HB>
+__global__ __launch_bounds__(StateShape<N>::THREADS) void ssd_chunk_state_kernel(Params p) {
+    using S = StateShape<N>;
+    constexpr int kThreads = S::THREADS;
+    constexpr int kWaves = S::WAVES;
+    constexpr int PTW = S::PTW;
+    constexpr int PPT = S::PPT;
+    constexpr int XV = PPT / 8;  // 16-byte x vectors per token per thread
 
-    __shared__ float s_w[HW][kChunk];
-    __shared__ float s_red[HW][4];
-    __shared__ __attribute__((aligned(16))) uint32_t s_xt[HW][kHeadDim * XT_STRIDE];
-    __shared__ __attribute__((aligned(16))) uint32_t s_bt[N * BT_STRIDE];
+    __shared__ float s_red[kWaves];
+    __shared__ __attribute__((aligned(16))) uint32_t s_xt[kHeadDim * XT_STRIDE];
 
-    const int nhg = p.H / HW;
+    const int nhb = p.H / HB;
     const int id = blockIdx.x;
     const int xcd = id & 7;
     const int slot = id >> 3;
-    const int c = (slot / nhg) * 8 + xcd;
-    const int hg = slot - (slot / nhg) * nhg;
+    const int c = (slot / nhb) * 8 + xcd;
+    const int hb = slot - (slot / nhb) * nhb;
     if (c >= p.meta[0]) return;
     const int4 dsc = p.desc[c];
     const int64_t t0 = dsc.y;
     const int len = dsc.z;
-    const int h_first = hg * HW;
+    const int h_first = hb * HB;
     const int g = h_first / (p.H / p.G);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -67,170 +81,153 @@ __global__ __launch_bounds__(256 * HW) void ssd_chunk_state_kernel(Params p) {
     const int l32 = lane & 31;
     const int hl = lane >> 5;
     const int sb = p.bexp[(int64_t)c * p.G + g];
-    const float b_scale = ldexpf(1.0f, sb);
+    const int nks = (len + 15) / 16;  // K-steps of 16 tokens
 
-    // ---- weights w_j = exp2(cs2_last - cs2_j) * dts_j  (0 past the chunk end)
-    for (int e = tid; e < HW * kChunk; e += kThreads) {
-        const int hh = e >> 8, j = e & 255;
-        const int64_t crow = ((int64_t)c * p.H + h_first + hh) * kChunk;
-        s_w[hh][j] = exp2f(p.cs2[crow + kChunk - 1] - p.cs2[crow + j]) * p.dts[crow + j];
-    }
-    __syncthreads();
+    // this wavefront's tiles: n tile nt, p tiles pt0 .. pt0+PTW-1
+    const int nt = wave % S::NT;
+    const int pt0 = PTW == 2 ? 0 : wave / S::NT;
 
-    // ---- weighted x: thread = (head, half of p, token pair); max magnitude per head
-    const int xh = tid >> 8;
-    const int pair = tid & 127;
-    const int ph = (tid >> 7) & 1;
+    // ---- B^T fragments of n tile nt: row n = 32 nt + l32, tokens 16 k + 8 hl .. +8
+    u32x4 bq[16];
     {
-        float xv[2][32];
-        float mloc = 0.0f;
+        const uint16_t *bt = p.bt16 + (((int64_t)c * p.G + g) * N + 32 * nt + l32) * kChunk + 8 * hl;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) bq[k] = *reinterpret_cast<const u32x4 *>(bt + 16 * k);
+    }
+
+    // ---- per-head inputs: thread = (p part, token pair)
+    const int pair = tid & 127;
+    const int pp = tid >> 7;  // p part: p = pp * PPT ..
+    u32x4 xr[2][XV];
+    float cs_tok[2], dt_tok[2], cs_last;
+    auto load_head = [&](int h) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int j = pair * 2 + e;
-            const float w = s_w[xh][j];
-            if (j < len) {
-                const u32x4 *src = reinterpret_cast<const u32x4 *>(
-                    p.x + ((t0 + j) * p.H + h_first + xh) * kHeadDim + ph * 32);
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(
+                p.x + ((t0 + min(j, len - 1)) * p.H + h) * kHeadDim + pp * PPT);
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const u32x4 qv = src[v];
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        xv[e][v * 8 + 2 * k] = w * __uint_as_float(qv[k] << 16);
-                        xv[e][v * 8 + 2 * k + 1] = w * __uint_as_float(qv[k] & 0xFFFF0000u);
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int k = 0; k < 32; ++k) xv[e][k] = 0.0f;
-            }
-#pragma unroll
-            for (int k = 0; k < 32; ++k) mloc = fmaxf(mloc, fabsf(xv[e][k]));
-        }
-        mloc = wave_max(mloc);
-        if (lane == 0) s_red[xh][(wave & 3)] = mloc;
-        __syncthreads();
-        const float mx = fmaxf(fmaxf(s_red[xh][0], s_red[xh][1]), fmaxf(s_red[xh][2], s_red[xh][3]));
-        const float xs = ldexpf(1.0f, f16_scale_exponent(mx));
-#pragma unroll
-        for (int k = 0; k < 32; ++k) {
-            const int row = ph * 32 + k;
-            // token pair `pair` sits in 16-byte chunk pair/4 of the row
-            s_xt[xh][row * XT_STRIDE + swz(row, (pair >> 2) << 2) + (pair & 3)] =
-                pack_f16x2(xv[0][k] * xs, xv[1][k] * xs);
-        }
-    }
-    const float mx_own = fmaxf(fmaxf(s_red[wave >> 2][0], s_red[wave >> 2][1]),
-                               fmaxf(s_red[wave >> 2][2], s_red[wave >> 2][3]));
-    const int sx_own = f16_scale_exponent(mx_own);
-
-    // ---- B^T staging: item = (8-wide n chunk, token pair); 4 lanes cover 4 n chunks
-    auto load_b = [&](int ks, u32x4 (&r)[2][(ITEMS + kThreads - 1) / kThreads]) {
-#pragma unroll
-        for (int it = 0; it < (ITEMS + kThreads - 1) / kThreads; ++it) {
-            const int item = tid + it * kThreads;
-            const int tp = (item >> 2) & 15;
-            const int nc = ((item >> 6) << 2) | (item & 3);
-            r[0][it] = r[1][it] = u32x4{0u, 0u, 0u, 0u};
-            if (item < ITEMS) {
-                const int j = ks * 32 + 2 * tp;
-                if (j < len)
-                    r[0][it] = *reinterpret_cast<const u32x4 *>(p.B + ((t0 + j) * p.G + g) * N + nc * 8);
-                if (j + 1 < len)
-                    r[1][it] = *reinterpret_cast<const u32x4 *>(p.B + ((t0 + j + 1) * p.G + g) * N + nc * 8);
-            }
+            for (int v = 0; v < XV; ++v) xr[e][v] = src[v];
+            const int64_t crow = ((int64_t)c * p.H + h) * kChunk;
+            cs_tok[e] = p.cs2[crow + j];
+            dt_tok[e] = p.dts[crow + j];  // 0 past the chunk end
+            cs_last = p.cs2[crow + kChunk - 1];
         }
     };
-    auto store_b = [&](const u32x4 (&r)[2][(ITEMS + kThreads - 1) / kThreads]) {
+    load_head(h_first);
+
+    for (int hh = 0; hh < HB; ++hh) {
+        const int h = h_first + hh;
 #pragma unroll
-        for (int it = 0; it < (ITEMS + kThreads - 1) / kThreads; ++it) {
-            const int item = tid + it * kThreads;
-            if (item < ITEMS) {
-                const int tp = (item >> 2) & 15;
-                const int nc = ((item >> 6) << 2) | (item & 3);
+        for (int k = 0; k < 16; ++k) asm volatile("" : "+v"(bq[k]));
+
+        // ---- weighted x, its maximum magnitude over the chunk and head
+        float xv[2][PPT];
+        float mloc = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const float w = fast_exp2(cs_last - cs_tok[e]) * dt_tok[e];
+#pragma unroll
+            for (int v = 0; v < XV; ++v)
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    const float a0 = __uint_as_float(r[0][it][k] << 16) * b_scale;
-                    const float a1 = __uint_as_float(r[0][it][k] & 0xFFFF0000u) * b_scale;
-                    const float c0 = __uint_as_float(r[1][it][k] << 16) * b_scale;
-                    const float c1 = __uint_as_float(r[1][it][k] & 0xFFFF0000u) * b_scale;
-                    const int n0 = nc * 8 + 2 * k;
-                    s_bt[n0 * BT_STRIDE + swz(n0, (tp >> 2) << 2) + (tp & 3)] = pack_f16x2(a0, c0);
-                    s_bt[(n0 + 1) * BT_STRIDE + swz(n0 + 1, (tp >> 2) << 2) + (tp & 3)] = pack_f16x2(a1, c1);
+                    xv[e][v * 8 + 2 * k] = w * __uint_as_float(xr[e][v][k] << 16);
+                    xv[e][v * 8 + 2 * k + 1] = w * __uint_as_float(xr[e][v][k] & 0xFFFF0000u);
+                }
+#pragma unroll
+            for (int k = 0; k < PPT; ++k) mloc = fmaxf(mloc, fabsf(xv[e][k]));
+        }
+        if (hh + 1 < HB) load_head(h + 1);  // next head's inputs in flight from here on
+        mloc = wave_max(mloc);
+        __syncthreads();  // the previous head's x^T and s_red reads are done
+        if (lane == 0) s_red[wave] = mloc;
+        __syncthreads();
+        float mx = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, s_red[w]);
+        const int sx = f16_scale_exponent(mx);
+        const float xs = ldexpf(1.0f, sx);
+#pragma unroll
+        for (int k = 0; k < PPT; ++k) {
+            const int row = pp * PPT + k;
+            // token pair `pair` sits in 16-byte chunk pair/4 of the row
+            s_xt[row * XT_STRIDE + swz(row, (pair >> 2) << 2) + (pair & 3)] =
+                pack_f16x2(xv[0][k] * xs, xv[1][k] * xs);
+        }
+        __syncthreads();
+
+        // ---- S^T tiles: rows n (tile nt), columns p (tiles pt0..)
+        f32x16 acc[PTW];
+#pragma unroll
+        for (int u = 0; u < PTW; ++u) acc[u] = f32x16{};
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            if (k < nks) {
+                const f16x8 bf = __builtin_bit_cast(f16x8, bq[k]);
+#pragma unroll
+                for (int u = 0; u < PTW; ++u) {
+                    const int xrow = (pt0 + u) * 32 + l32;
+                    const f16x8 xf = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4 *>(
+                        s_xt + xrow * XT_STRIDE + swz(xrow, 8 * k + 4 * hl)));
+                    acc[u] = mfma32_f16(bf, xf, acc[u]);
                 }
             }
         }
-    };
 
-    // tiles of this wavefront: p tile pt, n tiles nt0 .. nt0+TPW-1
-    const int wl = wave & 3;
-    const int pt = (wl * TPW) / NT;
-    const int nt0 = (wl * TPW) % NT;
-    f32x16 acc[TPW];
+        // ---- store S[c][h][p][n] as fp16, one power-of-two exponent per tile:
+        // the accumulator is 2^(sx+sb) S; rescale so that the tile's max |S|
+        // lands in [2^14, 2^15) (relative rounding 2^-11 per element)
+        uint16_t *dst = p.states + ((int64_t)c * p.H + h) * kHeadDim * N;
+        int32_t *sexp = p.sexp + ((int64_t)c * p.H + h) * 2 * S::NT;
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) acc[u] = f32x16{};
-
-    u32x4 br[2][(ITEMS + kThreads - 1) / kThreads];
-    const int nslices = (len + 31) / 32;
-    load_b(0, br);
-    for (int ks = 0; ks < nslices; ++ks) {
-        __syncthreads();  // previous slice consumed (and x^T written)
-        store_b(br);
-        if (ks + 1 < nslices) load_b(ks + 1, br);
-        __syncthreads();
+        for (int u = 0; u < PTW; ++u) {
+            float am = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const int arow = pt * 32 + l32;
-            const f16x8 af = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4 *>(
-                s_xt[wave >> 2] + arow * XT_STRIDE + swz(arow, ks * 16 + kk * 8 + hl * 4)));
+            for (int e = 0; e < 16; ++e) am = fmaxf(am, fabsf(acc[u][e]));
+            am = wave_max(am);
+            const int se = f16_scale_exponent(am);  // stored S = 2^se * acc = 2^(se + sx + sb) S
+            const float rescale = ldexpf(1.0f, se);
+            const int pt = pt0 + u;
+            if (lane == 0) sexp[pt * S::NT + nt] = se + sx + sb;
+            uint16_t *row = dst + (int64_t)(pt * 32 + l32) * N;
 #pragma unroll
-            for (int u = 0; u < TPW; ++u) {
-                const int brow = (nt0 + u) * 32 + l32;
-                const f16x8 bf = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4 *>(
-                    s_bt + brow * BT_STRIDE + swz(brow, kk * 8 + hl * 4)));
-                acc[u] = mfma32_f16(af, bf, acc[u]);
+            for (int a = 0; a < 4; ++a) {
+                const int n = nt * 32 + 8 * a + 4 * hl;
+                uint2 v;
+                v.x = pack_f16x2(acc[u][4 * a] * rescale, acc[u][4 * a + 1] * rescale);
+                v.y = pack_f16x2(acc[u][4 * a + 2] * rescale, acc[u][4 * a + 3] * rescale);
+                *reinterpret_cast<uint2 *>(row + n) = v;
             }
-        }
-    }
-
-    // ---- store S[c][h][p][n] as fp16 with one power-of-two exponent per
-    // (chunk, head): the accumulator is 2^(sx+sb) S; rescale it so that
-    // max |S| lands in [2^14, 2^15) (relative rounding 2^-11 per element).
-    float am = 0.f;
-#pragma unroll
-    for (int u = 0; u < TPW; ++u)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) am = fmaxf(am, fabsf(acc[u][e]));
-    am = wave_max(am);
-    __syncthreads();  // all s_red reads above are done
-    if (lane == 0) s_red[wave >> 2][wave & 3] = am;
-    __syncthreads();
-    const float amax = fmaxf(fmaxf(s_red[wave >> 2][0], s_red[wave >> 2][1]),
-                             fmaxf(s_red[wave >> 2][2], s_red[wave >> 2][3]));
-    const int se = f16_scale_exponent(amax);  // stored S = 2^se * acc = 2^(se + sx + sb) S
-    const float rescale = ldexpf(1.0f, se);
-    const int h_own = h_first + (wave >> 2);
-    if ((wave & 3) == 0 && lane == 0) p.sexp[(int64_t)c * p.H + h_own] = se + sx_own + sb;
-    uint16_t *dst = p.states + ((int64_t)c * p.H + h_own) * kHeadDim * N;
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-        const int n = (nt0 + u) * 32 + l32;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int pp = pt * 32 + 8 * (e >> 2) + 4 * hl + (e & 3);
-            dst[pp * N + n] = __builtin_bit_cast(uint16_t, (_Float16)(acc[u][e] * rescale));
         }
     }
 }
 
+// Heads per workgroup: the largest of 8, 4, 2, 1 that divides the heads of a
+// group and still gives at least two workgroups per compute unit.
+static int state_heads_per_block(const Params &p) {
+    const int hg = p.H / p.G;
+    const int64_t chunks = (p.nchunks_max + 7) / 8 * 8;
+    for (int hb = 8; hb > 1; hb /= 2)
+        if (hg % hb == 0 && chunks * (p.H / hb) >= 2 * (int64_t)p.num_cus) return hb;
+    return 1;
+}
+
+template <int N, int HB>
+static hipError_t launch_nh(const Params &p, hipStream_t s) {
+    const int64_t slots = (p.nchunks_max + 7) / 8 * (p.H / HB);
+    hipLaunchKernelGGL((ssd_chunk_state_kernel<N, HB>), dim3((unsigned)(slots * 8)), dim3(StateShape<N>::THREADS), 0,
+                       s, p);
+    return hipGetLastError();
+}
+
 template <int N>
 static hipError_t launch_n(const Params &p, hipStream_t s) {
-    const int hw = ((p.H / p.G) % 2 == 0) ? 2 : 1;
-    const int64_t slots = (p.nchunks_max + 7) / 8 * (p.H / hw);
-    const dim3 grid((unsigned)(slots * 8));
-    if (hw == 2) hipLaunchKernelGGL((ssd_chunk_state_kernel<N, 2>), grid, dim3(512), 0, s, p);
-    else hipLaunchKernelGGL((ssd_chunk_state_kernel<N, 1>), grid, dim3(256), 0, s, p);
-    return hipGetLastError();
+    switch (state_heads_per_block(p)) {
+    case 8: return launch_nh<N, 8>(p, s);
+    case 4: return launch_nh<N, 4>(p, s);
+    case 2: return launch_nh<N, 2>(p, s);
+    default: return launch_nh<N, 1>(p, s);
+    }
 }
 
 hipError_t launch_chunk_state(const Params &p, hipStream_t s) {

@@ -16,7 +16,7 @@
 // no tokens writes its initial state (or zeros) back.
 //
 // Chunk contributions arrive as fp16 under one power-of-two exponent per
-// (chunk, head).  The chain is fp32.  h_in only feeds the outputs y; it is stored as fp16
+// 32x32 tile of (chunk, head).  The chain is fp32.  h_in only feeds the outputs y; it is stored as fp16
 // with one power-of-two scale per row p (11 significant bits: bf16's 8 would
 // put the off-diagonal part's rounding error near the tolerance of y).
 // Each thread owns four consecutive (p, n) elements of one (sequence, head),
@@ -49,7 +49,11 @@ __global__ __launch_bounds__(256) void ssd_state_passing_kernel(Params p) {
     float4 st = init ? *pool4 : make_float4(0.f, 0.f, 0.f, 0.f);
     const int64_t stride = (int64_t)p.H * head_elems;  // one chunk of states
     const uint16_t *S = p.states + ((int64_t)k0 * p.H + h) * head_elems + e0;
-    const int32_t *sexp = p.sexp + (int64_t)k0 * p.H + h;
+    // exponent of this thread's 32x32 tile (p / 32, n / 32) in each chunk
+    const int NT = p.N / 32;
+    const int tile = (int)((e0 / p.N) >> 5) * NT + (int)((e0 % p.N) >> 5);
+    const int32_t *sexp = p.sexp + ((int64_t)k0 * p.H + h) * 2 * NT + tile;
+    const int64_t sexp_stride = (int64_t)p.H * 2 * NT;
     const float *cs_last = p.cs2 + ((int64_t)k0 * p.H + h) * kChunk + kChunk - 1;
     const int64_t cs_stride = (int64_t)p.H * kChunk;
     uint16_t *hin = p.hin + ((int64_t)k0 * p.H + h) * head_elems + e0;
@@ -67,7 +71,7 @@ __global__ __launch_bounds__(256) void ssd_state_passing_kernel(Params p) {
         d[q] = 0.f;
         if (q < nk) {
             s[q] = *reinterpret_cast<const uint2 *>(S + q * stride);
-            se[q] = sexp[q * p.H];
+            se[q] = sexp[q * sexp_stride];
             d[q] = cs_last[q * cs_stride];
         }
     }
@@ -95,7 +99,7 @@ __global__ __launch_bounds__(256) void ssd_state_passing_kernel(Params p) {
                 st.w = dec * st.w + f16_bits_to_float(s[q].y >> 16) * us;
                 if (k + kDepth < nk) {  // refill this ring slot kDepth chunks ahead
                     s[q] = *reinterpret_cast<const uint2 *>(S + (int64_t)(k + kDepth) * stride);
-                    se[q] = sexp[(int64_t)(k + kDepth) * p.H];
+                    se[q] = sexp[(int64_t)(k + kDepth) * sexp_stride];
                     d[q] = cs_last[(int64_t)(k + kDepth) * cs_stride];
                 }
             }

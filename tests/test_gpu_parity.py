@@ -152,14 +152,19 @@ def test_intermediates_match_chunked_oracle():
     dts = w[L["dts"]:L["dts"] + ncm * H * 256 * 4].view(np.float32).reshape(ncm, H, 256)
     cs2 = w[L["cs2"]:L["cs2"] + ncm * H * 256 * 4].view(np.float32).reshape(ncm, H, 256)
     S16 = w[L["states"]:L["states"] + ncm * H * P * N * 2].view(np.float16).reshape(ncm, H, P, N)
-    sexp = w[L["sexp"]:L["sexp"] + ncm * H * 4].view(np.int32).reshape(ncm, H)
-    S = S16.astype(np.float64) * np.exp2(-sexp.astype(np.float64))[..., None, None]
-    cbt = w[L["cbt"]:L["cbt"] + ncm * 2 * 36 * 1024 * 4].view(np.float32).reshape(ncm, 2, 36, 64, 16)
+    sexp = w[L["sexp"]:L["sexp"] + ncm * H * 2 * (N // 32) * 4].view(np.int32).reshape(ncm, H, 2, N // 32)
+    sfac = np.exp2(-sexp.astype(np.float64)).repeat(32, axis=2).repeat(32, axis=3)  # per element (p, n)
+    S = S16.astype(np.float64) * sfac
+    cbt16 = w[L["cbt"]:L["cbt"] + ncm * 2 * 36 * 1024 * 2].view(np.float16).reshape(ncm, 2, 36, 64, 16)
+    gexp = w[L["gexp"]:L["gexp"] + ncm * 2 * 4].view(np.int32).reshape(ncm, 2)
+    cbt = cbt16.astype(np.float64) * np.exp2(-gexp.astype(np.float64))[..., None, None, None]
     hin16 = w[L["hin"]:L["hin"] + ncm * H * P * N * 2].view(np.float16).reshape(ncm, H, P, N)
     hexp = w[L["hexp"]:L["hexp"] + ncm * H * P * 4].view(np.int32).reshape(ncm, H, P)
     hin = hin16.astype(np.float64) * np.exp2(-hexp.astype(np.float64))[..., None]
     bexp = w[L["bexp"]:L["bexp"] + ncm * 2 * 4].view(np.int32).reshape(ncm, 2)
     cexp = w[L["cexp"]:L["cexp"] + ncm * 2 * 4].view(np.int32).reshape(ncm, 2)
+    cf16 = w[L["cf16"]:L["cf16"] + ncm * 2 * 256 * N * 2].view(np.float16).reshape(ncm, 2, 256, N)
+    bt16 = w[L["bt16"]:L["bt16"] + ncm * 2 * N * 256 * 2].view(np.float16).reshape(ncm, 2, N, 256)
     ref = chunked_scan(prob, 256, keep_intermediates=True)["chunks"]
     qsl = prob["query_start_loc"]
     for rec in ref:
@@ -183,15 +188,28 @@ def test_intermediates_match_chunked_oracle():
         GT[:l, :l] = Bc @ Cc.T  # G^T[j][i] = B_j . C_i
         lane = np.arange(64)[:, None]
         e = np.arange(16)[None, :]
+        gm = 0.0
         for rb in range(8):
             for t in range(rb + 1):
                 jj = 32 * t + 8 * (e // 4) + 4 * (lane // 32) + e % 4
                 ii = 32 * rb + lane % 32
-                np.testing.assert_allclose(cbt[c, g, rb * (rb + 1) // 2 + t], GT[jj, ii], rtol=1e-5, atol=1e-3)
+                np.testing.assert_allclose(cbt[c, g, rb * (rb + 1) // 2 + t], GT[jj, ii], rtol=2.0 ** -11,
+                                           atol=np.abs(GT).max() * 2.0 ** -24)
+                gm = max(gm, np.abs(GT[jj, ii]).max())
+        # the tiles' exponent puts their largest magnitude in [2^14, 2^15)
+        if gm > 0:
+            assert 2.0 ** 14 <= gm * 2.0 ** gexp[c, g] < 2.0 ** 15
         for arr, ex in (("B", bexp), ("C", cexp)):
             vals = prob[arr].reshape(T, 2, N)[t0:t0 + l, g]
             mx = np.max((vals.astype(np.uint32) << 16).view(np.float32).__abs__())
             assert 2.0 ** 14 <= mx * 2.0 ** ex[c, g] < 2.0 ** 15
+        # fp16 copies: C (token-major) and B^T (token-contiguous), scaled, zero past the chunk end
+        Cs = np.zeros((256, N))
+        Cs[:l] = Cc * 2.0 ** cexp[c, g]
+        Bs = np.zeros((N, 256))
+        Bs[:, :l] = Bc.T * 2.0 ** bexp[c, g]
+        np.testing.assert_allclose(cf16[c, g].astype(np.float64), Cs, rtol=2.0 ** -11, atol=2.0 ** -24 * 2.0 ** 15)
+        np.testing.assert_allclose(bt16[c, g].astype(np.float64), Bs, rtol=2.0 ** -11, atol=2.0 ** -24 * 2.0 ** 15)
 
 
 # --------------------------------------------------------------- invariants
