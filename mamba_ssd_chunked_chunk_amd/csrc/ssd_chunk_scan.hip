@@ -137,25 +137,34 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
     const int pair = tid >> 2;
     u32x4 hreg[HVEC];
     u32x4 xr[2][2];
+    // the head's table entries: token (tid & 255)'s cs2 and dts, row (tid & 63)'s
+    // h_in exponent, and D.  Plain unconditional loads, used only at the next
+    // staging, so they stay in flight during the current head's products.
+    float tab_cs = 0.f, tab_dt = 0.f, dh_next = 0.f;
+    int tab_hx = 0;
     auto load_head = [&](int h) {
+        const int64_t r = ((int64_t)c * p.H + h) * kChunk + (tid & (kChunk - 1));
+        tab_cs = p.cs2[r];
+        tab_dt = p.dts[r];
+        tab_hx = p.hexp[((int64_t)c * p.H + h) * kHeadDim + (tid & (kHeadDim - 1))];
+        dh_next = p.D ? p.D[h] : 0.0f;
         const uint16_t *hin_head = p.hin + ((int64_t)c * p.H + h) * kHeadDim * N;
 #pragma unroll
         for (int it = 0; it < HVEC; ++it)
             hreg[it] = *reinterpret_cast<const u32x4 *>(hin_head + (tid + it * kThreads) * 8);
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-            const int j = pair * 2 + e;
-            // rows past the chunk end read the last row and are zeroed (len >= 1)
-            const u32x4 *src = reinterpret_cast<const u32x4 *>(
-                p.x + ((t0 + min(j, len - 1)) * p.H + h) * kHeadDim + pq * 16);
-            const u32x4 a = src[0], b = src[1];
-            const bool ok = j < len;
-            xr[e][0] = ok ? a : u32x4{};
-            xr[e][1] = ok ? b : u32x4{};
+            // rows past the chunk end read the last row (len >= 1); they are
+            // zeroed when staged
+            const int j = min(pair * 2 + e, len - 1);
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(p.x + ((t0 + j) * p.H + h) * kHeadDim + pq * 16);
+            xr[e][0] = src[0];
+            xr[e][1] = src[1];
         }
     };
     load_head(h_first);
 
+#pragma unroll
     for (int hh = 0; hh < HB; ++hh) {
         const int h = h_first + hh;
         // keep the per-group operands opaque across heads, so values derived
@@ -173,15 +182,14 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
         const int i_l = 32 * rb + l32;
         const int pq = tid & 3;
         const int pair = tid >> 2;
-        const int64_t crow2 = ((int64_t)c * p.H + h) * kChunk;
         __syncthreads();  // the previous head's LDS reads are done
         if (tid < kChunk) {
-            sm.cs2[tid] = p.cs2[crow2 + tid];
-            sm.dts[tid] = p.dts[crow2 + tid];
+            sm.cs2[tid] = tab_cs;
+            sm.dts[tid] = tab_dt;
         } else if (tid < kChunk + kHeadDim) {
-            sm.hs[tid - kChunk] = ldexpf(1.0f, -p.hexp[((int64_t)c * p.H + h) * kHeadDim + (tid - kChunk)]);
+            sm.hs[tid - kChunk] = ldexpf(1.0f, -tab_hx);
         }
-        const float dh = p.D ? p.D[h] : 0.0f;
+        const float dh = dh_next;
 
         // ---- stage h_in and x^T (each x row scaled by its own 2^xe)
 #pragma unroll
@@ -194,6 +202,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
             uint32_t mrow[2];
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
+                if (pair * 2 + e >= len) xr[e][0] = xr[e][1] = u32x4{};  // past the chunk end
                 uint32_t m = 0;
 #pragma unroll
                 for (int a = 0; a < 2; ++a)

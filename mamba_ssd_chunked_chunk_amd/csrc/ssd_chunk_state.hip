@@ -81,7 +81,6 @@ __global__ __launch_bounds__(StateShape<N>::THREADS) void ssd_chunk_state_kernel
     const int l32 = lane & 31;
     const int hl = lane >> 5;
     const int sb = p.bexp[(int64_t)c * p.G + g];
-    const int nks = (len + 15) / 16;  // K-steps of 16 tokens
 
     // this wavefront's tiles: n tile nt, p tiles pt0 .. pt0+PTW-1
     const int nt = wave % S::NT;
@@ -116,6 +115,7 @@ __global__ __launch_bounds__(StateShape<N>::THREADS) void ssd_chunk_state_kernel
     };
     load_head(h_first);
 
+#pragma unroll
     for (int hh = 0; hh < HB; ++hh) {
         const int h = h_first + hh;
 #pragma unroll
@@ -160,17 +160,16 @@ __global__ __launch_bounds__(StateShape<N>::THREADS) void ssd_chunk_state_kernel
         f32x16 acc[PTW];
 #pragma unroll
         for (int u = 0; u < PTW; ++u) acc[u] = f32x16{};
+        // all 16 K-steps: both operands are zero past the chunk end
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
-            if (k < nks) {
-                const f16x8 bf = __builtin_bit_cast(f16x8, bq[k]);
+            const f16x8 bf = __builtin_bit_cast(f16x8, bq[k]);
 #pragma unroll
-                for (int u = 0; u < PTW; ++u) {
-                    const int xrow = (pt0 + u) * 32 + l32;
-                    const f16x8 xf = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4 *>(
-                        s_xt + xrow * XT_STRIDE + swz(xrow, 8 * k + 4 * hl)));
-                    acc[u] = mfma32_f16(bf, xf, acc[u]);
-                }
+            for (int u = 0; u < PTW; ++u) {
+                const int xrow = (pt0 + u) * 32 + l32;
+                const f16x8 xf = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4 *>(
+                    s_xt + xrow * XT_STRIDE + swz(xrow, 8 * k + 4 * hl)));
+                acc[u] = mfma32_f16(bf, xf, acc[u]);
             }
         }
 

@@ -134,10 +134,23 @@ __device__ __forceinline__ float wave_incl_scan(float v) {
     return v;
 }
 
+// Maximum over a 64-lane wavefront for values >= 0 (magnitudes), with DPP
+// row operations instead of LDS permutes: within rows of 16 lanes, then
+// across rows with the row broadcasts (lanes a DPP step leaves unwritten
+// contribute 0, which cannot raise a maximum of non-negative values); the
+// total lands in lane 63 and is read back as a uniform value.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_max_step(float v) {
+    return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, false)));
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
-    return v;
+    v = dpp_max_step<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+    v = dpp_max_step<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+    v = dpp_max_step<0x141, 0xF>(v);  // row_half_mirror
+    v = dpp_max_step<0x140, 0xF>(v);  // row_mirror
+    v = dpp_max_step<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v = dpp_max_step<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
