@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 3
+#define SSD_ABI_VERSION 5
 #define SSD_MAX_DSTATE 256  /* largest dstate, as in "mamba2_ssd_scan", comptime MAX_DSTATE */
 
 typedef enum ssd_status {
@@ -88,8 +88,6 @@ typedef struct ssd_problem {
  *   desc      int32[nchunks_max][4]       {sequence, first token, length, 0}
  *   dts       fp32[nchunks_max][H][256]   dts per token, 0 past the chunk end
  *   cs2       fp32[nchunks_max][H][256]   log2(e) * inclusive sum of A*dts
- *   bexp      int32[nchunks_max][G]       power-of-two exponent applied to B
- *   cexp      int32[nchunks_max][G]       power-of-two exponent applied to C
  *   cbt       fp16[nchunks_max][G][36][64][16]  G^T[j][i] = C_i . B_j of the
  *                                         chunk, as the 36 lower-triangular
  *                                         32x32 tiles (row block rb, column
@@ -99,10 +97,6 @@ typedef struct ssd_problem {
  *                                         + 4(l/32) + e%4, i = 32rb + l%32;
  *                                         scaled by 2^gexp[c][g]
  *   gexp      int32[nchunks_max][G]       exponent of each cbt block
- *   cf16      fp16[nchunks_max][G][256][N] C * 2^cexp of the chunk's tokens,
- *                                         rows past the chunk end zero
- *   bt16      fp16[nchunks_max][G][N][256] B^T * 2^bexp (token index
- *                                         contiguous), zero past the chunk end
  *   states    fp16[nchunks_max][H][P][N]  chunk's own state contribution,
  *                                         element (p, n) scaled by
  *                                         2^sexp[c][h][p/32][n/32]
@@ -113,7 +107,7 @@ typedef struct ssd_problem {
 typedef struct ssd_workspace_layout {
     size_t total_bytes;
     int64_t nchunks_max;
-    size_t meta, chunk_off, desc, dts, cs2, bexp, cexp, cbt, gexp, cf16, bt16, states, sexp, hin, hexp;
+    size_t meta, chunk_off, desc, dts, cs2, cbt, gexp, states, sexp, hin, hexp;
 } ssd_workspace_layout;
 
 /* ABI version of the loaded library (SSD_ABI_VERSION it was built with). */

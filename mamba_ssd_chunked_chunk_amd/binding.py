@@ -45,9 +45,7 @@ class ssd_workspace_layout(ctypes.Structure):
     _fields_ = [("total_bytes", ctypes.c_size_t), ("nchunks_max", ctypes.c_int64),
                 ("meta", ctypes.c_size_t), ("chunk_off", ctypes.c_size_t),
                 ("desc", ctypes.c_size_t), ("dts", ctypes.c_size_t), ("cs2", ctypes.c_size_t),
-                ("bexp", ctypes.c_size_t), ("cexp", ctypes.c_size_t), ("cbt", ctypes.c_size_t), ("gexp", ctypes.c_size_t),
-                ("cf16", ctypes.c_size_t), ("bt16", ctypes.c_size_t),
-                ("states", ctypes.c_size_t), ("sexp", ctypes.c_size_t),
+                ("cbt", ctypes.c_size_t), ("gexp", ctypes.c_size_t), ("states", ctypes.c_size_t), ("sexp", ctypes.c_size_t),
                 ("hin", ctypes.c_size_t), ("hexp", ctypes.c_size_t)]
 
 
@@ -55,7 +53,7 @@ _lock = threading.Lock()
 _lib = None
 
 # SSD_ABI_VERSION of include/ssd.h that the ctypes structures below mirror
-ABI_VERSION = 3
+ABI_VERSION = 5
 
 
 def load_library():

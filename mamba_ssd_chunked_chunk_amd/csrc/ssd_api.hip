@@ -47,12 +47,8 @@ void layout_of(const ssd_problem *p, ssd_workspace_layout *L) {
     L->desc = off;      off = align_up(off + (size_t)ncm * 4 * sizeof(int32_t));
     L->dts = off;       off = align_up(off + (size_t)ncm * H * ssd::kChunk * sizeof(float));
     L->cs2 = off;       off = align_up(off + (size_t)ncm * H * ssd::kChunk * sizeof(float));
-    L->bexp = off;      off = align_up(off + (size_t)ncm * G * sizeof(int32_t));
-    L->cexp = off;      off = align_up(off + (size_t)ncm * G * sizeof(int32_t));
     L->cbt = off;       off = align_up(off + (size_t)ncm * G * 36 * 64 * 16 * sizeof(uint16_t));
     L->gexp = off;      off = align_up(off + (size_t)ncm * G * sizeof(int32_t));
-    L->cf16 = off;      off = align_up(off + (size_t)ncm * G * ssd::kChunk * (size_t)p->dstate * sizeof(uint16_t));
-    L->bt16 = off;      off = align_up(off + (size_t)ncm * G * ssd::kChunk * (size_t)p->dstate * sizeof(uint16_t));
     L->states = off;    off = align_up(off + (size_t)ncm * H * PN * sizeof(uint16_t));
     L->sexp = off;      off = align_up(off + (size_t)ncm * H * 2 * ((size_t)p->dstate / 32) * sizeof(int32_t));
     L->hin = off;       off = align_up(off + (size_t)ncm * H * PN * sizeof(uint16_t));
@@ -162,13 +158,9 @@ static ssd_status run_scan(
     p.desc = reinterpret_cast<int4 *>(ws + L.desc);
     p.dts = reinterpret_cast<float *>(ws + L.dts);
     p.cs2 = reinterpret_cast<float *>(ws + L.cs2);
-    p.bexp = reinterpret_cast<int32_t *>(ws + L.bexp);
-    p.cexp = reinterpret_cast<int32_t *>(ws + L.cexp);
     p.hexp = reinterpret_cast<int32_t *>(ws + L.hexp);
     p.cbt = reinterpret_cast<uint16_t *>(ws + L.cbt);
     p.gexp = reinterpret_cast<int32_t *>(ws + L.gexp);
-    p.cf16 = reinterpret_cast<uint16_t *>(ws + L.cf16);
-    p.bt16 = reinterpret_cast<uint16_t *>(ws + L.bt16);
     p.states = reinterpret_cast<uint16_t *>(ws + L.states);
     p.sexp = reinterpret_cast<int32_t *>(ws + L.sexp);
     p.hin = reinterpret_cast<uint16_t *>(ws + L.hin);

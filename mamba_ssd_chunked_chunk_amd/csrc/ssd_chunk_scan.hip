@@ -16,9 +16,11 @@
 // eight wavefronts, one 32-row block each; the two wavefronts that share a
 // SIMD own row blocks k and 7-k, so each SIMD handles 9 of the 36
 // lower-triangular 32x32 tiles.  The operands the heads of a group share,
-// the wavefront's C rows (registers) and its C.B^T tiles (LDS), are loaded
-// once and stay on chip while the workgroup walks its heads; each head's x
-// and h_in are loaded into registers during the previous head's products.  Workgroups
+// the wavefront's C rows (registers, converted here to fp16 under a
+// per-wavefront power of two) and its C.B^T tiles (from the prep step, LDS),
+// are loaded once and stay on chip while the workgroup walks its heads; each
+// head's x and h_in are loaded into registers during the previous head's
+// products.  Workgroups
 // are numbered so that all head blocks of a chunk land on one XCD (dispatch
 // is round-robin over the 8 XCDs) and share C and the tiles in its L2.
 // Row blocks that start past the chunk end skip their products.
@@ -26,13 +28,11 @@
 // MFMA layout (v_mfma_f32_32x32x16).  Every product is formed transposed,
 // y^T[p][i], so each lane ends up with 4 consecutive p of one token i (one
 // 8-byte store of 4 bf16) and the per-token factors are per-lane scalars.
-// C.B^T is stored transposed (rows j, columns i) in accumulator order, so a
-// tile's 16 values per lane (all at one i, at j = 8a + 4(l/32) + b) are
-// directly the B-operand layout of M^T for x^T*M^T: the 16 j of the first
-// K-step are {0..3, 8..11} for lanes 0-31 and {4..7, 12..15} for lanes 32-63
-// (a permutation of 0..15), likewise 16..31 for the second; x^T is read from
-// LDS in the same order.  C comes as the prep step's fp16 copy (scaled,
-// zero past the chunk end), one 16-byte load per lane and K-step.
+// C.B^T is stored transposed (rows j, columns i) in accumulator order, so a tile's 16 values per lane (all at one i, at j = 8a + 4(l/32) +
+// b) are directly the B-operand layout of M^T for x^T*M^T: the 16 j of the
+// first K-step are {0..3, 8..11} for lanes 0-31 and {4..7, 12..15} for lanes
+// 32-63 (a permutation of 0..15), likewise 16..31 for the second; x^T is read
+// from LDS in the same order.
 //
 // Decay without one exp2 per element.  For a tile strictly below the
 // diagonal block (all j < 32*rb <= i), exp2(cs2_i - cs2_j) =
@@ -43,8 +43,8 @@
 //
 // Precision.  M and h_in are rounded to fp16 (11-bit significand) under
 // power-of-two scales that keep them far from overflow (one per head for M,
-// one per row for h_in); C and C.B^T were rounded to fp16 after power-of-two
-// scalings per (chunk, group), and each x row is converted after its own
+// one per row for h_in); C and C.B^T are rounded to fp16 after power-of-two
+// scalings (per row block, per chunk and group), and each x row is converted after its own
 // power-of-two scaling, compensated inside M.  All products accumulate in
 // fp32.  bf16 (8 bits) for M or h_in would put the rounding error, which
 // scales with the typical size of y rather than with each y, close to the
@@ -108,19 +108,24 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
     const bool active = 32 * rb < len;  // wavefront-uniform
     const int i_l = 32 * rb + l32;      // this lane's token (column of y^T)
 
-    // ---- per-group operands, kept in registers for all heads
-    // fp16 C row i_l (zero past the chunk end), 8 values per K-step
+    // ---- per-group operands of this wavefront's row block, prepared once for all heads
+    // C row i_l (raw bf16), 8 values per K-step.  Rows past the chunk end
+    // repeat its last row: their outputs are never stored, and in C.B^T they
+    // only meet x rows that are zero, so they just need to be finite.
     u32x4 cq[KS];
+    const int64_t rstride = (int64_t)p.G * N;  // elements between consecutive tokens of B and C
     {
-        const uint16_t *crow = p.cf16 + (((int64_t)c * p.G + g) * kChunk + i_l) * N + 8 * hl;
-        const uint16_t *cbt = p.cbt + (((int64_t)c * p.G + g) * 36 + rb * (rb + 1) / 2) * 1024 + lane * 16;
+        const uint16_t *crow = p.C + (t0 + min(i_l, len - 1)) * rstride + (int64_t)g * N + 8 * hl;
 #pragma unroll
         for (int k = 0; k < KS; ++k) cq[k] = *reinterpret_cast<const u32x4 *>(crow + 16 * k);
-        // this row block's tiles into LDS, each lane its own 32 bytes (read
-        // back only by the same lane, so no barrier is needed)
+    }
+    // this row block's C.B^T tiles (from the prep step) into LDS, each lane its
+    // own 32 bytes, read back only by the same lane (no barrier needed)
+    {
+        const uint16_t *cbt = p.cbt + (((int64_t)c * p.G + g) * 36 + rb * (rb + 1) / 2) * 1024 + lane * 16;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            if (t <= rb) {
+            if (t <= rb && 32 * t < len) {
                 const u32x4 a = *reinterpret_cast<const u32x4 *>(cbt + t * 1024);
                 const u32x4 b = *reinterpret_cast<const u32x4 *>(cbt + t * 1024 + 8);
                 u32x4 *d = reinterpret_cast<u32x4 *>(sm.g) + (rb * (rb + 1) / 2 + t) * 128 + lane;
@@ -129,8 +134,26 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
             }
         }
     }
-    const int sc = p.cexp[(int64_t)c * p.G + g];
     const int sg = p.gexp[(int64_t)c * p.G + g];
+    // C rows to fp16 under this wavefront's exponent sc
+    int sc;
+    {
+        uint32_t m = 0;
+#pragma unroll
+        for (int k = 0; k < KS; ++k)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) m = max(m, max(cq[k][q] & 0x7FFFu, (cq[k][q] >> 16) & 0x7FFFu));
+        sc = f16_scale_exponent(wave_max(__uint_as_float(m << 16)));
+        const float cs = ldexpf(1.0f, sc);
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+            u32x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                o[q] = pack_f16x2(__uint_as_float(cq[k][q] << 16) * cs, __uint_as_float(cq[k][q] & 0xFFFF0000u) * cs);
+            cq[k] = o;
+        }
+    }
 
     // ---- per-head inputs: thread = (quarter of p, token pair) for x, 16-byte vectors of h_in
     const int pq = tid & 3;
@@ -280,7 +303,6 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
         const float dgrow = fast_exp2(fmaxf(0.f, sm.cs2[kChunk - 1] - sm.cs2[0]));
         const int smx = f16_scale_exponent(gbound * wmax * dgrow + fabsf(dh) * emax);
         const float m_scale = ldexpf(1.0f, smx);
-        const float mg = ldexpf(1.0f, smx - sg);  // takes the fp16 tiles to the M scale
         const float cs_i = sm.cs2[i_l];
 
         // undo the C and h_in scalings, decay column i by exp2(cs2_i), move to the M scale
@@ -300,13 +322,16 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
         }
 
         // ---- diagonal block: (2^xe x)^T (2^smx M 2^-xe)^T, M from the C.B^T tiles
-        const float u = fast_exp2(cs_i - sm.cs2[32 * rb]) * mg;
+        const float u0 = fast_exp2(cs_i - sm.cs2[32 * rb]) * m_scale;
+        const float gsc = ldexpf(1.0f, -sg);  // undoes the tiles' scaling
         const float dx = dh * ldexpf(1.0f, -sm.xexp[i_l]) * m_scale;  // D on the diagonal
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             if (t <= rb && 32 * t < len) {
                 const u32x4 *gp = reinterpret_cast<const u32x4 *>(sm.g) + (rb * (rb + 1) / 2 + t) * 128 + lane;
                 const u32x4 gt[2] = {gp[0], gp[64]};
+                const float u = u0 * gsc;
+                const float mg = m_scale * gsc;
                 float mv[16];
                 if (t < rb) {
 #pragma unroll

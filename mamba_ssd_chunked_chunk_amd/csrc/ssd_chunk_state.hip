@@ -12,8 +12,8 @@
 // w_j * x is not exact in 16 bits; fp16 (11-bit significand) keeps the
 // final-state error near 2e-4 where bf16 (8 bits) would give about 1.6e-3.
 // w*x is scaled by the power of two that puts its maximum (per chunk and
-// head) in [2^14, 2^15); B arrives from the prep step already converted under
-// its own power of two per chunk and group.  S itself is stored as fp16
+// head) in [2^14, 2^15), and each 32-column slice of B by its own (so bf16 ->
+// fp16 is exact but for values 2^24 below the slice's maximum).  S itself is stored as fp16
 // under one power-of-two exponent per 32x32 tile of (chunk, head), the net
 // exponent of all scalings, so the reader undoes them exactly; its rounding
 // adds about 3e-4 relative error to the final states and halves the states
@@ -22,9 +22,11 @@
 // Work split: one workgroup = one chunk and a block of HB heads of one group.
 // The products are formed transposed, S^T[n][p] = sum_j B^T[n][j] (w_j
 // x_j[p]); each wavefront owns one n tile and one or both p tiles, and keeps
-// the B^T fragments of its n tile (16 K-steps of 16 tokens, from the prep
-// step's token-contiguous fp16 copy) in registers while the workgroup walks
-// its heads, so B is read once per block of heads.  Each head's weighted x is
+// the B^T fragments of its n tile (16 K-steps of 16 tokens) in registers
+// while the workgroup walks its heads, so B is read and converted once per
+// block of heads: the wavefront loads its 32 columns of B for every token,
+// stages them (128 tokens at a time) in an LDS region of its own and reads
+// them back token-contiguous.  Each head's weighted x is
 // staged in LDS, transposed to [p][token] (fp16 pairs of tokens per dword;
 // 16-byte chunks of rows 16..31 of every 32-row block swapped pairwise so the
 // 32 rows an MFMA operand reads fall on distinct banks); the next head's x,
@@ -60,8 +62,10 @@ __global__ __launch_bounds__(StateShape<N>::THREADS) void ssd_chunk_state_kernel
     constexpr int PPT = S::PPT;
     constexpr int XV = PPT / 8;  // 16-byte x vectors per token per thread
 
+    constexpr int BR = 20;  // dwords per staged B row: 32 bf16 + 16-byte pad
     __shared__ float s_red[kWaves];
     __shared__ __attribute__((aligned(16))) uint32_t s_xt[kHeadDim * XT_STRIDE];
+    __shared__ __attribute__((aligned(16))) uint32_t s_b[kWaves][128 * BR];
 
     const int nhb = p.H / HB;
     const int id = blockIdx.x;
@@ -80,18 +84,55 @@ __global__ __launch_bounds__(StateShape<N>::THREADS) void ssd_chunk_state_kernel
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31;
     const int hl = lane >> 5;
-    const int sb = p.bexp[(int64_t)c * p.G + g];
 
     // this wavefront's tiles: n tile nt, p tiles pt0 .. pt0+PTW-1
     const int nt = wave % S::NT;
     const int pt0 = PTW == 2 ? 0 : wave / S::NT;
 
-    // ---- B^T fragments of n tile nt: row n = 32 nt + l32, tokens 16 k + 8 hl .. +8
+    // ---- B^T fragments of n tile nt: row n = 32 nt + l32, tokens 16 k + 8 hl .. +8,
+    // as fp16 scaled by 2^sb (sb: this n tile's exponent)
     u32x4 bq[16];
+    int sb;
     {
-        const uint16_t *bt = p.bt16 + (((int64_t)c * p.G + g) * N + 32 * nt + l32) * kChunk + 8 * hl;
+        // lane: token (lane / 4) + 16 s, 16-byte chunk lane % 4 of the tile's 64 bytes
+        const int64_t rstride = (int64_t)p.G * N;
+        const uint16_t *bcol = p.B + (t0 * p.G + g) * N + 32 * nt + 8 * (lane & 3);
+        u32x4 raw[16];
 #pragma unroll
-        for (int k = 0; k < 16; ++k) bq[k] = *reinterpret_cast<const u32x4 *>(bt + 16 * k);
+        for (int s2 = 0; s2 < 16; ++s2) {
+            const int j = (lane >> 2) + 16 * s2;
+            raw[s2] = *reinterpret_cast<const u32x4 *>(bcol + min(j, len - 1) * rstride);
+            if (j >= len) raw[s2] = u32x4{};
+        }
+        uint32_t m = 0;
+#pragma unroll
+        for (int s2 = 0; s2 < 16; ++s2)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) m = max(m, max(raw[s2][k] & 0x7FFFu, (raw[s2][k] >> 16) & 0x7FFFu));
+        sb = f16_scale_exponent(wave_max(__uint_as_float(m << 16)));
+        const float bs = ldexpf(1.0f, sb);
+        uint32_t *reg = s_b[wave];
+        const uint16_t *reg16 = reinterpret_cast<const uint16_t *>(reg);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            // rows = tokens 128 half .. +128 (wavefront-private region; LDS
+            // accesses of one wavefront complete in order)
+#pragma unroll
+            for (int s2 = 0; s2 < 8; ++s2)
+                *reinterpret_cast<u32x4 *>(reg + ((lane >> 2) + 16 * s2) * BR + 4 * (lane & 3)) = raw[8 * half + s2];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int r0 = 16 * k + 8 * hl;  // local row of the fragment's first token
+                u32x4 f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t lo = reg16[(r0 + 2 * q) * 2 * BR + l32];
+                    const uint32_t hi = reg16[(r0 + 2 * q + 1) * 2 * BR + l32];
+                    f[q] = pack_f16x2(__uint_as_float(lo << 16) * bs, __uint_as_float(hi << 16) * bs);
+                }
+                bq[8 * half + k] = f;
+            }
+        }
     }
 
     // ---- per-head inputs: thread = (p part, token pair)

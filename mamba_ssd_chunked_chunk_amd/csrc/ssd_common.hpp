@@ -50,12 +50,8 @@ struct Params {
     int4 *desc;          // [nchunks_max]: {seq, t0, len, 0}
     float *dts;          // [nchunks_max][H][256]
     float *cs2;          // [nchunks_max][H][256]
-    int32_t *bexp;       // [nchunks_max][G]   exponent applied to B before fp16
-    int32_t *cexp;       // [nchunks_max][G]   exponent applied to C before fp16
     uint16_t *cbt;       // [nchunks_max][G][36][64][16] fp16 C.B^T tiles * 2^gexp, accumulator order
     int32_t *gexp;       // [nchunks_max][G]
-    uint16_t *cf16;      // [nchunks_max][G][256][N] fp16 C * 2^cexp, zero past the chunk end
-    uint16_t *bt16;      // [nchunks_max][G][N][256] fp16 B^T * 2^bexp, zero past the chunk end
     uint16_t *states;    // [nchunks_max][H][P][N] fp16, scaled by 2^sexp
     int32_t *sexp;       // [nchunks_max][H][2][N/32]: per 32x32 tile (p tile, n tile)
     uint16_t *hin;       // [nchunks_max][H][P][N] fp16, row p scaled by 2^hexp

@@ -1,6 +1,6 @@
 // Step 0 + step 1 of the scan: the chunk table and the per-chunk cumulative
-// decay ("chunk_cumsum"), plus the per-(chunk, group) products that do not
-// depend on the head: C.B^T and the power-of-two exponents of B and C.
+// decay ("chunk_cumsum"), plus the per-(chunk, group) product that does not
+// depend on the head: C.B^T.
 //
 // Chunk table: sequence b owns ceil(len_b / 256) chunks (none when empty);
 // chunk c of the call is found from the exclusive prefix sum of those counts,
@@ -32,13 +32,6 @@
 //   under one power-of-two exponent per (chunk, group) that puts their
 //   maximum magnitude in [2^14, 2^15).
 //
-// Per group (blockIdx.y == 1 + G + g): fp16 copies of the chunk's C and B,
-//   the operands of the later fp16 products, converted once per group rather
-//   than once per head.  Each is scaled by the power of two that puts its
-//   maximum magnitude in [2^14, 2^15) (bf16 -> fp16 is then exact but for
-//   values 2^24 below the maximum), rows past the chunk end are zero, C keeps
-//   its [token][n] layout and B is transposed to [n][token] so that a
-//   contraction over tokens reads 8 consecutive tokens as one 16-byte load.
 #include "ssd_common.hpp"
 
 namespace ssd {
@@ -48,107 +41,6 @@ constexpr int kPrepThreads = 512;
 constexpr int kHeadBlock = 16;
 constexpr int R_STRIDE = 20;  // dwords per staged row of 32 bf16 + pad
 }  // namespace
-
-// max of the bf16 magnitudes (as bits) of 8 values
-__device__ __forceinline__ uint32_t max_mag8(const u32x4 v) {
-    uint32_t m = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) m = max(m, max(v[k] & 0x7FFFu, (v[k] >> 16) & 0x7FFFu));
-    return m;
-}
-
-// exponent s putting a bf16 magnitude (as bits) in [2^14, 2^15) after scaling
-// by 2^s (0 for a zero maximum): the exponent field sits in bits 7..14
-__device__ __forceinline__ int bf16_scale_exponent(uint32_t mm) {
-    return mm == 0 ? 0 : 14 - ((int)(mm >> 7) - 127);
-}
-
-template <int N>
-__device__ void convert_group(const Params &p, int c, int g, int64_t t0, int len, uint32_t (&s_umax)[8][2]) {
-    constexpr int CV = kChunk * N / 8 / kPrepThreads;  // 16-byte vectors of C per thread
-    constexpr int NB = (kChunk / 8) * (N / 8);           // 8 tokens x 8 n blocks of B
-    constexpr int BB = (NB + kPrepThreads - 1) / kPrepThreads;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int64_t rstride = (int64_t)p.G * N;  // elements between consecutive tokens
-    const uint16_t *Cg = p.C + (t0 * p.G + g) * N;
-    const uint16_t *Bg = p.B + (t0 * p.G + g) * N;
-
-    u32x4 cv[CV];
-    u32x4 bv[BB][8];
-    uint32_t cm = 0, bm = 0;
-#pragma unroll
-    for (int it = 0; it < CV; ++it) {
-        const int v = tid + it * kPrepThreads;
-        const int j = v / (N / 8), q = v % (N / 8);
-        cv[it] = j < len ? *reinterpret_cast<const u32x4 *>(Cg + j * rstride + 8 * q) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int it = 0; it < BB; ++it) {
-        const int b = tid + it * kPrepThreads;
-        const int tb = b / (N / 8), q = b % (N / 8);
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int j = 8 * tb + r;
-            bv[it][r] = (b < NB && j < len) ? *reinterpret_cast<const u32x4 *>(Bg + j * rstride + 8 * q)
-                                            : u32x4{0u, 0u, 0u, 0u};
-        }
-    }
-#pragma unroll
-    for (int it = 0; it < CV; ++it) cm = max(cm, max_mag8(cv[it]));
-#pragma unroll
-    for (int it = 0; it < BB; ++it)
-#pragma unroll
-        for (int r = 0; r < 8; ++r) bm = max(bm, max_mag8(bv[it][r]));
-    bm = wave_max_u32(bm);
-    cm = wave_max_u32(cm);
-    if (lane == 0) { s_umax[wave][0] = bm; s_umax[wave][1] = cm; }
-    __syncthreads();
-    uint32_t bmm = 0, cmm = 0;
-#pragma unroll
-    for (int w = 0; w < 8; ++w) { bmm = max(bmm, s_umax[w][0]); cmm = max(cmm, s_umax[w][1]); }
-    const int sb = bf16_scale_exponent(bmm), sc = bf16_scale_exponent(cmm);
-    if (tid == 0) {
-        p.bexp[(int64_t)c * p.G + g] = sb;
-        p.cexp[(int64_t)c * p.G + g] = sc;
-    }
-    const float bs = ldexpf(1.0f, sb), cs = ldexpf(1.0f, sc);
-
-    // C: same layout, 8 values per 16-byte vector
-    uint16_t *cdst = p.cf16 + ((int64_t)c * p.G + g) * kChunk * N;
-#pragma unroll
-    for (int it = 0; it < CV; ++it) {
-        const int v = tid + it * kPrepThreads;
-        u32x4 o;
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            o[k] = pack_f16x2(__uint_as_float(cv[it][k] << 16) * cs, __uint_as_float(cv[it][k] & 0xFFFF0000u) * cs);
-        *reinterpret_cast<u32x4 *>(cdst + (int64_t)v * 8) = o;
-    }
-    // B^T: the 8x8 block (tokens 8tb.., n 8q..) transposed in registers;
-    // dword k of row n holds tokens 2k and 2k+1
-    uint16_t *bdst = p.bt16 + ((int64_t)c * p.G + g) * N * kChunk;
-#pragma unroll
-    for (int it = 0; it < BB; ++it) {
-        const int b = tid + it * kPrepThreads;
-        if (b < NB) {
-            const int tb = b / (N / 8), q = b % (N / 8);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                u32x4 o;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const uint32_t w0 = bv[it][2 * k][e >> 1], w1 = bv[it][2 * k + 1][e >> 1];
-                    const float f0 = __uint_as_float((e & 1) ? (w0 & 0xFFFF0000u) : (w0 << 16));
-                    const float f1 = __uint_as_float((e & 1) ? (w1 & 0xFFFF0000u) : (w1 << 16));
-                    o[k] = pack_f16x2(f0 * bs, f1 * bs);
-                }
-                *reinterpret_cast<u32x4 *>(bdst + (int64_t)(8 * q + e) * kChunk + 8 * tb) = o;
-            }
-        }
-    }
-}
 
 template <int N>
 __global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(Params p) {
@@ -162,7 +54,6 @@ __global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(Params p) {
     __shared__ int s_wtot[8];
     __shared__ int s_loc[2];
     __shared__ float s_hsum[8][kHeadBlock];
-    __shared__ uint32_t s_umax[8][2];
     __shared__ float s_gmax[8];
     __shared__ __attribute__((aligned(16))) uint32_t s_b[kChunk * R_STRIDE];
     __shared__ __attribute__((aligned(16))) uint32_t s_c[kChunk * R_STRIDE];
@@ -248,11 +139,6 @@ __global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(Params p) {
                 }
             }
         }
-        return;
-    }
-
-    if (job > p.G) {
-        convert_group<N>(p, c, job - 1 - p.G, t0, len, s_umax);
         return;
     }
 
@@ -343,7 +229,7 @@ __global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(Params p) {
 }
 
 hipError_t launch_prep(const Params &p, hipStream_t s) {
-    const dim3 grid((unsigned)p.nchunks_max, (unsigned)(1 + 2 * p.G));
+    const dim3 grid((unsigned)p.nchunks_max, (unsigned)(1 + p.G));
     switch (p.N) {
     case 64: hipLaunchKernelGGL(ssd_prep_kernel<64>, grid, dim3(kPrepThreads), 0, s, p); break;
     case 128: hipLaunchKernelGGL(ssd_prep_kernel<128>, grid, dim3(kPrepThreads), 0, s, p); break;

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert binding.ssd_abi_version() == binding.ABI_VERSION == 3
+    assert binding.ssd_abi_version() == binding.ABI_VERSION == 5
     for code, name in binding.STATUS_NAMES.items():
         assert lib.ssd_status_string(code).decode().startswith(name)
     assert b"unknown" in lib.ssd_status_string(99)
@@ -55,13 +55,11 @@ def test_workspace_layout_arithmetic(lib):
     ncm = 1024 // 256 + 4
     assert L["nchunks_max"] == ncm
     assert L["total_bytes"] == binding.ssd_workspace_size(p)
-    offs = [L[k] for k in ("meta", "chunk_off", "desc", "dts", "cs2", "bexp", "cexp", "cbt", "gexp", "cf16", "bt16", "states", "sexp",
-                           "hin", "hexp")]
+    offs = [L[k] for k in ("meta", "chunk_off", "desc", "dts", "cs2", "cbt", "gexp", "states", "sexp", "hin", "hexp")]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert L["cbt"] - L["cs2"] >= ncm * 16 * 256 * 4
     assert L["gexp"] - L["cbt"] >= ncm * 1 * 36 * 64 * 16 * 2
-    assert L["cf16"] - L["gexp"] >= ncm * 1 * 4
-    assert L["bt16"] - L["cf16"] >= ncm * 1 * 256 * 256 * 2
-    assert L["states"] - L["bt16"] >= ncm * 1 * 256 * 256 * 2
+    assert L["states"] - L["gexp"] >= ncm * 1 * 4
     assert L["sexp"] - L["states"] >= ncm * 16 * 64 * 256 * 2
     assert L["hin"] - L["sexp"] >= ncm * 16 * 2 * 8 * 4
     assert L["hexp"] - L["hin"] >= ncm * 16 * 64 * 256 * 2

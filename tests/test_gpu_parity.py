@@ -155,16 +155,12 @@ def test_intermediates_match_chunked_oracle():
     sexp = w[L["sexp"]:L["sexp"] + ncm * H * 2 * (N // 32) * 4].view(np.int32).reshape(ncm, H, 2, N // 32)
     sfac = np.exp2(-sexp.astype(np.float64)).repeat(32, axis=2).repeat(32, axis=3)  # per element (p, n)
     S = S16.astype(np.float64) * sfac
-    cbt16 = w[L["cbt"]:L["cbt"] + ncm * 2 * 36 * 1024 * 2].view(np.float16).reshape(ncm, 2, 36, 64, 16)
-    gexp = w[L["gexp"]:L["gexp"] + ncm * 2 * 4].view(np.int32).reshape(ncm, 2)
-    cbt = cbt16.astype(np.float64) * np.exp2(-gexp.astype(np.float64))[..., None, None, None]
     hin16 = w[L["hin"]:L["hin"] + ncm * H * P * N * 2].view(np.float16).reshape(ncm, H, P, N)
     hexp = w[L["hexp"]:L["hexp"] + ncm * H * P * 4].view(np.int32).reshape(ncm, H, P)
     hin = hin16.astype(np.float64) * np.exp2(-hexp.astype(np.float64))[..., None]
-    bexp = w[L["bexp"]:L["bexp"] + ncm * 2 * 4].view(np.int32).reshape(ncm, 2)
-    cexp = w[L["cexp"]:L["cexp"] + ncm * 2 * 4].view(np.int32).reshape(ncm, 2)
-    cf16 = w[L["cf16"]:L["cf16"] + ncm * 2 * 256 * N * 2].view(np.float16).reshape(ncm, 2, 256, N)
-    bt16 = w[L["bt16"]:L["bt16"] + ncm * 2 * N * 256 * 2].view(np.float16).reshape(ncm, 2, N, 256)
+    cbt16 = w[L["cbt"]:L["cbt"] + ncm * 2 * 36 * 1024 * 2].view(np.float16).reshape(ncm, 2, 36, 64, 16)
+    gexp = w[L["gexp"]:L["gexp"] + ncm * 2 * 4].view(np.int32).reshape(ncm, 2)
+    cbt = cbt16.astype(np.float64) * np.exp2(-gexp.astype(np.float64))[..., None, None, None]
     ref = chunked_scan(prob, 256, keep_intermediates=True)["chunks"]
     qsl = prob["query_start_loc"]
     for rec in ref:
@@ -178,10 +174,9 @@ def test_intermediates_match_chunked_oracle():
         assert np.max(np.abs(cs2[c, h, :l] - cs2_ref)) <= tol
         assert frob_rel(S[c, h], rec["S"]) <= 1e-3
         assert frob_rel(hin[c, h], rec["h_in"]) <= 1e-3
-        # the B / C exponents put the chunk's max magnitude in [2^14, 2^15)
+        # C.B^T tiles (stored transposed, in MFMA accumulator order) against the plain product
         T = prob["total_len"]
         g = h // 2
-        # C.B^T tiles (stored transposed, in MFMA accumulator order) against the plain product
         Bc = bf16_to_f64(prob["B"]).reshape(T, 2, N)[t0:t0 + l, g]
         Cc = bf16_to_f64(prob["C"]).reshape(T, 2, N)[t0:t0 + l, g]
         GT = np.zeros((256, 256))
@@ -199,17 +194,6 @@ def test_intermediates_match_chunked_oracle():
         # the tiles' exponent puts their largest magnitude in [2^14, 2^15)
         if gm > 0:
             assert 2.0 ** 14 <= gm * 2.0 ** gexp[c, g] < 2.0 ** 15
-        for arr, ex in (("B", bexp), ("C", cexp)):
-            vals = prob[arr].reshape(T, 2, N)[t0:t0 + l, g]
-            mx = np.max((vals.astype(np.uint32) << 16).view(np.float32).__abs__())
-            assert 2.0 ** 14 <= mx * 2.0 ** ex[c, g] < 2.0 ** 15
-        # fp16 copies: C (token-major) and B^T (token-contiguous), scaled, zero past the chunk end
-        Cs = np.zeros((256, N))
-        Cs[:l] = Cc * 2.0 ** cexp[c, g]
-        Bs = np.zeros((N, 256))
-        Bs[:, :l] = Bc.T * 2.0 ** bexp[c, g]
-        np.testing.assert_allclose(cf16[c, g].astype(np.float64), Cs, rtol=2.0 ** -11, atol=2.0 ** -24 * 2.0 ** 15)
-        np.testing.assert_allclose(bt16[c, g].astype(np.float64), Bs, rtol=2.0 ** -11, atol=2.0 ** -24 * 2.0 ** 15)
 
 
 # --------------------------------------------------------------- invariants
