@@ -19,6 +19,7 @@ namespace ssd {
 constexpr int kChunk = 256;      // chunk length (tokens)
 constexpr int kHeadDim = 64;     // P supported by this build
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -120,13 +121,20 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
     return v;
 }
 
+// Inclusive sum over a 64-lane wavefront with DPP: shifts by 1, 2, 4 and 8
+// within rows of 16 lanes (lanes without a source add 0), then the row
+// broadcasts carry each row's total into the rows above it.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_add_step(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, true));
+}
 __device__ __forceinline__ float wave_incl_scan(float v) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        float o = __shfl_up(v, d, 64);
-        if (lane >= d) v += o;
-    }
+    v = dpp_add_step<0x111, 0xF>(v);  // row_shr:1
+    v = dpp_add_step<0x112, 0xF>(v);  // row_shr:2
+    v = dpp_add_step<0x114, 0xF>(v);  // row_shr:4
+    v = dpp_add_step<0x118, 0xF>(v);  // row_shr:8
+    v = dpp_add_step<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v = dpp_add_step<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
     return v;
 }
 
@@ -139,6 +147,16 @@ template <int CTRL, int ROWS>
 __device__ __forceinline__ float dpp_max_step(float v) {
     return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, false)));
 }
+// Maximum over each aligned group of 16 lanes (a DPP row), for values >= 0;
+// every lane of the row receives it.
+__device__ __forceinline__ float row16_max(float v) {
+    v = dpp_max_step<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+    v = dpp_max_step<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+    v = dpp_max_step<0x141, 0xF>(v);  // row_half_mirror
+    v = dpp_max_step<0x140, 0xF>(v);  // row_mirror
+    return v;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
     v = dpp_max_step<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
     v = dpp_max_step<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
@@ -170,9 +188,17 @@ __device__ __forceinline__ float pow2i(int k) {
     return __uint_as_float((uint32_t)(k + 127) << 23);
 }
 
-// softplus(v) = log(1 + e^v), without overflow.
+// softplus(v) = log(1 + e^v) = max(v, 0) + log1p(e^-|v|), without overflow.
+// e^-|v| and the logarithm use the hardware exp2 / log2; log1p(z) is taken as
+// log(u) * z / (u - 1) with u = 1 + z rounded, which cancels the rounding of
+// u (Goldberg, "What every computer scientist should know about
+// floating-point arithmetic", the log1p formula), so small z keep their
+// relative accuracy.
 __device__ __forceinline__ float softplus_f(float v) {
-    return fmaxf(v, 0.0f) + log1pf(expf(-fabsf(v)));
+    const float z = fast_exp2(-fabsf(v) * kLog2e);  // in (0, 1]
+    const float u = 1.0f + z;
+    const float l = u == 1.0f ? z : __builtin_amdgcn_logf(u) * (kLn2 * z / (u - 1.0f));
+    return fmaxf(v, 0.0f) + l;
 }
 
 // Exponent e with 2^e <= |m| < 2^(e+1) for a finite positive float m.

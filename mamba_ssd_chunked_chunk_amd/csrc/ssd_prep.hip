@@ -42,6 +42,96 @@ constexpr int kHeadBlock = 16;
 constexpr int R_STRIDE = 20;  // dwords per staged row of 32 bf16 + pad
 }  // namespace
 
+// The C.B^T tiles of row block RB (t <= RB) for chunk c and group g, run by
+// one wavefront of the workgroup; the row block is a template parameter so
+// that the number of tiles, and with it every MFMA, is fixed at compile time.
+template <int N, int RB>
+__device__ __forceinline__ void gram_tiles(const Params &p, int c, int g, int64_t t0, int len, uint32_t *s_b,
+                                           uint32_t *s_c, float *s_gmax) {
+    constexpr int KS = N / 32;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int l32 = lane & 31;
+    const int hl = lane >> 5;
+    constexpr int PD = KS < 3 ? KS : 3;  // slices in flight
+    u32x4 rbv[PD][2], rcv[PD][2];
+    auto load_slice = [&](int ks, int d) {
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int j = (tid + it * kPrepThreads) >> 2;
+            const int v = tid & 3;
+            // rows past the chunk end repeat its last row: the tiles' entries
+            // there meet only zero x rows or unstored outputs later
+            const int64_t off = ((t0 + min(j, len - 1)) * p.G + g) * N + ks * 32 + v * 8;
+            rbv[d][it] = *reinterpret_cast<const u32x4 *>(p.B + off);
+            rcv[d][it] = *reinterpret_cast<const u32x4 *>(p.C + off);
+        }
+    };
+    f32x16 accg[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) accg[t] = f32x16{};
+
+#pragma unroll
+    for (int d = 0; d < PD; ++d) load_slice(d, d);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        __syncthreads();  // previous slice consumed
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int j = (tid + it * kPrepThreads) >> 2;
+            const int v = tid & 3;
+            *reinterpret_cast<u32x4 *>(s_b + j * R_STRIDE + v * 4) = rbv[ks % PD][it];
+            *reinterpret_cast<u32x4 *>(s_c + j * R_STRIDE + v * 4) = rcv[ks % PD][it];
+        }
+        if (ks + PD < KS) load_slice(ks + PD, ks % PD);  // in flight during the next slices' MFMAs
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const bf16x8 cb = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4 *>(s_c + (32 * RB + l32) * R_STRIDE + 8 * kk + 4 * hl));
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                if (t <= RB) {
+                    const bf16x8 bb = __builtin_bit_cast(
+                        bf16x8, *reinterpret_cast<const u32x4 *>(s_b + (32 * t + l32) * R_STRIDE + 8 * kk + 4 * hl));
+                    accg[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bb, cb, accg[t], 0, 0, 0);
+                }
+            }
+        }
+    }
+    // one power-of-two scale for all tiles of the chunk and group
+    float gm = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+        if (t <= RB)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) gm = fmaxf(gm, fabsf(accg[t][e]));
+    gm = wave_max(gm);
+    if (lane == 0) s_gmax[wave] = gm;
+    __syncthreads();
+    float gmax = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) gmax = fmaxf(gmax, s_gmax[w]);
+    const int sg = f16_scale_exponent(gmax);
+    if (tid == 0) p.gexp[(int64_t)c * p.G + g] = sg;
+    const float gs = ldexpf(1.0f, sg);
+    // tiles in accumulator order: tile rb(rb+1)/2 + t, 64 lanes x 16 fp16
+    uint16_t *dst = p.cbt + ((int64_t)c * p.G + g) * 36 * 1024;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        if (t <= RB) {
+            u32x4 *o = reinterpret_cast<u32x4 *>(dst + (RB * (RB + 1) / 2 + t) * 1024 + lane * 16);
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                o[q] = u32x4{pack_f16x2(accg[t][8 * q] * gs, accg[t][8 * q + 1] * gs),
+                             pack_f16x2(accg[t][8 * q + 2] * gs, accg[t][8 * q + 3] * gs),
+                             pack_f16x2(accg[t][8 * q + 4] * gs, accg[t][8 * q + 5] * gs),
+                             pack_f16x2(accg[t][8 * q + 6] * gs, accg[t][8 * q + 7] * gs)};
+        }
+    }
+}
+
 template <int N>
 __global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(Params p) {
     constexpr int KS = N / 32;
@@ -100,14 +190,18 @@ __global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(Params p) {
 
     if (job == 0) {
         if (tid == 0) p.desc[c] = make_int4(b, (int)t0, len, 0);
-        // ---- dts and cs2: thread = token (threads past 255 hold zeros), 16 heads at a time
-        const int j = tid;
+        // ---- dts and cs2: thread = (token j, half of a 16-head block); each
+        // half-block of 8 heads is scanned over the 256 tokens by 4 wavefronts
+        const int j = tid & (kChunk - 1);
+        const int half = tid >> 8;
+        const int wq = wave & 3;  // wavefront within the half
         const bool valid = j < len;
         for (int hb = 0; hb < p.H; hb += kHeadBlock) {
-            float d[kHeadBlock], a[kHeadBlock];
+            constexpr int K = kHeadBlock / 2;
+            float d[K], a[K];
 #pragma unroll
-            for (int k = 0; k < kHeadBlock; ++k) {
-                const int h = hb + k;
+            for (int k = 0; k < K; ++k) {
+                const int h = hb + half * K + k;
                 float ds = 0.0f;
                 if (valid && h < p.H) {
                     const float v = p.dt[(t0 + j) * p.H + h] + (p.dt_bias ? p.dt_bias[h] : 0.0f);
@@ -118,113 +212,41 @@ __global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(Params p) {
             }
             // inclusive scan over the tokens, per head
 #pragma unroll
-            for (int k = 0; k < kHeadBlock; ++k) a[k] = wave_incl_scan(a[k]);
+            for (int k = 0; k < K; ++k) a[k] = wave_incl_scan(a[k]);
             __syncthreads();  // s_hsum free from the previous head block
             if (lane == 63) {
 #pragma unroll
-                for (int k = 0; k < kHeadBlock; ++k) s_hsum[wave][k] = a[k];
+                for (int k = 0; k < K; ++k) s_hsum[wave][k] = a[k];
             }
             __syncthreads();
-            if (j < kChunk) {
 #pragma unroll
-                for (int k = 0; k < kHeadBlock; ++k) {
-                    float off = 0.0f;
-                    for (int w = 0; w < wave; ++w) off += s_hsum[w][k];
-                    const int h = hb + k;
-                    if (h < p.H) {
-                        const int64_t row = ((int64_t)c * p.H + h) * kChunk + j;
-                        p.dts[row] = d[k];
-                        p.cs2[row] = (off + a[k]) * kLog2e;
-                    }
+            for (int k = 0; k < K; ++k) {
+                float off = 0.0f;
+#pragma unroll
+                for (int w = 0; w < 3; ++w) off += w < wq ? s_hsum[4 * half + w][k] : 0.0f;
+                const int h = hb + half * K + k;
+                if (h < p.H) {
+                    const int64_t row = ((int64_t)c * p.H + h) * kChunk + j;
+                    p.dts[row] = d[k];
+                    p.cs2[row] = (off + a[k]) * kLog2e;
                 }
             }
         }
         return;
     }
 
-    // ---- group g: C.B^T tiles
+    // ---- group g: C.B^T tiles; SIMD k (= wave & 3) runs row blocks k and 7-k
     const int g = job - 1;
     const int wv = __builtin_amdgcn_readfirstlane(wave);
-    const int rb = (wv >> 2) ? 7 - (wv & 3) : (wv & 3);
-    const int l32 = lane & 31;
-    const int hl = lane >> 5;
-
-    constexpr int PD = KS < 3 ? KS : 3;  // slices in flight
-    u32x4 rbv[PD][2], rcv[PD][2];
-    auto load_slice = [&](int ks, int d) {
-#pragma unroll
-        for (int it = 0; it < 2; ++it) {
-            const int j = (tid + it * kPrepThreads) >> 2;
-            const int v = tid & 3;
-            rbv[d][it] = rcv[d][it] = u32x4{0u, 0u, 0u, 0u};
-            if (j < len) {
-                const int64_t off = ((t0 + j) * p.G + g) * N + ks * 32 + v * 8;
-                rbv[d][it] = *reinterpret_cast<const u32x4 *>(p.B + off);
-                rcv[d][it] = *reinterpret_cast<const u32x4 *>(p.C + off);
-            }
-        }
-    };
-    f32x16 accg[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) accg[t] = f32x16{};
-
-#pragma unroll
-    for (int d = 0; d < PD; ++d) load_slice(d, d);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        __syncthreads();  // previous slice consumed
-#pragma unroll
-        for (int it = 0; it < 2; ++it) {
-            const int j = (tid + it * kPrepThreads) >> 2;
-            const int v = tid & 3;
-            *reinterpret_cast<u32x4 *>(s_b + j * R_STRIDE + v * 4) = rbv[ks % PD][it];
-            *reinterpret_cast<u32x4 *>(s_c + j * R_STRIDE + v * 4) = rcv[ks % PD][it];
-        }
-        if (ks + PD < KS) load_slice(ks + PD, ks % PD);  // in flight during the next slices' MFMAs
-        __syncthreads();
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const bf16x8 cb = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const u32x4 *>(s_c + (32 * rb + l32) * R_STRIDE + 8 * kk + 4 * hl));
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                if (t <= rb) {
-                    const bf16x8 bb = __builtin_bit_cast(
-                        bf16x8, *reinterpret_cast<const u32x4 *>(s_b + (32 * t + l32) * R_STRIDE + 8 * kk + 4 * hl));
-                    accg[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bb, cb, accg[t], 0, 0, 0);
-                }
-            }
-        }
-    }
-    // one power-of-two scale for all tiles of the chunk and group
-    float gm = 0.f;
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-        if (t <= rb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) gm = fmaxf(gm, fabsf(accg[t][e]));
-    gm = wave_max(gm);
-    if (lane == 0) s_gmax[wave] = gm;
-    __syncthreads();
-    float gmax = 0.f;
-#pragma unroll
-    for (int w = 0; w < 8; ++w) gmax = fmaxf(gmax, s_gmax[w]);
-    const int sg = f16_scale_exponent(gmax);
-    if (tid == 0) p.gexp[(int64_t)c * p.G + g] = sg;
-    const float gs = ldexpf(1.0f, sg);
-    // tiles in accumulator order: tile rb(rb+1)/2 + t, 64 lanes x 16 fp16
-    uint16_t *dst = p.cbt + ((int64_t)c * p.G + g) * 36 * 1024;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        if (t <= rb) {
-            u32x4 *o = reinterpret_cast<u32x4 *>(dst + (rb * (rb + 1) / 2 + t) * 1024 + lane * 16);
-#pragma unroll
-            for (int q = 0; q < 2; ++q)
-                o[q] = u32x4{pack_f16x2(accg[t][8 * q] * gs, accg[t][8 * q + 1] * gs),
-                             pack_f16x2(accg[t][8 * q + 2] * gs, accg[t][8 * q + 3] * gs),
-                             pack_f16x2(accg[t][8 * q + 4] * gs, accg[t][8 * q + 5] * gs),
-                             pack_f16x2(accg[t][8 * q + 6] * gs, accg[t][8 * q + 7] * gs)};
-        }
+    switch ((wv >> 2) ? 7 - (wv & 3) : (wv & 3)) {
+    case 0: gram_tiles<N, 0>(p, c, g, t0, len, s_b, s_c, s_gmax); break;
+    case 1: gram_tiles<N, 1>(p, c, g, t0, len, s_b, s_c, s_gmax); break;
+    case 2: gram_tiles<N, 2>(p, c, g, t0, len, s_b, s_c, s_gmax); break;
+    case 3: gram_tiles<N, 3>(p, c, g, t0, len, s_b, s_c, s_gmax); break;
+    case 4: gram_tiles<N, 4>(p, c, g, t0, len, s_b, s_c, s_gmax); break;
+    case 5: gram_tiles<N, 5>(p, c, g, t0, len, s_b, s_c, s_gmax); break;
+    case 6: gram_tiles<N, 6>(p, c, g, t0, len, s_b, s_c, s_gmax); break;
+    default: gram_tiles<N, 7>(p, c, g, t0, len, s_b, s_c, s_gmax); break;
     }
 }
 

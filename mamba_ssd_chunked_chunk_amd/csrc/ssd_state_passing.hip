@@ -83,7 +83,10 @@ __global__ __launch_bounds__(256) void ssd_state_passing_kernel(Params p) {
                 // h_in row p as fp16, scaled by the power of two that puts the
                 // row's max |h| in [2^14, 2^15); the N/4 lanes of one row share it
                 float m = fmaxf(fmaxf(fabsf(st.x), fabsf(st.y)), fmaxf(fabsf(st.z), fabsf(st.w)));
-                for (int dd = p.N / 8; dd >= 1; dd >>= 1) m = fmaxf(m, __shfl_xor(m, dd, 64));
+                // row max: rows are N/4 consecutive lanes (16, 32 or 64)
+                m = row16_max(m);
+                if (p.N >= 128) m = fmaxf(m, __shfl_xor(m, 16, 64));
+                if (p.N >= 256) m = fmaxf(m, __shfl_xor(m, 32, 64));
                 const int sh = f16_scale_exponent(m);
                 const float sc = ldexpf(1.0f, sh);
                 uint2 hv;
@@ -91,7 +94,7 @@ __global__ __launch_bounds__(256) void ssd_state_passing_kernel(Params p) {
                 hv.y = pack_f16x2(st.z * sc, st.w * sc);
                 *reinterpret_cast<uint2 *>(hin + (int64_t)k * stride) = hv;
                 if (e0 % p.N == 0) hexp[(int64_t)k * p.H * kHeadDim] = sh;
-                const float dec = exp2f(d[q]);
+                const float dec = fast_exp2(d[q]);
                 const float us = ldexpf(1.0f, -se[q]);
                 st.x = dec * st.x + f16_bits_to_float(s[q].x & 0xFFFFu) * us;
                 st.y = dec * st.y + f16_bits_to_float(s[q].x >> 16) * us;

@@ -188,12 +188,14 @@ def test_intermediates_match_chunked_oracle():
             for t in range(rb + 1):
                 jj = 32 * t + 8 * (e // 4) + 4 * (lane // 32) + e % 4
                 ii = 32 * rb + lane % 32
-                np.testing.assert_allclose(cbt[c, g, rb * (rb + 1) // 2 + t], GT[jj, ii], rtol=2.0 ** -11,
-                                           atol=np.abs(GT).max() * 2.0 ** -24)
+                inside = (jj < l) & (ii < l)  # entries past the chunk end are unspecified
+                np.testing.assert_allclose(cbt[c, g, rb * (rb + 1) // 2 + t][inside], GT[jj, ii][inside],
+                                           rtol=2.0 ** -11, atol=np.abs(GT).max() * 2.0 ** -24)
                 gm = max(gm, np.abs(GT[jj, ii]).max())
-        # the tiles' exponent puts their largest magnitude in [2^14, 2^15)
+        # the tiles' exponent keeps their largest magnitude below 2^15, and the
+        # chunk's own entries reach at least 2^13 (rows past the end repeat rows)
         if gm > 0:
-            assert 2.0 ** 14 <= gm * 2.0 ** gexp[c, g] < 2.0 ** 15
+            assert 2.0 ** 13 <= gm * 2.0 ** gexp[c, g] < 2.0 ** 15
 
 
 # --------------------------------------------------------------- invariants
