@@ -223,20 +223,24 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
         }
         {
             uint32_t mrow[2];
+            if (len < kChunk) {  // wavefront-uniform: only a partial chunk has rows to clear
+#pragma unroll
+                for (int e = 0; e < 2; ++e)
+                    if (pair * 2 + e >= len) xr[e][0] = xr[e][1] = u32x4{};  // past the chunk end
+            }
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                if (pair * 2 + e >= len) xr[e][0] = xr[e][1] = u32x4{};  // past the chunk end
-                uint32_t m = 0;
+                // max bf16 magnitude of the token's 64 values: packed 16-bit
+                // maxima within the thread, then over the 4 lanes holding it
+                u16x2 m2 = u16x2{0, 0};
 #pragma unroll
                 for (int a = 0; a < 2; ++a)
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const uint32_t lo = xr[e][a][k] & 0x7FFFu, hi = (xr[e][a][k] >> 16) & 0x7FFFu;
-                        m = max(m, max(lo, hi));
-                    }
-                // row max over the 4 lanes holding this token
-                m = max(m, (uint32_t)__shfl_xor((int)m, 1, 64));
-                mrow[e] = max(m, (uint32_t)__shfl_xor((int)m, 2, 64));
+                    for (int k = 0; k < 4; ++k)
+                        m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, xr[e][a][k] & 0x7FFF7FFFu));
+                uint32_t m = max((uint32_t)m2[0], (uint32_t)m2[1]);
+                m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+                mrow[e] = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false));  // [2,3,0,1]
             }
             const int xe0 = mrow[0] == 0 ? 0 : 14 - ((int)(mrow[0] >> 7) - 127);
             const int xe1 = mrow[1] == 0 ? 0 : 14 - ((int)(mrow[1] >> 7) - 127);
@@ -396,12 +400,14 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
 }
 
 // Heads per workgroup: the largest of 8, 4, 2, 1 that divides the heads of a
-// group and still gives at least two workgroups per compute unit.
+// group and still gives at least one workgroup per compute unit (a workgroup
+// fills a compute unit; more heads per workgroup amortise its shared
+// operands).
 static int heads_per_block(const Params &p) {
     const int hg = p.H / p.G;
     const int64_t chunks = (p.nchunks_max + 7) / 8 * 8;
     for (int hb = 8; hb > 1; hb /= 2)
-        if (hg % hb == 0 && chunks * (p.H / hb) >= 2 * (int64_t)p.num_cus) return hb;
+        if (hg % hb == 0 && chunks * (p.H / hb) >= (int64_t)p.num_cus) return hb;
     return 1;
 }
 

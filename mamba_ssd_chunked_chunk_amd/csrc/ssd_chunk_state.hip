@@ -243,12 +243,14 @@ __global__ __launch_bounds__(StateShape<N>::THREADS) void ssd_chunk_state_kernel
 }
 
 // Heads per workgroup: the largest of 8, 4, 2, 1 that divides the heads of a
-// group and still gives at least two workgroups per compute unit.
+// group and still gives at least one workgroup per compute unit (a workgroup
+// fills a compute unit; more heads per workgroup amortise its shared
+// operands).
 static int state_heads_per_block(const Params &p) {
     const int hg = p.H / p.G;
     const int64_t chunks = (p.nchunks_max + 7) / 8 * 8;
     for (int hb = 8; hb > 1; hb /= 2)
-        if (hg % hb == 0 && chunks * (p.H / hb) >= 2 * (int64_t)p.num_cus) return hb;
+        if (hg % hb == 0 && chunks * (p.H / hb) >= (int64_t)p.num_cus) return hb;
     return 1;
 }
 
