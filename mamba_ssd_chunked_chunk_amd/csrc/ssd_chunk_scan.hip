@@ -72,8 +72,12 @@ struct __attribute__((aligned(16))) ScanSmem {
     float red[8][2];
 };
 
-__device__ __forceinline__ float h2f(uint32_t w, int hi) {
-    return f16_bits_to_float(hi ? (w >> 16) : (w & 0xFFFFu));
+// One fp16 half of a packed dword times a float, as a single mixed-precision
+// FMA with a zero addend (v_fma_mix_f32: the fp16 operand is read directly,
+// the product rounded once).
+__device__ __forceinline__ float hmul(uint32_t w, int hi, float f) {
+    const f16x2 h2 = __builtin_bit_cast(f16x2, w);
+    return __builtin_fmaf((float)h2[hi], f, 0.0f);
 }
 }  // namespace
 
@@ -342,10 +346,10 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
                     for (int a = 0; a < 4; ++a) {
                         const float4 v4 = *reinterpret_cast<const float4 *>(sm.v + rb * kChunk + 32 * t + 8 * a + 4 * hl);
                         const uint32_t w0 = gt[a >> 1][2 * (a & 1)], w1 = gt[a >> 1][2 * (a & 1) + 1];
-                        mv[4 * a + 0] = h2f(w0, 0) * (v4.x * u);
-                        mv[4 * a + 1] = h2f(w0, 1) * (v4.y * u);
-                        mv[4 * a + 2] = h2f(w1, 0) * (v4.z * u);
-                        mv[4 * a + 3] = h2f(w1, 1) * (v4.w * u);
+                        mv[4 * a + 0] = hmul(w0, 0, v4.x * u);
+                        mv[4 * a + 1] = hmul(w0, 1, v4.y * u);
+                        mv[4 * a + 2] = hmul(w1, 0, v4.z * u);
+                        mv[4 * a + 3] = hmul(w1, 1, v4.w * u);
                     }
                 } else {
 #pragma unroll
@@ -359,7 +363,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
                         for (int b = 0; b < 4; ++b) {
                             const int j = j0 + b;
                             const uint32_t w = gt[a >> 1][2 * (a & 1) + (b >> 1)];
-                            float val = h2f(w, b & 1) * fast_exp2(cs_i - cj[b]) * wj[b] * mg;
+                            float val = hmul(w, b & 1, fast_exp2(cs_i - cj[b]) * (wj[b] * mg));
                             if (j == i_l) val += dx;
                             mv[4 * a + b] = j <= i_l ? val : 0.f;
                         }
