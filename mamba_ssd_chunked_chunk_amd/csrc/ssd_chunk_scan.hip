@@ -37,18 +37,24 @@
 // Decay without one exp2 per element.  For a tile strictly below the
 // diagonal block (all j < 32*rb <= i), exp2(cs2_i - cs2_j) =
 // exp2(cs2_i - cs2_r) * exp2(cs2_r - cs2_j) with r = 32*rb; both factors are
-// at most 1 for A <= 0.  The second factor (times dts_j and the x row scale)
-// is tabulated once per head in LDS; only the diagonal tile evaluates exp2
-// per element.  The skip term D*x is folded into the diagonal of M.
+// at most 1 for A <= 0.  The second factor, times dts_j and the x block
+// scale, is tabulated once per head in LDS as fp16 in each lane's operand
+// order, so such a tile's M operand is the C.B^T tile times the table, eight
+// packed fp16 multiplies per lane; the first factor depends only on the
+// lane's row i and is applied once per head, in fp32, to a second
+// accumulator that collects those tiles.  Only the diagonal tile evaluates
+// exp2 per element.  The skip term D*x is folded into the diagonal of M.
 //
 // Precision.  M and h_in are rounded to fp16 (11-bit significand) under
-// power-of-two scales that keep them far from overflow (one per head for M,
-// one per row for h_in); C and C.B^T are rounded to fp16 after power-of-two
-// scalings (per row block, per chunk and group), and each x row is converted after its own
-// power-of-two scaling, compensated inside M.  All products accumulate in
-// fp32.  bf16 (8 bits) for M or h_in would put the rounding error, which
-// scales with the typical size of y rather than with each y, close to the
-// tolerance wherever y is near zero.
+// power-of-two scales that keep them far from overflow (one per wavefront
+// and head for the diagonal M tile, one per head for the table, one per row
+// for h_in); C and C.B^T are rounded to fp16 after power-of-two scalings (per
+// row block, per chunk and group), and each 32-token block of x after its
+// own power-of-two scaling, compensated inside M or the table.  The product
+// of a C.B^T tile and the table is rounded to fp16 once more.  All products
+// accumulate in fp32.  bf16 (8 bits) for M or h_in would put the rounding
+// error, which scales with the typical size of y rather than with each y,
+// close to the tolerance wherever y is near zero.
 #include "ssd_common.hpp"
 
 namespace ssd {
@@ -63,13 +69,14 @@ struct __attribute__((aligned(16))) ScanSmem {
     uint32_t g[36 * 2 * 64 * 4];  // the chunk's fp16 C.B^T tiles: [tile][half][lane] 16-byte runs
     uint32_t h[kHeadDim * H_STRIDE];
     uint32_t xt[kHeadDim * XT_STRIDE];
-    float v[8 * kChunk];  // row block r: exp2(cs2[32r]-cs2[j]) * dts_j * 2^-xe_j, j < 32r
+    // row block r, column tile t < r: fp16 pairs of
+    // exp2(cs2[32r] - cs2[j]) * dts_j * 2^-(xe_t + kw), dword
+    // r*128 + t*16 + hl*8 + 2a + bh holding j = 32t + 8a + 4hl + 2bh (+1)
+    uint32_t v[8 * 128];
     float cs2[kChunk];
     float dts[kChunk];
-    float wx[kChunk];     // dts_j * 2^-xe_j
-    int xexp[kChunk];
     float hs[kHeadDim];   // 2^-hexp[p]
-    float red[8][2];
+    int xexp[8];          // x exponent of each 32-token block
 };
 
 // One fp16 half of a packed dword times a float, as a single mixed-precision
@@ -78,6 +85,93 @@ struct __attribute__((aligned(16))) ScanSmem {
 __device__ __forceinline__ float hmul(uint32_t w, int hi, float f) {
     const f16x2 h2 = __builtin_bit_cast(f16x2, w);
     return __builtin_fmaf((float)h2[hi], f, 0.0f);
+}
+// Product of two fp16 pairs (v_pk_mul_f16).
+__device__ __forceinline__ uint32_t hmul2(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, a) * __builtin_bit_cast(f16x2, b));
+}
+
+// x^T rows (32*pt + l32) of column tile t as the two A operands of a K = 32 step.
+template <int N>
+__device__ __forceinline__ void x_operands(const ScanSmem<N> &sm, int l32, int hl, int t, int pt, f16x8 &x0, f16x8 &x1) {
+    const uint2 *row = reinterpret_cast<const uint2 *>(sm.xt + (32 * pt + l32) * XT_STRIDE + 16 * t + 2 * hl);
+    const uint2 xa = row[0], xb = row[2], xc = row[4], xd = row[6];
+    x0 = __builtin_bit_cast(f16x8, u32x4{xa.x, xa.y, xb.x, xb.y});
+    x1 = __builtin_bit_cast(f16x8, u32x4{xc.x, xc.y, xd.x, xd.y});
+}
+
+// The diagonal block of row block RB for one head, added to acc (in units of
+// 2^smx):
+//   tiles t < RB:  acc2 += (2^xe x)^T (C.B^T 2^sg (.) table), one product per
+//                  tile, then acc += acc2 * exp2(cs2_i - cs2[32 RB]) * 2^(kw - sg) * 2^smx
+//   tile t = RB:   M per element, exp2(cs2_i - cs2_j) dts_j 2^-xe C.B^T_ij
+//                  (j <= i) plus D 2^-xe on the diagonal, in units of 2^smx.
+// rs = exp2(cs2_i - cs2[32 RB]) * 2^(kw - sg + smx); mg = 2^(smx - sg - xe_RB);
+// dx = D 2^(smx - xe_RB).
+template <int N, int RB>
+__device__ __forceinline__ void diag_block(const ScanSmem<N> &sm, f32x16 (&acc)[2], int lane, float cs_i, float rs,
+                                           float mg, float dx) {
+    const int l32 = lane & 31;
+    const int hl = lane >> 5;
+    const int i_l = 32 * RB + l32;
+    const u32x4 *gbase = reinterpret_cast<const u32x4 *>(sm.g) + (RB * (RB + 1) / 2) * 128 + lane;
+    if constexpr (RB > 0) {
+        f32x16 acc2[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+        for (int t = 0; t < RB; ++t) {
+            const u32x4 g0 = gbase[t * 128], g1 = gbase[t * 128 + 64];
+            const u32x4 *vp = reinterpret_cast<const u32x4 *>(sm.v + RB * 128 + t * 16 + hl * 8);
+            const u32x4 v0 = vp[0], v1 = vp[1];
+            u32x4 m0, m1;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                m0[q] = hmul2(g0[q], v0[q]);
+                m1[q] = hmul2(g1[q], v1[q]);
+            }
+            const f16x8 mf0 = __builtin_bit_cast(f16x8, m0), mf1 = __builtin_bit_cast(f16x8, m1);
+#pragma unroll
+            for (int pt = 0; pt < 2; ++pt) {
+                f16x8 x0, x1;
+                x_operands(sm, l32, hl, t, pt, x0, x1);
+                acc2[pt] = mfma32_f16(x0, mf0, acc2[pt]);
+                acc2[pt] = mfma32_f16(x1, mf1, acc2[pt]);
+            }
+        }
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[pt][e] = __builtin_fmaf(acc2[pt][e], rs, acc[pt][e]);
+    }
+    // the diagonal tile
+    const u32x4 gt[2] = {gbase[RB * 128], gbase[RB * 128 + 64]};
+    float mv[16];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const int j0 = 32 * RB + 8 * a + 4 * hl;
+        const float4 c4 = *reinterpret_cast<const float4 *>(sm.cs2 + j0);
+        const float4 d4 = *reinterpret_cast<const float4 *>(sm.dts + j0);
+        const float cj[4] = {c4.x, c4.y, c4.z, c4.w};
+        const float dj[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int j = j0 + b;
+            const uint32_t w = gt[a >> 1][2 * (a & 1) + (b >> 1)];
+            float val = hmul(w, b & 1, fast_exp2(cs_i - cj[b]) * (dj[b] * mg));
+            if (j == i_l) val += dx;
+            mv[4 * a + b] = j <= i_l ? val : 0.f;
+        }
+    }
+    const f16x8 mf0 = __builtin_bit_cast(f16x8, u32x4{pack_f16x2(mv[0], mv[1]), pack_f16x2(mv[2], mv[3]),
+                                                      pack_f16x2(mv[4], mv[5]), pack_f16x2(mv[6], mv[7])});
+    const f16x8 mf1 = __builtin_bit_cast(f16x8, u32x4{pack_f16x2(mv[8], mv[9]), pack_f16x2(mv[10], mv[11]),
+                                                      pack_f16x2(mv[12], mv[13]), pack_f16x2(mv[14], mv[15])});
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt) {
+        f16x8 x0, x1;
+        x_operands(sm, l32, hl, RB, pt, x0, x1);
+        acc[pt] = mfma32_f16(x0, mf0, acc[pt]);
+        acc[pt] = mfma32_f16(x1, mf1, acc[pt]);
+    }
 }
 }  // namespace
 
@@ -218,7 +312,8 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
         }
         const float dh = dh_next;
 
-        // ---- stage h_in and x^T (each x row scaled by its own 2^xe)
+        // ---- stage h_in and x^T (each 32-token block, one wavefront's
+        // tokens, scaled by its own 2^xe)
 #pragma unroll
         for (int it = 0; it < HVEC; ++it) {
             const int idx = tid + it * kThreads;
@@ -226,65 +321,63 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
             *reinterpret_cast<u32x4 *>(sm.h + row * H_STRIDE + v * 4) = hreg[it];
         }
         {
-            uint32_t mrow[2];
             if (len < kChunk) {  // wavefront-uniform: only a partial chunk has rows to clear
 #pragma unroll
                 for (int e = 0; e < 2; ++e)
                     if (pair * 2 + e >= len) xr[e][0] = xr[e][1] = u32x4{};  // past the chunk end
             }
+            // max bf16 magnitude of the block: packed 16-bit maxima within
+            // the thread, then over the wavefront
+            u16x2 m2 = u16x2{0, 0};
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                // max bf16 magnitude of the token's 64 values: packed 16-bit
-                // maxima within the thread, then over the 4 lanes holding it
-                u16x2 m2 = u16x2{0, 0};
+            for (int e = 0; e < 2; ++e)
 #pragma unroll
                 for (int a = 0; a < 2; ++a)
 #pragma unroll
                     for (int k = 0; k < 4; ++k)
                         m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, xr[e][a][k] & 0x7FFF7FFFu));
-                uint32_t m = max((uint32_t)m2[0], (uint32_t)m2[1]);
-                m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
-                mrow[e] = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false));  // [2,3,0,1]
-            }
-            const int xe0 = mrow[0] == 0 ? 0 : 14 - ((int)(mrow[0] >> 7) - 127);
-            const int xe1 = mrow[1] == 0 ? 0 : 14 - ((int)(mrow[1] >> 7) - 127);
-            if (pq == 0) {
-                sm.xexp[pair * 2] = xe0;
-                sm.xexp[pair * 2 + 1] = xe1;
-            }
-            const float s0 = ldexpf(1.0f, xe0), s1 = ldexpf(1.0f, xe1);
+            const uint32_t m = max((uint32_t)m2[0], (uint32_t)m2[1]);
+            const int xe = f16_scale_exponent(wave_max(__uint_as_float(m << 16)));
+            if (lane == 0) sm.xexp[wave] = xe;
+            const float s0 = ldexpf(1.0f, xe);
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
                 const uint32_t a = xr[0][k >> 3][(k >> 1) & 3];
                 const uint32_t b = xr[1][k >> 3][(k >> 1) & 3];
                 const float lo = __uint_as_float((k & 1) ? (a & 0xFFFF0000u) : (a << 16));
                 const float hi = __uint_as_float((k & 1) ? (b & 0xFFFF0000u) : (b << 16));
-                sm.xt[(pq * 16 + k) * XT_STRIDE + pair] = pack_f16x2(lo * s0, hi * s1);
+                sm.xt[(pq * 16 + k) * XT_STRIDE + pair] = pack_f16x2(lo * s0, hi * s0);
             }
         }
         __syncthreads();
         if (hh + 1 < HB) load_head(h + 1);  // next head's inputs in flight during this head's products
 
-        // ---- decay tables and the bound on |M|
+        // ---- per-wavefront bounds (every wavefront derives the same values):
+        // wmax = max |dts_j| 2^-xe_t(j), emax = max 2^-xe_t, dgrow = the
+        // chunk's total growth when A > 0 (1 otherwise)
+        const float4 d4 = *reinterpret_cast<const float4 *>(sm.dts + 4 * lane);
+        const float ex = ldexpf(1.0f, -sm.xexp[lane >> 3]);
+        const float wmax = wave_max(fmaxf(fmaxf(fabsf(d4.x), fabsf(d4.y)), fmaxf(fabsf(d4.z), fabsf(d4.w))) * ex);
+        const float emax = wave_max(ex);
+        const float dgrow = fast_exp2(fmaxf(0.f, sm.cs2[kChunk - 1] - sm.cs2[0]));
+        // table scale 2^-kw with |table| <= 1
+        const float vbound = wmax * dgrow;
+        const int kw = vbound > 0.f ? min((int)((__float_as_uint(vbound) >> 23) & 0xFF) - 126, 126) : 0;
+        // ---- decay table of the tiles below the diagonal blocks
 #pragma unroll
-        for (int it = 0; it < 8 * kChunk / kThreads; ++it) {
-            const int e = tid + it * kThreads;
-            const int r = e >> 8;
-            const int j = e & 255;
-            float val = 0.f;
-            if (j < 32 * r) val = ldexpf(fast_exp2(sm.cs2[32 * r] - sm.cs2[j]) * sm.dts[j], -sm.xexp[j]);
-            sm.v[e] = val;
+        for (int it = 0; it < 2; ++it) {
+            const int d = tid + it * kThreads;
+            const int r = d >> 7;
+            const int t = (d >> 4) & 7;
+            if (t < r) {
+                const int j = 32 * t + 8 * ((d >> 1) & 3) + 4 * ((d >> 3) & 1) + 2 * (d & 1);
+                const float2 c2 = *reinterpret_cast<const float2 *>(sm.cs2 + j);
+                const float2 w2 = *reinterpret_cast<const float2 *>(sm.dts + j);
+                const float cr = sm.cs2[32 * r];
+                const float sc_t = ldexpf(1.0f, -(sm.xexp[t] + kw));
+                sm.v[d] = pack_f16x2(fast_exp2(cr - c2.x) * w2.x * sc_t, fast_exp2(cr - c2.y) * w2.y * sc_t);
+            }
         }
-        float wmax = 0.f, emax = 0.f;
-        if (tid < kChunk) {
-            emax = ldexpf(1.0f, -sm.xexp[tid]);
-            wmax = sm.dts[tid] * emax;
-            sm.wx[tid] = wmax;
-            wmax = fabsf(wmax);
-        }
-        wmax = wave_max(wmax);
-        emax = wave_max(emax);
-        if (lane == 0) { sm.red[wave][0] = wmax; sm.red[wave][1] = emax; }
 
         // ---- off-diagonal part: y^T_off = h_in (LDS) x C^T (registers)
         f32x16 acc[2] = {f32x16{}, f32x16{}};
@@ -300,17 +393,13 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
                 }
             }
         }
-        __syncthreads();  // tables and red[] complete
-        wmax = fmaxf(fmaxf(sm.red[0][0], sm.red[1][0]), fmaxf(sm.red[2][0], sm.red[3][0]));
-        emax = fmaxf(fmaxf(sm.red[0][1], sm.red[1][1]), fmaxf(sm.red[2][1], sm.red[3][1]));
+        __syncthreads();  // the table is complete
         if (!active) continue;  // wavefront-uniform; no barrier before the next head's
         // |2^-xe M| <= |G| * max(dts 2^-xe) * (decay <= 1, or the chunk's total
         // growth when A > 0) + |D| max(2^-xe) on the diagonal, with
         // |G| < 2^(15 - sg) from the tiles' scaling
         const float gbound = ldexpf(1.0f, 15 - sg);
-        const float dgrow = fast_exp2(fmaxf(0.f, sm.cs2[kChunk - 1] - sm.cs2[0]));
         const int smx = f16_scale_exponent(gbound * wmax * dgrow + fabsf(dh) * emax);
-        const float m_scale = ldexpf(1.0f, smx);
         const float cs_i = sm.cs2[i_l];
 
         // undo the C and h_in scalings, decay column i by exp2(cs2_i), move to the M scale
@@ -329,59 +418,21 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
             }
         }
 
-        // ---- diagonal block: (2^xe x)^T (2^smx M 2^-xe)^T, M from the C.B^T tiles
-        const float u0 = fast_exp2(cs_i - sm.cs2[32 * rb]) * m_scale;
-        const float gsc = ldexpf(1.0f, -sg);  // undoes the tiles' scaling
-        const float dx = dh * ldexpf(1.0f, -sm.xexp[i_l]) * m_scale;  // D on the diagonal
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            if (t <= rb && 32 * t < len) {
-                const u32x4 *gp = reinterpret_cast<const u32x4 *>(sm.g) + (rb * (rb + 1) / 2 + t) * 128 + lane;
-                const u32x4 gt[2] = {gp[0], gp[64]};
-                const float u = u0 * gsc;
-                const float mg = m_scale * gsc;
-                float mv[16];
-                if (t < rb) {
-#pragma unroll
-                    for (int a = 0; a < 4; ++a) {
-                        const float4 v4 = *reinterpret_cast<const float4 *>(sm.v + rb * kChunk + 32 * t + 8 * a + 4 * hl);
-                        const uint32_t w0 = gt[a >> 1][2 * (a & 1)], w1 = gt[a >> 1][2 * (a & 1) + 1];
-                        mv[4 * a + 0] = hmul(w0, 0, v4.x * u);
-                        mv[4 * a + 1] = hmul(w0, 1, v4.y * u);
-                        mv[4 * a + 2] = hmul(w1, 0, v4.z * u);
-                        mv[4 * a + 3] = hmul(w1, 1, v4.w * u);
-                    }
-                } else {
-#pragma unroll
-                    for (int a = 0; a < 4; ++a) {
-                        const int j0 = 32 * t + 8 * a + 4 * hl;
-                        const float4 c4 = *reinterpret_cast<const float4 *>(sm.cs2 + j0);
-                        const float4 w4 = *reinterpret_cast<const float4 *>(sm.wx + j0);
-                        const float cj[4] = {c4.x, c4.y, c4.z, c4.w};
-                        const float wj[4] = {w4.x, w4.y, w4.z, w4.w};
-#pragma unroll
-                        for (int b = 0; b < 4; ++b) {
-                            const int j = j0 + b;
-                            const uint32_t w = gt[a >> 1][2 * (a & 1) + (b >> 1)];
-                            float val = hmul(w, b & 1, fast_exp2(cs_i - cj[b]) * (wj[b] * mg));
-                            if (j == i_l) val += dx;
-                            mv[4 * a + b] = j <= i_l ? val : 0.f;
-                        }
-                    }
-                }
-                const f16x8 mf0 = __builtin_bit_cast(f16x8, u32x4{pack_f16x2(mv[0], mv[1]), pack_f16x2(mv[2], mv[3]),
-                                                                  pack_f16x2(mv[4], mv[5]), pack_f16x2(mv[6], mv[7])});
-                const f16x8 mf1 = __builtin_bit_cast(f16x8, u32x4{pack_f16x2(mv[8], mv[9]), pack_f16x2(mv[10], mv[11]),
-                                                                  pack_f16x2(mv[12], mv[13]), pack_f16x2(mv[14], mv[15])});
-#pragma unroll
-                for (int pt = 0; pt < 2; ++pt) {
-                    const uint2 *row = reinterpret_cast<const uint2 *>(sm.xt + (32 * pt + l32) * XT_STRIDE + 16 * t + 2 * hl);
-                    const uint2 xa = row[0], xb = row[2], xc = row[4], xd = row[6];
-                    const f16x8 x0 = __builtin_bit_cast(f16x8, u32x4{xa.x, xa.y, xb.x, xb.y});
-                    const f16x8 x1 = __builtin_bit_cast(f16x8, u32x4{xc.x, xc.y, xd.x, xd.y});
-                    acc[pt] = mfma32_f16(x0, mf0, acc[pt]);
-                    acc[pt] = mfma32_f16(x1, mf1, acc[pt]);
-                }
+        // ---- diagonal block, specialised per row block
+        {
+            const int xr_e = sm.xexp[rb];
+            const float rs = ldexpf(fast_exp2(cs_i - sm.cs2[32 * rb]), kw - sg + smx);
+            const float mg = ldexpf(1.0f, smx - sg - xr_e);
+            const float dx = ldexpf(dh, smx - xr_e);
+            switch (rb) {
+            case 0: diag_block<N, 0>(sm, acc, lane, cs_i, rs, mg, dx); break;
+            case 1: diag_block<N, 1>(sm, acc, lane, cs_i, rs, mg, dx); break;
+            case 2: diag_block<N, 2>(sm, acc, lane, cs_i, rs, mg, dx); break;
+            case 3: diag_block<N, 3>(sm, acc, lane, cs_i, rs, mg, dx); break;
+            case 4: diag_block<N, 4>(sm, acc, lane, cs_i, rs, mg, dx); break;
+            case 5: diag_block<N, 5>(sm, acc, lane, cs_i, rs, mg, dx); break;
+            case 6: diag_block<N, 6>(sm, acc, lane, cs_i, rs, mg, dx); break;
+            default: diag_block<N, 7>(sm, acc, lane, cs_i, rs, mg, dx); break;
             }
         }
 
