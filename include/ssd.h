@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 5
+#define SSD_ABI_VERSION 6
 #define SSD_MAX_DSTATE 256  /* largest dstate, as in "mamba2_ssd_scan", comptime MAX_DSTATE */
 
 typedef enum ssd_status {
@@ -95,7 +95,9 @@ typedef struct ssd_problem {
  *                                         each in MFMA accumulator order: lane
  *                                         l, element e holds j = 32t + 8(e/4)
  *                                         + 4(l/32) + e%4, i = 32rb + l%32;
- *                                         scaled by 2^gexp[c][g]
+ *                                         scaled by 2^gexp[c][g]; the
+ *                                         diagonal tiles (t = rb) hold 0
+ *                                         where j > i
  *   gexp      int32[nchunks_max][G]       exponent of each cbt block
  *   states    fp16[nchunks_max][H][P][N]  chunk's own state contribution,
  *                                         element (p, n) scaled by
@@ -103,11 +105,14 @@ typedef struct ssd_problem {
  *   sexp      int32[nchunks_max][H][2][N/32]  exponent of each 32x32 tile
  *   hin       fp16[nchunks_max][H][P][N]  state entering the chunk, row p
  *                                         scaled by 2^hexp[c][h][p]
- *   hexp      int32[nchunks_max][H][P]    exponent of each hin row           */
+ *   hexp      int32[nchunks_max][H][P]    exponent of each hin row
+ *   xexp      int32[nchunks_max][H]       2^xexp puts the chunk's largest |x|
+ *                                         of the head in [2^14, 2^15) (0 if
+ *                                         all zero)                          */
 typedef struct ssd_workspace_layout {
     size_t total_bytes;
     int64_t nchunks_max;
-    size_t meta, chunk_off, desc, dts, cs2, cbt, gexp, states, sexp, hin, hexp;
+    size_t meta, chunk_off, desc, dts, cs2, cbt, gexp, states, sexp, hin, hexp, xexp;
 } ssd_workspace_layout;
 
 /* ABI version of the loaded library (SSD_ABI_VERSION it was built with). */

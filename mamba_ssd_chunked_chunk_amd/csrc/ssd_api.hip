@@ -53,6 +53,7 @@ void layout_of(const ssd_problem *p, ssd_workspace_layout *L) {
     L->sexp = off;      off = align_up(off + (size_t)ncm * H * 2 * ((size_t)p->dstate / 32) * sizeof(int32_t));
     L->hin = off;       off = align_up(off + (size_t)ncm * H * PN * sizeof(uint16_t));
     L->hexp = off;      off = align_up(off + (size_t)ncm * H * (size_t)p->head_dim * sizeof(int32_t));
+    L->xexp = off;      off = align_up(off + (size_t)ncm * H * sizeof(int32_t));
     L->total_bytes = off;
 }
 
@@ -159,6 +160,7 @@ static ssd_status run_scan(
     p.dts = reinterpret_cast<float *>(ws + L.dts);
     p.cs2 = reinterpret_cast<float *>(ws + L.cs2);
     p.hexp = reinterpret_cast<int32_t *>(ws + L.hexp);
+    p.xexp = reinterpret_cast<int32_t *>(ws + L.xexp);
     p.cbt = reinterpret_cast<uint16_t *>(ws + L.cbt);
     p.gexp = reinterpret_cast<int32_t *>(ws + L.gexp);
     p.states = reinterpret_cast<uint16_t *>(ws + L.states);

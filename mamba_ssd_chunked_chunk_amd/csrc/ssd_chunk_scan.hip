@@ -73,10 +73,12 @@ struct __attribute__((aligned(16))) ScanSmem {
     // exp2(cs2[32r] - cs2[j]) * dts_j * 2^-(xe_t + kw), dword
     // r*128 + t*16 + hl*8 + 2a + bh holding j = 32t + 8a + 4hl + 2bh (+1)
     uint32_t v[8 * 128];
-    float cs2[kChunk];
-    float dts[kChunk];
-    float hs[kHeadDim];   // 2^-hexp[p]
-    int xexp[8];          // x exponent of each 32-token block
+    // per-head tables, double-buffered: head k uses buffer k & 1
+    float cs2[2][kChunk];
+    float dts[2][kChunk];
+    float hs[2][kHeadDim];  // 2^-hexp[p]
+    float dd[2];            // D of the head
+    int xexp[2];            // x exponent of the chunk and head
 };
 
 // One fp16 half of a packed dword times a float, as a single mixed-precision
@@ -101,16 +103,19 @@ __device__ __forceinline__ void x_operands(const ScanSmem<N> &sm, int l32, int h
 }
 
 // The diagonal block of row block RB for one head, added to acc (in units of
-// 2^smx):
+// 2^smx; x is staged as 2^xe x):
 //   tiles t < RB:  acc2 += (2^xe x)^T (C.B^T 2^sg (.) table), one product per
-//                  tile, then acc += acc2 * exp2(cs2_i - cs2[32 RB]) * 2^(kw - sg) * 2^smx
-//   tile t = RB:   M per element, exp2(cs2_i - cs2_j) dts_j 2^-xe C.B^T_ij
-//                  (j <= i) plus D 2^-xe on the diagonal, in units of 2^smx.
-// rs = exp2(cs2_i - cs2[32 RB]) * 2^(kw - sg + smx); mg = 2^(smx - sg - xe_RB);
-// dx = D 2^(smx - xe_RB).
+//                  tile, then acc += acc2 * rs,
+//                  rs = exp2(cs2_i - cs2[32 RB]) * 2^(kw - sg - xe + smx)
+//   tile t = RB:   M per element, exp2(cs2_i - cs2_j) dts_j C.B^T_ij times
+//                  mg = 2^(smx - sg - xe), plus dx = D 2^(smx - xe) on the
+//                  diagonal.  The tile is zero where j > i; there the exp2
+//                  argument is capped at the chunk's total log2 growth (0 for
+//                  A <= 0), which leaves every j <= i unchanged and keeps the
+//                  masked products finite.
 template <int N, int RB>
-__device__ __forceinline__ void diag_block(const ScanSmem<N> &sm, f32x16 (&acc)[2], int lane, float cs_i, float rs,
-                                           float mg, float dx) {
+__device__ __forceinline__ void diag_block(const ScanSmem<N> &sm, const float *cs2, const float *dts, f32x16 (&acc)[2],
+                                           int lane, float cs_i, float rs, float mg, float dx, float cap) {
     const int l32 = lane & 31;
     const int hl = lane >> 5;
     const int i_l = 32 * RB + l32;
@@ -148,17 +153,16 @@ __device__ __forceinline__ void diag_block(const ScanSmem<N> &sm, f32x16 (&acc)[
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
         const int j0 = 32 * RB + 8 * a + 4 * hl;
-        const float4 c4 = *reinterpret_cast<const float4 *>(sm.cs2 + j0);
-        const float4 d4 = *reinterpret_cast<const float4 *>(sm.dts + j0);
+        const float4 c4 = *reinterpret_cast<const float4 *>(cs2 + j0);
+        const float4 d4 = *reinterpret_cast<const float4 *>(dts + j0);
         const float cj[4] = {c4.x, c4.y, c4.z, c4.w};
         const float dj[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const int j = j0 + b;
             const uint32_t w = gt[a >> 1][2 * (a & 1) + (b >> 1)];
-            float val = hmul(w, b & 1, fast_exp2(cs_i - cj[b]) * (dj[b] * mg));
-            if (j == i_l) val += dx;
-            mv[4 * a + b] = j <= i_l ? val : 0.f;
+            const float val = hmul(w, b & 1, fast_exp2(fminf(cs_i - cj[b], cap)) * (dj[b] * mg));
+            mv[4 * a + b] = j == i_l ? val + dx : val;
         }
     }
     const f16x8 mf0 = __builtin_bit_cast(f16x8, u32x4{pack_f16x2(mv[0], mv[1]), pack_f16x2(mv[2], mv[3]),
@@ -253,26 +257,34 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
         }
     }
 
-    // ---- per-head inputs: thread = (quarter of p, token pair) for x, 16-byte vectors of h_in
-    const int pq = tid & 3;
-    const int pair = tid >> 2;
+    // ---- per-head inputs.  Two phases per head k, each closed by a barrier:
+    //   P(k): stage x^T(k), build the decay table, off-diagonal products
+    //   Q(k): diagonal blocks and y(k); stage h_in and the tables of head k+1
+    // so the VALU-heavy staging of one part overlaps the products of the
+    // other.  Loads run one phase pair ahead: h_in and tables of head k+2 are
+    // issued at the end of Q(k), x of head k+1 after staging x^T(k).  They are
+    // unconditional (past the last head they repeat it), so the compiler's
+    // wait counts never assume a later load is missing and wait for all.
+    const int pq = tid & 3;     // x staging: quarter of p
+    const int pair = tid >> 2;  // x staging: token pair
     u32x4 hreg[HVEC];
     u32x4 xr[2][2];
-    // the head's table entries: token (tid & 255)'s cs2 and dts, row (tid & 63)'s
-    // h_in exponent, and D.  Plain unconditional loads, used only at the next
-    // staging, so they stay in flight during the current head's products.
-    float tab_cs = 0.f, tab_dt = 0.f, dh_next = 0.f;
-    int tab_hx = 0;
-    auto load_head = [&](int h) {
+    float tab_cs = 0.f, tab_dt = 0.f, tab_dh = 0.f;
+    int tab_hx = 0, tab_xe = 0;
+    const float *dsrc = p.D ? p.D : p.A;  // a valid address either way; D = 0 when absent
+    auto load_tabs = [&](int h) {
         const int64_t r = ((int64_t)c * p.H + h) * kChunk + (tid & (kChunk - 1));
         tab_cs = p.cs2[r];
         tab_dt = p.dts[r];
         tab_hx = p.hexp[((int64_t)c * p.H + h) * kHeadDim + (tid & (kHeadDim - 1))];
-        dh_next = p.D ? p.D[h] : 0.0f;
+        tab_dh = dsrc[h];
+        tab_xe = p.xexp[(int64_t)c * p.H + h];
         const uint16_t *hin_head = p.hin + ((int64_t)c * p.H + h) * kHeadDim * N;
 #pragma unroll
         for (int it = 0; it < HVEC; ++it)
             hreg[it] = *reinterpret_cast<const u32x4 *>(hin_head + (tid + it * kThreads) * 8);
+    };
+    auto load_x = [&](int h) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             // rows past the chunk end read the last row (len >= 1); they are
@@ -283,11 +295,41 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
             xr[e][1] = src[1];
         }
     };
-    load_head(h_first);
-
+    const bool has_d = p.D != nullptr;
+    auto stage_tabs = [&](int b) {
+        if (tid < kChunk) {
+            sm.cs2[b][tid] = tab_cs;
+            sm.dts[b][tid] = tab_dt;
+        } else if (tid < kChunk + kHeadDim) {
+            sm.hs[b][tid - kChunk] = ldexpf(1.0f, -tab_hx);
+        } else if (tid == kChunk + kHeadDim) {
+            sm.dd[b] = has_d ? tab_dh : 0.0f;
+            sm.xexp[b] = tab_xe;
+        }
 #pragma unroll
+        for (int it = 0; it < HVEC; ++it) {
+            const int idx = tid + it * kThreads;
+            const int row = idx / (N / 8), v = idx - row * (N / 8);
+            *reinterpret_cast<u32x4 *>(sm.h + row * H_STRIDE + v * 4) = hreg[it];
+        }
+    };
+    const int h_last = h_first + HB - 1;
+    load_tabs(h_first);
+    load_x(h_first);
+    stage_tabs(0);
+    // the first head's x is complete before the next loads are issued, so at
+    // the loop head, on either path, x is older than everything still in flight
+#pragma unroll
+    for (int e = 0; e < 2; ++e) asm volatile("" : "+v"(xr[e][0]), "+v"(xr[e][1]));
+    load_tabs(min(h_first + 1, h_last));
+    __syncthreads();
+
+#pragma unroll 1
     for (int hh = 0; hh < HB; ++hh) {
         const int h = h_first + hh;
+        const int b = hh & 1;
+        const float *cs2 = sm.cs2[b];
+        const float *dts = sm.dts[b];
         // keep the per-group operands opaque across heads, so values derived
         // from them (fp32 copies of the tiles) are not hoisted out of the loop
         // and held in registers for all heads
@@ -303,66 +345,54 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
         const int i_l = 32 * rb + l32;
         const int pq = tid & 3;
         const int pair = tid >> 2;
-        __syncthreads();  // the previous head's LDS reads are done
-        if (tid < kChunk) {
-            sm.cs2[tid] = tab_cs;
-            sm.dts[tid] = tab_dt;
-        } else if (tid < kChunk + kHeadDim) {
-            sm.hs[tid - kChunk] = ldexpf(1.0f, -tab_hx);
-        }
-        const float dh = dh_next;
 
-        // ---- stage h_in and x^T (each 32-token block, one wavefront's
-        // tokens, scaled by its own 2^xe)
-#pragma unroll
-        for (int it = 0; it < HVEC; ++it) {
-            const int idx = tid + it * kThreads;
-            const int row = idx / (N / 8), v = idx - row * (N / 8);
-            *reinterpret_cast<u32x4 *>(sm.h + row * H_STRIDE + v * 4) = hreg[it];
-        }
+        // ======== P(hh)
+        // ---- x^T: one power of two for the chunk and head, none where x
+        // already sits well inside fp16's normal range
+        const int xe_raw = sm.xexp[b];
+        const float dh = sm.dd[b];
+        const int xe = (xe_raw >= 0 && xe_raw <= 20) ? 0 : xe_raw;
         {
             if (len < kChunk) {  // wavefront-uniform: only a partial chunk has rows to clear
 #pragma unroll
                 for (int e = 0; e < 2; ++e)
                     if (pair * 2 + e >= len) xr[e][0] = xr[e][1] = u32x4{};  // past the chunk end
             }
-            // max bf16 magnitude of the block: packed 16-bit maxima within
-            // the thread, then over the wavefront
-            u16x2 m2 = u16x2{0, 0};
+            if (xe == 0) {
 #pragma unroll
-            for (int e = 0; e < 2; ++e)
+                for (int k = 0; k < 16; ++k) {
+                    const uint32_t a = xr[0][k >> 3][(k >> 1) & 3];
+                    const uint32_t b2 = xr[1][k >> 3][(k >> 1) & 3];
+                    sm.xt[(pq * 16 + k) * XT_STRIDE + pair] =
+                        pack_f16x2(__uint_as_float((k & 1) ? (a & 0xFFFF0000u) : (a << 16)),
+                                   __uint_as_float((k & 1) ? (b2 & 0xFFFF0000u) : (b2 << 16)));
+                }
+            } else {
+                const float s0 = ldexpf(1.0f, xe);
 #pragma unroll
-                for (int a = 0; a < 2; ++a)
-#pragma unroll
-                    for (int k = 0; k < 4; ++k)
-                        m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, xr[e][a][k] & 0x7FFF7FFFu));
-            const uint32_t m = max((uint32_t)m2[0], (uint32_t)m2[1]);
-            const int xe = f16_scale_exponent(wave_max(__uint_as_float(m << 16)));
-            if (lane == 0) sm.xexp[wave] = xe;
-            const float s0 = ldexpf(1.0f, xe);
-#pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                const uint32_t a = xr[0][k >> 3][(k >> 1) & 3];
-                const uint32_t b = xr[1][k >> 3][(k >> 1) & 3];
-                const float lo = __uint_as_float((k & 1) ? (a & 0xFFFF0000u) : (a << 16));
-                const float hi = __uint_as_float((k & 1) ? (b & 0xFFFF0000u) : (b << 16));
-                sm.xt[(pq * 16 + k) * XT_STRIDE + pair] = pack_f16x2(lo * s0, hi * s0);
+                for (int k = 0; k < 16; ++k) {
+                    const uint32_t a = xr[0][k >> 3][(k >> 1) & 3];
+                    const uint32_t b2 = xr[1][k >> 3][(k >> 1) & 3];
+                    sm.xt[(pq * 16 + k) * XT_STRIDE + pair] =
+                        pack_f16x2(__uint_as_float((k & 1) ? (a & 0xFFFF0000u) : (a << 16)) * s0,
+                                   __uint_as_float((k & 1) ? (b2 & 0xFFFF0000u) : (b2 << 16)) * s0);
+                }
             }
         }
-        __syncthreads();
-        if (hh + 1 < HB) load_head(h + 1);  // next head's inputs in flight during this head's products
+        load_x(min(h + 1, h_last));  // next head's x in flight during this head's products
 
-        // ---- per-wavefront bounds (every wavefront derives the same values):
-        // wmax = max |dts_j| 2^-xe_t(j), emax = max 2^-xe_t, dgrow = the
-        // chunk's total growth when A > 0 (1 otherwise)
-        const float4 d4 = *reinterpret_cast<const float4 *>(sm.dts + 4 * lane);
-        const float ex = ldexpf(1.0f, -sm.xexp[lane >> 3]);
-        const float wmax = wave_max(fmaxf(fmaxf(fabsf(d4.x), fabsf(d4.y)), fmaxf(fabsf(d4.z), fabsf(d4.w))) * ex);
-        const float emax = wave_max(ex);
-        const float dgrow = fast_exp2(fmaxf(0.f, sm.cs2[kChunk - 1] - sm.cs2[0]));
-        // table scale 2^-kw with |table| <= 1
-        const float vbound = wmax * dgrow;
+        // ---- bounds, the same in every wavefront: dmax = max |dts|, dgrow =
+        // the chunk's total growth when A > 0 (1 otherwise)
+        const float4 d4 = *reinterpret_cast<const float4 *>(dts + 4 * lane);
+        const float dmax = wave_max(fmaxf(fmaxf(fabsf(d4.x), fabsf(d4.y)), fmaxf(fabsf(d4.z), fabsf(d4.w))));
+        const float cap = fmaxf(0.f, cs2[kChunk - 1] - cs2[0]);
+        const float dgrow = fast_exp2(cap);
+        // table scale 2^-kw with |table| < 1
+        const float vbound = dmax * dgrow;
         const int kw = vbound > 0.f ? min((int)((__float_as_uint(vbound) >> 23) & 0xFF) - 126, 126) : 0;
+        // |M| in units of 2^-xe: |G| dts (decay <= dgrow) < 2^(15 - sg) dmax dgrow, plus |D| on the diagonal
+        const int smx = f16_scale_exponent(ldexpf(ldexpf(dmax * dgrow, 15 - sg) + fabsf(dh), -xe));
+
         // ---- decay table of the tiles below the diagonal blocks
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
@@ -371,86 +401,93 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
             const int t = (d >> 4) & 7;
             if (t < r) {
                 const int j = 32 * t + 8 * ((d >> 1) & 3) + 4 * ((d >> 3) & 1) + 2 * (d & 1);
-                const float2 c2 = *reinterpret_cast<const float2 *>(sm.cs2 + j);
-                const float2 w2 = *reinterpret_cast<const float2 *>(sm.dts + j);
-                const float cr = sm.cs2[32 * r];
-                const float sc_t = ldexpf(1.0f, -(sm.xexp[t] + kw));
-                sm.v[d] = pack_f16x2(fast_exp2(cr - c2.x) * w2.x * sc_t, fast_exp2(cr - c2.y) * w2.y * sc_t);
+                const float2 c2 = *reinterpret_cast<const float2 *>(cs2 + j);
+                const float2 w2 = *reinterpret_cast<const float2 *>(dts + j);
+                const float cr = cs2[32 * r];
+                const float sk = ldexpf(1.0f, -kw);
+                sm.v[d] = pack_f16x2(fast_exp2(cr - c2.x) * w2.x * sk, fast_exp2(cr - c2.y) * w2.y * sk);
             }
         }
 
-        // ---- off-diagonal part: y^T_off = h_in (LDS) x C^T (registers)
-        f32x16 acc[2] = {f32x16{}, f32x16{}};
-        if (active) {
+        // ---- off-diagonal part: y^T_off = h_in (LDS) x C^T (registers).
+        // Wavefronts past the chunk end run it too and discard it.
+        f32x16 acc[2];
 #pragma unroll
-            for (int k = 0; k < KS; ++k) {
-                const f16x8 cf = __builtin_bit_cast(f16x8, cq[k]);
+        for (int k = 0; k < KS; ++k) {
+            const f16x8 cf = __builtin_bit_cast(f16x8, cq[k]);
+#pragma unroll
+            for (int pt = 0; pt < 2; ++pt) {
+                const f16x8 hf = __builtin_bit_cast(
+                    f16x8, *reinterpret_cast<const u32x4 *>(sm.h + (32 * pt + l32) * H_STRIDE + 8 * k + 4 * hl));
+                acc[pt] = mfma32_f16(hf, cf, k == 0 ? f32x16{} : acc[pt]);
+            }
+        }
+        __syncthreads();  // x^T and the table are complete; h_in is no longer read
+
+        // ======== Q(hh)
+        if (active) {  // wavefront-uniform
+            const float cs_i = cs2[i_l];
+            // undo the C and h_in scalings, decay column i by exp2(cs2_i), move to the M scale
+            {
+                const float f = ldexpf(fast_exp2(cs_i), smx - sc);
 #pragma unroll
                 for (int pt = 0; pt < 2; ++pt) {
-                    const f16x8 hf = __builtin_bit_cast(
-                        f16x8, *reinterpret_cast<const u32x4 *>(sm.h + (32 * pt + l32) * H_STRIDE + 8 * k + 4 * hl));
-                    acc[pt] = mfma32_f16(hf, cf, acc[pt]);
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) {
+                        const float4 s4 = *reinterpret_cast<const float4 *>(sm.hs[b] + 32 * pt + 8 * a + 4 * hl);
+                        acc[pt][4 * a + 0] *= f * s4.x;
+                        acc[pt][4 * a + 1] *= f * s4.y;
+                        acc[pt][4 * a + 2] *= f * s4.z;
+                        acc[pt][4 * a + 3] *= f * s4.w;
+                    }
+                }
+            }
+            // ---- diagonal block, specialised per row block
+            {
+                const float rs = ldexpf(fast_exp2(cs_i - cs2[32 * rb]), kw - sg - xe + smx);
+                const float mg = ldexpf(1.0f, smx - sg - xe);
+                const float dx = ldexpf(dh, smx - xe);
+                switch (rb) {
+                case 0: diag_block<N, 0>(sm, cs2, dts, acc, lane, cs_i, rs, mg, dx, cap); break;
+                case 1: diag_block<N, 1>(sm, cs2, dts, acc, lane, cs_i, rs, mg, dx, cap); break;
+                case 2: diag_block<N, 2>(sm, cs2, dts, acc, lane, cs_i, rs, mg, dx, cap); break;
+                case 3: diag_block<N, 3>(sm, cs2, dts, acc, lane, cs_i, rs, mg, dx, cap); break;
+                case 4: diag_block<N, 4>(sm, cs2, dts, acc, lane, cs_i, rs, mg, dx, cap); break;
+                case 5: diag_block<N, 5>(sm, cs2, dts, acc, lane, cs_i, rs, mg, dx, cap); break;
+                case 6: diag_block<N, 6>(sm, cs2, dts, acc, lane, cs_i, rs, mg, dx, cap); break;
+                default: diag_block<N, 7>(sm, cs2, dts, acc, lane, cs_i, rs, mg, dx, cap); break;
+                }
+            }
+            // ---- back to unit scale, store bf16.  Lane l holds p = 8a + 4(l/32)
+            // + 0..3 of token i_l for a = 0..3; for each pair of groups (a, a+1)
+            // one v_permlane32_swap per dword trades the upper half-wavefront's
+            // group a for the lower one's group a+1, so lanes l and l+32 (same
+            // token) each hold 8 consecutive p: one 16-byte store, 32
+            // contiguous bytes per token.
+            if (i_l < len) {  // the same for lanes l and l+32
+                const float inv = ldexpf(1.0f, -smx);
+                uint16_t *dst = p.y + ((t0 + i_l) * p.H + h) * kHeadDim + 8 * hl;
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt) {
+#pragma unroll
+                    for (int a = 0; a < 4; a += 2) {
+                        const uint32_t a0 = pack_bf16x2(acc[pt][4 * a] * inv, acc[pt][4 * a + 1] * inv);
+                        const uint32_t a1 = pack_bf16x2(acc[pt][4 * a + 2] * inv, acc[pt][4 * a + 3] * inv);
+                        const uint32_t b0 = pack_bf16x2(acc[pt][4 * a + 4] * inv, acc[pt][4 * a + 5] * inv);
+                        const uint32_t b1 = pack_bf16x2(acc[pt][4 * a + 6] * inv, acc[pt][4 * a + 7] * inv);
+                        const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+                        const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+                        *reinterpret_cast<u32x4 *>(dst + 32 * pt + 8 * a) = u32x4{s0[0], s1[0], s0[1], s1[1]};
+                    }
                 }
             }
         }
-        __syncthreads();  // the table is complete
-        if (!active) continue;  // wavefront-uniform; no barrier before the next head's
-        // |2^-xe M| <= |G| * max(dts 2^-xe) * (decay <= 1, or the chunk's total
-        // growth when A > 0) + |D| max(2^-xe) on the diagonal, with
-        // |G| < 2^(15 - sg) from the tiles' scaling
-        const float gbound = ldexpf(1.0f, 15 - sg);
-        const int smx = f16_scale_exponent(gbound * wmax * dgrow + fabsf(dh) * emax);
-        const float cs_i = sm.cs2[i_l];
-
-        // undo the C and h_in scalings, decay column i by exp2(cs2_i), move to the M scale
-        {
-            const float f = ldexpf(fast_exp2(cs_i), smx - sc);
-#pragma unroll
-            for (int pt = 0; pt < 2; ++pt) {
-#pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    const float4 s4 = *reinterpret_cast<const float4 *>(sm.hs + 32 * pt + 8 * a + 4 * hl);
-                    acc[pt][4 * a + 0] *= f * s4.x;
-                    acc[pt][4 * a + 1] *= f * s4.y;
-                    acc[pt][4 * a + 2] *= f * s4.z;
-                    acc[pt][4 * a + 3] *= f * s4.w;
-                }
-            }
-        }
-
-        // ---- diagonal block, specialised per row block
-        {
-            const int xr_e = sm.xexp[rb];
-            const float rs = ldexpf(fast_exp2(cs_i - sm.cs2[32 * rb]), kw - sg + smx);
-            const float mg = ldexpf(1.0f, smx - sg - xr_e);
-            const float dx = ldexpf(dh, smx - xr_e);
-            switch (rb) {
-            case 0: diag_block<N, 0>(sm, acc, lane, cs_i, rs, mg, dx); break;
-            case 1: diag_block<N, 1>(sm, acc, lane, cs_i, rs, mg, dx); break;
-            case 2: diag_block<N, 2>(sm, acc, lane, cs_i, rs, mg, dx); break;
-            case 3: diag_block<N, 3>(sm, acc, lane, cs_i, rs, mg, dx); break;
-            case 4: diag_block<N, 4>(sm, acc, lane, cs_i, rs, mg, dx); break;
-            case 5: diag_block<N, 5>(sm, acc, lane, cs_i, rs, mg, dx); break;
-            case 6: diag_block<N, 6>(sm, acc, lane, cs_i, rs, mg, dx); break;
-            default: diag_block<N, 7>(sm, acc, lane, cs_i, rs, mg, dx); break;
-            }
-        }
-
-        // ---- back to unit scale, store bf16: 4 consecutive p of token i_l per 8-byte write
-        if (i_l < len) {
-            const float inv = ldexpf(1.0f, -smx);
-            uint16_t *dst = p.y + ((t0 + i_l) * p.H + h) * kHeadDim + 4 * hl;
-#pragma unroll
-            for (int pt = 0; pt < 2; ++pt) {
-#pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    uint2 v;
-                    v.x = pack_bf16x2(acc[pt][4 * a] * inv, acc[pt][4 * a + 1] * inv);
-                    v.y = pack_bf16x2(acc[pt][4 * a + 2] * inv, acc[pt][4 * a + 3] * inv);
-                    *reinterpret_cast<uint2 *>(dst + 32 * pt + 8 * a) = v;
-                }
-            }
-        }
+        // h_in and tables of the next head, then those of the one after in
+        // flight.  Also after the last head (restaging it into the spare
+        // buffer), so every path back to the loop head passes the same loads.
+        stage_tabs(b ^ 1);
+        load_tabs(min(h + 2, h_last));
+        __syncthreads();
     }
 }
 

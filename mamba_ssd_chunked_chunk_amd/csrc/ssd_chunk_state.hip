@@ -32,6 +32,8 @@
 // 32 rows an MFMA operand reads fall on distinct banks); the next head's x,
 // dts and cs2 are loaded into registers during the current head's products.
 // Each lane ends up with 4 consecutive n of one p, stored as one 8-byte write.
+// The exponent that scales the chunk's largest |x| of each head into
+// [2^14, 2^15) is stored for the chunk-scan step, which stages x under it.
 #include "ssd_common.hpp"
 
 namespace ssd {
@@ -63,7 +65,7 @@ __global__ __launch_bounds__(StateShape<N>::THREADS) void ssd_chunk_state_kernel
     constexpr int XV = PPT / 8;  // 16-byte x vectors per token per thread
 
     constexpr int BR = 20;  // dwords per staged B row: 32 bf16 + 16-byte pad
-    __shared__ float s_red[kWaves];
+    __shared__ float s_red[kWaves][2];
     __shared__ __attribute__((aligned(16))) uint32_t s_xt[kHeadDim * XT_STRIDE];
     __shared__ __attribute__((aligned(16))) uint32_t s_b[kWaves][128 * BR];
 
@@ -162,9 +164,11 @@ __global__ __launch_bounds__(StateShape<N>::THREADS) void ssd_chunk_state_kernel
 #pragma unroll
         for (int k = 0; k < 16; ++k) asm volatile("" : "+v"(bq[k]));
 
-        // ---- weighted x, its maximum magnitude over the chunk and head
+        // ---- weighted x, its maximum magnitude over the chunk and head, and
+        // that of x itself (rows past the chunk end repeat its last row)
         float xv[2][PPT];
         float mloc = 0.0f;
+        u16x2 mraw2 = u16x2{0, 0};
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const float w = fast_exp2(cs_last - cs_tok[e]) * dt_tok[e];
@@ -177,16 +181,23 @@ __global__ __launch_bounds__(StateShape<N>::THREADS) void ssd_chunk_state_kernel
                 }
 #pragma unroll
             for (int k = 0; k < PPT; ++k) mloc = fmaxf(mloc, fabsf(xv[e][k]));
+#pragma unroll
+            for (int v = 0; v < XV; ++v)
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    mraw2 = __builtin_elementwise_max(mraw2, __builtin_bit_cast(u16x2, xr[e][v][k] & 0x7FFF7FFFu));
         }
         if (hh + 1 < HB) load_head(h + 1);  // next head's inputs in flight from here on
         mloc = wave_max(mloc);
+        const float mraw = wave_max(__uint_as_float(max((uint32_t)mraw2[0], (uint32_t)mraw2[1]) << 16));
         __syncthreads();  // the previous head's x^T and s_red reads are done
-        if (lane == 0) s_red[wave] = mloc;
+        if (lane == 0) { s_red[wave][0] = mloc; s_red[wave][1] = mraw; }
         __syncthreads();
-        float mx = 0.f;
+        float mx = 0.f, mxr = 0.f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, s_red[w]);
+        for (int w = 0; w < kWaves; ++w) { mx = fmaxf(mx, s_red[w][0]); mxr = fmaxf(mxr, s_red[w][1]); }
         const int sx = f16_scale_exponent(mx);
+        if (tid == 0) p.xexp[(int64_t)c * p.H + h] = f16_scale_exponent(mxr);
         const float xs = ldexpf(1.0f, sx);
 #pragma unroll
         for (int k = 0; k < PPT; ++k) {

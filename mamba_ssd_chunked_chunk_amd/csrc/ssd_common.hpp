@@ -58,6 +58,7 @@ struct Params {
     int32_t *sexp;       // [nchunks_max][H][2][N/32]: per 32x32 tile (p tile, n tile)
     uint16_t *hin;       // [nchunks_max][H][P][N] fp16, row p scaled by 2^hexp
     int32_t *hexp;       // [nchunks_max][H][P]
+    int32_t *xexp;       // [nchunks_max][H]: 2^xexp puts the chunk's max |x| of the head in [2^14, 2^15)
 };
 
 // ---------------------------------------------------------------- helpers

@@ -20,8 +20,9 @@
 //
 // Per group (blockIdx.y == 1 + g):
 //   G^T[j][i] = sum_n B[t0+j,g,n] C[t0+i,g,n] for the causal tiles (j <= i
-//   blockwise), the "attention-like" intra-chunk scores of "Mamba chunk scan
-//   with segsum" (description) before decay.  They are shared by every head
+//   blockwise; the diagonal tiles hold zeros where j > i), the
+//   "attention-like" intra-chunk scores of "Mamba chunk scan with segsum"
+//   (description) before decay.  They are shared by every head
 //   of the group, so they are formed once here (bf16 MFMA on the exact bf16
 //   inputs, fp32 accumulate) and stored in MFMA accumulator order, so the
 //   chunk-scan step reads each lane's 16 values as one 64-byte run.
@@ -100,6 +101,11 @@ __device__ __forceinline__ void gram_tiles(const Params &p, int c, int g, int64_
             }
         }
     }
+    // the diagonal tile keeps only j <= i (element e of lane l: j - 32 RB =
+    // 8(e/4) + 4(l/32) + e%4, i - 32 RB = l%32), so readers need no mask
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+        if (8 * (e >> 2) + 4 * hl + (e & 3) > l32) accg[RB][e] = 0.f;
     // one power-of-two scale for all tiles of the chunk and group
     float gm = 0.f;
 #pragma unroll

@@ -161,6 +161,7 @@ def test_intermediates_match_chunked_oracle():
     cbt16 = w[L["cbt"]:L["cbt"] + ncm * 2 * 36 * 1024 * 2].view(np.float16).reshape(ncm, 2, 36, 64, 16)
     gexp = w[L["gexp"]:L["gexp"] + ncm * 2 * 4].view(np.int32).reshape(ncm, 2)
     cbt = cbt16.astype(np.float64) * np.exp2(-gexp.astype(np.float64))[..., None, None, None]
+    xexp = w[L["xexp"]:L["xexp"] + ncm * H * 4].view(np.int32).reshape(ncm, H)
     ref = chunked_scan(prob, 256, keep_intermediates=True)["chunks"]
     qsl = prob["query_start_loc"]
     for rec in ref:
@@ -181,6 +182,12 @@ def test_intermediates_match_chunked_oracle():
         Cc = bf16_to_f64(prob["C"]).reshape(T, 2, N)[t0:t0 + l, g]
         GT = np.zeros((256, 256))
         GT[:l, :l] = Bc @ Cc.T  # G^T[j][i] = B_j . C_i
+        # x exponent of the chunk and head: 2^xexp puts the largest |x| in [2^14, 2^15)
+        xm = np.abs(bf16_to_f64(prob["x"]).reshape(T, H, P)[t0:t0 + l, h]).max()
+        if xm > 0:
+            assert 2.0 ** 14 <= xm * 2.0 ** xexp[c, h] < 2.0 ** 15
+        else:
+            assert xexp[c, h] == 0
         lane = np.arange(64)[:, None]
         e = np.arange(16)[None, :]
         gm = 0.0
@@ -189,7 +196,8 @@ def test_intermediates_match_chunked_oracle():
                 jj = 32 * t + 8 * (e // 4) + 4 * (lane // 32) + e % 4
                 ii = 32 * rb + lane % 32
                 inside = (jj < l) & (ii < l)  # entries past the chunk end are unspecified
-                np.testing.assert_allclose(cbt[c, g, rb * (rb + 1) // 2 + t][inside], GT[jj, ii][inside],
+                want = np.where(jj <= ii, GT[jj, ii], 0.0)  # the diagonal tile is zero above its diagonal
+                np.testing.assert_allclose(cbt[c, g, rb * (rb + 1) // 2 + t][inside], want[inside],
                                            rtol=2.0 ** -11, atol=np.abs(GT).max() * 2.0 ** -24)
                 gm = max(gm, np.abs(GT[jj, ii]).max())
         # the tiles' exponent keeps their largest magnitude below 2^15, and the
