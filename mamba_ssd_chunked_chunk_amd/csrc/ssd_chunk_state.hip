@@ -31,7 +31,8 @@
 // 16-byte chunks of rows 16..31 of every 32-row block swapped pairwise so the
 // 32 rows an MFMA operand reads fall on distinct banks); the next head's x,
 // dts and cs2 are loaded into registers during the current head's products.
-// Each lane ends up with 4 consecutive n of one p, stored as one 8-byte write.
+// Each lane ends up with 4 consecutive n of one p; lanes l and l+32 trade
+// halves so that each stores 8 consecutive n as one 16-byte write.
 // The exponent that scales the chunk's largest |x| of each head into
 // [2^14, 2^15) is stored for the chunk-scan step, which stages x under it.
 #include "ssd_common.hpp"
@@ -240,14 +241,19 @@ __global__ __launch_bounds__(StateShape<N>::THREADS) void ssd_chunk_state_kernel
             const float rescale = ldexpf(1.0f, se);
             const int pt = pt0 + u;
             if (lane == 0) sexp[pt * S::NT + nt] = se + sx + sb;
-            uint16_t *row = dst + (int64_t)(pt * 32 + l32) * N;
+            // lane l holds n = 8a + 4(l/32) + 0..3 of row p; per pair of groups
+            // (a, a+1) a v_permlane32_swap per dword gives lanes l and l+32
+            // 8 consecutive n each: one 16-byte store, 32 contiguous bytes per row
+            uint16_t *row = dst + (int64_t)(pt * 32 + l32) * N + nt * 32 + 8 * hl;
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const int n = nt * 32 + 8 * a + 4 * hl;
-                uint2 v;
-                v.x = pack_f16x2(acc[u][4 * a] * rescale, acc[u][4 * a + 1] * rescale);
-                v.y = pack_f16x2(acc[u][4 * a + 2] * rescale, acc[u][4 * a + 3] * rescale);
-                *reinterpret_cast<uint2 *>(row + n) = v;
+            for (int a = 0; a < 4; a += 2) {
+                const uint32_t a0 = pack_f16x2(acc[u][4 * a] * rescale, acc[u][4 * a + 1] * rescale);
+                const uint32_t a1 = pack_f16x2(acc[u][4 * a + 2] * rescale, acc[u][4 * a + 3] * rescale);
+                const uint32_t b0 = pack_f16x2(acc[u][4 * a + 4] * rescale, acc[u][4 * a + 5] * rescale);
+                const uint32_t b1 = pack_f16x2(acc[u][4 * a + 6] * rescale, acc[u][4 * a + 7] * rescale);
+                const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+                *reinterpret_cast<u32x4 *>(row + 8 * a) = u32x4{s0[0], s1[0], s0[1], s1[1]};
             }
         }
     }
