@@ -16,28 +16,46 @@
 // no tokens writes its initial state (or zeros) back.
 //
 // Chunk contributions arrive as fp16 under one power-of-two exponent per
-// 32x32 tile of (chunk, head).  The chain is fp32.  h_in only feeds the outputs y; it is stored as fp16
-// with one power-of-two scale per row p (11 significant bits: bf16's 8 would
-// put the off-diagonal part's rounding error near the tolerance of y).
-// Each thread owns four consecutive (p, n) elements of one (sequence, head),
-// reads its pool element before the sequence's loop and writes it after, so
-// the in-place read-then-write of a slot never races.  The chunk
-// contributions are loaded kDepth chunks ahead of their use, so that many
-// loads per thread are in flight while the chain advances.
+// 32x32 tile of (chunk, head).  The chain is fp32.  h_in only feeds the
+// outputs y; it is stored as fp16 with one power-of-two scale per row p (11
+// significant bits: bf16's 8 would put the off-diagonal part's rounding error
+// near the tolerance of y).  Each thread owns eight consecutive (p, n)
+// elements of one (sequence, head) (16-byte loads and stores), reads its pool
+// elements before the sequence's loop and writes them after, so the in-place
+// read-then-write of a slot never races.  The chunk contributions are loaded
+// kDepth chunks ahead of their use, so that many loads per thread are in
+// flight while the chain advances.  A row p spans N/8 lanes; its maximum is
+// taken with DPP within rows of 16 lanes and a v_permlane16_swap across them.
 #include "ssd_common.hpp"
 
 namespace ssd {
 
 namespace {
-constexpr int kDepth = 4;
-}
+constexpr int kDepth = 8;
+constexpr int kPer = 8;  // elements per thread
 
+// maximum over the aligned groups of LANES (8, 16 or 32) lanes, for values >= 0
+template <int LANES>
+__device__ __forceinline__ float row_max(float m) {
+    m = dpp_max_step<0xB1, 0xF>(m);  // quad_perm [1,0,3,2]
+    m = dpp_max_step<0x4E, 0xF>(m);  // quad_perm [2,3,0,1]
+    m = dpp_max_step<0x141, 0xF>(m); // row_half_mirror: groups of 8
+    if constexpr (LANES >= 16) m = dpp_max_step<0x140, 0xF>(m);  // row_mirror: rows of 16
+    if constexpr (LANES >= 32) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+        m = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));  // rows 2r and 2r+1
+    }
+    return m;
+}
+}  // namespace
+
+template <int N>
 __global__ __launch_bounds__(256) void ssd_state_passing_kernel(Params p) {
     const int b = blockIdx.x;
     const int h = blockIdx.y;
-    const int64_t head_elems = (int64_t)kHeadDim * p.N;
-    const int64_t e0 = ((int64_t)blockIdx.z * 256 + threadIdx.x) * 4;
-    if (e0 >= head_elems) return;
+    constexpr int64_t head_elems = (int64_t)kHeadDim * N;  // a multiple of 256 * kPer
+    const int64_t e0 = ((int64_t)blockIdx.z * 256 + threadIdx.x) * kPer;
+    if (e0 >= head_elems) return;  // whole workgroups only
 
     // clamped to the table so malformed query_start_loc cannot index past it
     const int k1 = (int)min((int64_t)p.chunk_off[b + 1], p.nchunks_max);
@@ -46,76 +64,95 @@ __global__ __launch_bounds__(256) void ssd_state_passing_kernel(Params p) {
     const bool init = p.has_init != nullptr && p.has_init[b] != 0;
     float4 *pool4 = reinterpret_cast<float4 *>(p.pool + (slot * p.H + h) * head_elems + e0);
 
-    float4 st = init ? *pool4 : make_float4(0.f, 0.f, 0.f, 0.f);
+    float st[kPer];
+    {
+        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 lo = init ? pool4[0] : z, hi = init ? pool4[1] : z;
+        st[0] = lo.x; st[1] = lo.y; st[2] = lo.z; st[3] = lo.w;
+        st[4] = hi.x; st[5] = hi.y; st[6] = hi.z; st[7] = hi.w;
+    }
     const int64_t stride = (int64_t)p.H * head_elems;  // one chunk of states
     const uint16_t *S = p.states + ((int64_t)k0 * p.H + h) * head_elems + e0;
     // exponent of this thread's 32x32 tile (p / 32, n / 32) in each chunk
-    const int NT = p.N / 32;
-    const int tile = (int)((e0 / p.N) >> 5) * NT + (int)((e0 % p.N) >> 5);
+    const int NT = N / 32;
+    const int tile = (int)((e0 / N) >> 5) * NT + (int)((e0 % N) >> 5);
     const int32_t *sexp = p.sexp + ((int64_t)k0 * p.H + h) * 2 * NT + tile;
     const int64_t sexp_stride = (int64_t)p.H * 2 * NT;
     const float *cs_last = p.cs2 + ((int64_t)k0 * p.H + h) * kChunk + kChunk - 1;
     const int64_t cs_stride = (int64_t)p.H * kChunk;
     uint16_t *hin = p.hin + ((int64_t)k0 * p.H + h) * head_elems + e0;
-    int32_t *hexp = p.hexp + ((int64_t)k0 * p.H + h) * kHeadDim + e0 / p.N;
+    int32_t *hexp = p.hexp + ((int64_t)k0 * p.H + h) * kHeadDim + e0 / N;
     const int nk = k1 - k0;
 
-    // ring of the next kDepth chunk contributions: fp16 values, their exponent, cs2_last
-    uint2 s[kDepth];
-    int se[kDepth];
-    float d[kDepth];
+    // one link of the chain: store h_in of chunk k (row-scaled fp16), then
+    // advance the state by chunk k's decay and contribution
+    auto link = [&](int k, const u32x4 &sv, int sev, float dv) {
+        // h_in row p as fp16, scaled by the power of two that puts the row's
+        // max |h| in [2^14, 2^15)
+        float m = 0.f;
 #pragma unroll
-    for (int q = 0; q < kDepth; ++q) {
-        s[q] = make_uint2(0u, 0u);
-        se[q] = 0;
-        d[q] = 0.f;
-        if (q < nk) {
-            s[q] = *reinterpret_cast<const uint2 *>(S + q * stride);
-            se[q] = sexp[q * sexp_stride];
-            d[q] = cs_last[q * cs_stride];
+        for (int e = 0; e < kPer; ++e) m = fmaxf(m, fabsf(st[e]));
+        m = row_max<N / kPer>(m);
+        const int sh = f16_scale_exponent(m);
+        const float sc = ldexpf(1.0f, sh);
+        u32x4 hv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hv[e] = pack_f16x2(st[2 * e] * sc, st[2 * e + 1] * sc);
+        *reinterpret_cast<u32x4 *>(hin + (int64_t)k * stride) = hv;
+        hexp[(int64_t)k * p.H * kHeadDim] = sh;  // every lane of the row: the same value
+        const float dec = fast_exp2(dv);
+        const float us = ldexpf(1.0f, -sev);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            st[2 * e] = dec * st[2 * e] + f16_bits_to_float(sv[e] & 0xFFFFu) * us;
+            st[2 * e + 1] = dec * st[2 * e + 1] + f16_bits_to_float(sv[e] >> 16) * us;
         }
-    }
-    for (int kb = 0; kb < nk; kb += kDepth) {
+    };
+    // chunk k's contribution, exponent and decay (k clamped into the sequence)
+    auto fetch = [&](int k, u32x4 &sv, int &sev, float &dv) {
+        const int kk = min(k, nk - 1);
+        sv = *reinterpret_cast<const u32x4 *>(S + (int64_t)kk * stride);
+        sev = sexp[(int64_t)kk * sexp_stride];
+        dv = cs_last[(int64_t)kk * cs_stride];
+    };
+    int kb = 0;
+    if (nk >= kDepth) {
+        // ring of the next kDepth chunks; full rounds of kDepth links, each
+        // refilling its slot kDepth chunks ahead (past the end: the last chunk again)
+        u32x4 s[kDepth];
+        int se[kDepth];
+        float d[kDepth];
 #pragma unroll
-        for (int q = 0; q < kDepth; ++q) {
-            const int k = kb + q;
-            if (k < nk) {
-                // h_in row p as fp16, scaled by the power of two that puts the
-                // row's max |h| in [2^14, 2^15); the N/4 lanes of one row share it
-                float m = fmaxf(fmaxf(fabsf(st.x), fabsf(st.y)), fmaxf(fabsf(st.z), fabsf(st.w)));
-                // row max: rows are N/4 consecutive lanes (16, 32 or 64)
-                m = row16_max(m);
-                if (p.N >= 128) m = fmaxf(m, __shfl_xor(m, 16, 64));
-                if (p.N >= 256) m = fmaxf(m, __shfl_xor(m, 32, 64));
-                const int sh = f16_scale_exponent(m);
-                const float sc = ldexpf(1.0f, sh);
-                uint2 hv;
-                hv.x = pack_f16x2(st.x * sc, st.y * sc);
-                hv.y = pack_f16x2(st.z * sc, st.w * sc);
-                *reinterpret_cast<uint2 *>(hin + (int64_t)k * stride) = hv;
-                if (e0 % p.N == 0) hexp[(int64_t)k * p.H * kHeadDim] = sh;
-                const float dec = fast_exp2(d[q]);
-                const float us = ldexpf(1.0f, -se[q]);
-                st.x = dec * st.x + f16_bits_to_float(s[q].x & 0xFFFFu) * us;
-                st.y = dec * st.y + f16_bits_to_float(s[q].x >> 16) * us;
-                st.z = dec * st.z + f16_bits_to_float(s[q].y & 0xFFFFu) * us;
-                st.w = dec * st.w + f16_bits_to_float(s[q].y >> 16) * us;
-                if (k + kDepth < nk) {  // refill this ring slot kDepth chunks ahead
-                    s[q] = *reinterpret_cast<const uint2 *>(S + (int64_t)(k + kDepth) * stride);
-                    se[q] = sexp[(int64_t)(k + kDepth) * sexp_stride];
-                    d[q] = cs_last[(int64_t)(k + kDepth) * cs_stride];
-                }
+        for (int q = 0; q < kDepth; ++q) fetch(q, s[q], se[q], d[q]);
+        for (; kb + kDepth <= nk; kb += kDepth) {
+#pragma unroll
+            for (int q = 0; q < kDepth; ++q) {
+                link(kb + q, s[q], se[q], d[q]);
+                fetch(kb + q + kDepth, s[q], se[q], d[q]);
             }
         }
     }
-    *pool4 = st;
+    for (; kb < nk; ++kb) {  // the rest, one chunk at a time
+        u32x4 sv;
+        int sev;
+        float dv;
+        fetch(kb, sv, sev, dv);
+        link(kb, sv, sev, dv);
+    }
+    pool4[0] = make_float4(st[0], st[1], st[2], st[3]);
+    pool4[1] = make_float4(st[4], st[5], st[6], st[7]);
 }
 
 hipError_t launch_state_passing(const Params &p, hipStream_t s) {
     const int64_t head_elems = (int64_t)kHeadDim * p.N;
-    const unsigned zb = (unsigned)((head_elems / 4 + 255) / 256);
+    const unsigned zb = (unsigned)((head_elems / kPer + 255) / 256);
     dim3 grid((unsigned)p.batch, (unsigned)p.H, zb);
-    hipLaunchKernelGGL(ssd_state_passing_kernel, grid, dim3(256), 0, s, p);
+    switch (p.N) {
+    case 64: hipLaunchKernelGGL(ssd_state_passing_kernel<64>, grid, dim3(256), 0, s, p); break;
+    case 128: hipLaunchKernelGGL(ssd_state_passing_kernel<128>, grid, dim3(256), 0, s, p); break;
+    case 256: hipLaunchKernelGGL(ssd_state_passing_kernel<256>, grid, dim3(256), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
