@@ -102,67 +102,64 @@ __device__ __forceinline__ void x_operands(const ScanSmem<N> &sm, int l32, int h
     x1 = __builtin_bit_cast(f16x8, u32x4{xc.x, xc.y, xd.x, xd.y});
 }
 
-// The diagonal block of row block RB for one head, added to acc (in units of
-// 2^smx; x is staged as 2^xe x):
-//   tiles t < RB:  acc2 += (2^xe x)^T (C.B^T 2^sg (.) table), one product per
-//                  tile, then acc += acc2 * rs,
-//                  rs = exp2(cs2_i - cs2[32 RB]) * 2^(kw - sg - xe + smx)
-//   tile t = RB:   M per element, exp2(cs2_i - cs2_j) dts_j C.B^T_ij times
-//                  mg = 2^(smx - sg - xe), plus dx = D 2^(smx - xe) on the
-//                  diagonal.  The tile is zero where j > i; there the exp2
-//                  argument is capped at the chunk's total log2 growth (0 for
-//                  A <= 0), which leaves every j <= i unchanged and keeps the
-//                  masked products finite.
+// The tiles of row block RB strictly below its diagonal tile, for one head:
+//   acc2 = sum_{t < RB} (2^xe x_t)^T (C.B^T_t 2^sg (.) table_t)
+// one product per tile; the caller scales acc2 per lane (row i) and adds it.
 template <int N, int RB>
-__device__ __forceinline__ void diag_block(const ScanSmem<N> &sm, const float *cs2, const float *dts, f32x16 (&acc)[2],
-                                           int lane, float cs_i, float rs, float mg, float dx, float cap) {
+__device__ __forceinline__ void below_diag(const ScanSmem<N> &sm, f32x16 (&acc2)[2], int lane) {
     const int l32 = lane & 31;
     const int hl = lane >> 5;
-    const int i_l = 32 * RB + l32;
     const u32x4 *gbase = reinterpret_cast<const u32x4 *>(sm.g) + (RB * (RB + 1) / 2) * 128 + lane;
-    if constexpr (RB > 0) {
-        f32x16 acc2[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-        for (int t = 0; t < RB; ++t) {
-            const u32x4 g0 = gbase[t * 128], g1 = gbase[t * 128 + 64];
-            const u32x4 *vp = reinterpret_cast<const u32x4 *>(sm.v + RB * 128 + t * 16 + hl * 8);
-            const u32x4 v0 = vp[0], v1 = vp[1];
-            u32x4 m0, m1;
+    for (int t = 0; t < RB; ++t) {
+        const u32x4 g0 = gbase[t * 128], g1 = gbase[t * 128 + 64];
+        const u32x4 *vp = reinterpret_cast<const u32x4 *>(sm.v + RB * 128 + t * 16 + hl * 8);
+        const u32x4 v0 = vp[0], v1 = vp[1];
+        u32x4 m0, m1;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                m0[q] = hmul2(g0[q], v0[q]);
-                m1[q] = hmul2(g1[q], v1[q]);
-            }
-            const f16x8 mf0 = __builtin_bit_cast(f16x8, m0), mf1 = __builtin_bit_cast(f16x8, m1);
-#pragma unroll
-            for (int pt = 0; pt < 2; ++pt) {
-                f16x8 x0, x1;
-                x_operands(sm, l32, hl, t, pt, x0, x1);
-                acc2[pt] = mfma32_f16(x0, mf0, acc2[pt]);
-                acc2[pt] = mfma32_f16(x1, mf1, acc2[pt]);
-            }
+        for (int q = 0; q < 4; ++q) {
+            m0[q] = hmul2(g0[q], v0[q]);
+            m1[q] = hmul2(g1[q], v1[q]);
         }
+        const f16x8 mf0 = __builtin_bit_cast(f16x8, m0), mf1 = __builtin_bit_cast(f16x8, m1);
 #pragma unroll
-        for (int pt = 0; pt < 2; ++pt)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[pt][e] = __builtin_fmaf(acc2[pt][e], rs, acc[pt][e]);
+        for (int pt = 0; pt < 2; ++pt) {
+            f16x8 x0, x1;
+            x_operands(sm, l32, hl, t, pt, x0, x1);
+            acc2[pt] = mfma32_f16(x0, mf0, acc2[pt]);
+            acc2[pt] = mfma32_f16(x1, mf1, acc2[pt]);
+        }
     }
-    // the diagonal tile
-    const u32x4 gt[2] = {gbase[RB * 128], gbase[RB * 128 + 64]};
+}
+
+// The diagonal tile (t = rb) of row block rb, added to acc in units of
+// 2^smx (x staged as 2^xe x): M per element,
+//   exp2(cs2_i - cs2_j + lmg) dts_j C.B^T_ij  with lmg = smx - sg - xe,
+// plus dx = D 2^(smx - xe) on the diagonal.  ci = cs2_i + lmg.  The tile is
+// zero where j > i; there the exp2 argument is capped at the chunk's total
+// log2 growth (0 for A <= 0), plus lmg (capm), which leaves every j <= i
+// unchanged and keeps the masked products finite.
+template <int N>
+__device__ __forceinline__ void diag_tile(const ScanSmem<N> &sm, const float *cs2, const float *dts, f32x16 (&acc)[2],
+                                          int lane, int rb, float ci, float capm, float dx) {
+    const int l32 = lane & 31;
+    const int hl = lane >> 5;
+    const int i_l = 32 * rb + l32;
+    const u32x4 *gp = reinterpret_cast<const u32x4 *>(sm.g) + (rb * (rb + 1) / 2 + rb) * 128 + lane;
+    const u32x4 gt[2] = {gp[0], gp[64]};
     float mv[16];
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-        const int j0 = 32 * RB + 8 * a + 4 * hl;
+        const int j0 = 32 * rb + 8 * a + 4 * hl;
         const float4 c4 = *reinterpret_cast<const float4 *>(cs2 + j0);
         const float4 d4 = *reinterpret_cast<const float4 *>(dts + j0);
         const float cj[4] = {c4.x, c4.y, c4.z, c4.w};
         const float dj[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            const int j = j0 + b;
             const uint32_t w = gt[a >> 1][2 * (a & 1) + (b >> 1)];
-            const float val = hmul(w, b & 1, fast_exp2(fminf(cs_i - cj[b], cap)) * (dj[b] * mg));
-            mv[4 * a + b] = j == i_l ? val + dx : val;
+            const float val = hmul(w, b & 1, fast_exp2(fminf(ci - cj[b], capm)) * dj[b]);
+            mv[4 * a + b] = j0 + b == i_l ? val + dx : val;
         }
     }
     const f16x8 mf0 = __builtin_bit_cast(f16x8, u32x4{pack_f16x2(mv[0], mv[1]), pack_f16x2(mv[2], mv[3]),
@@ -172,7 +169,7 @@ __device__ __forceinline__ void diag_block(const ScanSmem<N> &sm, const float *c
 #pragma unroll
     for (int pt = 0; pt < 2; ++pt) {
         f16x8 x0, x1;
-        x_operands(sm, l32, hl, RB, pt, x0, x1);
+        x_operands(sm, l32, hl, rb, pt, x0, x1);
         acc[pt] = mfma32_f16(x0, mf0, acc[pt]);
         acc[pt] = mfma32_f16(x1, mf1, acc[pt]);
     }
@@ -442,21 +439,30 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
                     }
                 }
             }
-            // ---- diagonal block, specialised per row block
-            {
-                const float rs = ldexpf(fast_exp2(cs_i - cs2[32 * rb]), kw - sg - xe + smx);
-                const float mg = ldexpf(1.0f, smx - sg - xe);
-                const float dx = ldexpf(dh, smx - xe);
+            // ---- diagonal block: the tiles below its diagonal tile (code
+            // specialised per row block), scaled per row and added, then the
+            // diagonal tile itself
+            if (rb > 0) {  // wavefront-uniform
+                f32x16 acc2[2] = {f32x16{}, f32x16{}};
                 switch (rb) {
-                case 0: diag_block<N, 0>(sm, cs2, dts, acc, lane, cs_i, rs, mg, dx, cap); break;
-                case 1: diag_block<N, 1>(sm, cs2, dts, acc, lane, cs_i, rs, mg, dx, cap); break;
-                case 2: diag_block<N, 2>(sm, cs2, dts, acc, lane, cs_i, rs, mg, dx, cap); break;
-                case 3: diag_block<N, 3>(sm, cs2, dts, acc, lane, cs_i, rs, mg, dx, cap); break;
-                case 4: diag_block<N, 4>(sm, cs2, dts, acc, lane, cs_i, rs, mg, dx, cap); break;
-                case 5: diag_block<N, 5>(sm, cs2, dts, acc, lane, cs_i, rs, mg, dx, cap); break;
-                case 6: diag_block<N, 6>(sm, cs2, dts, acc, lane, cs_i, rs, mg, dx, cap); break;
-                default: diag_block<N, 7>(sm, cs2, dts, acc, lane, cs_i, rs, mg, dx, cap); break;
+                case 1: below_diag<N, 1>(sm, acc2, lane); break;
+                case 2: below_diag<N, 2>(sm, acc2, lane); break;
+                case 3: below_diag<N, 3>(sm, acc2, lane); break;
+                case 4: below_diag<N, 4>(sm, acc2, lane); break;
+                case 5: below_diag<N, 5>(sm, acc2, lane); break;
+                case 6: below_diag<N, 6>(sm, acc2, lane); break;
+                default: below_diag<N, 7>(sm, acc2, lane); break;
                 }
+                // exp2(cs2_i - cs2[32 rb]) * 2^(kw - sg - xe + smx)
+                const float rs = ldexpf(fast_exp2(cs_i - cs2[32 * rb]), kw - sg - xe + smx);
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) acc[pt][e] = __builtin_fmaf(acc2[pt][e], rs, acc[pt][e]);
+            }
+            {
+                const float lmg = (float)(smx - sg - xe);
+                diag_tile(sm, cs2, dts, acc, lane, rb, cs_i + lmg, cap + lmg, ldexpf(dh, smx - xe));
             }
             // ---- back to unit scale, store bf16.  Lane l holds p = 8a + 4(l/32)
             // + 0..3 of token i_l for a = 0..3; for each pair of groups (a, a+1)

@@ -73,12 +73,15 @@ __device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
     return __builtin_bit_cast(uint16_t, b);
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)float_to_bf16_bits(lo) | ((uint32_t)float_to_bf16_bits(hi) << 16);
-}
-
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// two floats -> two bf16 (nearest even) in one dword: one v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const bf16x2 h = __builtin_convertvector((f32x2){lo, hi}, bf16x2);
+    return __builtin_bit_cast(uint32_t, h);
+}
 
 // two floats -> two fp16 (nearest even) in one dword: v_cvt_pk_f16_f32 on gfx950
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
