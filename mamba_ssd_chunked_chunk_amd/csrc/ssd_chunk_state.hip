@@ -66,8 +66,8 @@ __global__ __launch_bounds__(StateShape<N>::THREADS) void ssd_chunk_state_kernel
     constexpr int XV = PPT / 8;  // 16-byte x vectors per token per thread
 
     constexpr int BR = 20;  // dwords per staged B row: 32 bf16 + 16-byte pad
-    __shared__ float s_red[kWaves][2];
-    __shared__ __attribute__((aligned(16))) uint32_t s_xt[kHeadDim * XT_STRIDE];
+    __shared__ float s_red[2][kWaves][2];
+    __shared__ __attribute__((aligned(16))) uint32_t s_xt[2][kHeadDim * XT_STRIDE];
     __shared__ __attribute__((aligned(16))) uint32_t s_b[kWaves][128 * BR];
 
     const int nhb = p.H / HB;
@@ -138,9 +138,17 @@ __global__ __launch_bounds__(StateShape<N>::THREADS) void ssd_chunk_state_kernel
         }
     }
 
-    // ---- per-head inputs: thread = (p part, token pair)
+    // ---- per-head inputs: thread = (p part, token pair).  The head loop is
+    // software-pipelined over two phases, each closed by a barrier:
+    //   A(k): the MFMAs of head k (x^T of head k in buffer k & 1), meanwhile
+    //         weighting x of head k+1 and its wavefront maxima
+    //   B(k): staging x^T of head k+1 into the other buffer, storing S of head k
+    // so the products of one head overlap the VALU work of the next.  Inputs
+    // are loaded two heads ahead; past the last head the loads repeat it (no
+    // branch, so the compiler's wait counts stay exact).
     const int pair = tid & 127;
     const int pp = tid >> 7;  // p part: p = pp * PPT ..
+    const int h_last = h_first + HB - 1;
     u32x4 xr[2][XV];
     float cs_tok[2], dt_tok[2], cs_last;
     auto load_head = [&](int h) {
@@ -157,17 +165,10 @@ __global__ __launch_bounds__(StateShape<N>::THREADS) void ssd_chunk_state_kernel
             cs_last = p.cs2[crow + kChunk - 1];
         }
     };
-    load_head(h_first);
-
-#pragma unroll
-    for (int hh = 0; hh < HB; ++hh) {
-        const int h = h_first + hh;
-#pragma unroll
-        for (int k = 0; k < 16; ++k) asm volatile("" : "+v"(bq[k]));
-
-        // ---- weighted x, its maximum magnitude over the chunk and head, and
-        // that of x itself (rows past the chunk end repeat its last row)
-        float xv[2][PPT];
+    // weighted x of the loaded head into xv, the wavefront maxima of |w x| and
+    // |x| into s_red[b] (rows past the chunk end repeat its last row, with w = 0)
+    float xv[2][PPT];
+    auto weigh = [&](int b) {
         float mloc = 0.0f;
         u16x2 mraw2 = u16x2{0, 0};
 #pragma unroll
@@ -179,41 +180,64 @@ __global__ __launch_bounds__(StateShape<N>::THREADS) void ssd_chunk_state_kernel
                 for (int k = 0; k < 4; ++k) {
                     xv[e][v * 8 + 2 * k] = w * __uint_as_float(xr[e][v][k] << 16);
                     xv[e][v * 8 + 2 * k + 1] = w * __uint_as_float(xr[e][v][k] & 0xFFFF0000u);
+                    mraw2 = __builtin_elementwise_max(mraw2, __builtin_bit_cast(u16x2, xr[e][v][k] & 0x7FFF7FFFu));
                 }
 #pragma unroll
             for (int k = 0; k < PPT; ++k) mloc = fmaxf(mloc, fabsf(xv[e][k]));
-#pragma unroll
-            for (int v = 0; v < XV; ++v)
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    mraw2 = __builtin_elementwise_max(mraw2, __builtin_bit_cast(u16x2, xr[e][v][k] & 0x7FFF7FFFu));
         }
-        if (hh + 1 < HB) load_head(h + 1);  // next head's inputs in flight from here on
         mloc = wave_max(mloc);
         const float mraw = wave_max(__uint_as_float(max((uint32_t)mraw2[0], (uint32_t)mraw2[1]) << 16));
-        __syncthreads();  // the previous head's x^T and s_red reads are done
-        if (lane == 0) { s_red[wave][0] = mloc; s_red[wave][1] = mraw; }
-        __syncthreads();
+        s_red[b][wave][0] = mloc;  // the same value from every lane
+        s_red[b][wave][1] = mraw;
+    };
+    // x^T of the weighed head into s_xt[b] under the power of two that puts
+    // its maximum in [2^14, 2^15); returns that exponent.  Also stores the
+    // head's x exponent for the chunk-scan step.
+    auto stage = [&](int b, int h) -> int {
         float mx = 0.f, mxr = 0.f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) { mx = fmaxf(mx, s_red[w][0]); mxr = fmaxf(mxr, s_red[w][1]); }
+        for (int w = 0; w < kWaves; ++w) { mx = fmaxf(mx, s_red[b][w][0]); mxr = fmaxf(mxr, s_red[b][w][1]); }
         const int sx = f16_scale_exponent(mx);
-        if (tid == 0) p.xexp[(int64_t)c * p.H + h] = f16_scale_exponent(mxr);
+        p.xexp[(int64_t)c * p.H + h] = f16_scale_exponent(mxr);  // the same value from every thread
         const float xs = ldexpf(1.0f, sx);
 #pragma unroll
         for (int k = 0; k < PPT; ++k) {
             const int row = pp * PPT + k;
             // token pair `pair` sits in 16-byte chunk pair/4 of the row
-            s_xt[row * XT_STRIDE + swz(row, (pair >> 2) << 2) + (pair & 3)] =
+            s_xt[b][row * XT_STRIDE + swz(row, (pair >> 2) << 2) + (pair & 3)] =
                 pack_f16x2(xv[0][k] * xs, xv[1][k] * xs);
         }
-        __syncthreads();
+        return sx;
+    };
 
-        // ---- S^T tiles: rows n (tile nt), columns p (tiles pt0..)
-        f32x16 acc[PTW];
+    // ---- prologue: head 0 weighed and staged, head 1 in flight
+    load_head(h_first);
+    weigh(0);
+    load_head(min(h_first + 1, h_last));
+    __syncthreads();
+    int sx = stage(0, h_first);
+    __syncthreads();
+
 #pragma unroll
-        for (int u = 0; u < PTW; ++u) acc[u] = f32x16{};
-        // all 16 K-steps: both operands are zero past the chunk end
+    for (int hh = 0; hh < HB; ++hh) {
+        const int h = h_first + hh;
+        const int b = hh & 1;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) asm volatile("" : "+v"(bq[k]));
+        // this head's prefetched inputs are first touched here: otherwise the
+        // scheduler hoists their unpacking into the previous head, right
+        // behind the loads, and the wait for them stalls that head
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+#pragma unroll
+            for (int v = 0; v < XV; ++v) asm volatile("" : "+v"(xr[e][v]));
+            asm volatile("" : "+v"(cs_tok[e]), "+v"(dt_tok[e]));
+        }
+        asm volatile("" : "+v"(cs_last));
+
+        // ======== A(hh): S^T tiles of head hh (rows n of tile nt, columns p of
+        // tiles pt0..); all 16 K-steps: both operands are zero past the chunk end
+        f32x16 acc[PTW];
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
             const f16x8 bf = __builtin_bit_cast(f16x8, bq[k]);
@@ -221,13 +245,19 @@ __global__ __launch_bounds__(StateShape<N>::THREADS) void ssd_chunk_state_kernel
             for (int u = 0; u < PTW; ++u) {
                 const int xrow = (pt0 + u) * 32 + l32;
                 const f16x8 xf = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4 *>(
-                    s_xt + xrow * XT_STRIDE + swz(xrow, 8 * k + 4 * hl)));
-                acc[u] = mfma32_f16(bf, xf, acc[u]);
+                    s_xt[b] + xrow * XT_STRIDE + swz(xrow, 8 * k + 4 * hl)));
+                acc[u] = mfma32_f16(bf, xf, k == 0 ? f32x16{} : acc[u]);
             }
         }
+        // meanwhile: the next head weighed, the one after it in flight
+        weigh(b ^ 1);
+        load_head(min(h + 2, h_last));
+        __syncthreads();  // x^T of head hh is no longer read; s_red[b ^ 1] complete
 
-        // ---- store S[c][h][p][n] as fp16, one power-of-two exponent per tile:
-        // the accumulator is 2^(sx+sb) S; rescale so that the tile's max |S|
+        // ======== B(hh): stage the next head, store S of this one
+        const int sx_next = stage(b ^ 1, min(h + 1, h_last));
+        // S[c][h][p][n] as fp16, one power-of-two exponent per tile: the
+        // accumulator is 2^(sx+sb) S; rescale so that the tile's max |S|
         // lands in [2^14, 2^15) (relative rounding 2^-11 per element)
         uint16_t *dst = p.states + ((int64_t)c * p.H + h) * kHeadDim * N;
         int32_t *sexp = p.sexp + ((int64_t)c * p.H + h) * 2 * S::NT;
@@ -240,7 +270,9 @@ __global__ __launch_bounds__(StateShape<N>::THREADS) void ssd_chunk_state_kernel
             const int se = f16_scale_exponent(am);  // stored S = 2^se * acc = 2^(se + sx + sb) S
             const float rescale = ldexpf(1.0f, se);
             const int pt = pt0 + u;
-            if (lane == 0) sexp[pt * S::NT + nt] = se + sx + sb;
+            // every lane stores the same value: no branch, so the compiler
+            // counts this store on every path and its waits stay exact
+            sexp[pt * S::NT + nt] = se + sx + sb;
             // lane l holds n = 8a + 4(l/32) + 0..3 of row p; per pair of groups
             // (a, a+1) a v_permlane32_swap per dword gives lanes l and l+32
             // 8 consecutive n each: one 16-byte store, 32 contiguous bytes per row
@@ -256,6 +288,8 @@ __global__ __launch_bounds__(StateShape<N>::THREADS) void ssd_chunk_state_kernel
                 *reinterpret_cast<u32x4 *>(row + 8 * a) = u32x4{s0[0], s1[0], s0[1], s1[1]};
             }
         }
+        sx = sx_next;
+        __syncthreads();  // x^T of the next head complete
     }
 }
 
