@@ -37,20 +37,20 @@
 // Decay without one exp2 per element.  For a tile strictly below the
 // diagonal block (all j < 32*rb <= i), exp2(cs2_i - cs2_j) =
 // exp2(cs2_i - cs2_r) * exp2(cs2_r - cs2_j) with r = 32*rb; both factors are
-// at most 1 for A <= 0.  The second factor, times dts_j and the x block
-// scale, is tabulated once per head in LDS as fp16 in each lane's operand
-// order, so such a tile's M operand is the C.B^T tile times the table, eight
+// at most 1 for A <= 0.  The second factor, times dts_j, is tabulated once
+// per head in LDS as fp16 in each lane's operand order, so such a tile's M operand is the C.B^T tile times the table, eight
 // packed fp16 multiplies per lane; the first factor depends only on the
 // lane's row i and is applied once per head, in fp32, to a second
 // accumulator that collects those tiles.  Only the diagonal tile evaluates
 // exp2 per element.  The skip term D*x is folded into the diagonal of M.
 //
 // Precision.  M and h_in are rounded to fp16 (11-bit significand) under
-// power-of-two scales that keep them far from overflow (one per wavefront
-// and head for the diagonal M tile, one per head for the table, one per row
-// for h_in); C and C.B^T are rounded to fp16 after power-of-two scalings (per
-// row block, per chunk and group), and each 32-token block of x after its
-// own power-of-two scaling, compensated inside M or the table.  The product
+// power-of-two scales that keep them far from overflow (one per head for
+// the diagonal M tile and for the table, one per row for h_in); C and C.B^T
+// are rounded to fp16 after power-of-two scalings (per row block, per chunk
+// and group), and x after one power of two per chunk and head (none while
+// its largest magnitude is in [2^-6, 2^15)), compensated inside M or the
+// accumulator scale.  The product
 // of a C.B^T tile and the table is rounded to fp16 once more.  All products
 // accumulate in fp32.  bf16 (8 bits) for M or h_in would put the rounding
 // error, which scales with the typical size of y rather than with each y,
