@@ -126,11 +126,17 @@ def roofline_entry(name, alg, t_us, traffic=None):
 
 
 def kernel_sources_hash():
+    """Hash of the kernel sources with comments and runs of white space
+    removed: counters stay valid across edits that change no code."""
+    import re
     csrc = os.path.join(ROOT, "mamba_ssd_chunked_chunk_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".hpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+            text = open(os.path.join(csrc, f), encoding="utf-8").read()
+            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", " ", text)
+            h.update((f + ":" + " ".join(text.split()) + "\n").encode())
     return h.hexdigest()[:16]
 
 
