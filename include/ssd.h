@@ -164,11 +164,14 @@ int ssd_kernel_count(void);
 const char *ssd_kernel_name(int i);
 
 /* Same computation as ssd_chunk_scan_varlen_fwd_inplace; additionally
- * records events[i] (each a hipEvent_t created by the caller, passed as
- * void*) on `stream` just before kernel i is enqueued and
- * events[ssd_kernel_count()] after the last one, so a caller can time each
- * step with hipEventElapsedTime.  n_events must equal ssd_kernel_count()+1
- * (SSD_ERR_NULL_ARG / SSD_ERR_BAD_SHAPE otherwise, before any launch).     */
+ * records events (each a hipEvent_t created by the caller, passed as void*)
+ * through the kernels' own dispatches, so no command is enqueued between
+ * kernels: events[0] when kernel 0 starts and events[i+1] when kernel i
+ * completes.  hipEventElapsedTime(events[i], events[i+1]) is then kernel i's
+ * time (with the gap before it, for i > 0) and (events[0],
+ * events[ssd_kernel_count()]) the whole call.  n_events must equal
+ * ssd_kernel_count()+1 (SSD_ERR_NULL_ARG / SSD_ERR_BAD_SHAPE otherwise,
+ * before any launch).                                                      */
 ssd_status ssd_chunk_scan_varlen_fwd_inplace_profiled(
     const ssd_problem *prob,
     void *y, const void *x, const float *dt, const float *A,

@@ -168,15 +168,15 @@ static ssd_status run_scan(
     p.hin = reinterpret_cast<uint16_t *>(ws + L.hin);
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t (*const launchers[kNumKernels])(const ssd::Params &, hipStream_t) = {
+    hipError_t (*const launchers[kNumKernels])(const ssd::Params &, const ssd::Launch &) = {
         ssd::launch_prep, ssd::launch_chunk_state, ssd::launch_state_passing, ssd::launch_chunk_scan};
     for (int k = 0; k < kNumKernels; ++k) {
-        if (events && hipEventRecord(static_cast<hipEvent_t>(events[k]), s) != hipSuccess)
-            return SSD_ERR_HIP;
-        if (launchers[k](p, s) != hipSuccess) return SSD_ERR_HIP;
+        // events, if any, are recorded by the dispatches themselves: the start
+        // of the first kernel and the end of every kernel
+        const ssd::Launch l{s, events && k == 0 ? static_cast<hipEvent_t>(events[0]) : nullptr,
+                            events ? static_cast<hipEvent_t>(events[k + 1]) : nullptr};
+        if (launchers[k](p, l) != hipSuccess) return SSD_ERR_HIP;
     }
-    if (events && hipEventRecord(static_cast<hipEvent_t>(events[kNumKernels]), s) != hipSuccess)
-        return SSD_ERR_HIP;
     return SSD_OK;
 }
 

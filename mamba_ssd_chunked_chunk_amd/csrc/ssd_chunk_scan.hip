@@ -510,27 +510,26 @@ static int heads_per_block(const Params &p) {
 }
 
 template <int N, int HB>
-static hipError_t launch_nh(const Params &p, hipStream_t s) {
+static hipError_t launch_nh(const Params &p, const Launch &l) {
     const int64_t slots = (p.nchunks_max + 7) / 8 * (p.H / HB);
-    hipLaunchKernelGGL((ssd_chunk_scan_kernel<N, HB>), dim3((unsigned)(slots * 8)), dim3(kThreads), 0, s, p);
-    return hipGetLastError();
+    return launch_kernel(ssd_chunk_scan_kernel<N, HB>, dim3((unsigned)(slots * 8)), dim3(kThreads), l, p);
 }
 
 template <int N>
-static hipError_t launch_n(const Params &p, hipStream_t s) {
+static hipError_t launch_n(const Params &p, const Launch &l) {
     switch (heads_per_block(p)) {
-    case 8: return launch_nh<N, 8>(p, s);
-    case 4: return launch_nh<N, 4>(p, s);
-    case 2: return launch_nh<N, 2>(p, s);
-    default: return launch_nh<N, 1>(p, s);
+    case 8: return launch_nh<N, 8>(p, l);
+    case 4: return launch_nh<N, 4>(p, l);
+    case 2: return launch_nh<N, 2>(p, l);
+    default: return launch_nh<N, 1>(p, l);
     }
 }
 
-hipError_t launch_chunk_scan(const Params &p, hipStream_t s) {
+hipError_t launch_chunk_scan(const Params &p, const Launch &l) {
     switch (p.N) {
-    case 64: return launch_n<64>(p, s);
-    case 128: return launch_n<128>(p, s);
-    case 256: return launch_n<256>(p, s);
+    case 64: return launch_n<64>(p, l);
+    case 128: return launch_n<128>(p, l);
+    case 256: return launch_n<256>(p, l);
     default: return hipErrorInvalidValue;
     }
 }

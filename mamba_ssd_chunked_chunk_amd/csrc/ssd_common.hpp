@@ -11,6 +11,7 @@
 // keep the prefix sums in log2 units ("cs2") and call the hardware exp2.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -215,8 +216,22 @@ __device__ __forceinline__ int float_exponent(float m) {
 
 // Host-side launchers (one per kernel file).
 namespace ssd {
-hipError_t launch_prep(const Params &p, hipStream_t s);
-hipError_t launch_chunk_state(const Params &p, hipStream_t s);
-hipError_t launch_state_passing(const Params &p, hipStream_t s);
-hipError_t launch_chunk_scan(const Params &p, hipStream_t s);
+// Where a kernel is launched: the stream, and events (or null) that the
+// kernel's own dispatch records when it starts and when it completes, so
+// timing adds no commands between kernels.
+struct Launch {
+    hipStream_t stream;
+    hipEvent_t start;
+    hipEvent_t stop;
+};
+template <typename K>
+inline hipError_t launch_kernel(K kernel, dim3 grid, dim3 block, const Launch &l, const Params &p) {
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, l.stream, l.start, l.stop, 0, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_prep(const Params &p, const Launch &l);
+hipError_t launch_chunk_state(const Params &p, const Launch &l);
+hipError_t launch_state_passing(const Params &p, const Launch &l);
+hipError_t launch_chunk_scan(const Params &p, const Launch &l);
 }  // namespace ssd

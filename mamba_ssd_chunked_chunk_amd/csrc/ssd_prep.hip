@@ -43,19 +43,33 @@ constexpr int kHeadBlock = 16;
 constexpr int R_STRIDE = 20;  // dwords per staged row of 32 bf16 + pad
 }  // namespace
 
-// The C.B^T tiles of row block RB (t <= RB) for chunk c and group g, run by
-// one wavefront of the workgroup; the row block is a template parameter so
-// that the number of tiles, and with it every MFMA, is fixed at compile time.
-template <int N, int RB>
+// Tiles of the C.B^T job per wavefront.  SIMD s (= W & 3) owns row blocks s
+// and 7-s, 9 tiles: its first wavefront (W < 4) takes all of row block s and
+// the first 4-s tiles of row block 7-s (5 tiles), its second wavefront the
+// other 4 tiles of row block 7-s.  Tile i of wavefront W is (row block
+// tile_rb, column block tile_t), with t <= rb.
+__host__ __device__ constexpr int gram_ntiles(int W) { return W < 4 ? 5 : 4; }
+__host__ __device__ constexpr int gram_tile_rb(int W, int i) {
+    return W < 4 ? (i <= (W & 3) ? (W & 3) : 7 - (W & 3)) : 7 - (W & 3);
+}
+__host__ __device__ constexpr int gram_tile_t(int W, int i) {
+    return W < 4 ? (i <= (W & 3) ? i : i - ((W & 3) + 1)) : (4 - (W & 3)) + i;
+}
+
+// The C.B^T tiles of wavefront W (above) for chunk c and group g.  W is a
+// template parameter so that the tile list, and with it every MFMA, is fixed
+// at compile time.
+template <int N, int W>
 __device__ __forceinline__ void gram_tiles(const Params &p, int c, int g, int64_t t0, int len, uint32_t *s_b,
                                            uint32_t *s_c, float *s_gmax) {
     constexpr int KS = N / 32;
+    constexpr int NTW = gram_ntiles(W);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int l32 = lane & 31;
     const int hl = lane >> 5;
-    constexpr int PD = KS < 3 ? KS : 3;  // slices in flight
+    constexpr int PD = KS < 4 ? KS : 4;  // slices in flight
     u32x4 rbv[PD][2], rcv[PD][2];
     auto load_slice = [&](int ks, int d) {
 #pragma unroll
@@ -69,9 +83,9 @@ __device__ __forceinline__ void gram_tiles(const Params &p, int c, int g, int64_
             rcv[d][it] = *reinterpret_cast<const u32x4 *>(p.C + off);
         }
     };
-    f32x16 accg[8];
+    f32x16 accg[NTW];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) accg[t] = f32x16{};
+    for (int i = 0; i < NTW; ++i) accg[i] = f32x16{};
 
 #pragma unroll
     for (int d = 0; d < PD; ++d) load_slice(d, d);
@@ -89,30 +103,31 @@ __device__ __forceinline__ void gram_tiles(const Params &p, int c, int g, int64_
         __syncthreads();
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            const bf16x8 cb = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const u32x4 *>(s_c + (32 * RB + l32) * R_STRIDE + 8 * kk + 4 * hl));
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                if (t <= RB) {
-                    const bf16x8 bb = __builtin_bit_cast(
-                        bf16x8, *reinterpret_cast<const u32x4 *>(s_b + (32 * t + l32) * R_STRIDE + 8 * kk + 4 * hl));
-                    accg[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bb, cb, accg[t], 0, 0, 0);
-                }
+            for (int i = 0; i < NTW; ++i) {
+                const int rb = gram_tile_rb(W, i), t = gram_tile_t(W, i);
+                const bf16x8 cb = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const u32x4 *>(s_c + (32 * rb + l32) * R_STRIDE + 8 * kk + 4 * hl));
+                const bf16x8 bb = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const u32x4 *>(s_b + (32 * t + l32) * R_STRIDE + 8 * kk + 4 * hl));
+                accg[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bb, cb, accg[i], 0, 0, 0);
             }
         }
     }
-    // the diagonal tile keeps only j <= i (element e of lane l: j - 32 RB =
-    // 8(e/4) + 4(l/32) + e%4, i - 32 RB = l%32), so readers need no mask
+    // the diagonal tiles keep only j <= i (element e of lane l: j - 32 rb =
+    // 8(e/4) + 4(l/32) + e%4, i - 32 rb = l%32), so readers need no mask
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
-        if (8 * (e >> 2) + 4 * hl + (e & 3) > l32) accg[RB][e] = 0.f;
+    for (int i = 0; i < NTW; ++i)
+        if (gram_tile_rb(W, i) == gram_tile_t(W, i))
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                if (8 * (e >> 2) + 4 * hl + (e & 3) > l32) accg[i][e] = 0.f;
     // one power-of-two scale for all tiles of the chunk and group
     float gm = 0.f;
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-        if (t <= RB)
+    for (int i = 0; i < NTW; ++i)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) gm = fmaxf(gm, fabsf(accg[t][e]));
+        for (int e = 0; e < 16; ++e) gm = fmaxf(gm, fabsf(accg[i][e]));
     gm = wave_max(gm);
     if (lane == 0) s_gmax[wave] = gm;
     __syncthreads();
@@ -125,16 +140,15 @@ __device__ __forceinline__ void gram_tiles(const Params &p, int c, int g, int64_
     // tiles in accumulator order: tile rb(rb+1)/2 + t, 64 lanes x 16 fp16
     uint16_t *dst = p.cbt + ((int64_t)c * p.G + g) * 36 * 1024;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        if (t <= RB) {
-            u32x4 *o = reinterpret_cast<u32x4 *>(dst + (RB * (RB + 1) / 2 + t) * 1024 + lane * 16);
+    for (int i = 0; i < NTW; ++i) {
+        const int rb = gram_tile_rb(W, i), t = gram_tile_t(W, i);
+        u32x4 *o = reinterpret_cast<u32x4 *>(dst + (rb * (rb + 1) / 2 + t) * 1024 + lane * 16);
 #pragma unroll
-            for (int q = 0; q < 2; ++q)
-                o[q] = u32x4{pack_f16x2(accg[t][8 * q] * gs, accg[t][8 * q + 1] * gs),
-                             pack_f16x2(accg[t][8 * q + 2] * gs, accg[t][8 * q + 3] * gs),
-                             pack_f16x2(accg[t][8 * q + 4] * gs, accg[t][8 * q + 5] * gs),
-                             pack_f16x2(accg[t][8 * q + 6] * gs, accg[t][8 * q + 7] * gs)};
-        }
+        for (int q = 0; q < 2; ++q)
+            o[q] = u32x4{pack_f16x2(accg[i][8 * q] * gs, accg[i][8 * q + 1] * gs),
+                         pack_f16x2(accg[i][8 * q + 2] * gs, accg[i][8 * q + 3] * gs),
+                         pack_f16x2(accg[i][8 * q + 4] * gs, accg[i][8 * q + 5] * gs),
+                         pack_f16x2(accg[i][8 * q + 6] * gs, accg[i][8 * q + 7] * gs)};
     }
 }
 
@@ -241,10 +255,10 @@ __global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(Params p) {
         return;
     }
 
-    // ---- group g: C.B^T tiles; SIMD k (= wave & 3) runs row blocks k and 7-k
+    // ---- group g: C.B^T tiles; SIMD k (= wave & 3) runs the 9 tiles of row
+    // blocks k and 7-k, split 5 + 4 between its two wavefronts
     const int g = job - 1;
-    const int wv = __builtin_amdgcn_readfirstlane(wave);
-    switch ((wv >> 2) ? 7 - (wv & 3) : (wv & 3)) {
+    switch (__builtin_amdgcn_readfirstlane(wave)) {
     case 0: gram_tiles<N, 0>(p, c, g, t0, len, s_b, s_c, s_gmax); break;
     case 1: gram_tiles<N, 1>(p, c, g, t0, len, s_b, s_c, s_gmax); break;
     case 2: gram_tiles<N, 2>(p, c, g, t0, len, s_b, s_c, s_gmax); break;
@@ -256,15 +270,14 @@ __global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(Params p) {
     }
 }
 
-hipError_t launch_prep(const Params &p, hipStream_t s) {
+hipError_t launch_prep(const Params &p, const Launch &l) {
     const dim3 grid((unsigned)p.nchunks_max, (unsigned)(1 + p.G));
     switch (p.N) {
-    case 64: hipLaunchKernelGGL(ssd_prep_kernel<64>, grid, dim3(kPrepThreads), 0, s, p); break;
-    case 128: hipLaunchKernelGGL(ssd_prep_kernel<128>, grid, dim3(kPrepThreads), 0, s, p); break;
-    case 256: hipLaunchKernelGGL(ssd_prep_kernel<256>, grid, dim3(kPrepThreads), 0, s, p); break;
+    case 64: return launch_kernel(ssd_prep_kernel<64>, grid, dim3(kPrepThreads), l, p);
+    case 128: return launch_kernel(ssd_prep_kernel<128>, grid, dim3(kPrepThreads), l, p);
+    case 256: return launch_kernel(ssd_prep_kernel<256>, grid, dim3(kPrepThreads), l, p);
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace ssd

@@ -143,17 +143,16 @@ __global__ __launch_bounds__(256) void ssd_state_passing_kernel(Params p) {
     pool4[1] = make_float4(st[4], st[5], st[6], st[7]);
 }
 
-hipError_t launch_state_passing(const Params &p, hipStream_t s) {
+hipError_t launch_state_passing(const Params &p, const Launch &l) {
     const int64_t head_elems = (int64_t)kHeadDim * p.N;
     const unsigned zb = (unsigned)((head_elems / kPer + 255) / 256);
     dim3 grid((unsigned)p.batch, (unsigned)p.H, zb);
     switch (p.N) {
-    case 64: hipLaunchKernelGGL(ssd_state_passing_kernel<64>, grid, dim3(256), 0, s, p); break;
-    case 128: hipLaunchKernelGGL(ssd_state_passing_kernel<128>, grid, dim3(256), 0, s, p); break;
-    case 256: hipLaunchKernelGGL(ssd_state_passing_kernel<256>, grid, dim3(256), 0, s, p); break;
+    case 64: return launch_kernel(ssd_state_passing_kernel<64>, grid, dim3(256), l, p);
+    case 128: return launch_kernel(ssd_state_passing_kernel<128>, grid, dim3(256), l, p);
+    case 256: return launch_kernel(ssd_state_passing_kernel<256>, grid, dim3(256), l, p);
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace ssd
