@@ -189,11 +189,8 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
     const int xcd = id & 7;
     const int slot = id >> 3;
     const int c = (slot / nhb) * 8 + xcd;
+    const int cc = min(c, (int)p.nchunks_max - 1);  // a row of the chunk tables
     const int hb = slot - (slot / nhb) * nhb;
-    if (c >= p.meta[0]) return;
-    const int4 dsc = p.desc[c];
-    const int64_t t0 = dsc.y;
-    const int len = dsc.z;
     const int h_first = hb * HB;
     const int g = h_first / (p.H / p.G);
 
@@ -204,55 +201,9 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
     const int hl = lane >> 5;
     // row block of this wavefront: SIMD k (= wave & 3) runs blocks k and 7-k
     const int rb = (wave >> 2) ? 7 - (wave & 3) : (wave & 3);
-    const bool active = 32 * rb < len;  // wavefront-uniform
     const int i_l = 32 * rb + l32;      // this lane's token (column of y^T)
-
-    // ---- per-group operands of this wavefront's row block, prepared once for all heads
-    // C row i_l (raw bf16), 8 values per K-step.  Rows past the chunk end
-    // repeat its last row: their outputs are never stored, and in C.B^T they
-    // only meet x rows that are zero, so they just need to be finite.
-    u32x4 cq[KS];
-    const int64_t rstride = (int64_t)p.G * N;  // elements between consecutive tokens of B and C
-    {
-        const uint16_t *crow = p.C + (t0 + min(i_l, len - 1)) * rstride + (int64_t)g * N + 8 * hl;
-#pragma unroll
-        for (int k = 0; k < KS; ++k) cq[k] = *reinterpret_cast<const u32x4 *>(crow + 16 * k);
-    }
-    // this row block's C.B^T tiles (from the prep step) into LDS, each lane its
-    // own 32 bytes, read back only by the same lane (no barrier needed)
-    {
-        const uint16_t *cbt = p.cbt + (((int64_t)c * p.G + g) * 36 + rb * (rb + 1) / 2) * 1024 + lane * 16;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            if (t <= rb && 32 * t < len) {
-                const u32x4 a = *reinterpret_cast<const u32x4 *>(cbt + t * 1024);
-                const u32x4 b = *reinterpret_cast<const u32x4 *>(cbt + t * 1024 + 8);
-                u32x4 *d = reinterpret_cast<u32x4 *>(sm.g) + (rb * (rb + 1) / 2 + t) * 128 + lane;
-                d[0] = a;
-                d[64] = b;
-            }
-        }
-    }
-    const int sg = p.gexp[(int64_t)c * p.G + g];
-    // C rows to fp16 under this wavefront's exponent sc
-    int sc;
-    {
-        uint32_t m = 0;
-#pragma unroll
-        for (int k = 0; k < KS; ++k)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) m = max(m, max(cq[k][q] & 0x7FFFu, (cq[k][q] >> 16) & 0x7FFFu));
-        sc = f16_scale_exponent(wave_max(__uint_as_float(m << 16)));
-        const float cs = ldexpf(1.0f, sc);
-#pragma unroll
-        for (int k = 0; k < KS; ++k) {
-            u32x4 o;
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                o[q] = pack_f16x2(__uint_as_float(cq[k][q] << 16) * cs, __uint_as_float(cq[k][q] & 0xFFFF0000u) * cs);
-            cq[k] = o;
-        }
-    }
+    int64_t t0 = 0;  // the chunk's first token and length, once the chunk table is read
+    int len = 1;
 
     // ---- per-head inputs.  Two phases per head k, each closed by a barrier:
     //   P(k): stage x^T(k), build the decay table, off-diagonal products
@@ -270,13 +221,13 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
     int tab_hx = 0, tab_xe = 0;
     const float *dsrc = p.D ? p.D : p.A;  // a valid address either way; D = 0 when absent
     auto load_tabs = [&](int h) {
-        const int64_t r = ((int64_t)c * p.H + h) * kChunk + (tid & (kChunk - 1));
+        const int64_t r = ((int64_t)cc * p.H + h) * kChunk + (tid & (kChunk - 1));
         tab_cs = p.cs2[r];
         tab_dt = p.dts[r];
-        tab_hx = p.hexp[((int64_t)c * p.H + h) * kHeadDim + (tid & (kHeadDim - 1))];
+        tab_hx = p.hexp[((int64_t)cc * p.H + h) * kHeadDim + (tid & (kHeadDim - 1))];
         tab_dh = dsrc[h];
-        tab_xe = p.xexp[(int64_t)c * p.H + h];
-        const uint16_t *hin_head = p.hin + ((int64_t)c * p.H + h) * kHeadDim * N;
+        tab_xe = p.xexp[(int64_t)cc * p.H + h];
+        const uint16_t *hin_head = p.hin + ((int64_t)cc * p.H + h) * kHeadDim * N;
 #pragma unroll
         for (int it = 0; it < HVEC; ++it)
             hreg[it] = *reinterpret_cast<const u32x4 *>(hin_head + (tid + it * kThreads) * 8);
@@ -311,8 +262,78 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
         }
     };
     const int h_last = h_first + HB - 1;
+    // ---- loads that need only the chunk index go out before the chunk
+    // table is read: this head's tables and h_in, the row block's C.B^T
+    // tiles (all eight loads; past the row block's last tile they repeat it:
+    // behind the wavefront-dependent condition each load would wait for the
+    // previous one).  Workgroups past the chunk count read row cc, inside
+    // the tables, and leave.
+    const int nchunks = p.meta[0];
+    const int4 dsc = p.desc[cc];
     load_tabs(h_first);
+    u32x4 ga[8], gb[8];
+    {
+        const uint16_t *cbt = p.cbt + (((int64_t)cc * p.G + g) * 36 + rb * (rb + 1) / 2) * 1024 + lane * 16;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int tt = min(t, rb);
+            ga[t] = *reinterpret_cast<const u32x4 *>(cbt + tt * 1024);
+            gb[t] = *reinterpret_cast<const u32x4 *>(cbt + tt * 1024 + 8);
+        }
+    }
+    // keeps the loads above ahead of the chunk-count test (they would
+    // otherwise be moved behind it, and wait for it)
+    asm volatile("" ::: "memory");
+    if (c >= nchunks) return;
+    t0 = dsc.y;
+    len = dsc.z;
+    const bool active = 32 * rb < len;  // wavefront-uniform
     load_x(h_first);
+
+    // ---- per-group operands of this wavefront's row block, prepared once for all heads
+    // C row i_l (raw bf16), 8 values per K-step.  Rows past the chunk end
+    // repeat its last row: their outputs are never stored, and in C.B^T they
+    // only meet x rows that are zero, so they just need to be finite.
+    u32x4 cq[KS];
+    const int64_t rstride = (int64_t)p.G * N;  // elements between consecutive tokens of B and C
+    {
+        const uint16_t *crow = p.C + (t0 + min(i_l, len - 1)) * rstride + (int64_t)g * N + 8 * hl;
+#pragma unroll
+        for (int k = 0; k < KS; ++k) cq[k] = *reinterpret_cast<const u32x4 *>(crow + 16 * k);
+    }
+    // this row block's C.B^T tiles into LDS, each lane its own 32 bytes, read
+    // back only by the same lane (no barrier needed)
+    {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            if (t <= rb && 32 * t < len) {
+                u32x4 *d = reinterpret_cast<u32x4 *>(sm.g) + (rb * (rb + 1) / 2 + t) * 128 + lane;
+                d[0] = ga[t];
+                d[64] = gb[t];
+            }
+        }
+    }
+    const int sg = p.gexp[(int64_t)c * p.G + g];
+    // C rows to fp16 under this wavefront's exponent sc
+    int sc;
+    {
+        uint32_t m = 0;
+#pragma unroll
+        for (int k = 0; k < KS; ++k)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) m = max(m, max(cq[k][q] & 0x7FFFu, (cq[k][q] >> 16) & 0x7FFFu));
+        sc = f16_scale_exponent(wave_max(__uint_as_float(m << 16)));
+        const float cs = ldexpf(1.0f, sc);
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+            u32x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                o[q] = pack_f16x2(__uint_as_float(cq[k][q] << 16) * cs, __uint_as_float(cq[k][q] & 0xFFFF0000u) * cs);
+            cq[k] = o;
+        }
+    }
+
     stage_tabs(0);
     // the first head's x is complete before the next loads are issued, so at
     // the loop head, on either path, x is older than everything still in flight

@@ -92,52 +92,6 @@ __global__ __launch_bounds__(StateShape<N>::THREADS) void ssd_chunk_state_kernel
     const int nt = wave % S::NT;
     const int pt0 = PTW == 2 ? 0 : wave / S::NT;
 
-    // ---- B^T fragments of n tile nt: row n = 32 nt + l32, tokens 16 k + 8 hl .. +8,
-    // as fp16 scaled by 2^sb (sb: this n tile's exponent)
-    u32x4 bq[16];
-    int sb;
-    {
-        // lane: token (lane / 4) + 16 s, 16-byte chunk lane % 4 of the tile's 64 bytes
-        const int64_t rstride = (int64_t)p.G * N;
-        const uint16_t *bcol = p.B + (t0 * p.G + g) * N + 32 * nt + 8 * (lane & 3);
-        u32x4 raw[16];
-#pragma unroll
-        for (int s2 = 0; s2 < 16; ++s2) {
-            const int j = (lane >> 2) + 16 * s2;
-            raw[s2] = *reinterpret_cast<const u32x4 *>(bcol + min(j, len - 1) * rstride);
-            if (j >= len) raw[s2] = u32x4{};
-        }
-        uint32_t m = 0;
-#pragma unroll
-        for (int s2 = 0; s2 < 16; ++s2)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) m = max(m, max(raw[s2][k] & 0x7FFFu, (raw[s2][k] >> 16) & 0x7FFFu));
-        sb = f16_scale_exponent(wave_max(__uint_as_float(m << 16)));
-        const float bs = ldexpf(1.0f, sb);
-        uint32_t *reg = s_b[wave];
-        const uint16_t *reg16 = reinterpret_cast<const uint16_t *>(reg);
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            // rows = tokens 128 half .. +128 (wavefront-private region; LDS
-            // accesses of one wavefront complete in order)
-#pragma unroll
-            for (int s2 = 0; s2 < 8; ++s2)
-                *reinterpret_cast<u32x4 *>(reg + ((lane >> 2) + 16 * s2) * BR + 4 * (lane & 3)) = raw[8 * half + s2];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int r0 = 16 * k + 8 * hl;  // local row of the fragment's first token
-                u32x4 f;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t lo = reg16[(r0 + 2 * q) * 2 * BR + l32];
-                    const uint32_t hi = reg16[(r0 + 2 * q + 1) * 2 * BR + l32];
-                    f[q] = pack_f16x2(__uint_as_float(lo << 16) * bs, __uint_as_float(hi << 16) * bs);
-                }
-                bq[8 * half + k] = f;
-            }
-        }
-    }
-
     // ---- per-head inputs: thread = (p part, token pair).  The head loop is
     // software-pipelined over two phases, each closed by a barrier:
     //   A(k): the MFMAs of head k (x^T of head k in buffer k & 1), meanwhile
@@ -210,8 +164,56 @@ __global__ __launch_bounds__(StateShape<N>::THREADS) void ssd_chunk_state_kernel
         return sx;
     };
 
-    // ---- prologue: head 0 weighed and staged, head 1 in flight
+    // the first head's inputs are in flight while the B^T fragments are prepared
     load_head(h_first);
+
+    // ---- B^T fragments of n tile nt: row n = 32 nt + l32, tokens 16 k + 8 hl .. +8,
+    // as fp16 scaled by 2^sb (sb: this n tile's exponent)
+    u32x4 bq[16];
+    int sb;
+    {
+        // lane: token (lane / 4) + 16 s, 16-byte chunk lane % 4 of the tile's 64 bytes
+        const int64_t rstride = (int64_t)p.G * N;
+        const uint16_t *bcol = p.B + (t0 * p.G + g) * N + 32 * nt + 8 * (lane & 3);
+        u32x4 raw[16];
+#pragma unroll
+        for (int s2 = 0; s2 < 16; ++s2) {
+            const int j = (lane >> 2) + 16 * s2;
+            raw[s2] = *reinterpret_cast<const u32x4 *>(bcol + min(j, len - 1) * rstride);
+            if (j >= len) raw[s2] = u32x4{};
+        }
+        uint32_t m = 0;
+#pragma unroll
+        for (int s2 = 0; s2 < 16; ++s2)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) m = max(m, max(raw[s2][k] & 0x7FFFu, (raw[s2][k] >> 16) & 0x7FFFu));
+        sb = f16_scale_exponent(wave_max(__uint_as_float(m << 16)));
+        const float bs = ldexpf(1.0f, sb);
+        uint32_t *reg = s_b[wave];
+        const uint16_t *reg16 = reinterpret_cast<const uint16_t *>(reg);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            // rows = tokens 128 half .. +128 (wavefront-private region; LDS
+            // accesses of one wavefront complete in order)
+#pragma unroll
+            for (int s2 = 0; s2 < 8; ++s2)
+                *reinterpret_cast<u32x4 *>(reg + ((lane >> 2) + 16 * s2) * BR + 4 * (lane & 3)) = raw[8 * half + s2];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int r0 = 16 * k + 8 * hl;  // local row of the fragment's first token
+                u32x4 f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t lo = reg16[(r0 + 2 * q) * 2 * BR + l32];
+                    const uint32_t hi = reg16[(r0 + 2 * q + 1) * 2 * BR + l32];
+                    f[q] = pack_f16x2(__uint_as_float(lo << 16) * bs, __uint_as_float(hi << 16) * bs);
+                }
+                bq[8 * half + k] = f;
+            }
+        }
+    }
+
+    // ---- prologue: head 0 weighed and staged, head 1 in flight
     weigh(0);
     load_head(min(h_first + 1, h_last));
     __syncthreads();
