@@ -61,7 +61,12 @@ namespace ssd {
 
 namespace {
 constexpr int kThreads = 512;
-constexpr int XT_STRIDE = 130;  // dwords per x^T row: 128 token pairs + pad (8-byte aligned rows)
+// x^T rows: 128 token pairs + pad (8-byte aligned rows).  Row p keeps token
+// pair q at column q ^ (16 * ((p >> 4) & 3)): the staging stores, where the
+// four lanes of a token pair write rows 16 apart (32 banks apart at this
+// stride), then fall in distinct banks; the swizzle moves whole 16-pair
+// groups, so reads stay contiguous.
+constexpr int XT_STRIDE = 130;
 
 template <int N>
 struct __attribute__((aligned(16))) ScanSmem {
@@ -79,14 +84,14 @@ struct __attribute__((aligned(16))) ScanSmem {
     float hs[2][kHeadDim];  // 2^-hexp[p]
     float dd[2];            // D of the head
     int xexp[2];            // x exponent of the chunk and head
+    float dmx[2][4];        // max |dts| over each quarter of the chunk's tokens
 };
 
-// One fp16 half of a packed dword times a float, as a single mixed-precision
-// FMA with a zero addend (v_fma_mix_f32: the fp16 operand is read directly,
-// the product rounded once).
-__device__ __forceinline__ float hmul(uint32_t w, int hi, float f) {
+// One fp16 half of a packed dword times a float plus a float, as a single
+// mixed-precision FMA (v_fma_mix_f32: the fp16 operand is read directly).
+__device__ __forceinline__ float hfma(uint32_t w, int hi, float f, float c) {
     const f16x2 h2 = __builtin_bit_cast(f16x2, w);
-    return __builtin_fmaf((float)h2[hi], f, 0.0f);
+    return __builtin_fmaf((float)h2[hi], f, c);
 }
 // Product of two fp16 pairs (v_pk_mul_f16).
 __device__ __forceinline__ uint32_t hmul2(uint32_t a, uint32_t b) {
@@ -96,38 +101,55 @@ __device__ __forceinline__ uint32_t hmul2(uint32_t a, uint32_t b) {
 // x^T rows (32*pt + l32) of column tile t as the two A operands of a K = 32 step.
 template <int N>
 __device__ __forceinline__ void x_operands(const ScanSmem<N> &sm, int l32, int hl, int t, int pt, f16x8 &x0, f16x8 &x1) {
-    const uint2 *row = reinterpret_cast<const uint2 *>(sm.xt + (32 * pt + l32) * XT_STRIDE + 16 * t + 2 * hl);
+    const int sw = (2 * pt + (l32 >> 4)) & 3;  // the row's swizzle
+    const uint2 *row = reinterpret_cast<const uint2 *>(sm.xt + (32 * pt + l32) * XT_STRIDE + 16 * (t ^ sw) + 2 * hl);
     const uint2 xa = row[0], xb = row[2], xc = row[4], xd = row[6];
     x0 = __builtin_bit_cast(f16x8, u32x4{xa.x, xa.y, xb.x, xb.y});
     x1 = __builtin_bit_cast(f16x8, u32x4{xc.x, xc.y, xd.x, xd.y});
 }
 
 // The tiles of row block RB strictly below its diagonal tile, for one head:
-//   acc2 = sum_{t < RB} (2^xe x_t)^T (C.B^T_t 2^sg (.) table_t)
-// one product per tile; the caller scales acc2 per lane (row i) and adds it.
+//   acc += sum_{t < RB} (2^xe x_t)^T (C.B^T_t 2^sg (.) table_t)
+// one product per tile; the caller scales acc per lane (row i) afterwards.
 template <int N, int RB>
-__device__ __forceinline__ void below_diag(const ScanSmem<N> &sm, f32x16 (&acc2)[2], int lane) {
+__device__ __forceinline__ void below_diag(const ScanSmem<N> &sm, f32x16 (&acc)[2], int lane) {
     const int l32 = lane & 31;
     const int hl = lane >> 5;
     const u32x4 *gbase = reinterpret_cast<const u32x4 *>(sm.g) + (RB * (RB + 1) / 2) * 128 + lane;
+    // the C.B^T and table operands of tile t + 1 are read during tile t's
+    // products, its x^T operands at its start
+    struct Ops {
+        u32x4 g0, g1, v0, v1;
+    };
+    auto fetch = [&](int t, Ops &o) {
+        o.g0 = gbase[t * 128];
+        o.g1 = gbase[t * 128 + 64];
+        const u32x4 *vp = reinterpret_cast<const u32x4 *>(sm.v + RB * 128 + t * 16 + hl * 8);
+        o.v0 = vp[0];
+        o.v1 = vp[1];
+    };
+    Ops ops[2];
+    fetch(0, ops[0]);
 #pragma unroll
     for (int t = 0; t < RB; ++t) {
-        const u32x4 g0 = gbase[t * 128], g1 = gbase[t * 128 + 64];
-        const u32x4 *vp = reinterpret_cast<const u32x4 *>(sm.v + RB * 128 + t * 16 + hl * 8);
-        const u32x4 v0 = vp[0], v1 = vp[1];
+        const Ops &o = ops[t & 1];
+        f16x8 x[2][2];
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt) x_operands(sm, l32, hl, t, pt, x[pt][0], x[pt][1]);
+        if (t + 1 < RB) fetch(t + 1, ops[(t + 1) & 1]);
+        // keeps the reads ahead (the scheduler would sink them to their use)
+        __builtin_amdgcn_sched_barrier(0);
         u32x4 m0, m1;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            m0[q] = hmul2(g0[q], v0[q]);
-            m1[q] = hmul2(g1[q], v1[q]);
+            m0[q] = hmul2(o.g0[q], o.v0[q]);
+            m1[q] = hmul2(o.g1[q], o.v1[q]);
         }
         const f16x8 mf0 = __builtin_bit_cast(f16x8, m0), mf1 = __builtin_bit_cast(f16x8, m1);
 #pragma unroll
         for (int pt = 0; pt < 2; ++pt) {
-            f16x8 x0, x1;
-            x_operands(sm, l32, hl, t, pt, x0, x1);
-            acc2[pt] = mfma32_f16(x0, mf0, acc2[pt]);
-            acc2[pt] = mfma32_f16(x1, mf1, acc2[pt]);
+            acc[pt] = mfma32_f16(x[pt][0], mf0, acc[pt]);
+            acc[pt] = mfma32_f16(x[pt][1], mf1, acc[pt]);
         }
     }
 }
@@ -144,7 +166,7 @@ __device__ __forceinline__ void diag_tile(const ScanSmem<N> &sm, const float *cs
                                           int lane, int rb, float ci, float capm, float dx) {
     const int l32 = lane & 31;
     const int hl = lane >> 5;
-    const int i_l = 32 * rb + l32;
+    const int dl = l32 - 4 * hl;  // the lane's diagonal element is the one with 8a + b == dl
     const u32x4 *gp = reinterpret_cast<const u32x4 *>(sm.g) + (rb * (rb + 1) / 2 + rb) * 128 + lane;
     const u32x4 gt[2] = {gp[0], gp[64]};
     float mv[16];
@@ -158,8 +180,7 @@ __device__ __forceinline__ void diag_tile(const ScanSmem<N> &sm, const float *cs
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const uint32_t w = gt[a >> 1][2 * (a & 1) + (b >> 1)];
-            const float val = hmul(w, b & 1, fast_exp2(fminf(ci - cj[b], capm)) * dj[b]);
-            mv[4 * a + b] = j0 + b == i_l ? val + dx : val;
+            mv[4 * a + b] = hfma(w, b & 1, fast_exp2(fminf(ci - cj[b], capm)) * dj[b], 8 * a + b == dl ? dx : 0.0f);
         }
     }
     const f16x8 mf0 = __builtin_bit_cast(f16x8, u32x4{pack_f16x2(mv[0], mv[1]), pack_f16x2(mv[2], mv[3]),
@@ -245,9 +266,11 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
     };
     const bool has_d = p.D != nullptr;
     auto stage_tabs = [&](int b) {
-        if (tid < kChunk) {
+        if (tid < kChunk) {  // four whole wavefronts
             sm.cs2[b][tid] = tab_cs;
             sm.dts[b][tid] = tab_dt;
+            const float m = wave_max(fabsf(tab_dt));
+            if ((tid & 63) == 0) sm.dmx[b][tid >> 6] = m;
         } else if (tid < kChunk + kHeadDim) {
             sm.hs[b][tid - kChunk] = ldexpf(1.0f, -tab_hx);
         } else if (tid == kChunk + kHeadDim) {
@@ -365,6 +388,40 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
         const int pair = tid >> 2;
 
         // ======== P(hh)
+        // ---- off-diagonal part: y^T_off = h_in (LDS) x C^T (registers).
+        // Wavefronts past the chunk end run it too and discard it.  Of the
+        // two wavefronts on a SIMD, the one with the lower row block runs
+        // these products first and the staging below after them, the other
+        // the reverse, so one's matrix products overlap the other's
+        // vector work.
+        f32x16 acc[2];
+        auto offdiag = [&] {
+            // h_in fragments read kPre K-steps ahead of their products
+            constexpr int kPre = KS < 4 ? KS : 4;
+            const uint32_t *hrow = sm.h + l32 * H_STRIDE + 4 * hl;
+            u32x4 hb[kPre][2];
+#pragma unroll
+            for (int k = 0; k < kPre; ++k)
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt)
+                    hb[k][pt] = *reinterpret_cast<const u32x4 *>(hrow + 32 * pt * H_STRIDE + 8 * k);
+#pragma unroll
+            for (int k = 0; k < KS; ++k) {
+                const f16x8 cf = __builtin_bit_cast(f16x8, cq[k]);
+                const u32x4 h0 = hb[k % kPre][0], h1 = hb[k % kPre][1];
+                if (k + kPre < KS) {
+#pragma unroll
+                    for (int pt = 0; pt < 2; ++pt)
+                        hb[k % kPre][pt] = *reinterpret_cast<const u32x4 *>(hrow + 32 * pt * H_STRIDE + 8 * (k + kPre));
+                }
+                // keeps the reads ahead (the scheduler would sink them to their use)
+                __builtin_amdgcn_sched_barrier(0);
+                acc[0] = mfma32_f16(__builtin_bit_cast(f16x8, h0), cf, k == 0 ? f32x16{} : acc[0]);
+                acc[1] = mfma32_f16(__builtin_bit_cast(f16x8, h1), cf, k == 0 ? f32x16{} : acc[1]);
+            }
+        };
+        if (rb < 4) offdiag();
+
         // ---- x^T: one power of two for the chunk and head, none where x
         // already sits well inside fp16's normal range
         const int xe_raw = sm.xexp[b];
@@ -381,7 +438,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
                 for (int k = 0; k < 16; ++k) {
                     const uint32_t a = xr[0][k >> 3][(k >> 1) & 3];
                     const uint32_t b2 = xr[1][k >> 3][(k >> 1) & 3];
-                    sm.xt[(pq * 16 + k) * XT_STRIDE + pair] =
+                    sm.xt[(pq * 16 + k) * XT_STRIDE + (pair ^ (16 * pq))] =
                         pack_f16x2(__uint_as_float((k & 1) ? (a & 0xFFFF0000u) : (a << 16)),
                                    __uint_as_float((k & 1) ? (b2 & 0xFFFF0000u) : (b2 << 16)));
                 }
@@ -391,7 +448,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
                 for (int k = 0; k < 16; ++k) {
                     const uint32_t a = xr[0][k >> 3][(k >> 1) & 3];
                     const uint32_t b2 = xr[1][k >> 3][(k >> 1) & 3];
-                    sm.xt[(pq * 16 + k) * XT_STRIDE + pair] =
+                    sm.xt[(pq * 16 + k) * XT_STRIDE + (pair ^ (16 * pq))] =
                         pack_f16x2(__uint_as_float((k & 1) ? (a & 0xFFFF0000u) : (a << 16)) * s0,
                                    __uint_as_float((k & 1) ? (b2 & 0xFFFF0000u) : (b2 << 16)) * s0);
                 }
@@ -401,8 +458,8 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
 
         // ---- bounds, the same in every wavefront: dmax = max |dts|, dgrow =
         // the chunk's total growth when A > 0 (1 otherwise)
-        const float4 d4 = *reinterpret_cast<const float4 *>(dts + 4 * lane);
-        const float dmax = wave_max(fmaxf(fmaxf(fabsf(d4.x), fabsf(d4.y)), fmaxf(fabsf(d4.z), fabsf(d4.w))));
+        const float4 dm4 = *reinterpret_cast<const float4 *>(sm.dmx[b]);
+        const float dmax = fmaxf(fmaxf(dm4.x, dm4.y), fmaxf(dm4.z, dm4.w));
         const float cap = fmaxf(0.f, cs2[kChunk - 1] - cs2[0]);
         const float dgrow = fast_exp2(cap);
         // table scale 2^-kw with |table| < 1
@@ -427,64 +484,59 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
             }
         }
 
-        // ---- off-diagonal part: y^T_off = h_in (LDS) x C^T (registers).
-        // Wavefronts past the chunk end run it too and discard it.
-        f32x16 acc[2];
-#pragma unroll
-        for (int k = 0; k < KS; ++k) {
-            const f16x8 cf = __builtin_bit_cast(f16x8, cq[k]);
-#pragma unroll
-            for (int pt = 0; pt < 2; ++pt) {
-                const f16x8 hf = __builtin_bit_cast(
-                    f16x8, *reinterpret_cast<const u32x4 *>(sm.h + (32 * pt + l32) * H_STRIDE + 8 * k + 4 * hl));
-                acc[pt] = mfma32_f16(hf, cf, k == 0 ? f32x16{} : acc[pt]);
-            }
-        }
+        // ---- this lane's row factors for Q (see there), formed ahead of the barrier
+        const float cs_i = cs2[i_l];
+        const float cr = cs2[32 * rb];
+        // the off-diagonal products' scale: exp2(cs2_i) in the M scale for row
+        // block 0, exp2(cs2[32 rb]) in the scale of the tiles below the
+        // diagonal block for the others
+        float fq = rb > 0 ? ldexpf(fast_exp2(cr), sg + xe - sc - kw) : ldexpf(fast_exp2(cs_i), smx - sc);
+        // exp2(cs2_i - cs2[32 rb]) * 2^(kw - sg - xe + smx): below-diagonal scale to the M scale
+        float rs = ldexpf(fast_exp2(cs_i - cr), kw - sg - xe + smx);
+        const float lmg = (float)(smx - sg - xe);
+        float ci = cs_i + lmg;
+        asm volatile("" : "+v"(fq), "+v"(rs), "+v"(ci));
+
+        if (rb >= 4) offdiag();
         __syncthreads();  // x^T and the table are complete; h_in is no longer read
 
         // ======== Q(hh)
         if (active) {  // wavefront-uniform
-            const float cs_i = cs2[i_l];
-            // undo the C and h_in scalings, decay column i by exp2(cs2_i), move to the M scale
-            {
-                const float f = ldexpf(fast_exp2(cs_i), smx - sc);
+            // undo the C and h_in scalings and decay column i: in row block 0
+            // by exp2(cs2_i), in the M scale; in the others by exp2(cs2[32 rb])
+            // only, in the scale of the tiles below the diagonal block, which
+            // then accumulate onto it before the rest of the decay
+            // (exp2(cs2_i - cs2[32 rb])) is applied per row
 #pragma unroll
-                for (int pt = 0; pt < 2; ++pt) {
+            for (int pt = 0; pt < 2; ++pt) {
 #pragma unroll
-                    for (int a = 0; a < 4; ++a) {
-                        const float4 s4 = *reinterpret_cast<const float4 *>(sm.hs[b] + 32 * pt + 8 * a + 4 * hl);
-                        acc[pt][4 * a + 0] *= f * s4.x;
-                        acc[pt][4 * a + 1] *= f * s4.y;
-                        acc[pt][4 * a + 2] *= f * s4.z;
-                        acc[pt][4 * a + 3] *= f * s4.w;
-                    }
+                for (int a = 0; a < 4; ++a) {
+                    const float4 s4 = *reinterpret_cast<const float4 *>(sm.hs[b] + 32 * pt + 8 * a + 4 * hl);
+                    acc[pt][4 * a + 0] *= fq * s4.x;
+                    acc[pt][4 * a + 1] *= fq * s4.y;
+                    acc[pt][4 * a + 2] *= fq * s4.z;
+                    acc[pt][4 * a + 3] *= fq * s4.w;
                 }
             }
             // ---- diagonal block: the tiles below its diagonal tile (code
-            // specialised per row block), scaled per row and added, then the
-            // diagonal tile itself
+            // specialised per row block), then the per-row decay to the M
+            // scale, then the diagonal tile itself
             if (rb > 0) {  // wavefront-uniform
-                f32x16 acc2[2] = {f32x16{}, f32x16{}};
                 switch (rb) {
-                case 1: below_diag<N, 1>(sm, acc2, lane); break;
-                case 2: below_diag<N, 2>(sm, acc2, lane); break;
-                case 3: below_diag<N, 3>(sm, acc2, lane); break;
-                case 4: below_diag<N, 4>(sm, acc2, lane); break;
-                case 5: below_diag<N, 5>(sm, acc2, lane); break;
-                case 6: below_diag<N, 6>(sm, acc2, lane); break;
-                default: below_diag<N, 7>(sm, acc2, lane); break;
+                case 1: below_diag<N, 1>(sm, acc, lane); break;
+                case 2: below_diag<N, 2>(sm, acc, lane); break;
+                case 3: below_diag<N, 3>(sm, acc, lane); break;
+                case 4: below_diag<N, 4>(sm, acc, lane); break;
+                case 5: below_diag<N, 5>(sm, acc, lane); break;
+                case 6: below_diag<N, 6>(sm, acc, lane); break;
+                default: below_diag<N, 7>(sm, acc, lane); break;
                 }
-                // exp2(cs2_i - cs2[32 rb]) * 2^(kw - sg - xe + smx)
-                const float rs = ldexpf(fast_exp2(cs_i - cs2[32 * rb]), kw - sg - xe + smx);
 #pragma unroll
                 for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) acc[pt][e] = __builtin_fmaf(acc2[pt][e], rs, acc[pt][e]);
+                    for (int e = 0; e < 16; ++e) acc[pt][e] *= rs;
             }
-            {
-                const float lmg = (float)(smx - sg - xe);
-                diag_tile(sm, cs2, dts, acc, lane, rb, cs_i + lmg, cap + lmg, ldexpf(dh, smx - xe));
-            }
+            diag_tile(sm, cs2, dts, acc, lane, rb, ci, cap + lmg, ldexpf(dh, smx - xe));
             // ---- back to unit scale, store bf16.  Lane l holds p = 8a + 4(l/32)
             // + 0..3 of token i_l for a = 0..3; for each pair of groups (a, a+1)
             // one v_permlane32_swap per dword trades the upper half-wavefront's
