@@ -44,6 +44,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--entry", choices=("inplace", "separate"), default="inplace",
+                    help="entry point to time: the in-place pool operation (default) or the one with "
+                         "separate initial_states / final_states (sequences without an initial state "
+                         "start from zero rows; none at all passes NULL)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU oracle time for the baseline sample")
     ap.add_argument("--summarize-profile", metavar="DIR",
@@ -268,13 +272,16 @@ def summarize_profile(root, workload):
 
 # ------------------------------------------------------------------ CPU leg
 
-def cpu_baseline(prob, min_seconds):
+def cpu_baseline(prob, min_seconds, entry="inplace"):
     import oracle
     T = prob["total_len"]
     t0 = time.perf_counter()
     reps = 0
     while True:
-        oracle.recurrence(prob, want_pool=False, want_final=False)
+        if entry == "inplace":
+            oracle.recurrence(prob, want_pool=False, want_final=False)
+        else:
+            oracle.recurrence_separate(prob, None)
         reps += 1
         if time.perf_counter() - t0 >= min_seconds:
             break
@@ -320,18 +327,33 @@ def main():
     def P(t):
         return None if t is None else ctypes.c_void_p(t.data_ptr())
 
-    args_ptrs = [P(d["y"]), P(d["x"]), P(d["dt"]), P(d["A"]), P(d["B"]), P(d["C"]), P(d["D"]),
-                 P(d["dt_bias"]), P(d["pool"]), P(d["query_start_loc"]), P(d["has_initial_state"]),
-                 P(d["cache_indices"]), P(ws), ctypes.c_size_t(ws.numel()), ctypes.c_void_p(stream.cuda_stream)]
+    tail = [P(ws), ctypes.c_size_t(ws.numel()), ctypes.c_void_p(stream.cuda_stream)]
+    if args.entry == "inplace":
+        args_ptrs = [P(d["y"]), P(d["x"]), P(d["dt"]), P(d["A"]), P(d["B"]), P(d["C"]), P(d["D"]),
+                     P(d["dt_bias"]), P(d["pool"]), P(d["query_start_loc"]), P(d["has_initial_state"]),
+                     P(d["cache_indices"])] + tail
+        f_plain, f_prof = lib.ssd_chunk_scan_varlen_fwd_inplace, lib.ssd_chunk_scan_varlen_fwd_inplace_profiled
+    else:
+        # the same sequences' initial states as rows of their own tensor
+        init_t = None
+        hi = prob.get("has_initial_state")
+        if hi is not None and np.any(hi):
+            rows = d["pool"].index_select(0, d["cache_indices"].long())
+            init_t = torch.where(d["has_initial_state"].bool()[:, None, None, None], rows,
+                                 torch.zeros_like(rows)).contiguous()
+        final_t = torch.empty((prob["batch"],) + tuple(d["pool"].shape[1:]), dtype=torch.float32, device=dev)
+        args_ptrs = [P(d["y"]), P(d["x"]), P(d["dt"]), P(d["A"]), P(d["B"]), P(d["C"]), P(d["D"]),
+                     P(d["dt_bias"]), P(init_t), P(final_t), P(d["query_start_loc"])] + tail
+        f_plain, f_prof = lib.ssd_chunk_scan_varlen_fwd, lib.ssd_chunk_scan_varlen_fwd_profiled
 
     ev_sets = [[hip.event() for _ in range(nk + 1)] for _ in range(args.steps)]
 
     def call(events=None):
         if events is None:
-            st = lib.ssd_chunk_scan_varlen_fwd_inplace(ctypes.byref(ps), *args_ptrs)
+            st = f_plain(ctypes.byref(ps), *args_ptrs)
         else:
             arr = (ctypes.c_void_p * (nk + 1))(*[e.value for e in events])
-            st = lib.ssd_chunk_scan_varlen_fwd_inplace_profiled(ctypes.byref(ps), *args_ptrs, arr, nk + 1)
+            st = f_prof(ctypes.byref(ps), *args_ptrs, arr, nk + 1)
         if st != 0:
             raise RuntimeError(lib.ssd_status_string(st).decode())
 
@@ -389,7 +411,8 @@ def main():
         "config": {"workload": args.workload, "batch": prob["batch"], "seq_len": prob["seqlens"][0]
                    if len(set(prob["seqlens"])) == 1 else None, "tokens": T, "nheads": prob["nheads"],
                    "head_dim": prob["head_dim"], "ngroups": prob["ngroups"], "dstate": prob["dstate"],
-                   "chunk_size": CHUNK, "parallelism": "single-gpu"},
+                   "chunk_size": CHUNK, "parallelism": "single-gpu",
+                   **({} if args.entry == "inplace" else {"entry": "separate initial/final states"})},
         "us_per_call": {"mean": round(ms * 1e3, 2), "median": round(statistics.median(per_call) * 1e3, 2),
                         "p10": round(float(np.percentile(per_call, 10)) * 1e3, 2),
                         "p90": round(float(np.percentile(per_call, 90)) * 1e3, 2),
@@ -402,7 +425,7 @@ def main():
         "wall_s_timed_region": round(wall, 3),
     }
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(prob, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(prob, args.cpu_seconds, args.entry)
     print(json.dumps(out))
 
 

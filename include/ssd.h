@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 6
+#define SSD_ABI_VERSION 7
 #define SSD_MAX_DSTATE 256  /* largest dstate, as in "mamba2_ssd_scan", comptime MAX_DSTATE */
 
 typedef enum ssd_status {
@@ -178,6 +178,46 @@ ssd_status ssd_chunk_scan_varlen_fwd_inplace_profiled(
     const void *B, const void *C, const float *D, const float *dt_bias,
     float *ssm_pool, const int32_t *query_start_loc,
     const uint8_t *has_initial_state, const uint32_t *cache_indices,
+    void *workspace, size_t workspace_bytes, void *stream,
+    void *const *events, int n_events);
+
+/* Varlen SSD forward prefill with separate initial and final states: the
+ * same operation, where sequence b starts from initial_states[b] (or zero)
+ * and its final state goes to final_states[b] ("mamba2_ssd_scan", Modular
+ * MAX kernels docs, the paragraph after "Per-token recurrence": the state
+ * resets to zero or to initial_states at each query_start_loc boundary, and
+ * final_states of shape (batch, nheads, head_dim, dstate) is written at
+ * each sequence end; "Mamba2SSDChunkScanVarlenFwd" is the operation the
+ * in-place one is described against).
+ *   y, x, dt, A, B, C, D, dt_bias, query_start_loc, workspace: as for
+ *                     ssd_chunk_scan_varlen_fwd_inplace (prob->max_slots is
+ *                     not used).
+ *   initial_states    IN   fp32 [batch,H,P,N] or NULL (every sequence starts
+ *                     from zero); when given, every sequence starts from its
+ *                     row (no per-sequence flag).
+ *   final_states      OUT  fp32 [batch,H,P,N]: every row is written, also
+ *                     for zero-length sequences (their initial state).  It
+ *                     may be the same buffer as initial_states (each element
+ *                     is read before it is written); it must not overlap any
+ *                     other argument.
+ * Errors as for the in-place entry point; final_states NULL gives
+ * SSD_ERR_NULL_ARG.                                                        */
+ssd_status ssd_chunk_scan_varlen_fwd(
+    const ssd_problem *prob,
+    void *y, const void *x, const float *dt, const float *A,
+    const void *B, const void *C, const float *D, const float *dt_bias,
+    const float *initial_states, float *final_states,
+    const int32_t *query_start_loc,
+    void *workspace, size_t workspace_bytes, void *stream);
+
+/* ssd_chunk_scan_varlen_fwd with the events of
+ * ssd_chunk_scan_varlen_fwd_inplace_profiled.                              */
+ssd_status ssd_chunk_scan_varlen_fwd_profiled(
+    const ssd_problem *prob,
+    void *y, const void *x, const float *dt, const float *A,
+    const void *B, const void *C, const float *D, const float *dt_bias,
+    const float *initial_states, float *final_states,
+    const int32_t *query_start_loc,
     void *workspace, size_t workspace_bytes, void *stream,
     void *const *events, int n_events);
 

@@ -24,7 +24,7 @@ STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_NULL_ARG", 2: "SSD_ERR_BAD_SHAPE", 3: "
 EXPORTED = ("ssd_abi_version", "ssd_status_string", "ssd_workspace_size",
             "ssd_workspace_get_layout", "ssd_chunk_scan_varlen_fwd_inplace",
             "ssd_kernel_count", "ssd_kernel_name", "ssd_chunk_scan_varlen_fwd_inplace_profiled",
-            "ssd_validate_inputs")
+            "ssd_chunk_scan_varlen_fwd", "ssd_chunk_scan_varlen_fwd_profiled", "ssd_validate_inputs")
 
 
 class SsdError(RuntimeError):
@@ -53,7 +53,7 @@ _lock = threading.Lock()
 _lib = None
 
 # SSD_ABI_VERSION of include/ssd.h that the ctypes structures below mirror
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 
 def load_library():
@@ -88,6 +88,11 @@ def load_library():
             lib.ssd_chunk_scan_varlen_fwd_inplace_profiled.restype = ctypes.c_int
             lib.ssd_chunk_scan_varlen_fwd_inplace_profiled.argtypes = (
                 [PP] + [V] * 13 + [ctypes.c_size_t, V, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int])
+            lib.ssd_chunk_scan_varlen_fwd.restype = ctypes.c_int
+            lib.ssd_chunk_scan_varlen_fwd.argtypes = [PP] + [V] * 12 + [ctypes.c_size_t, V]
+            lib.ssd_chunk_scan_varlen_fwd_profiled.restype = ctypes.c_int
+            lib.ssd_chunk_scan_varlen_fwd_profiled.argtypes = (
+                [PP] + [V] * 12 + [ctypes.c_size_t, V, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int])
             lib.ssd_validate_inputs.restype = ctypes.c_int
             lib.ssd_validate_inputs.argtypes = [PP, V, V, V]
             _lib = lib
@@ -213,6 +218,49 @@ def ssd_chunk_scan_varlen_fwd_inplace(y, x, dt, A, B, C, D, dt_bias, ssm_pool, q
         _ptr(cache_indices), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
         ctypes.c_void_p(st.cuda_stream))
     _check(status, "ssd_chunk_scan_varlen_fwd_inplace")
+    return workspace
+
+
+def ssd_chunk_scan_varlen_fwd(y, x, dt, A, B, C, D, dt_bias, initial_states, final_states,
+                              query_start_loc, *, dt_softplus=True, workspace=None, stream=None):
+    """Varlen SSD forward with separate initial and final states (see
+    include/ssd.h): sequence b starts from ``initial_states[b]`` (fp32
+    [batch,H,P,N], or None/empty for zero) and its final state is written to
+    ``final_states[b]`` (fp32 [batch,H,P,N]).  Other tensors as for
+    ssd_chunk_scan_varlen_fwd_inplace.  Returns the workspace tensor.
+    """
+    import torch
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("libssd runs on a HIP device; got tensors on " + str(dev))
+    T, H, P = x.shape
+    if B.dim() != 3:
+        raise ValueError("B must be [T, G, N]")
+    G, N = B.shape[1], B.shape[2]
+    batch = query_start_loc.numel() - 1
+    _need(y, "y", torch.bfloat16, (T, H, P), dev)
+    _need(x, "x", torch.bfloat16, (T, H, P), dev)
+    _need(dt, "dt", torch.float32, (T, H), dev)
+    _need(A, "A", torch.float32, (H,), dev)
+    _need(B, "B", torch.bfloat16, (T, G, N), dev)
+    _need(C, "C", torch.bfloat16, (T, G, N), dev)
+    D = _opt(D, "D", torch.float32, (H,), dev)
+    dt_bias = _opt(dt_bias, "dt_bias", torch.float32, (H,), dev)
+    initial_states = _opt(initial_states, "initial_states", torch.float32, (batch, H, P, N), dev)
+    _need(final_states, "final_states", torch.float32, (batch, H, P, N), dev)
+    _need(query_start_loc, "query_start_loc", torch.int32, (batch + 1,), dev)
+    prob = make_problem(T, batch, H, P, G, N, max(batch, 1), dt_softplus)
+    need = ssd_workspace_size(prob)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    elif workspace.dtype != torch.uint8 or workspace.numel() < need or workspace.device != dev:
+        raise ValueError(f"workspace must be a uint8 tensor of >= {need} bytes on {dev}")
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    status = load_library().ssd_chunk_scan_varlen_fwd(
+        ctypes.byref(prob), _ptr(y), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+        _ptr(dt_bias), _ptr(initial_states), _ptr(final_states), _ptr(query_start_loc),
+        _ptr(workspace), ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(st.cuda_stream))
+    _check(status, "ssd_chunk_scan_varlen_fwd")
     return workspace
 
 

@@ -1,8 +1,11 @@
 // C ABI of libssd: argument checks, workspace carve and launch order.
 // The entry points and their conventions are declared in include/ssd.h.
-// The argument order of the compute entry point follows the execute method
-// of "Mamba2SSDChunkScanVarlenFwdInplace" (Modular Mojo struct docs); the
-// device context becomes a HIP stream.
+// The argument order of the in-place compute entry point follows the execute
+// method of "Mamba2SSDChunkScanVarlenFwdInplace" (Modular Mojo struct docs);
+// the device context becomes a HIP stream.  The other compute entry point
+// (initial_states in, final_states out: "mamba2_ssd_scan", the paragraph
+// after "Per-token recurrence") runs the same kernels with a different
+// source and destination for the state chain.
 #include <string.h>
 
 #include <vector>
@@ -102,22 +105,30 @@ int ssd_kernel_count(void) { return kNumKernels; }
 
 const char *ssd_kernel_name(int i) { return (i >= 0 && i < kNumKernels) ? kKernelNames[i] : nullptr; }
 
+// Where the state chain starts and ends (see Params::state_in).
+struct StateIO {
+    const float *in;
+    float *out;
+    const uint8_t *has_init;
+    const uint32_t *cache_idx;
+    bool init_all;
+};
+
 static ssd_status run_scan(
     const ssd_problem *prob, void *y, const void *x, const float *dt, const float *A,
-    const void *B, const void *C, const float *D, const float *dt_bias, float *ssm_pool,
-    const int32_t *query_start_loc, const uint8_t *has_initial_state,
-    const uint32_t *cache_indices, void *workspace, size_t workspace_bytes, void *stream,
-    void *const *events) {
+    const void *B, const void *C, const float *D, const float *dt_bias,
+    const int32_t *query_start_loc, const StateIO &sio, void *workspace, size_t workspace_bytes,
+    void *stream, void *const *events) {
     ssd_status st = check_problem(prob);
     if (st != SSD_OK) return st;
     const bool has_tokens = prob->total_len > 0;
-    if (A == nullptr || ssm_pool == nullptr || query_start_loc == nullptr || cache_indices == nullptr)
+    if (A == nullptr || sio.out == nullptr || query_start_loc == nullptr || (sio.init_all && sio.in == nullptr))
         return SSD_ERR_NULL_ARG;
     if (has_tokens && (y == nullptr || x == nullptr || dt == nullptr || B == nullptr || C == nullptr))
         return SSD_ERR_NULL_ARG;
     if (!aligned(y, 16) || !aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) ||
-        !aligned(ssm_pool, 16) || !aligned(dt, 4) || !aligned(A, 4) || !aligned(D, 4) ||
-        !aligned(dt_bias, 4) || !aligned(query_start_loc, 4) || !aligned(cache_indices, 4))
+        !aligned(sio.out, 16) || !aligned(sio.in, 16) || !aligned(dt, 4) || !aligned(A, 4) ||
+        !aligned(D, 4) || !aligned(dt_bias, 4) || !aligned(query_start_loc, 4) || !aligned(sio.cache_idx, 4))
         return SSD_ERR_BAD_SHAPE;
     ssd_workspace_layout L;
     layout_of(prob, &L);
@@ -150,10 +161,12 @@ static ssd_status run_scan(
     p.C = static_cast<const uint16_t *>(C);
     p.D = D;
     p.dt_bias = dt_bias;
-    p.pool = ssm_pool;
     p.qsl = query_start_loc;
-    p.has_init = has_initial_state;
-    p.cache_idx = cache_indices;
+    p.state_in = sio.in;
+    p.state_out = sio.out;
+    p.has_init = sio.has_init;
+    p.cache_idx = sio.cache_idx;
+    p.init_all = sio.init_all ? 1 : 0;
     p.meta = reinterpret_cast<int32_t *>(ws + L.meta);
     p.chunk_off = reinterpret_cast<int32_t *>(ws + L.chunk_off);
     p.desc = reinterpret_cast<int4 *>(ws + L.desc);
@@ -180,13 +193,44 @@ static ssd_status run_scan(
     return SSD_OK;
 }
 
+static ssd_status inplace(const ssd_problem *prob, void *y, const void *x, const float *dt, const float *A,
+                          const void *B, const void *C, const float *D, const float *dt_bias, float *ssm_pool,
+                          const int32_t *query_start_loc, const uint8_t *has_initial_state,
+                          const uint32_t *cache_indices, void *workspace, size_t workspace_bytes, void *stream,
+                          void *const *events) {
+    if (ssm_pool == nullptr || cache_indices == nullptr) return SSD_ERR_NULL_ARG;
+    const StateIO sio{ssm_pool, ssm_pool, has_initial_state, cache_indices, false};
+    return run_scan(prob, y, x, dt, A, B, C, D, dt_bias, query_start_loc, sio, workspace, workspace_bytes,
+                    stream, events);
+}
+
+static ssd_status separate(const ssd_problem *prob, void *y, const void *x, const float *dt, const float *A,
+                           const void *B, const void *C, const float *D, const float *dt_bias,
+                           const float *initial_states, float *final_states, const int32_t *query_start_loc,
+                           void *workspace, size_t workspace_bytes, void *stream, void *const *events) {
+    if (prob == nullptr) return SSD_ERR_NULL_ARG;
+    ssd_problem q = *prob;  // no pool: the state tensors have one slot per sequence
+    q.max_slots = q.batch;
+    const StateIO sio{initial_states, final_states, nullptr, nullptr, initial_states != nullptr};
+    return run_scan(&q, y, x, dt, A, B, C, D, dt_bias, query_start_loc, sio, workspace, workspace_bytes,
+                    stream, events);
+}
+
+static ssd_status check_events(void *const *events, int n_events) {
+    if (events == nullptr) return SSD_ERR_NULL_ARG;
+    if (n_events != kNumKernels + 1) return SSD_ERR_BAD_SHAPE;
+    for (int k = 0; k <= kNumKernels; ++k)
+        if (events[k] == nullptr) return SSD_ERR_NULL_ARG;
+    return SSD_OK;
+}
+
 ssd_status ssd_chunk_scan_varlen_fwd_inplace(
     const ssd_problem *prob, void *y, const void *x, const float *dt, const float *A,
     const void *B, const void *C, const float *D, const float *dt_bias, float *ssm_pool,
     const int32_t *query_start_loc, const uint8_t *has_initial_state,
     const uint32_t *cache_indices, void *workspace, size_t workspace_bytes, void *stream) {
-    return run_scan(prob, y, x, dt, A, B, C, D, dt_bias, ssm_pool, query_start_loc,
-                    has_initial_state, cache_indices, workspace, workspace_bytes, stream, nullptr);
+    return inplace(prob, y, x, dt, A, B, C, D, dt_bias, ssm_pool, query_start_loc, has_initial_state,
+                   cache_indices, workspace, workspace_bytes, stream, nullptr);
 }
 
 ssd_status ssd_chunk_scan_varlen_fwd_inplace_profiled(
@@ -195,12 +239,30 @@ ssd_status ssd_chunk_scan_varlen_fwd_inplace_profiled(
     const int32_t *query_start_loc, const uint8_t *has_initial_state,
     const uint32_t *cache_indices, void *workspace, size_t workspace_bytes, void *stream,
     void *const *events, int n_events) {
-    if (events == nullptr) return SSD_ERR_NULL_ARG;
-    if (n_events != kNumKernels + 1) return SSD_ERR_BAD_SHAPE;
-    for (int k = 0; k <= kNumKernels; ++k)
-        if (events[k] == nullptr) return SSD_ERR_NULL_ARG;
-    return run_scan(prob, y, x, dt, A, B, C, D, dt_bias, ssm_pool, query_start_loc,
-                    has_initial_state, cache_indices, workspace, workspace_bytes, stream, events);
+    const ssd_status st = check_events(events, n_events);
+    if (st != SSD_OK) return st;
+    return inplace(prob, y, x, dt, A, B, C, D, dt_bias, ssm_pool, query_start_loc, has_initial_state,
+                   cache_indices, workspace, workspace_bytes, stream, events);
+}
+
+ssd_status ssd_chunk_scan_varlen_fwd(
+    const ssd_problem *prob, void *y, const void *x, const float *dt, const float *A,
+    const void *B, const void *C, const float *D, const float *dt_bias, const float *initial_states,
+    float *final_states, const int32_t *query_start_loc, void *workspace, size_t workspace_bytes,
+    void *stream) {
+    return separate(prob, y, x, dt, A, B, C, D, dt_bias, initial_states, final_states, query_start_loc,
+                    workspace, workspace_bytes, stream, nullptr);
+}
+
+ssd_status ssd_chunk_scan_varlen_fwd_profiled(
+    const ssd_problem *prob, void *y, const void *x, const float *dt, const float *A,
+    const void *B, const void *C, const float *D, const float *dt_bias, const float *initial_states,
+    float *final_states, const int32_t *query_start_loc, void *workspace, size_t workspace_bytes,
+    void *stream, void *const *events, int n_events) {
+    const ssd_status st = check_events(events, n_events);
+    if (st != SSD_OK) return st;
+    return separate(prob, y, x, dt, A, B, C, D, dt_bias, initial_states, final_states, query_start_loc,
+                    workspace, workspace_bytes, stream, events);
 }
 
 ssd_status ssd_validate_inputs(const ssd_problem *prob, const int32_t *query_start_loc,

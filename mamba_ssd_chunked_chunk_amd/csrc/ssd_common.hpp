@@ -43,10 +43,18 @@ struct Params {
     const float *dt, *A;
     const uint16_t *B, *C;
     const float *D, *dt_bias;
-    float *pool;
     const int32_t *qsl;
+    // where each sequence's state starts and ends, [slots][H][P][N] fp32:
+    // slot cache_idx[b] (b when cache_idx is null) of state_in, read when
+    // init_all or has_init[b] (has_init may be null: no sequence), and of
+    // state_out, written with the final state.  The in-place operation passes
+    // the pool for both; the other one initial_states (or null, never read)
+    // and final_states, with no slot indices.
+    const float *state_in;
+    float *state_out;
     const uint8_t *has_init;
     const uint32_t *cache_idx;
+    int init_all;
     // workspace carve (device)
     int32_t *meta;       // [4]: nchunks
     int32_t *chunk_off;  // [batch+1]

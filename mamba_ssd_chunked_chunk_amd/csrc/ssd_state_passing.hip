@@ -1,17 +1,20 @@
 // Steps 3 and 5 of the scan: the inter-chunk state recurrence ("state_passing")
-// and the in-place pool write-back.
+// and the final-state write (into the pool in place, or to final_states).
 //
 // For sequence b, head h and every state element (p, n), walking the
-// sequence's chunks k in order:
-//   h_in[first]  = has_initial_state[b] ? ssm_pool[cache_indices[b]][h][p][n] : 0
+// sequence's chunks k in order (slot = cache_indices[b] for the in-place
+// operation, b for the other one):
+//   h_in[first]  = initial ? state_in[slot][h][p][n] : 0
 //   h_in[k + 1]  = exp(cs_last(k)) * h_in[k] + S[k]
 //   final        = exp(cs_last(K-1)) * h_in[K-1] + S[K-1]
-//   ssm_pool[cache_indices[b]][h][p][n] = final
+//   state_out[slot][h][p][n] = final
 // This is the "inter-chunk state recurrence with exponential decay" of
 // "Mamba chunk scan with segsum" (description); the reset at each sequence
-// start and the final state at each sequence end come from "mamba2_ssd_scan"
-// ("Per-token recurrence"); reading the initial state from, and writing the
-// final state to, slot cache_indices[b] of the pool is
+// start (to zero or the initial state) and the final state at each sequence
+// end come from "mamba2_ssd_scan" ("Per-token recurrence", and the paragraph
+// after it: final_states of shape (batch, nheads, head_dim, dstate)); reading
+// the initial state from, and writing the final state to, slot
+// cache_indices[b] of the pool (initial when has_initial_state[b]) is
 // "Mamba2SSDChunkScanVarlenFwdInplace" (struct description).  A sequence with
 // no tokens writes its initial state (or zeros) back.
 //
@@ -20,9 +23,9 @@
 // outputs y; it is stored as fp16 with one power-of-two scale per row p (11
 // significant bits: bf16's 8 would put the off-diagonal part's rounding error
 // near the tolerance of y).  Each thread owns eight consecutive (p, n)
-// elements of one (sequence, head) (16-byte loads and stores), reads its pool
-// elements before the sequence's loop and writes them after, so the in-place
-// read-then-write of a slot never races.  The chunk contributions are loaded
+// elements of one (sequence, head) (16-byte loads and stores), reads its
+// initial elements before the sequence's loop and writes the final ones
+// after, so the in-place read-then-write of a slot never races.  The chunk contributions are loaded
 // kDepth chunks ahead of their use, so that many loads per thread are in
 // flight while the chain advances.  A row p spans N/8 lanes; its maximum is
 // taken with DPP within rows of 16 lanes and a v_permlane16_swap across them.
@@ -60,14 +63,17 @@ __global__ __launch_bounds__(256) void ssd_state_passing_kernel(Params p) {
     // clamped to the table so malformed query_start_loc cannot index past it
     const int k1 = (int)min((int64_t)p.chunk_off[b + 1], p.nchunks_max);
     const int k0 = min(p.chunk_off[b], k1);
-    const int64_t slot = p.cache_idx[b];
-    const bool init = p.has_init != nullptr && p.has_init[b] != 0;
-    float4 *pool4 = reinterpret_cast<float4 *>(p.pool + (slot * p.H + h) * head_elems + e0);
+    const int64_t slot = p.cache_idx != nullptr ? (int64_t)p.cache_idx[b] : (int64_t)b;
+    const bool init = p.init_all != 0 || (p.has_init != nullptr && p.has_init[b] != 0);
+    const int64_t off = (slot * p.H + h) * head_elems + e0;
+    // state_in is null only when no sequence reads it
+    const float4 *in4 = reinterpret_cast<const float4 *>((p.state_in != nullptr ? p.state_in : p.state_out) + off);
+    float4 *out4 = reinterpret_cast<float4 *>(p.state_out + off);
 
     float st[kPer];
     {
         const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-        const float4 lo = init ? pool4[0] : z, hi = init ? pool4[1] : z;
+        const float4 lo = init ? in4[0] : z, hi = init ? in4[1] : z;
         st[0] = lo.x; st[1] = lo.y; st[2] = lo.z; st[3] = lo.w;
         st[4] = hi.x; st[5] = hi.y; st[6] = hi.z; st[7] = hi.w;
     }
@@ -139,8 +145,8 @@ __global__ __launch_bounds__(256) void ssd_state_passing_kernel(Params p) {
         fetch(kb, sv, sev, dv);
         link(kb, sv, sev, dv);
     }
-    pool4[0] = make_float4(st[0], st[1], st[2], st[3]);
-    pool4[1] = make_float4(st[4], st[5], st[6], st[7]);
+    out4[0] = make_float4(st[0], st[1], st[2], st[3]);
+    out4[1] = make_float4(st[4], st[5], st[6], st[7]);
 }
 
 hipError_t launch_state_passing(const Params &p, const Launch &l) {

@@ -45,6 +45,14 @@ def run(d: dict, workspace=None, stream=None):
         dt_softplus=d["dt_softplus"], workspace=workspace, stream=stream)
 
 
+def run_fwd(d: dict, initial_states, final_states, workspace=None, stream=None):
+    """One call of the scan with separate initial/final states (asynchronous)."""
+    return binding.ssd_chunk_scan_varlen_fwd(
+        d["y"], d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["dt_bias"], initial_states,
+        final_states, d["query_start_loc"], dt_softplus=d["dt_softplus"], workspace=workspace,
+        stream=stream)
+
+
 def problem_struct(d: dict):
     T, H, P = d["x"].shape
     G, N = d["B"].shape[1], d["B"].shape[2]

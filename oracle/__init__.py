@@ -11,7 +11,9 @@ Two independent formulations:
   * ``recurrence``: the per-token recurrence in C, fp64, OpenMP over
     (sequence, head) -- the plain definition ("mamba2_ssd_scan", section
     "Per-token recurrence"; in-place pool semantics from
-    "Mamba2SSDChunkScanVarlenFwdInplace").
+    "Mamba2SSDChunkScanVarlenFwdInplace").  ``recurrence_separate`` is the
+    same recurrence with separate initial and final states (the paragraph
+    after "Per-token recurrence").
   * ``chunked_scan`` (``oracle.chunked``): the segment-sum / chunked
     reformulation in NumPy fp64 ("Mamba chunk scan with segsum",
     description), with per-chunk intermediates.
@@ -124,3 +126,30 @@ def recurrence(prob: dict, *, seqs: tuple[int, int] | None = None,
     if rc != 0:
         raise ValueError(f"oracle rejected the problem (code {rc})")
     return dict(y=y, final=final, pool=pool_out)
+
+
+def recurrence_separate(prob: dict, initial_states=None, *, seqs: tuple[int, int] | None = None):
+    """The operation with separate initial and final states ("mamba2_ssd_scan",
+    the paragraph after "Per-token recurrence": the state resets to zero, or
+    to initial_states, at each query_start_loc boundary, and final_states
+    (batch, nheads, head_dim, dstate) is written at each sequence end).
+
+    Sequence b starts from ``initial_states[b]`` (fp32 [batch,H,P,N]) when it
+    is given, else from zero; the problem's pool, has_initial_state and
+    cache_indices are ignored.  It runs ``recurrence`` with the initial states
+    as a pool of one slot per sequence, every sequence flagged.  Returns
+    dict(y=[T,H,P] f64, final=[batch,H,P,N] f64).
+    """
+    H, P, N = prob["nheads"], prob["head_dim"], prob["dstate"]
+    batch = len(prob["query_start_loc"]) - 1
+    q = dict(prob)
+    if initial_states is None:
+        q["pool"] = np.zeros((1, H, P, N), np.float32)
+        q["has_initial_state"] = None
+        q["cache_indices"] = np.zeros(batch, np.uint32)
+    else:
+        q["pool"] = np.ascontiguousarray(initial_states, dtype=np.float32).reshape(batch, H, P, N)
+        q["has_initial_state"] = np.ones(batch, np.uint8)
+        q["cache_indices"] = np.arange(batch, dtype=np.uint32)
+    r = recurrence(q, seqs=seqs, want_pool=False, want_final=True)
+    return dict(y=r["y"], final=r["final"])

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert binding.ssd_abi_version() == binding.ABI_VERSION == 6
+    assert binding.ssd_abi_version() == binding.ABI_VERSION == 7
     for code, name in binding.STATUS_NAMES.items():
         assert lib.ssd_status_string(code).decode().startswith(name)
     assert b"unknown" in lib.ssd_status_string(99)
@@ -109,6 +109,34 @@ def test_null_and_workspace_errors_before_launch(lib):
     a = list(args)
     a[6] = a[7] = a[10] = None
     assert f(ctypes.byref(p), *a, need - 1, None) == 4
+
+
+def test_separate_states_errors_before_launch(lib):
+    p = _prob()
+    f = lib.ssd_chunk_scan_varlen_fwd
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails its host checks
+    args = [fake] * 12  # y x dt A B C D dt_bias initial final qsl workspace
+    need = binding.ssd_workspace_size(p)
+    assert f(None, *args, need, None) == 1
+    # each required pointer NULL in turn (y, x, dt, A, B, C, final_states, qsl)
+    for idx in (0, 1, 2, 3, 4, 5, 9, 10):
+        a = list(args)
+        a[idx] = None
+        assert f(ctypes.byref(p), *a, need, None) == 1, idx
+    # misaligned state tensors
+    for idx in (8, 9):
+        a = list(args)
+        a[idx] = ctypes.c_void_p((1 << 20) + 8)
+        assert f(ctypes.byref(p), *a, need, None) == 2, idx
+    # workspace too small; optional D, dt_bias and initial_states may be NULL
+    a = list(args)
+    a[6] = a[7] = a[8] = None
+    assert f(ctypes.byref(p), *a, need - 1, None) == 4
+    # the profiled form checks its events first
+    g = lib.ssd_chunk_scan_varlen_fwd_profiled
+    assert g(ctypes.byref(p), *args, need, None, None, 5) == 1
+    ev = (ctypes.c_void_p * 5)(*([fake] * 5))
+    assert g(ctypes.byref(p), *args, need, None, ev, 4) == 2
 
 
 def test_validate_inputs_host_errors(lib):

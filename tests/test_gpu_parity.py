@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 from oracle.chunked import chunked_scan
-from ssd_testlib import bf16_to_f64, frob_rel, small_problem, sub_batch
+from ssd_testlib import bf16_to_f64, clone, frob_rel, small_problem, sub_batch
 
 torch = pytest.importorskip("torch")
 from mamba_ssd_chunked_chunk_amd import binding, torch_io  # noqa: E402
@@ -277,6 +277,70 @@ def test_validate_inputs_on_device():
 
 
 # ------------------------------------------------ workloads at full size
+
+# ---------------------------------- separate initial and final states
+
+def run_separate(prob, initial_states, *, aliased=False):
+    """The entry point with separate states; final_states starts as NaN (or
+    is the initial-states buffer itself when ``aliased``)."""
+    d = torch_io.upload(prob, "cuda")
+    batch = len(prob["query_start_loc"]) - 1
+    H, P, N = prob["nheads"], prob["head_dim"], prob["dstate"]
+    init_t = None if initial_states is None else torch.from_numpy(initial_states).cuda()
+    if aliased:
+        final_t = init_t
+    else:
+        final_t = torch.full((batch, H, P, N), float("nan"), dtype=torch.float32, device="cuda")
+    torch_io.run_fwd(d, init_t, final_t)
+    torch.cuda.synchronize()
+    return d, final_t
+
+
+def random_states(prob, seed, scale=0.5):
+    batch = len(prob["query_start_loc"]) - 1
+    shape = (batch, prob["nheads"], prob["head_dim"], prob["dstate"])
+    return (np.random.default_rng(seed).standard_normal(shape) * scale).astype(np.float32)
+
+
+@pytest.mark.parametrize("with_init", [True, False], ids=["initial", "zero"])
+def test_separate_states_match_oracle(with_init):
+    prob = small_problem([300, 0, 513, 17], H=4, P=64, G=2, N=128, seed=71, init="none")
+    init = random_states(prob, 171) if with_init else None
+    d, fin = run_separate(prob, init)
+    ref = oracle.recurrence_separate(prob, init)
+    assert_y(y_host(d), ref["y"], "separate states")
+    fh = fin.cpu().numpy()
+    for b in range(4):
+        assert_final(fh[b], ref["final"][b], f"seq {b}")
+    # the zero-length sequence hands its initial state (or zeros) straight through
+    want = init[1] if with_init else np.zeros_like(fh[1])
+    assert np.array_equal(fh[1].view(np.uint32), want.view(np.uint32))
+
+
+def test_separate_equals_inplace_bitwise():
+    prob = small_problem([700, 45, 0, 256], H=4, P=64, G=1, N=256, seed=72, init="none")
+    init = random_states(prob, 172)
+    # the same initial states placed in a pool at permuted slots
+    q = clone(prob)
+    slots = np.array([5, 0, 3, 1], np.uint32)
+    pool = np.full((6,) + init.shape[1:], np.nan, np.float32)
+    pool[slots] = init
+    q["pool"], q["cache_indices"], q["has_initial_state"] = pool, slots, np.ones(4, np.uint8)
+    d1, _ = gpu_run(q)
+    d2, fin = run_separate(prob, init)
+    assert torch.equal(d1["y"].view(torch.int16), d2["y"].view(torch.int16))
+    for b in range(4):
+        assert torch.equal(d1["pool"][int(slots[b])].view(torch.int32), fin[b].view(torch.int32)), b
+
+
+def test_separate_states_aliased_buffer():
+    prob = small_problem([400, 3, 0, 90], H=2, P=64, G=1, N=64, seed=73, init="none")
+    init = random_states(prob, 173)
+    d1, fin = run_separate(prob, init)
+    d2, fin2 = run_separate(prob, init.copy(), aliased=True)
+    assert torch.equal(d1["y"].view(torch.int16), d2["y"].view(torch.int16))
+    assert torch.equal(fin.view(torch.int32), fin2.view(torch.int32))
+
 
 @pytest.mark.parametrize("name,seqs", [
     ("fixed_4x4096_h16_n256", (1, 2)),

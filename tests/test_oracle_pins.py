@@ -241,6 +241,35 @@ def test_length_one_sequence_by_hand():
     np.testing.assert_allclose(out["final"][0, 0], h1, rtol=1e-13)
 
 
+# ------------------------------------- separate initial and final states
+
+def test_separate_states_by_hand():
+    # sequence 0: one token from a given initial state; sequence 1: no tokens
+    # (its final state is its initial state); sequence 2: one token from zero
+    # when no initial states are given
+    prob = small_problem([1, 0, 1], H=1, P=3, G=1, N=4, seed=61, init="none")
+    rng = np.random.default_rng(62)
+    s0 = rng.standard_normal((3, 1, 3, 4)).astype(np.float32)
+    x = bf16_to_f64(prob["x"]).reshape(2, 3)
+    Bv = bf16_to_f64(prob["B"]).reshape(2, 4)
+    Cv = bf16_to_f64(prob["C"]).reshape(2, 4)
+    dts = softplus(prob["dt"].reshape(2).astype(np.float64) + np.float64(prob["dt_bias"][0]))
+    r = np.exp(float(prob["A"][0]) * dts)
+    D = float(prob["D"][0])
+    for init in (s0, None):
+        out = oracle.recurrence_separate(prob, init)
+        h0a = s0[0, 0].astype(np.float64) if init is not None else np.zeros((3, 4))
+        h0c = s0[2, 0].astype(np.float64) if init is not None else np.zeros((3, 4))
+        ha = r[0] * h0a + dts[0] * np.outer(x[0], Bv[0])
+        hc = r[1] * h0c + dts[1] * np.outer(x[1], Bv[1])
+        np.testing.assert_allclose(out["y"].reshape(2, 3)[0], ha @ Cv[0] + D * x[0], rtol=1e-13)
+        np.testing.assert_allclose(out["y"].reshape(2, 3)[1], hc @ Cv[1] + D * x[1], rtol=1e-13)
+        np.testing.assert_allclose(out["final"][0, 0], ha, rtol=1e-13)
+        np.testing.assert_allclose(out["final"][2, 0], hc, rtol=1e-13)
+        want1 = s0[1, 0].astype(np.float64) if init is not None else np.zeros((3, 4))
+        assert np.array_equal(out["final"][1, 0], want1)
+
+
 # ----------------------------------------------- varlen: no cross-sequence bleed
 
 def test_varlen_isolation_concat_equals_separate():
