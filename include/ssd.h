@@ -46,8 +46,9 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 7
+#define SSD_ABI_VERSION 8
 #define SSD_MAX_DSTATE 256  /* largest dstate, as in "mamba2_ssd_scan", comptime MAX_DSTATE */
+#define SSD_SHORT_PATH_LIMIT 128  /* longest sequence the short path can take */
 
 typedef enum ssd_status {
     SSD_OK = 0,
@@ -83,6 +84,8 @@ typedef struct ssd_problem {
  * compute entry point leaves in the workspace, so tests can compare each
  * step with the oracle.  nchunks_max = floor(total_len / 256) + batch bounds
  * the number of chunks; chunk c of the call occupies row c of each table.
+ * Sequences taken by the short path (see ssd_set_short_path_max) have no
+ * chunks: chunk_off[b] == chunk_off[b+1] and no row of any table is theirs.
  *   meta      int32[4]                    {nchunks, 0, 0, 0}
  *   chunk_off int32[batch + 1]            first chunk of each sequence
  *   desc      int32[nchunks_max][4]       {sequence, first token, length, 0}
@@ -162,6 +165,22 @@ ssd_status ssd_chunk_scan_varlen_fwd_inplace(
  * (0 <= i < ssd_kernel_count(), launch order; NULL otherwise).            */
 int ssd_kernel_count(void);
 const char *ssd_kernel_name(int i);
+
+/* Short-sequence path.  At dstate 64 and 128, every sequence of 1 .. tokens
+ * tokens is scanned whole by one fused kernel ("ssd_short") instead of the
+ * chunked steps: the single-chunk case of the segment-sum form of "Mamba
+ * chunk scan with segsum" (description), with the final state written
+ * straight to its slot.  The route depends on the sequence's own length
+ * only (a sequence's results do not depend on the rest of the batch).
+ * Results agree with the chunked path within the documented tolerances, not
+ * bitwise.  tokens = 0 sends every sequence through the chunked steps (the
+ * faster choice for batches of mostly long sequences with a few short
+ * ones, where the short kernel runs after the chunked ones).  Process-wide
+ * setting, read when a compute call is enqueued (atomic; default
+ * SSD_SHORT_PATH_LIMIT).  Returns the previous value, or -1 (nothing
+ * changed) when tokens is outside 0 .. SSD_SHORT_PATH_LIMIT.  Host only;
+ * enqueues nothing.                                                         */
+int ssd_set_short_path_max(int tokens);
 
 /* Same computation as ssd_chunk_scan_varlen_fwd_inplace; additionally
  * records events (each a hipEvent_t created by the caller, passed as void*)

@@ -24,7 +24,8 @@ STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_NULL_ARG", 2: "SSD_ERR_BAD_SHAPE", 3: "
 EXPORTED = ("ssd_abi_version", "ssd_status_string", "ssd_workspace_size",
             "ssd_workspace_get_layout", "ssd_chunk_scan_varlen_fwd_inplace",
             "ssd_kernel_count", "ssd_kernel_name", "ssd_chunk_scan_varlen_fwd_inplace_profiled",
-            "ssd_chunk_scan_varlen_fwd", "ssd_chunk_scan_varlen_fwd_profiled", "ssd_validate_inputs")
+            "ssd_chunk_scan_varlen_fwd", "ssd_chunk_scan_varlen_fwd_profiled", "ssd_validate_inputs",
+            "ssd_set_short_path_max")
 
 
 class SsdError(RuntimeError):
@@ -53,7 +54,8 @@ _lock = threading.Lock()
 _lib = None
 
 # SSD_ABI_VERSION of include/ssd.h that the ctypes structures below mirror
-ABI_VERSION = 7
+ABI_VERSION = 8
+SHORT_PATH_LIMIT = 128  # SSD_SHORT_PATH_LIMIT
 
 
 def load_library():
@@ -95,6 +97,8 @@ def load_library():
                 [PP] + [V] * 12 + [ctypes.c_size_t, V, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int])
             lib.ssd_validate_inputs.restype = ctypes.c_int
             lib.ssd_validate_inputs.argtypes = [PP, V, V, V]
+            lib.ssd_set_short_path_max.restype = ctypes.c_int
+            lib.ssd_set_short_path_max.argtypes = [ctypes.c_int]
             _lib = lib
     return _lib
 
@@ -110,6 +114,15 @@ def make_problem(total_len, batch, nheads, head_dim, ngroups, dstate, max_slots,
                  dt_softplus=True, chunk_size=0) -> ssd_problem:
     return ssd_problem(int(total_len), int(batch), int(nheads), int(head_dim), int(ngroups),
                        int(dstate), int(max_slots), int(chunk_size), 1 if dt_softplus else 0)
+
+
+def ssd_set_short_path_max(tokens: int) -> int:
+    """Longest sequence the fused short-sequence kernel takes (0: none);
+    returns the previous setting."""
+    prev = load_library().ssd_set_short_path_max(int(tokens))
+    if prev < 0:
+        raise ValueError(f"short path maximum must be in 0..{SHORT_PATH_LIMIT}, got {tokens}")
+    return prev
 
 
 def ssd_abi_version() -> int:

@@ -8,6 +8,7 @@
 // source and destination for the state chain.
 #include <string.h>
 
+#include <atomic>
 #include <vector>
 
 #include "ssd.h"
@@ -16,6 +17,9 @@
 namespace {
 
 constexpr size_t kAlign = 256;
+
+// Longest sequence routed to the short-path kernel (dstate 64 and 128).
+std::atomic<int> g_short_max{ssd::kShortMax};
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -98,8 +102,13 @@ ssd_status ssd_workspace_get_layout(const ssd_problem *prob, ssd_workspace_layou
 }
 
 static const char *const kKernelNames[] = {"ssd_prep", "ssd_chunk_state", "ssd_state_passing",
-                                           "ssd_chunk_scan"};
-static constexpr int kNumKernels = 4;
+                                           "ssd_chunk_scan", "ssd_short"};
+static constexpr int kNumKernels = 5;
+
+int ssd_set_short_path_max(int tokens) {
+    if (tokens < 0 || tokens > SSD_SHORT_PATH_LIMIT) return -1;
+    return g_short_max.exchange(tokens);
+}
 
 int ssd_kernel_count(void) { return kNumKernels; }
 
@@ -167,6 +176,10 @@ static ssd_status run_scan(
     p.has_init = sio.has_init;
     p.cache_idx = sio.cache_idx;
     p.init_all = sio.init_all ? 1 : 0;
+    // the short path serves dstate 64 and 128; the route of a sequence
+    // depends on its own length only, so its results do not depend on the
+    // rest of the batch
+    p.short_max = p.N <= 128 ? g_short_max.load() : 0;
     p.meta = reinterpret_cast<int32_t *>(ws + L.meta);
     p.chunk_off = reinterpret_cast<int32_t *>(ws + L.chunk_off);
     p.desc = reinterpret_cast<int4 *>(ws + L.desc);
@@ -182,7 +195,8 @@ static ssd_status run_scan(
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t (*const launchers[kNumKernels])(const ssd::Params &, const ssd::Launch &) = {
-        ssd::launch_prep, ssd::launch_chunk_state, ssd::launch_state_passing, ssd::launch_chunk_scan};
+        ssd::launch_prep, ssd::launch_chunk_state, ssd::launch_state_passing, ssd::launch_chunk_scan,
+        ssd::launch_short};
     for (int k = 0; k < kNumKernels; ++k) {
         // events, if any, are recorded by the dispatches themselves: the start
         // of the first kernel and the end of every kernel

@@ -290,7 +290,12 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
     // tiles (all eight loads; past the row block's last tile they repeat it:
     // behind the wavefront-dependent condition each load would wait for the
     // previous one).  Workgroups past the chunk count read row cc, inside
-    // the tables, and leave.
+    // the tables, and leave.  At the dstates the short path serves (64 and
+    // 128) most rows can be empty (every sequence short): there the count is
+    // tested first and such workgroups load nothing.
+    if constexpr (N <= 128) {
+        if (c >= p.meta[0]) return;
+    }
     const int nchunks = p.meta[0];
     const int4 dsc = p.desc[cc];
     load_tabs(h_first);

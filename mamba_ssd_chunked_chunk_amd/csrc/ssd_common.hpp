@@ -21,6 +21,7 @@ constexpr int kChunk = 256;      // chunk length (tokens)
 constexpr int kHeadDim = 64;     // P supported by this build
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kShortMax = 128;   // longest sequence the short-path kernel takes
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -55,6 +56,9 @@ struct Params {
     const uint8_t *has_init;
     const uint32_t *cache_idx;
     int init_all;
+    // sequences of 1 .. short_max tokens are scanned whole by the short-path
+    // kernel and skipped by the chunked steps (0: none; at most kShortMax)
+    int short_max;
     // workspace carve (device)
     int32_t *meta;       // [4]: nchunks
     int32_t *chunk_off;  // [batch+1]
@@ -215,6 +219,11 @@ __device__ __forceinline__ float softplus_f(float v) {
     return fmaxf(v, 0.0f) + l;
 }
 
+// Whether a sequence of len tokens goes to the short-path kernel.
+__host__ __device__ __forceinline__ bool is_short_sequence(int len, int short_max) {
+    return len >= 1 && len <= short_max;
+}
+
 // Exponent e with 2^e <= |m| < 2^(e+1) for a finite positive float m.
 __device__ __forceinline__ int float_exponent(float m) {
     return (int)((__float_as_uint(m) >> 23) & 0xFF) - 127;
@@ -242,4 +251,5 @@ hipError_t launch_prep(const Params &p, const Launch &l);
 hipError_t launch_chunk_state(const Params &p, const Launch &l);
 hipError_t launch_state_passing(const Params &p, const Launch &l);
 hipError_t launch_chunk_scan(const Params &p, const Launch &l);
+hipError_t launch_short(const Params &p, const Launch &l);
 }  // namespace ssd

@@ -176,7 +176,7 @@ __global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(Params p) {
         int n = 0;
         if (b < p.batch) {
             const int len = p.qsl[b + 1] - p.qsl[b];
-            n = len > 0 ? (len + kChunk - 1) / kChunk : 0;
+            n = len > 0 && !is_short_sequence(len, p.short_max) ? (len + kChunk - 1) / kChunk : 0;
         }
         const int wincl = wave_incl_scan(n);
         __syncthreads();  // protects s_wtot from the previous round

@@ -16,7 +16,8 @@
 // the initial state from, and writing the final state to, slot
 // cache_indices[b] of the pool (initial when has_initial_state[b]) is
 // "Mamba2SSDChunkScanVarlenFwdInplace" (struct description).  A sequence with
-// no tokens writes its initial state (or zeros) back.
+// no tokens writes its initial state (or zeros) back; a short one (taken by
+// the short-path kernel) is skipped.
 //
 // Chunk contributions arrive as fp16 under one power-of-two exponent per
 // 32x32 tile of (chunk, head).  The chain is fp32.  h_in only feeds the
@@ -59,6 +60,7 @@ __global__ __launch_bounds__(256) void ssd_state_passing_kernel(Params p) {
     constexpr int64_t head_elems = (int64_t)kHeadDim * N;  // a multiple of 256 * kPer
     const int64_t e0 = ((int64_t)blockIdx.z * 256 + threadIdx.x) * kPer;
     if (e0 >= head_elems) return;  // whole workgroups only
+    if (is_short_sequence(p.qsl[b + 1] - p.qsl[b], p.short_max)) return;  // the short path writes it
 
     // clamped to the table so malformed query_start_loc cannot index past it
     const int k1 = (int)min((int64_t)p.chunk_off[b + 1], p.nchunks_max);

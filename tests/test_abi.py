@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert binding.ssd_abi_version() == binding.ABI_VERSION == 7
+    assert binding.ssd_abi_version() == binding.ABI_VERSION == 8
     for code, name in binding.STATUS_NAMES.items():
         assert lib.ssd_status_string(code).decode().startswith(name)
     assert b"unknown" in lib.ssd_status_string(99)
@@ -144,3 +144,22 @@ def test_validate_inputs_host_errors(lib):
     p = _prob()
     assert lib.ssd_validate_inputs(ctypes.byref(p), None, None, None) == 1
     assert lib.ssd_validate_inputs(ctypes.byref(_prob(batch=0)), None, None, None) == 2
+
+
+def test_short_path_setting_host_only(lib):
+    """The routing knob is host state: it returns the previous value, rejects
+    values outside 0..SSD_SHORT_PATH_LIMIT without changing anything, and the
+    kernel list names the fused short-sequence kernel last."""
+    prev = binding.ssd_set_short_path_max(binding.SHORT_PATH_LIMIT)
+    try:
+        assert binding.ssd_set_short_path_max(0) == binding.SHORT_PATH_LIMIT
+        assert binding.ssd_set_short_path_max(64) == 0
+        assert lib.ssd_set_short_path_max(-1) == -1
+        assert lib.ssd_set_short_path_max(binding.SHORT_PATH_LIMIT + 1) == -1
+        assert binding.ssd_set_short_path_max(binding.SHORT_PATH_LIMIT) == 64
+        with pytest.raises(ValueError):
+            binding.ssd_set_short_path_max(1000)
+    finally:
+        binding.ssd_set_short_path_max(prev)
+    names = [lib.ssd_kernel_name(i).decode() for i in range(lib.ssd_kernel_count())]
+    assert names == ["ssd_prep", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan", "ssd_short"]

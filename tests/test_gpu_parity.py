@@ -8,6 +8,7 @@ Intermediates left in the workspace are compared step by step with the
 chunked oracle (oracle.chunked) on small problems.
 """
 
+import contextlib
 import math
 
 import numpy as np
@@ -15,7 +16,7 @@ import pytest
 
 import oracle
 from oracle.chunked import chunked_scan
-from ssd_testlib import bf16_to_f64, clone, frob_rel, small_problem, sub_batch
+from ssd_testlib import bf16, bf16_to_f64, clone, frob_rel, small_problem, sub_batch
 
 torch = pytest.importorskip("torch")
 from mamba_ssd_chunked_chunk_amd import binding, torch_io  # noqa: E402
@@ -25,6 +26,17 @@ pytestmark = pytest.mark.gpu
 
 Y_RTOL = 2e-2
 FINAL_TOL = 1e-3
+
+
+@contextlib.contextmanager
+def short_path(tokens):
+    """Route sequences of 1..tokens tokens (dstate <= 128) to the fused short
+    kernel for the duration (0: every sequence through the chunked steps)."""
+    prev = binding.ssd_set_short_path_max(tokens)
+    try:
+        yield
+    finally:
+        binding.ssd_set_short_path_max(prev)
 
 
 def gpu_run(prob, **kw):
@@ -104,12 +116,74 @@ SMALL = {
 }
 
 
+@pytest.mark.parametrize("route", ["default", "chunked"])
 @pytest.mark.parametrize("name", list(SMALL))
-def test_small_cases(name):
+def test_small_cases(name, route):
+    """Every case under the default routing (short sequences at dstate <= 128
+    to the fused kernel) and with every sequence through the chunked steps."""
     spec = dict(SMALL[name])
     lens = spec.pop("seqlens")
     prob = small_problem(lens, seed=100 + len(name), **spec)
+    with short_path(binding.SHORT_PATH_LIMIT if route == "default" else 0):
+        full_check(prob)
+
+
+# lengths around the short-path limit and the fused kernel's 16-token K-steps
+# and 32-token row blocks, with empty and chunked neighbours
+MIXED_LENS = [1, 2, 15, 16, 17, 31, 32, 33, 0, 64, 95, 96, 97, 127, 128, 129, 255, 300]
+
+
+@pytest.mark.parametrize("N,G,init", [(64, 2, "bernoulli"), (128, 4, "all"), (128, 1, "none")])
+def test_short_path_mixed_lengths(N, G, init):
+    prob = small_problem(MIXED_LENS, H=8, P=64, G=G, N=N, seed=90 + N + G, init=init)
+    with short_path(binding.SHORT_PATH_LIMIT):
+        full_check(prob)
+
+
+@pytest.mark.parametrize("limit", [1, 33, 96])
+def test_short_path_limit_respected(limit):
+    """A lower limit moves the longer short sequences back to the chunked
+    steps: the chunk table holds exactly the sequences above the limit."""
+    prob = small_problem(MIXED_LENS, H=4, P=64, G=2, N=128, seed=95, init="bernoulli")
+    with short_path(limit):
+        d, ws = gpu_run(prob)
+    ref = oracle.recurrence(prob, want_pool=False)
+    assert_y(y_host(d), ref["y"], f"limit {limit}")
+    for b, slot in enumerate(prob["cache_indices"]):
+        assert_final(d["pool"][int(slot)].cpu().numpy(), ref["final"][b], f"seq {b}")
+    L = binding.ssd_workspace_get_layout(torch_io.problem_struct(d))
+    w = ws.cpu().numpy()
+    nch = int(w[L["meta"]:L["meta"] + 4].view(np.int32)[0])
+    assert nch == sum(-(-n // 256) for n in MIXED_LENS if n > limit)
+
+
+def test_short_path_extremes():
+    """Inputs that push the fused kernel's power-of-two scalings: large dt
+    without softplus (decays near 0 and weights of ~10), an all-zero x head
+    block, tiny B, and a huge initial state."""
+    prob = small_problem([96, 1, 128, 40], H=4, P=64, G=2, N=128, seed=97, init="all", dt_softplus=False)
+    T = prob["total_len"]
+    rng = np.random.default_rng(197)
+    prob["dt"] = rng.uniform(0.0, 10.0, prob["dt"].shape).astype(np.float32)
+    prob["dt_bias"] = np.zeros_like(prob["dt_bias"])
+    x = bf16_to_f64(prob["x"]).reshape(T, 4, 64)
+    x[96:97 + 128] = 0.0
+    prob["x"] = bf16(x)
+    Bm = bf16_to_f64(prob["B"]).reshape(T, 2, 128)
+    Bm[:, 1] *= 1e-6
+    prob["B"] = bf16(Bm)
+    prob["pool"] *= np.float32(1e4)
     full_check(prob)
+
+
+def test_short_nan_slot_not_read():
+    """A short sequence without an initial state must not read its slot."""
+    prob = small_problem([50, 7, 120], H=4, P=64, G=1, N=64, max_slots=5, seed=98, init=[0, 1, 0])
+    ci = prob["cache_indices"]
+    prob["pool"][ci[0]] = np.nan
+    prob["pool"][ci[2]] = np.nan
+    with short_path(binding.SHORT_PATH_LIMIT):
+        full_check(prob)
 
 
 @pytest.mark.parametrize("opt", ["no_D", "no_dt_bias", "no_has_init", "no_softplus"])
