@@ -95,7 +95,8 @@ def is_short(L, N, short_max):
 
 def algorithmic(prob, short_max=SHORT_MAX):
     """Compulsory bytes and chunked-method MFMA flops of the whole call and of
-    each kernel (units and formulas as stated in the design doc).  Sequences the
+    each kernel: bytes every call must move (x, y, B, C, dt, the pool slots
+    read and written) and the MFMA flops of the chunked form.  Sequences the
     short path takes count for ssd_short, the others for the chunked steps."""
     H, P, G, N = prob["nheads"], prob["head_dim"], prob["ngroups"], prob["dstate"]
     lens = prob["seqlens"]
@@ -317,7 +318,7 @@ def main():
         return
     if args.gpus != 1:
         print(json.dumps({"error": "libssd is a single-GPU library; this benchmark runs on exactly one "
-                                   "GPU (--gpus 1). Multi-GPU sharding is described in DESIGN.md, not run."}))
+                                   "GPU (--gpus 1); sharding over GPUs is not built."}))
         sys.exit(2)
 
     import numpy as np

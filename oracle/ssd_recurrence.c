@@ -28,7 +28,7 @@
  *   has_initial_state may be empty (absent).  The dt_softplus parameter
  *   (default true) selects whether softplus is applied to dt + dt_bias.
  *
- * Readings of points the pages leave open (each also listed in the design doc):
+ * Readings of points the pages leave open:
  *   - y[t] uses the state after token t's update (order of the two lines).
  *   - dt_softplus = 0: dts = dt + dt_bias (the bias is still added).
  *   - softplus(v) = log(1 + e^v) exactly, evaluated as
