@@ -239,18 +239,20 @@ def summarize_profile(root, workload, short_max=SHORT_MAX):
                 per[which]["raw"].setdefault(k, []).append(v)
     stats = list(csv.DictReader(open(os.path.join(root, "kt", "run_kernel_stats.csv"))))
     # the calls bench.py times are the ones that follow its cache-evicting fill
-    timed, after_fill = {}, False
+    # (a call's kernels run in order; a name seen again starts the next call)
+    timed, after_fill, seen = {}, False, set()
     trace = sorted(csv.DictReader(open(os.path.join(root, "kt", "run_kernel_trace.csv"))),
                    key=lambda r: int(r["Start_Timestamp"]))
     for r in trace:
         k = _short(r["Kernel_Name"])
         if "FillFunctor" in r["Kernel_Name"]:
-            after_fill = True
+            after_fill, seen = True, set()
         elif k.startswith("ssd_"):
+            if k in seen:
+                after_fill = False
+            seen.add(k)
             if after_fill:
                 timed.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-            if k == "ssd_short":  # the last kernel of a call
-                after_fill = False
         else:
             after_fill = False
     lines = ["| kernel | calls | avg µs | min µs | max µs | avg µs, timed calls | FETCH KiB/launch "
@@ -341,6 +343,12 @@ def main():
     hip = Hip()
     nk = lib.ssd_kernel_count()
     knames = [lib.ssd_kernel_name(i).decode() for i in range(nk)]
+    # ssd_short (the last kernel) is not launched where no sequence can take
+    # the short path (dstate 256, or the path off): its event is then only a
+    # marker on the stream, left out of the call time and the kernel list
+    n_run = nk if (prob["dstate"] <= 128 and args.short_max > 0) else nk - 1
+    assert knames[-1] == "ssd_short"
+    knames_run = knames[:n_run]
     stream = torch.cuda.current_stream(dev)
 
     def P(t):
@@ -389,10 +397,10 @@ def main():
     wall = time.perf_counter() - wall0
 
     per_call = []
-    per_kernel = {n: [] for n in knames}
+    per_kernel = {n: [] for n in knames_run}
     for evs in ev_sets:
-        per_call.append(hip.elapsed_ms(evs[0], evs[nk]))
-        for i, n in enumerate(knames):
+        per_call.append(hip.elapsed_ms(evs[0], evs[n_run]))
+        for i, n in enumerate(knames_run):
             per_kernel[n].append(hip.elapsed_ms(evs[i], evs[i + 1]))
     ms = statistics.fmean(per_call)
 
@@ -413,7 +421,7 @@ def main():
     roof = roofline_entry(dom, alg, kern_us[dom],
                           traffic_for(dom, args.workload) if args.short_max == SHORT_MAX else None)
     whole = roofline_entry("whole", alg, ms * 1e3)
-    per_kernel_roof = {n: roofline_entry(n, alg, kern_us[n]) for n in knames if alg[n]["bytes"] or alg[n]["flops"]}
+    per_kernel_roof = {n: roofline_entry(n, alg, kern_us[n]) for n in knames_run if alg[n]["bytes"] or alg[n]["flops"]}
 
     out = {
         "metric": METRIC,

@@ -162,7 +162,9 @@ ssd_status ssd_chunk_scan_varlen_fwd_inplace(
     void *workspace, size_t workspace_bytes, void *stream);
 
 /* Number of kernels one compute call enqueues, and the name of kernel i
- * (0 <= i < ssd_kernel_count(), launch order; NULL otherwise).            */
+ * (0 <= i < ssd_kernel_count(), launch order; NULL otherwise).  The last,
+ * "ssd_short", is not launched when no sequence can take the short path
+ * (dstate 256, or ssd_set_short_path_max(0)).                              */
 int ssd_kernel_count(void);
 const char *ssd_kernel_name(int i);
 
@@ -186,7 +188,8 @@ int ssd_set_short_path_max(int tokens);
  * records events (each a hipEvent_t created by the caller, passed as void*)
  * through the kernels' own dispatches, so no command is enqueued between
  * kernels: events[0] when kernel 0 starts and events[i+1] when kernel i
- * completes.  hipEventElapsedTime(events[i], events[i+1]) is then kernel i's
+ * completes (for a kernel that is not launched, the event is recorded on
+ * the stream at its place).  hipEventElapsedTime(events[i], events[i+1]) is then kernel i's
  * time (with the gap before it, for i > 0) and (events[0],
  * events[ssd_kernel_count()]) the whole call.  n_events must equal
  * ssd_kernel_count()+1 (SSD_ERR_NULL_ARG / SSD_ERR_BAD_SHAPE otherwise,

@@ -104,6 +104,7 @@ ssd_status ssd_workspace_get_layout(const ssd_problem *prob, ssd_workspace_layou
 static const char *const kKernelNames[] = {"ssd_prep", "ssd_chunk_state", "ssd_state_passing",
                                            "ssd_chunk_scan", "ssd_short"};
 static constexpr int kNumKernels = 5;
+static constexpr int kShortKernel = 4;
 
 int ssd_set_short_path_max(int tokens) {
     if (tokens < 0 || tokens > SSD_SHORT_PATH_LIMIT) return -1;
@@ -198,6 +199,13 @@ static ssd_status run_scan(
         ssd::launch_prep, ssd::launch_chunk_state, ssd::launch_state_passing, ssd::launch_chunk_scan,
         ssd::launch_short};
     for (int k = 0; k < kNumKernels; ++k) {
+        // no sequence can take the short path: its kernel would have nothing
+        // to do, so it is not launched (its completion event, if any, is
+        // recorded on the stream where it would have run)
+        if (k == kShortKernel && p.short_max == 0) {
+            if (events && hipEventRecord(static_cast<hipEvent_t>(events[k + 1]), s) != hipSuccess) return SSD_ERR_HIP;
+            continue;
+        }
         // events, if any, are recorded by the dispatches themselves: the start
         // of the first kernel and the end of every kernel
         const ssd::Launch l{s, events && k == 0 ? static_cast<hipEvent_t>(events[0]) : nullptr,

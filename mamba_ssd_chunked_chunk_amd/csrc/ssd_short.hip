@@ -551,7 +551,7 @@ hipError_t launch_short(const Params &p, const Launch &l) {
     switch (p.N) {
     case 64: return launch_kernel(ssd_short_kernel<64>, grid, dim3(kSThreads), l, p);
     case 128: return launch_kernel(ssd_short_kernel<128>, grid, dim3(kSThreads), l, p);
-    default:  // no sequence is short at other dstates: a one-workgroup no-op keeps the launch count fixed
+    default:  // no sequence is short at other dstates (not launched there); a one-workgroup no-op
         return launch_kernel(ssd_short_kernel<128>, dim3(1, 1, 1), dim3(kSThreads), l, p);  // p.N != 128: exits
     }
 }
