@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 8
+#define SSD_ABI_VERSION 9
 #define SSD_MAX_DSTATE 256  /* largest dstate, as in "mamba2_ssd_scan", comptime MAX_DSTATE */
 #define SSD_SHORT_PATH_LIMIT 128  /* longest sequence the short path can take */
 
@@ -84,9 +84,11 @@ typedef struct ssd_problem {
  * compute entry point leaves in the workspace, so tests can compare each
  * step with the oracle.  nchunks_max = floor(total_len / 256) + batch bounds
  * the number of chunks; chunk c of the call occupies row c of each table.
- * Sequences taken by the short path (see ssd_set_short_path_max) have no
- * chunks: chunk_off[b] == chunk_off[b+1] and no row of any table is theirs.
- *   meta      int32[4]                    {nchunks, 0, 0, 0}
+ * Sequences taken by the short path (see ssd_set_short_path_max; there a
+ * zero-length sequence is taken as well) have no chunks: chunk_off[b] ==
+ * chunk_off[b+1] and no row of any table is theirs.
+ *   meta      int32[4]                    {nchunks, nseq, 0, 0}: chunks, and
+ *                                         sequences the state chain walks
  *   chunk_off int32[batch + 1]            first chunk of each sequence
  *   desc      int32[nchunks_max][4]       {sequence, first token, length, 0}
  *   dts       fp32[nchunks_max][H][256]   dts per token, 0 past the chunk end
@@ -111,11 +113,16 @@ typedef struct ssd_problem {
  *   hexp      int32[nchunks_max][H][P]    exponent of each hin row
  *   xexp      int32[nchunks_max][H]       2^xexp puts the chunk's largest |x|
  *                                         of the head in [2^14, 2^15) (0 if
- *                                         all zero)                          */
+ *                                         all zero)
+ *   seq_list  int32[batch]                the nseq sequences the state chain
+ *                                         walks, in order (all of them when
+ *                                         no sequence can take the short
+ *                                         path; else those longer than its
+ *                                         limit)                             */
 typedef struct ssd_workspace_layout {
     size_t total_bytes;
     int64_t nchunks_max;
-    size_t meta, chunk_off, desc, dts, cs2, cbt, gexp, states, sexp, hin, hexp, xexp;
+    size_t meta, chunk_off, desc, dts, cs2, cbt, gexp, states, sexp, hin, hexp, xexp, seq_list;
 } ssd_workspace_layout;
 
 /* ABI version of the loaded library (SSD_ABI_VERSION it was built with). */

@@ -8,6 +8,7 @@
 // source and destination for the state chain.
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <vector>
 
@@ -61,6 +62,7 @@ void layout_of(const ssd_problem *p, ssd_workspace_layout *L) {
     L->hin = off;       off = align_up(off + (size_t)ncm * H * PN * sizeof(uint16_t));
     L->hexp = off;      off = align_up(off + (size_t)ncm * H * (size_t)p->head_dim * sizeof(int32_t));
     L->xexp = off;      off = align_up(off + (size_t)ncm * H * sizeof(int32_t));
+    L->seq_list = off;  off = align_up(off + (size_t)p->batch * sizeof(int32_t));
     L->total_bytes = off;
 }
 
@@ -181,6 +183,16 @@ static ssd_status run_scan(
     // depends on its own length only, so its results do not depend on the
     // rest of the batch
     p.short_max = p.N <= 128 ? g_short_max.load() : 0;
+    // with the short path on, only sequences longer than its limit reach the
+    // chunked steps: at most T / (short_max + 1) of them, with at most
+    // T / 256 + that many chunks; the launches are sized to these bounds
+    // (at least 1 each: a grid dimension cannot be 0, and prep's first
+    // workgroup publishes the chunk count and the sequence list)
+    p.nseq_grid = p.short_max > 0 ? (int)std::max<int64_t>(1, std::min<int64_t>(p.batch, p.T / (p.short_max + 1)))
+                                  : p.batch;
+    p.nchunks_grid = p.short_max > 0
+                         ? std::max<int64_t>(1, std::min<int64_t>(L.nchunks_max, p.T / ssd::kChunk + p.nseq_grid))
+                         : L.nchunks_max;
     p.meta = reinterpret_cast<int32_t *>(ws + L.meta);
     p.chunk_off = reinterpret_cast<int32_t *>(ws + L.chunk_off);
     p.desc = reinterpret_cast<int4 *>(ws + L.desc);
@@ -188,6 +200,7 @@ static ssd_status run_scan(
     p.cs2 = reinterpret_cast<float *>(ws + L.cs2);
     p.hexp = reinterpret_cast<int32_t *>(ws + L.hexp);
     p.xexp = reinterpret_cast<int32_t *>(ws + L.xexp);
+    p.seq_list = reinterpret_cast<int32_t *>(ws + L.seq_list);
     p.cbt = reinterpret_cast<uint16_t *>(ws + L.cbt);
     p.gexp = reinterpret_cast<int32_t *>(ws + L.gexp);
     p.states = reinterpret_cast<uint16_t *>(ws + L.states);

@@ -581,7 +581,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
 // shared operands and its start-up loads).
 static int heads_per_block(const Params &p) {
     const int hg = p.H / p.G;
-    const int64_t chunks = (p.nchunks_max + 7) / 8 * 8;
+    const int64_t chunks = (p.nchunks_grid + 7) / 8 * 8;
     for (int hb = 16; hb > 1; hb /= 2)
         if (hg % hb == 0 && chunks * (p.H / hb) >= (int64_t)p.num_cus) return hb;
     return 1;
@@ -589,7 +589,7 @@ static int heads_per_block(const Params &p) {
 
 template <int N, int HB>
 static hipError_t launch_nh(const Params &p, const Launch &l) {
-    const int64_t slots = (p.nchunks_max + 7) / 8 * (p.H / HB);
+    const int64_t slots = (p.nchunks_grid + 7) / 8 * (p.H / HB);
     return launch_kernel(ssd_chunk_scan_kernel<N, HB>, dim3((unsigned)(slots * 8)), dim3(kThreads), l, p);
 }
 

@@ -301,7 +301,7 @@ __global__ __launch_bounds__(StateShape<N>::THREADS) void ssd_chunk_state_kernel
 // operands).
 static int state_heads_per_block(const Params &p) {
     const int hg = p.H / p.G;
-    const int64_t chunks = (p.nchunks_max + 7) / 8 * 8;
+    const int64_t chunks = (p.nchunks_grid + 7) / 8 * 8;
     for (int hb = 8; hb > 1; hb /= 2)
         if (hg % hb == 0 && chunks * (p.H / hb) >= (int64_t)p.num_cus) return hb;
     return 1;
@@ -309,7 +309,7 @@ static int state_heads_per_block(const Params &p) {
 
 template <int N, int HB>
 static hipError_t launch_nh(const Params &p, const Launch &l) {
-    const int64_t slots = (p.nchunks_max + 7) / 8 * (p.H / HB);
+    const int64_t slots = (p.nchunks_grid + 7) / 8 * (p.H / HB);
     return launch_kernel(ssd_chunk_state_kernel<N, HB>, dim3((unsigned)(slots * 8)), dim3(StateShape<N>::THREADS), l,
                          p);
 }

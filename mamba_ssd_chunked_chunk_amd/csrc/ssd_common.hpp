@@ -56,9 +56,13 @@ struct Params {
     const uint8_t *has_init;
     const uint32_t *cache_idx;
     int init_all;
-    // sequences of 1 .. short_max tokens are scanned whole by the short-path
-    // kernel and skipped by the chunked steps (0: none; at most kShortMax)
+    // sequences of 0 .. short_max tokens are taken by the short-path kernel
+    // and skipped by the chunked steps (short_max 0: none; at most kShortMax)
     int short_max;
+    // launch sizes: chunks (<= nchunks_max) and sequences the chunked steps
+    // can see at most, given the routing
+    int64_t nchunks_grid;
+    int nseq_grid;
     // workspace carve (device)
     int32_t *meta;       // [4]: nchunks
     int32_t *chunk_off;  // [batch+1]
@@ -72,6 +76,7 @@ struct Params {
     uint16_t *hin;       // [nchunks_max][H][P][N] fp16, row p scaled by 2^hexp
     int32_t *hexp;       // [nchunks_max][H][P]
     int32_t *xexp;       // [nchunks_max][H]: 2^xexp puts the chunk's max |x| of the head in [2^14, 2^15)
+    int32_t *seq_list;   // [batch]: the meta[1] sequences the state chain walks
 };
 
 // ---------------------------------------------------------------- helpers
@@ -219,9 +224,10 @@ __device__ __forceinline__ float softplus_f(float v) {
     return fmaxf(v, 0.0f) + l;
 }
 
-// Whether a sequence of len tokens goes to the short-path kernel.
+// Whether a sequence of len tokens goes to the short-path kernel (with the
+// path on, zero-length sequences go there too).
 __host__ __device__ __forceinline__ bool is_short_sequence(int len, int short_max) {
-    return len >= 1 && len <= short_max;
+    return short_max > 0 && len <= short_max;
 }
 
 // Exponent e with 2^e <= |m| < 2^(e+1) for a finite positive float m.

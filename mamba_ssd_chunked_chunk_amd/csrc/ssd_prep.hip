@@ -176,7 +176,7 @@ __global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(Params p) {
         int n = 0;
         if (b < p.batch) {
             const int len = p.qsl[b + 1] - p.qsl[b];
-            n = len > 0 && !is_short_sequence(len, p.short_max) ? (len + kChunk - 1) / kChunk : 0;
+            n = !is_short_sequence(len, p.short_max) && len > 0 ? (len + kChunk - 1) / kChunk : 0;
         }
         const int wincl = wave_incl_scan(n);
         __syncthreads();  // protects s_wtot from the previous round
@@ -194,10 +194,31 @@ __global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(Params p) {
         }
         carry += total;
     }
-    if (c == 0 && job == 0 && tid == 0) {
-        p.chunk_off[p.batch] = carry;
-        p.meta[0] = carry;
-        p.meta[1] = 0; p.meta[2] = 0; p.meta[3] = 0;
+    if (c == 0 && job == 0) {
+        // the sequences the state chain walks: all of them when no sequence
+        // can take the short path, else those longer than its limit
+        int carry2 = 0;
+        for (int base = 0; base < p.batch; base += kPrepThreads) {
+            const int b = base + tid;
+            int f = 0;
+            if (b < p.batch) f = !is_short_sequence(p.qsl[b + 1] - p.qsl[b], p.short_max);
+            const int wincl = wave_incl_scan(f);
+            __syncthreads();
+            if (lane == 63) s_wtot[wave] = wincl;
+            __syncthreads();
+            int before = 0, total = 0;
+            for (int w = 0; w < 8; ++w) {
+                if (w < wave) before += s_wtot[w];
+                total += s_wtot[w];
+            }
+            if (f) p.seq_list[carry2 + before + wincl - 1] = b;
+            carry2 += total;
+        }
+        if (tid == 0) {
+            p.chunk_off[p.batch] = carry;
+            p.meta[0] = carry;
+            p.meta[1] = carry2; p.meta[2] = 0; p.meta[3] = 0;
+        }
     }
     __syncthreads();
     const int b = s_loc[0];
@@ -271,7 +292,7 @@ __global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(Params p) {
 }
 
 hipError_t launch_prep(const Params &p, const Launch &l) {
-    const dim3 grid((unsigned)p.nchunks_max, (unsigned)(1 + p.G));
+    const dim3 grid((unsigned)p.nchunks_grid, (unsigned)(1 + p.G));
     switch (p.N) {
     case 64: return launch_kernel(ssd_prep_kernel<64>, grid, dim3(kPrepThreads), l, p);
     case 128: return launch_kernel(ssd_prep_kernel<128>, grid, dim3(kPrepThreads), l, p);

@@ -1,7 +1,9 @@
 // Short sequences in one pass ("short path"): every sequence of 1 ..
 // short_max tokens (at most 128; dstate 64 or 128) is scanned whole by one
 // kernel, instead of going through the chunk table, the chunk-state and
-// state-passing steps and their fp16 intermediates in the workspace.
+// state-passing steps and their fp16 intermediates in the workspace.  With
+// the path on, zero-length sequences are also finished here (their final
+// state is the initial one, or zeros).
 //
 // For sequence b (tokens t0 .. t0+l-1), group g and each head h of the group,
 // with dts, cs2 = log2(e) * cumulative A*dts and the initial state h0 (the
@@ -86,6 +88,24 @@ __global__ __launch_bounds__(kSThreads) void ssd_short_kernel(Params p) {
     const int64_t t0 = p.qsl[b];
     const int len = p.qsl[b + 1] - (int)t0;
     if (p.N != N || !is_short_sequence(len, p.short_max)) return;  // the chunked path takes it
+    const int64_t slot = p.cache_idx != nullptr ? (int64_t)p.cache_idx[b] : (int64_t)b;
+    const bool init = p.init_all != 0 || (p.has_init != nullptr && p.has_init[b] != 0);
+    const int hg = p.H / p.G;
+    const int hpw = hg / (int)gridDim.z;
+    const int h_begin = g * hg + (int)blockIdx.z * hpw;
+    const int h_end = h_begin + hpw;
+    const float *state_src = p.state_in != nullptr ? p.state_in : p.state_out;
+    if (len == 0) {  // no tokens: the final state is the initial one (or zeros)
+        constexpr int64_t head_elems = (int64_t)kHeadDim * N;  // a multiple of 4 * kSThreads
+        for (int h = h_begin; h < h_end; ++h) {
+            const float *src = state_src + (slot * p.H + h) * head_elems;
+            float *dst = p.state_out + (slot * p.H + h) * head_elems;
+            if (init && src == dst) continue;  // in place: already there
+            for (int64_t e = 4 * (int64_t)threadIdx.x; e < head_elems; e += 4 * kSThreads)
+                *reinterpret_cast<f32x4 *>(dst + e) = init ? *reinterpret_cast<const f32x4 *>(src + e) : f32x4{};
+        }
+        return;
+    }
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -102,16 +122,9 @@ __global__ __launch_bounds__(kSThreads) void ssd_short_kernel(Params p) {
     const int nt = wave >> 1;           //             n tile
     const bool owner = nt < NT;         // wavefront-uniform
     const int nks = (len + 15) / 16;    // K-steps over tokens (wavefront-uniform)
-    const int64_t slot = p.cache_idx != nullptr ? (int64_t)p.cache_idx[b] : (int64_t)b;
-    const bool init = p.init_all != 0 || (p.has_init != nullptr && p.has_init[b] != 0);
-    const int hg = p.H / p.G;
-    const int hpw = hg / (int)gridDim.z;
-    const int h_begin = g * hg + (int)blockIdx.z * hpw;
-    const int h_end = h_begin + hpw;
     const int64_t rstride = (int64_t)p.G * N;  // elements between consecutive tokens of B and C
     const uint16_t *Bg = p.B + (t0 * p.G + g) * N;
     const uint16_t *Cg = p.C + (t0 * p.G + g) * N;
-    const float *state_src = p.state_in != nullptr ? p.state_in : p.state_out;
 
     // ---- B^T into LDS as fp16 under one power of two sb.  Thread item q:
     // token pair (lane), 8 n starting at 8 * (8q + wave)

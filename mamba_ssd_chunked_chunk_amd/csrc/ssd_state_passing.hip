@@ -16,8 +16,9 @@
 // the initial state from, and writing the final state to, slot
 // cache_indices[b] of the pool (initial when has_initial_state[b]) is
 // "Mamba2SSDChunkScanVarlenFwdInplace" (struct description).  A sequence with
-// no tokens writes its initial state (or zeros) back; a short one (taken by
-// the short-path kernel) is skipped.
+// no tokens writes its initial state (or zeros) back.  With the short path
+// on, the sequences it takes (zero-length ones included) are not walked: the
+// grid runs over the list of the others that prep writes.
 //
 // Chunk contributions arrive as fp16 under one power-of-two exponent per
 // 32x32 tile of (chunk, head).  The chain is fp32.  h_in only feeds the
@@ -53,14 +54,19 @@ __device__ __forceinline__ float row_max(float m) {
 }
 }  // namespace
 
-template <int N>
+// LIST: the grid's x walks the sequence list prep wrote (the short path is
+// on: only sequences longer than its limit are there), else the batch.
+template <int N, bool LIST>
 __global__ __launch_bounds__(256) void ssd_state_passing_kernel(Params p) {
-    const int b = blockIdx.x;
+    int b = blockIdx.x;
+    if constexpr (LIST) {
+        if (b >= p.meta[1]) return;
+        b = p.seq_list[b];
+    }
     const int h = blockIdx.y;
     constexpr int64_t head_elems = (int64_t)kHeadDim * N;  // a multiple of 256 * kPer
     const int64_t e0 = ((int64_t)blockIdx.z * 256 + threadIdx.x) * kPer;
     if (e0 >= head_elems) return;  // whole workgroups only
-    if (is_short_sequence(p.qsl[b + 1] - p.qsl[b], p.short_max)) return;  // the short path writes it
 
     // clamped to the table so malformed query_start_loc cannot index past it
     const int k1 = (int)min((int64_t)p.chunk_off[b + 1], p.nchunks_max);
@@ -154,11 +160,17 @@ __global__ __launch_bounds__(256) void ssd_state_passing_kernel(Params p) {
 hipError_t launch_state_passing(const Params &p, const Launch &l) {
     const int64_t head_elems = (int64_t)kHeadDim * p.N;
     const unsigned zb = (unsigned)((head_elems / kPer + 255) / 256);
-    dim3 grid((unsigned)p.batch, (unsigned)p.H, zb);
+    const bool list = p.short_max > 0;
+    dim3 grid((unsigned)(list ? p.nseq_grid : p.batch), (unsigned)p.H, zb);
     switch (p.N) {
-    case 64: return launch_kernel(ssd_state_passing_kernel<64>, grid, dim3(256), l, p);
-    case 128: return launch_kernel(ssd_state_passing_kernel<128>, grid, dim3(256), l, p);
-    case 256: return launch_kernel(ssd_state_passing_kernel<256>, grid, dim3(256), l, p);
+    case 64:
+        return list ? launch_kernel(ssd_state_passing_kernel<64, true>, grid, dim3(256), l, p)
+                    : launch_kernel(ssd_state_passing_kernel<64, false>, grid, dim3(256), l, p);
+    case 128:
+        return list ? launch_kernel(ssd_state_passing_kernel<128, true>, grid, dim3(256), l, p)
+                    : launch_kernel(ssd_state_passing_kernel<128, false>, grid, dim3(256), l, p);
+    case 256:  // the short path does not serve dstate 256
+        return launch_kernel(ssd_state_passing_kernel<256, false>, grid, dim3(256), l, p);
     default: return hipErrorInvalidValue;
     }
 }

@@ -151,6 +151,11 @@ WORKLOADS = {
     "short_512_h128_g8_n128": dict(
         seqlens=_uniform_short_lengths, nheads=128, head_dim=64, ngroups=8, dstate=128,
         max_slots=1024, init="all", pool_std=0.1, seed=20260004),
+    # one decode step: 512 sequences of one token each, same head shape, all
+    # resuming from a 1024-slot pool.
+    "decode_512_h128_g8_n128": dict(
+        seqlens=[1] * 512, nheads=128, head_dim=64, ngroups=8, dstate=128,
+        max_slots=1024, init="all", pool_std=0.1, seed=20260005),
 }
 
 WORKLOAD_ORDER = list(WORKLOADS)

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert binding.ssd_abi_version() == binding.ABI_VERSION == 8
+    assert binding.ssd_abi_version() == binding.ABI_VERSION == 9
     for code, name in binding.STATUS_NAMES.items():
         assert lib.ssd_status_string(code).decode().startswith(name)
     assert b"unknown" in lib.ssd_status_string(99)
@@ -56,7 +56,7 @@ def test_workspace_layout_arithmetic(lib):
     assert L["nchunks_max"] == ncm
     assert L["total_bytes"] == binding.ssd_workspace_size(p)
     offs = [L[k] for k in ("meta", "chunk_off", "desc", "dts", "cs2", "cbt", "gexp", "states", "sexp", "hin", "hexp",
-                           "xexp")]
+                           "xexp", "seq_list")]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert L["cbt"] - L["cs2"] >= ncm * 16 * 256 * 4
     assert L["gexp"] - L["cbt"] >= ncm * 1 * 36 * 64 * 16 * 2
@@ -65,7 +65,8 @@ def test_workspace_layout_arithmetic(lib):
     assert L["hin"] - L["sexp"] >= ncm * 16 * 2 * 8 * 4
     assert L["hexp"] - L["hin"] >= ncm * 16 * 64 * 256 * 2
     assert L["xexp"] - L["hexp"] >= ncm * 16 * 64 * 4
-    assert L["total_bytes"] - L["xexp"] >= ncm * 16 * 4
+    assert L["seq_list"] - L["xexp"] >= ncm * 16 * 4
+    assert L["total_bytes"] - L["seq_list"] >= 4 * 4
     assert L["cs2"] - L["dts"] >= ncm * 16 * 256 * 4
 
 
