@@ -36,6 +36,7 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16/fp16 MFMA, TFLOP/s
 CHUNK = 256
 SHORT_MAX = 128              # the library's default short-path maximum
+RECUR_MAX = 4                # of those, the longest the token-recurrence kernel takes
 
 
 def parse():
@@ -52,6 +53,9 @@ def parse():
     ap.add_argument("--short-max", type=int, default=SHORT_MAX,
                     help="longest sequence routed to the fused short-sequence kernel (dstate <= 128; "
                          "0 sends every sequence through the chunked steps)")
+    ap.add_argument("--state-dtype", choices=("f32", "bf16"), default="f32",
+                    help="storage type of the pool / states (bf16: rounded once per final state; the "
+                         "arithmetic stays fp32)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU oracle time for the baseline sample")
     ap.add_argument("--summarize-profile", metavar="DIR",
@@ -97,11 +101,12 @@ def algorithmic(prob, short_max=SHORT_MAX):
     """Compulsory bytes and chunked-method MFMA flops of the whole call and of
     each kernel: bytes every call must move (x, y, B, C, dt, the pool slots
     read and written) and the MFMA flops of the chunked form.  Sequences the
-    short path takes count for ssd_short, the others for the chunked steps."""
+    short path takes count for ssd_recur (up to RECUR_MAX tokens) or
+    ssd_short, the others for the chunked steps."""
     H, P, G, N = prob["nheads"], prob["head_dim"], prob["ngroups"], prob["dstate"]
     lens = prob["seqlens"]
     hi = prob.get("has_initial_state")
-    slot = H * P * N * 4
+    slot = H * P * N * (2 if prob.get("state_dtype", "f32") == "bf16" else 4)
 
     def part(seqs):
         T = sum(lens[b] for b in seqs)
@@ -119,18 +124,23 @@ def algorithmic(prob, short_max=SHORT_MAX):
                 f["cb"] += l * (l + 1) * N * G
         return bx, bbc, bdt, (n_init + len(seqs)) * slot, f
 
-    short = [b for b in range(len(lens)) if is_short(lens[b], N, short_max)]
+    recur_max = min(short_max, RECUR_MAX)
+    recur = [b for b in range(len(lens)) if is_short(lens[b], N, short_max) and lens[b] <= recur_max]
+    short = [b for b in range(len(lens)) if is_short(lens[b], N, short_max) and lens[b] > recur_max]
     chunked = [b for b in range(len(lens)) if not is_short(lens[b], N, short_max)]
     bx, bbc, bdt, pool_rw, f = part(chunked)
     sx, sbc, sdt, spool, sf = part(short)
+    rx, rbc, rdt, rpool, _ = part(recur)  # VALU recurrence: no MFMA flops
     fl = sum(f.values()) + sum(sf.values())
     return dict(
-        whole=dict(bytes=2 * (bx + sx) + 2 * (bbc + sbc) + bdt + sdt + pool_rw + spool, flops=fl),
+        whole=dict(bytes=2 * (bx + sx + rx) + 2 * (bbc + sbc + rbc) + bdt + sdt + rdt + pool_rw + spool + rpool,
+                   flops=fl),
         ssd_chunk_scan=dict(bytes=2 * bx + 2 * bbc + bdt, flops=f["off"] + f["diag"] + f["cb"]),
         ssd_chunk_state=dict(bytes=bx + bbc + bdt, flops=f["state"]),
         ssd_state_passing=dict(bytes=pool_rw, flops=0),
         ssd_prep=dict(bytes=bdt + bbc, flops=0),
         ssd_short=dict(bytes=2 * sx + 2 * sbc + sdt + spool, flops=sum(sf.values())),
+        ssd_recur=dict(bytes=2 * rx + 2 * rbc + rdt + rpool, flops=0),
     )
 
 
@@ -327,12 +337,14 @@ def main():
     import torch
 
     from mamba_ssd_chunked_chunk_amd import binding, torch_io
-    from mamba_ssd_chunked_chunk_amd.workloads import make_workload
+    from mamba_ssd_chunked_chunk_amd.workloads import make_workload, with_bf16_states
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     prob = make_workload(args.workload)
+    if args.state_dtype == "bf16":
+        prob = with_bf16_states(prob)
     T = prob["total_len"]
     d = torch_io.upload(prob, dev)
     ps = torch_io.problem_struct(d)
@@ -343,11 +355,11 @@ def main():
     hip = Hip()
     nk = lib.ssd_kernel_count()
     knames = [lib.ssd_kernel_name(i).decode() for i in range(nk)]
-    # ssd_short (the last kernel) is not launched where no sequence can take
-    # the short path (dstate 256, or the path off): its event is then only a
-    # marker on the stream, left out of the call time and the kernel list
-    n_run = nk if (prob["dstate"] <= 128 and args.short_max > 0) else nk - 1
-    assert knames[-1] == "ssd_short"
+    # the short path's kernels (the last two) are not launched where no
+    # sequence can take it (dstate 256, or the path off): their events are
+    # then only markers on the stream, left out of the call time and the list
+    assert knames[-2:] == ["ssd_short", "ssd_recur"]
+    n_run = nk if (prob["dstate"] <= 128 and args.short_max > 0) else nk - 2
     knames_run = knames[:n_run]
     stream = torch.cuda.current_stream(dev)
 
@@ -368,7 +380,7 @@ def main():
             rows = d["pool"].index_select(0, d["cache_indices"].long())
             init_t = torch.where(d["has_initial_state"].bool()[:, None, None, None], rows,
                                  torch.zeros_like(rows)).contiguous()
-        final_t = torch.empty((prob["batch"],) + tuple(d["pool"].shape[1:]), dtype=torch.float32, device=dev)
+        final_t = torch.empty((prob["batch"],) + tuple(d["pool"].shape[1:]), dtype=d["pool"].dtype, device=dev)
         args_ptrs = [P(d["y"]), P(d["x"]), P(d["dt"]), P(d["A"]), P(d["B"]), P(d["C"]), P(d["D"]),
                      P(d["dt_bias"]), P(init_t), P(final_t), P(d["query_start_loc"])] + tail
         f_plain, f_prof = lib.ssd_chunk_scan_varlen_fwd, lib.ssd_chunk_scan_varlen_fwd_profiled
@@ -419,7 +431,7 @@ def main():
     kern_us = {n: statistics.fmean(v) * 1e3 for n, v in per_kernel.items()}
     dom = max(kern_us, key=kern_us.get)
     roof = roofline_entry(dom, alg, kern_us[dom],
-                          traffic_for(dom, args.workload) if args.short_max == SHORT_MAX else None)
+                          traffic_for(dom, args.workload) if args.short_max == SHORT_MAX and args.state_dtype == "f32" else None)
     whole = roofline_entry("whole", alg, ms * 1e3)
     per_kernel_roof = {n: roofline_entry(n, alg, kern_us[n]) for n in knames_run if alg[n]["bytes"] or alg[n]["flops"]}
 
@@ -441,7 +453,8 @@ def main():
                    "head_dim": prob["head_dim"], "ngroups": prob["ngroups"], "dstate": prob["dstate"],
                    "chunk_size": CHUNK, "parallelism": "single-gpu",
                    **({} if args.entry == "inplace" else {"entry": "separate initial/final states"}),
-                   **({} if args.short_max == SHORT_MAX else {"short_path_max": args.short_max})},
+                   **({} if args.short_max == SHORT_MAX else {"short_path_max": args.short_max}),
+                   **({} if args.state_dtype == "f32" else {"state_dtype": "bf16 (storage)"})},
         "us_per_call": {"mean": round(ms * 1e3, 2), "median": round(statistics.median(per_call) * 1e3, 2),
                         "p10": round(float(np.percentile(per_call, 10)) * 1e3, 2),
                         "p90": round(float(np.percentile(per_call, 90)) * 1e3, 2),

@@ -46,9 +46,13 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 9
+#define SSD_ABI_VERSION 12
 #define SSD_MAX_DSTATE 256  /* largest dstate, as in "mamba2_ssd_scan", comptime MAX_DSTATE */
 #define SSD_SHORT_PATH_LIMIT 128  /* longest sequence the short path can take */
+#define SSD_RECUR_LIMIT 4         /* of those, the longest the token recurrence takes */
+/* element types of the state tensors (ssd_problem.state_dtype) */
+#define SSD_STATE_F32 0
+#define SSD_STATE_BF16 1
 
 typedef enum ssd_status {
     SSD_OK = 0,
@@ -65,7 +69,9 @@ typedef enum ssd_status {
  *   dt             [total_len, nheads]             fp32
  *   A, D, dt_bias  [nheads]                        fp32 (D, dt_bias optional)
  *   B, C           [total_len, ngroups, dstate]    bf16
- *   ssm_pool       [max_slots, nheads, head_dim, dstate]  fp32
+ *   ssm_pool       [max_slots, nheads, head_dim, dstate]  fp32, or bf16 with
+ *                  state_dtype = SSD_STATE_BF16 (also initial_states and
+ *                  final_states of the separate-states entry point)
  *   query_start_loc [batch + 1] int32, has_initial_state [batch] uint8
  *   (optional), cache_indices [batch] uint32                                */
 typedef struct ssd_problem {
@@ -78,6 +84,13 @@ typedef struct ssd_problem {
     int32_t max_slots;   /* leading dimension of ssm_pool; >= 1               */
     int32_t chunk_size;  /* 0 selects 256; this build supports 256 only       */
     int32_t dt_softplus; /* nonzero: dts = softplus(dt + dt_bias); zero: dt + dt_bias */
+    int32_t state_dtype; /* SSD_STATE_F32 or SSD_STATE_BF16: storage type of the states
+                          * ("Mamba2SSDChunkScanVarlenFwdInplace": execute's state_dtype
+                          * parameter; "Tensor shapes": a bf16 pool is storage only, the
+                          * scan accumulates in fp32).  With bf16, initial states are read
+                          * from bf16, the state chain and all arithmetic stay fp32, and
+                          * each final state is rounded to bf16 (nearest even) once, when
+                          * it is written */
 } ssd_problem;
 
 /* Offsets (bytes from the workspace base) and sizes of the intermediates the
@@ -87,8 +100,10 @@ typedef struct ssd_problem {
  * Sequences taken by the short path (see ssd_set_short_path_max; there a
  * zero-length sequence is taken as well) have no chunks: chunk_off[b] ==
  * chunk_off[b+1] and no row of any table is theirs.
- *   meta      int32[4]                    {nchunks, nseq, 0, 0}: chunks, and
- *                                         sequences the state chain walks
+ *   meta      int32[4]                    {nchunks, nseq, nrecur, 0}: chunks,
+ *                                         sequences the state chain walks,
+ *                                         sequences the token recurrence
+ *                                         takes
  *   chunk_off int32[batch + 1]            first chunk of each sequence
  *   desc      int32[nchunks_max][4]       {sequence, first token, length, 0}
  *   dts       fp32[nchunks_max][H][256]   dts per token, 0 past the chunk end
@@ -118,11 +133,14 @@ typedef struct ssd_problem {
  *                                         walks, in order (all of them when
  *                                         no sequence can take the short
  *                                         path; else those longer than its
- *                                         limit)                             */
+ *                                         limit)
+ *   recur_list int32[batch]               the nrecur sequences of 1 ..
+ *                                         min(limit, SSD_RECUR_LIMIT) tokens,
+ *                                         in order                           */
 typedef struct ssd_workspace_layout {
     size_t total_bytes;
     int64_t nchunks_max;
-    size_t meta, chunk_off, desc, dts, cs2, cbt, gexp, states, sexp, hin, hexp, xexp, seq_list;
+    size_t meta, chunk_off, desc, dts, cs2, cbt, gexp, states, sexp, hin, hexp, xexp, seq_list, recur_list;
 } ssd_workspace_layout;
 
 /* ABI version of the loaded library (SSD_ABI_VERSION it was built with). */
@@ -147,7 +165,8 @@ ssd_status ssd_workspace_get_layout(const ssd_problem *prob, ssd_workspace_layou
  *   B, C              IN   bf16 [T,G,N]
  *   D                 IN   fp32 [H] or NULL (treated as 0)
  *   dt_bias           IN   fp32 [H] or NULL (treated as 0)
- *   ssm_pool          IN/OUT fp32 [max_slots,H,P,N]: slot cache_indices[b] is
+ *   ssm_pool          IN/OUT fp32 (bf16 with state_dtype = SSD_STATE_BF16)
+ *                     [max_slots,H,P,N]: slot cache_indices[b] is
  *                     read as sequence b's initial state when
  *                     has_initial_state[b] != 0 (otherwise not read at all) and
  *                     overwritten with its final state (also for zero-length
@@ -164,22 +183,26 @@ ssd_status ssd_chunk_scan_varlen_fwd_inplace(
     const ssd_problem *prob,
     void *y, const void *x, const float *dt, const float *A,
     const void *B, const void *C, const float *D, const float *dt_bias,
-    float *ssm_pool, const int32_t *query_start_loc,
+    void *ssm_pool, const int32_t *query_start_loc,
     const uint8_t *has_initial_state, const uint32_t *cache_indices,
     void *workspace, size_t workspace_bytes, void *stream);
 
 /* Number of kernels one compute call enqueues, and the name of kernel i
- * (0 <= i < ssd_kernel_count(), launch order; NULL otherwise).  The last,
- * "ssd_short", is not launched when no sequence can take the short path
- * (dstate 256, or ssd_set_short_path_max(0)).                              */
+ * (0 <= i < ssd_kernel_count(), launch order; NULL otherwise).  The last
+ * two, "ssd_short" and "ssd_recur", serve the short path and are not
+ * launched when no sequence can take it (dstate 256, or
+ * ssd_set_short_path_max(0)).                                              */
 int ssd_kernel_count(void);
 const char *ssd_kernel_name(int i);
 
 /* Short-sequence path.  At dstate 64 and 128, every sequence of 1 .. tokens
- * tokens is scanned whole by one fused kernel ("ssd_short") instead of the
- * chunked steps: the single-chunk case of the segment-sum form of "Mamba
- * chunk scan with segsum" (description), with the final state written
- * straight to its slot.  The route depends on the sequence's own length
+ * tokens is scanned whole by one fused kernel instead of the chunked steps,
+ * with the final state written straight to its slot: sequences of up to
+ * SSD_RECUR_LIMIT tokens (decode steps) by the token recurrence of
+ * "mamba2_ssd_scan" ("Per-token recurrence") with the state split over the
+ * threads along dstate ("ssd_recur"), longer ones by the single-chunk case
+ * of the segment-sum form of "Mamba chunk scan with segsum" (description),
+ * on MFMA ("ssd_short").  Zero-length sequences are finished there too.  The route depends on the sequence's own length
  * only (a sequence's results do not depend on the rest of the batch).
  * Results agree with the chunked path within the documented tolerances, not
  * bitwise.  tokens = 0 sends every sequence through the chunked steps (the
@@ -205,7 +228,7 @@ ssd_status ssd_chunk_scan_varlen_fwd_inplace_profiled(
     const ssd_problem *prob,
     void *y, const void *x, const float *dt, const float *A,
     const void *B, const void *C, const float *D, const float *dt_bias,
-    float *ssm_pool, const int32_t *query_start_loc,
+    void *ssm_pool, const int32_t *query_start_loc,
     const uint8_t *has_initial_state, const uint32_t *cache_indices,
     void *workspace, size_t workspace_bytes, void *stream,
     void *const *events, int n_events);
@@ -221,10 +244,11 @@ ssd_status ssd_chunk_scan_varlen_fwd_inplace_profiled(
  *   y, x, dt, A, B, C, D, dt_bias, query_start_loc, workspace: as for
  *                     ssd_chunk_scan_varlen_fwd_inplace (prob->max_slots is
  *                     not used).
- *   initial_states    IN   fp32 [batch,H,P,N] or NULL (every sequence starts
+ *   initial_states    IN   fp32 (bf16 with state_dtype = SSD_STATE_BF16)
+ *                     [batch,H,P,N] or NULL (every sequence starts
  *                     from zero); when given, every sequence starts from its
  *                     row (no per-sequence flag).
- *   final_states      OUT  fp32 [batch,H,P,N]: every row is written, also
+ *   final_states      OUT  the same type [batch,H,P,N]: every row is written, also
  *                     for zero-length sequences (their initial state).  It
  *                     may be the same buffer as initial_states (each element
  *                     is read before it is written); it must not overlap any
@@ -235,7 +259,7 @@ ssd_status ssd_chunk_scan_varlen_fwd(
     const ssd_problem *prob,
     void *y, const void *x, const float *dt, const float *A,
     const void *B, const void *C, const float *D, const float *dt_bias,
-    const float *initial_states, float *final_states,
+    const void *initial_states, void *final_states,
     const int32_t *query_start_loc,
     void *workspace, size_t workspace_bytes, void *stream);
 
@@ -245,7 +269,7 @@ ssd_status ssd_chunk_scan_varlen_fwd_profiled(
     const ssd_problem *prob,
     void *y, const void *x, const float *dt, const float *A,
     const void *B, const void *C, const float *D, const float *dt_bias,
-    const float *initial_states, float *final_states,
+    const void *initial_states, void *final_states,
     const int32_t *query_start_loc,
     void *workspace, size_t workspace_bytes, void *stream,
     void *const *events, int n_events);

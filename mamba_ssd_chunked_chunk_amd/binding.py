@@ -39,7 +39,7 @@ class ssd_problem(ctypes.Structure):
                 ("nheads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("ngroups", ctypes.c_int32), ("dstate", ctypes.c_int32),
                 ("max_slots", ctypes.c_int32), ("chunk_size", ctypes.c_int32),
-                ("dt_softplus", ctypes.c_int32)]
+                ("dt_softplus", ctypes.c_int32), ("state_dtype", ctypes.c_int32)]
 
 
 class ssd_workspace_layout(ctypes.Structure):
@@ -48,14 +48,15 @@ class ssd_workspace_layout(ctypes.Structure):
                 ("desc", ctypes.c_size_t), ("dts", ctypes.c_size_t), ("cs2", ctypes.c_size_t),
                 ("cbt", ctypes.c_size_t), ("gexp", ctypes.c_size_t), ("states", ctypes.c_size_t), ("sexp", ctypes.c_size_t),
                 ("hin", ctypes.c_size_t), ("hexp", ctypes.c_size_t), ("xexp", ctypes.c_size_t),
-                ("seq_list", ctypes.c_size_t)]
+                ("seq_list", ctypes.c_size_t), ("recur_list", ctypes.c_size_t)]
 
 
 _lock = threading.Lock()
 _lib = None
 
 # SSD_ABI_VERSION of include/ssd.h that the ctypes structures below mirror
-ABI_VERSION = 9
+ABI_VERSION = 12
+STATE_F32, STATE_BF16 = 0, 1  # SSD_STATE_F32, SSD_STATE_BF16
 SHORT_PATH_LIMIT = 128  # SSD_SHORT_PATH_LIMIT
 
 
@@ -112,9 +113,20 @@ def _check(status: int, what: str):
 
 
 def make_problem(total_len, batch, nheads, head_dim, ngroups, dstate, max_slots,
-                 dt_softplus=True, chunk_size=0) -> ssd_problem:
+                 dt_softplus=True, chunk_size=0, state_dtype=STATE_F32) -> ssd_problem:
     return ssd_problem(int(total_len), int(batch), int(nheads), int(head_dim), int(ngroups),
-                       int(dstate), int(max_slots), int(chunk_size), 1 if dt_softplus else 0)
+                       int(dstate), int(max_slots), int(chunk_size), 1 if dt_softplus else 0,
+                       int(state_dtype))
+
+
+def _state_dtype(t, name):
+    """SSD_STATE_* of a state tensor (fp32 or bf16)."""
+    import torch
+    if t.dtype == torch.float32:
+        return STATE_F32
+    if t.dtype == torch.bfloat16:
+        return STATE_BF16
+    raise TypeError(f"{name}: expected float32 or bfloat16 states, got {t.dtype}")
 
 
 def ssd_set_short_path_max(tokens: int) -> int:
@@ -172,7 +184,8 @@ def _opt(t, name, dtype, shape, device):
 def problem_from_tensors(x, B, ssm_pool, query_start_loc, dt_softplus=True) -> ssd_problem:
     T, H, P = x.shape
     _, G, N = B.shape
-    return make_problem(T, query_start_loc.numel() - 1, H, P, G, N, ssm_pool.shape[0], dt_softplus)
+    return make_problem(T, query_start_loc.numel() - 1, H, P, G, N, ssm_pool.shape[0], dt_softplus,
+                        state_dtype=_state_dtype(ssm_pool, "ssm_pool"))
 
 
 def ssd_chunk_scan_varlen_fwd_inplace(y, x, dt, A, B, C, D, dt_bias, ssm_pool, query_start_loc,
@@ -187,7 +200,8 @@ def ssd_chunk_scan_varlen_fwd_inplace(y, x, dt, A, B, C, D, dt_bias, ssm_pool, q
     None/empty; cache_indices int32/uint32 [batch] (reinterpreted as uint32).
     ``workspace``: uint8 tensor of at least ssd_workspace_size() bytes, or
     None to allocate one.  Runs on ``stream`` (a torch.cuda.Stream) or the
-    current stream; asynchronous.  Returns the workspace tensor.
+    current stream; asynchronous.  Returns the workspace tensor.  A bf16
+    ssm_pool selects bf16 state storage (arithmetic stays fp32).
     """
     import torch
     dev = x.device
@@ -207,7 +221,8 @@ def ssd_chunk_scan_varlen_fwd_inplace(y, x, dt, A, B, C, D, dt_bias, ssm_pool, q
     _need(C, "C", torch.bfloat16, (T, G, N), dev)
     D = _opt(D, "D", torch.float32, (H,), dev)
     dt_bias = _opt(dt_bias, "dt_bias", torch.float32, (H,), dev)
-    _need(ssm_pool, "ssm_pool", torch.float32, (S, H, P, N), dev)
+    sd = _state_dtype(ssm_pool, "ssm_pool")
+    _need(ssm_pool, "ssm_pool", ssm_pool.dtype, (S, H, P, N), dev)
     _need(query_start_loc, "query_start_loc", torch.int32, (batch + 1,), dev)
     if has_initial_state is not None and has_initial_state.numel() > 0:
         if has_initial_state.dtype == torch.bool:
@@ -219,7 +234,7 @@ def ssd_chunk_scan_varlen_fwd_inplace(y, x, dt, A, B, C, D, dt_bias, ssm_pool, q
         raise TypeError("cache_indices must be int32 or uint32")
     if tuple(cache_indices.shape) != (batch,) or not cache_indices.is_contiguous() or cache_indices.device != dev:
         raise ValueError("cache_indices must be a contiguous [batch] tensor on the same device")
-    prob = make_problem(T, batch, H, P, G, N, S, dt_softplus)
+    prob = make_problem(T, batch, H, P, G, N, S, dt_softplus, state_dtype=sd)
     need = ssd_workspace_size(prob)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -238,9 +253,10 @@ def ssd_chunk_scan_varlen_fwd_inplace(y, x, dt, A, B, C, D, dt_bias, ssm_pool, q
 def ssd_chunk_scan_varlen_fwd(y, x, dt, A, B, C, D, dt_bias, initial_states, final_states,
                               query_start_loc, *, dt_softplus=True, workspace=None, stream=None):
     """Varlen SSD forward with separate initial and final states (see
-    include/ssd.h): sequence b starts from ``initial_states[b]`` (fp32
-    [batch,H,P,N], or None/empty for zero) and its final state is written to
-    ``final_states[b]`` (fp32 [batch,H,P,N]).  Other tensors as for
+    include/ssd.h): sequence b starts from ``initial_states[b]`` ([batch,H,P,N],
+    or None/empty for zero) and its final state is written to
+    ``final_states[b]`` ([batch,H,P,N]); both fp32, or both bf16 (bf16 state
+    storage, arithmetic in fp32).  Other tensors as for
     ssd_chunk_scan_varlen_fwd_inplace.  Returns the workspace tensor.
     """
     import torch
@@ -260,10 +276,13 @@ def ssd_chunk_scan_varlen_fwd(y, x, dt, A, B, C, D, dt_bias, initial_states, fin
     _need(C, "C", torch.bfloat16, (T, G, N), dev)
     D = _opt(D, "D", torch.float32, (H,), dev)
     dt_bias = _opt(dt_bias, "dt_bias", torch.float32, (H,), dev)
-    initial_states = _opt(initial_states, "initial_states", torch.float32, (batch, H, P, N), dev)
-    _need(final_states, "final_states", torch.float32, (batch, H, P, N), dev)
+    if final_states is None:
+        raise ValueError("final_states is required")
+    sd = _state_dtype(final_states, "final_states")
+    initial_states = _opt(initial_states, "initial_states", final_states.dtype, (batch, H, P, N), dev)
+    _need(final_states, "final_states", final_states.dtype, (batch, H, P, N), dev)
     _need(query_start_loc, "query_start_loc", torch.int32, (batch + 1,), dev)
-    prob = make_problem(T, batch, H, P, G, N, max(batch, 1), dt_softplus)
+    prob = make_problem(T, batch, H, P, G, N, max(batch, 1), dt_softplus, state_dtype=sd)
     need = ssd_workspace_size(prob)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)

@@ -32,6 +32,7 @@ ssd_status check_problem(const ssd_problem *p) {
         p->ngroups < 1 || p->dstate < 1 || p->max_slots < 1 || p->chunk_size < 0)
         return SSD_ERR_BAD_SHAPE;
     if (p->nheads % p->ngroups != 0) return SSD_ERR_BAD_SHAPE;
+    if (p->state_dtype != SSD_STATE_F32 && p->state_dtype != SSD_STATE_BF16) return SSD_ERR_UNSUPPORTED;
     if (p->total_len > INT32_MAX) return SSD_ERR_BAD_SHAPE;  // query_start_loc is int32
     if (p->dstate > SSD_MAX_DSTATE) return SSD_ERR_UNSUPPORTED;
     if (p->dstate != 64 && p->dstate != 128 && p->dstate != 256) return SSD_ERR_UNSUPPORTED;
@@ -63,6 +64,7 @@ void layout_of(const ssd_problem *p, ssd_workspace_layout *L) {
     L->hexp = off;      off = align_up(off + (size_t)ncm * H * (size_t)p->head_dim * sizeof(int32_t));
     L->xexp = off;      off = align_up(off + (size_t)ncm * H * sizeof(int32_t));
     L->seq_list = off;  off = align_up(off + (size_t)p->batch * sizeof(int32_t));
+    L->recur_list = off; off = align_up(off + (size_t)p->batch * sizeof(int32_t));
     L->total_bytes = off;
 }
 
@@ -103,10 +105,10 @@ ssd_status ssd_workspace_get_layout(const ssd_problem *prob, ssd_workspace_layou
     return SSD_OK;
 }
 
-static const char *const kKernelNames[] = {"ssd_prep", "ssd_chunk_state", "ssd_state_passing",
-                                           "ssd_chunk_scan", "ssd_short"};
-static constexpr int kNumKernels = 5;
-static constexpr int kShortKernel = 4;
+static const char *const kKernelNames[] = {"ssd_prep",       "ssd_chunk_state", "ssd_state_passing",
+                                           "ssd_chunk_scan", "ssd_short",       "ssd_recur"};
+static constexpr int kNumKernels = 6;
+static constexpr int kFirstShortKernel = 4;  // this and the later ones serve the short path
 
 int ssd_set_short_path_max(int tokens) {
     if (tokens < 0 || tokens > SSD_SHORT_PATH_LIMIT) return -1;
@@ -119,8 +121,8 @@ const char *ssd_kernel_name(int i) { return (i >= 0 && i < kNumKernels) ? kKerne
 
 // Where the state chain starts and ends (see Params::state_in).
 struct StateIO {
-    const float *in;
-    float *out;
+    const void *in;
+    void *out;
     const uint8_t *has_init;
     const uint32_t *cache_idx;
     bool init_all;
@@ -179,10 +181,12 @@ static ssd_status run_scan(
     p.has_init = sio.has_init;
     p.cache_idx = sio.cache_idx;
     p.init_all = sio.init_all ? 1 : 0;
+    p.state_bf16 = prob->state_dtype == SSD_STATE_BF16 ? 1 : 0;
     // the short path serves dstate 64 and 128; the route of a sequence
     // depends on its own length only, so its results do not depend on the
     // rest of the batch
     p.short_max = p.N <= 128 ? g_short_max.load() : 0;
+    p.recur_max = std::min(p.short_max, ssd::kRecurMax);
     // with the short path on, only sequences longer than its limit reach the
     // chunked steps: at most T / (short_max + 1) of them, with at most
     // T / 256 + that many chunks; the launches are sized to these bounds
@@ -201,6 +205,7 @@ static ssd_status run_scan(
     p.hexp = reinterpret_cast<int32_t *>(ws + L.hexp);
     p.xexp = reinterpret_cast<int32_t *>(ws + L.xexp);
     p.seq_list = reinterpret_cast<int32_t *>(ws + L.seq_list);
+    p.recur_list = reinterpret_cast<int32_t *>(ws + L.recur_list);
     p.cbt = reinterpret_cast<uint16_t *>(ws + L.cbt);
     p.gexp = reinterpret_cast<int32_t *>(ws + L.gexp);
     p.states = reinterpret_cast<uint16_t *>(ws + L.states);
@@ -210,12 +215,12 @@ static ssd_status run_scan(
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t (*const launchers[kNumKernels])(const ssd::Params &, const ssd::Launch &) = {
         ssd::launch_prep, ssd::launch_chunk_state, ssd::launch_state_passing, ssd::launch_chunk_scan,
-        ssd::launch_short};
+        ssd::launch_short, ssd::launch_recur};
     for (int k = 0; k < kNumKernels; ++k) {
-        // no sequence can take the short path: its kernel would have nothing
-        // to do, so it is not launched (its completion event, if any, is
-        // recorded on the stream where it would have run)
-        if (k == kShortKernel && p.short_max == 0) {
+        // no sequence can take the short path: its kernels would have nothing
+        // to do, so they are not launched (their completion events, if any,
+        // are recorded on the stream where they would have run)
+        if (k >= kFirstShortKernel && p.short_max == 0) {
             if (events && hipEventRecord(static_cast<hipEvent_t>(events[k + 1]), s) != hipSuccess) return SSD_ERR_HIP;
             continue;
         }
@@ -229,7 +234,7 @@ static ssd_status run_scan(
 }
 
 static ssd_status inplace(const ssd_problem *prob, void *y, const void *x, const float *dt, const float *A,
-                          const void *B, const void *C, const float *D, const float *dt_bias, float *ssm_pool,
+                          const void *B, const void *C, const float *D, const float *dt_bias, void *ssm_pool,
                           const int32_t *query_start_loc, const uint8_t *has_initial_state,
                           const uint32_t *cache_indices, void *workspace, size_t workspace_bytes, void *stream,
                           void *const *events) {
@@ -241,7 +246,7 @@ static ssd_status inplace(const ssd_problem *prob, void *y, const void *x, const
 
 static ssd_status separate(const ssd_problem *prob, void *y, const void *x, const float *dt, const float *A,
                            const void *B, const void *C, const float *D, const float *dt_bias,
-                           const float *initial_states, float *final_states, const int32_t *query_start_loc,
+                           const void *initial_states, void *final_states, const int32_t *query_start_loc,
                            void *workspace, size_t workspace_bytes, void *stream, void *const *events) {
     if (prob == nullptr) return SSD_ERR_NULL_ARG;
     ssd_problem q = *prob;  // no pool: the state tensors have one slot per sequence
@@ -261,7 +266,7 @@ static ssd_status check_events(void *const *events, int n_events) {
 
 ssd_status ssd_chunk_scan_varlen_fwd_inplace(
     const ssd_problem *prob, void *y, const void *x, const float *dt, const float *A,
-    const void *B, const void *C, const float *D, const float *dt_bias, float *ssm_pool,
+    const void *B, const void *C, const float *D, const float *dt_bias, void *ssm_pool,
     const int32_t *query_start_loc, const uint8_t *has_initial_state,
     const uint32_t *cache_indices, void *workspace, size_t workspace_bytes, void *stream) {
     return inplace(prob, y, x, dt, A, B, C, D, dt_bias, ssm_pool, query_start_loc, has_initial_state,
@@ -270,7 +275,7 @@ ssd_status ssd_chunk_scan_varlen_fwd_inplace(
 
 ssd_status ssd_chunk_scan_varlen_fwd_inplace_profiled(
     const ssd_problem *prob, void *y, const void *x, const float *dt, const float *A,
-    const void *B, const void *C, const float *D, const float *dt_bias, float *ssm_pool,
+    const void *B, const void *C, const float *D, const float *dt_bias, void *ssm_pool,
     const int32_t *query_start_loc, const uint8_t *has_initial_state,
     const uint32_t *cache_indices, void *workspace, size_t workspace_bytes, void *stream,
     void *const *events, int n_events) {
@@ -282,8 +287,8 @@ ssd_status ssd_chunk_scan_varlen_fwd_inplace_profiled(
 
 ssd_status ssd_chunk_scan_varlen_fwd(
     const ssd_problem *prob, void *y, const void *x, const float *dt, const float *A,
-    const void *B, const void *C, const float *D, const float *dt_bias, const float *initial_states,
-    float *final_states, const int32_t *query_start_loc, void *workspace, size_t workspace_bytes,
+    const void *B, const void *C, const float *D, const float *dt_bias, const void *initial_states,
+    void *final_states, const int32_t *query_start_loc, void *workspace, size_t workspace_bytes,
     void *stream) {
     return separate(prob, y, x, dt, A, B, C, D, dt_bias, initial_states, final_states, query_start_loc,
                     workspace, workspace_bytes, stream, nullptr);
@@ -291,8 +296,8 @@ ssd_status ssd_chunk_scan_varlen_fwd(
 
 ssd_status ssd_chunk_scan_varlen_fwd_profiled(
     const ssd_problem *prob, void *y, const void *x, const float *dt, const float *A,
-    const void *B, const void *C, const float *D, const float *dt_bias, const float *initial_states,
-    float *final_states, const int32_t *query_start_loc, void *workspace, size_t workspace_bytes,
+    const void *B, const void *C, const float *D, const float *dt_bias, const void *initial_states,
+    void *final_states, const int32_t *query_start_loc, void *workspace, size_t workspace_bytes,
     void *stream, void *const *events, int n_events) {
     const ssd_status st = check_events(events, n_events);
     if (st != SSD_OK) return st;

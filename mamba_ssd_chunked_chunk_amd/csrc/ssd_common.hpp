@@ -22,6 +22,7 @@ constexpr int kHeadDim = 64;     // P supported by this build
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kShortMax = 128;   // longest sequence the short-path kernel takes
+constexpr int kRecurMax = 4;     // longest sequence the token-recurrence kernel takes
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -45,14 +46,15 @@ struct Params {
     const uint16_t *B, *C;
     const float *D, *dt_bias;
     const int32_t *qsl;
-    // where each sequence's state starts and ends, [slots][H][P][N] fp32:
+    // where each sequence's state starts and ends, [slots][H][P][N] fp32 or bf16:
     // slot cache_idx[b] (b when cache_idx is null) of state_in, read when
     // init_all or has_init[b] (has_init may be null: no sequence), and of
     // state_out, written with the final state.  The in-place operation passes
     // the pool for both; the other one initial_states (or null, never read)
     // and final_states, with no slot indices.
-    const float *state_in;
-    float *state_out;
+    const void *state_in;   // fp32 or bf16 elements (state_bf16)
+    void *state_out;
+    int state_bf16;         // states stored as bf16 (arithmetic stays fp32)
     const uint8_t *has_init;
     const uint32_t *cache_idx;
     int init_all;
@@ -63,6 +65,9 @@ struct Params {
     // can see at most, given the routing
     int64_t nchunks_grid;
     int nseq_grid;
+    // of the short sequences, those of 1 .. recur_max tokens go to the
+    // token-recurrence kernel (0: none)
+    int recur_max;
     // workspace carve (device)
     int32_t *meta;       // [4]: nchunks
     int32_t *chunk_off;  // [batch+1]
@@ -77,6 +82,7 @@ struct Params {
     int32_t *hexp;       // [nchunks_max][H][P]
     int32_t *xexp;       // [nchunks_max][H]: 2^xexp puts the chunk's max |x| of the head in [2^14, 2^15)
     int32_t *seq_list;   // [batch]: the meta[1] sequences the state chain walks
+    int32_t *recur_list; // [batch]: the meta[2] sequences the token recurrence takes
 };
 
 // ---------------------------------------------------------------- helpers
@@ -161,6 +167,13 @@ __device__ __forceinline__ float wave_incl_scan(float v) {
     return v;
 }
 
+// v plus the value of another lane by a DPP pattern with a source for every
+// lane (quad permutations, row mirrors)
+template <int CTRL>
+__device__ __forceinline__ float dpp_add_all(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
 // Maximum over a 64-lane wavefront for values >= 0 (magnitudes), with DPP
 // row operations instead of LDS permutes: within rows of 16 lanes, then
 // across rows with the row broadcasts (lanes a DPP step leaves unwritten
@@ -224,6 +237,58 @@ __device__ __forceinline__ float softplus_f(float v) {
     return fmaxf(v, 0.0f) + l;
 }
 
+// ---- state storage: fp32, or bf16 (SB) rounded to nearest even when stored.
+// Consecutive elements idx .. idx+3 (or +7) of a state tensor as floats.
+__device__ __forceinline__ float bf16x2_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16x2_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+template <bool SB>
+__device__ __forceinline__ f32x4 load_state4(const void *base, int64_t idx) {
+    if constexpr (SB) {
+        const u32x2 v = *reinterpret_cast<const u32x2 *>(static_cast<const uint16_t *>(base) + idx);
+        return f32x4{bf16x2_lo(v[0]), bf16x2_hi(v[0]), bf16x2_lo(v[1]), bf16x2_hi(v[1])};
+    } else {
+        return *reinterpret_cast<const f32x4 *>(static_cast<const float *>(base) + idx);
+    }
+}
+template <bool SB>
+__device__ __forceinline__ void store_state4(void *base, int64_t idx, const f32x4 &v) {
+    if constexpr (SB)
+        *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(base) + idx) =
+            u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    else
+        *reinterpret_cast<f32x4 *>(static_cast<float *>(base) + idx) = v;
+}
+template <bool SB>
+__device__ __forceinline__ void load_state8(const void *base, int64_t idx, float (&o)[8]) {
+    if constexpr (SB) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(base) + idx);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            o[2 * k] = bf16x2_lo(v[k]);
+            o[2 * k + 1] = bf16x2_hi(v[k]);
+        }
+    } else {
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(static_cast<const float *>(base) + idx);
+        const f32x4 b = *reinterpret_cast<const f32x4 *>(static_cast<const float *>(base) + idx + 4);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            o[k] = a[k];
+            o[4 + k] = b[k];
+        }
+    }
+}
+template <bool SB>
+__device__ __forceinline__ void store_state8(void *base, int64_t idx, const float (&v)[8]) {
+    if constexpr (SB) {
+        *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(base) + idx) =
+            u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+    } else {
+        *reinterpret_cast<f32x4 *>(static_cast<float *>(base) + idx) = f32x4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<f32x4 *>(static_cast<float *>(base) + idx + 4) = f32x4{v[4], v[5], v[6], v[7]};
+    }
+}
+
 // Whether a sequence of len tokens goes to the short-path kernel (with the
 // path on, zero-length sequences go there too).
 __host__ __device__ __forceinline__ bool is_short_sequence(int len, int short_max) {
@@ -253,9 +318,21 @@ inline hipError_t launch_kernel(K kernel, dim3 grid, dim3 block, const Launch &l
     return hipGetLastError();
 }
 
+// Slices a group's heads are split into by the short-path kernels, whose
+// grid is (sequence, group, slice): more while the grid is small for the GPU
+// (not every sequence of the batch need be short; workgroups of the others
+// leave at once).
+inline int short_head_slices(const Params &p) {
+    const int hg = p.H / p.G;
+    int hz = 1;
+    while ((int64_t)p.batch * p.G * hz < 2 * (int64_t)p.num_cus && hg % (2 * hz) == 0) hz *= 2;
+    return hz;
+}
+
 hipError_t launch_prep(const Params &p, const Launch &l);
 hipError_t launch_chunk_state(const Params &p, const Launch &l);
 hipError_t launch_state_passing(const Params &p, const Launch &l);
 hipError_t launch_chunk_scan(const Params &p, const Launch &l);
 hipError_t launch_short(const Params &p, const Launch &l);
+hipError_t launch_recur(const Params &p, const Launch &l);
 }  // namespace ssd

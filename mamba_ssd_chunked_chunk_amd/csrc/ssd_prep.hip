@@ -197,12 +197,19 @@ __global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(Params p) {
     if (c == 0 && job == 0) {
         // the sequences the state chain walks: all of them when no sequence
         // can take the short path, else those longer than its limit
-        int carry2 = 0;
+        // and, in a second list, the sequences the token recurrence takes
+        // (both counts packed in one scan: low 16 bits and high 16 bits per
+        // round of kPrepThreads sequences)
+        int carry2 = 0, carry3 = 0;
         for (int base = 0; base < p.batch; base += kPrepThreads) {
             const int b = base + tid;
-            int f = 0;
-            if (b < p.batch) f = !is_short_sequence(p.qsl[b + 1] - p.qsl[b], p.short_max);
-            const int wincl = wave_incl_scan(f);
+            int f = 0, r = 0;
+            if (b < p.batch) {
+                const int len = p.qsl[b + 1] - p.qsl[b];
+                f = !is_short_sequence(len, p.short_max);
+                r = len >= 1 && len <= p.recur_max;
+            }
+            const int wincl = wave_incl_scan(f | (r << 16));
             __syncthreads();
             if (lane == 63) s_wtot[wave] = wincl;
             __syncthreads();
@@ -211,13 +218,16 @@ __global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(Params p) {
                 if (w < wave) before += s_wtot[w];
                 total += s_wtot[w];
             }
-            if (f) p.seq_list[carry2 + before + wincl - 1] = b;
-            carry2 += total;
+            const int incl = before + wincl;
+            if (f) p.seq_list[carry2 + (incl & 0xFFFF) - 1] = b;
+            if (r) p.recur_list[carry3 + (incl >> 16) - 1] = b;
+            carry2 += total & 0xFFFF;
+            carry3 += total >> 16;
         }
         if (tid == 0) {
             p.chunk_off[p.batch] = carry;
             p.meta[0] = carry;
-            p.meta[1] = carry2; p.meta[2] = 0; p.meta[3] = 0;
+            p.meta[1] = carry2; p.meta[2] = carry3; p.meta[3] = 0;
         }
     }
     __syncthreads();

@@ -75,7 +75,8 @@ __device__ __forceinline__ uint32_t bf16_absmax2(uint32_t m, uint32_t w) {
 }
 }  // namespace
 
-template <int N>
+// SB: states stored as bf16 (read widened to fp32, final state rounded once).
+template <int N, bool SB>
 __global__ __launch_bounds__(kSThreads) void ssd_short_kernel(Params p) {
     static_assert(N == 64 || N == 128, "the short path covers dstate 64 and 128");
     constexpr int NT = N / 32;  // n tiles
@@ -88,21 +89,22 @@ __global__ __launch_bounds__(kSThreads) void ssd_short_kernel(Params p) {
     const int64_t t0 = p.qsl[b];
     const int len = p.qsl[b + 1] - (int)t0;
     if (p.N != N || !is_short_sequence(len, p.short_max)) return;  // the chunked path takes it
+    if (len >= 1 && len <= p.recur_max) return;                      // the token-recurrence kernel takes it
     const int64_t slot = p.cache_idx != nullptr ? (int64_t)p.cache_idx[b] : (int64_t)b;
     const bool init = p.init_all != 0 || (p.has_init != nullptr && p.has_init[b] != 0);
     const int hg = p.H / p.G;
     const int hpw = hg / (int)gridDim.z;
     const int h_begin = g * hg + (int)blockIdx.z * hpw;
     const int h_end = h_begin + hpw;
-    const float *state_src = p.state_in != nullptr ? p.state_in : p.state_out;
+    const void *state_src = p.state_in != nullptr ? p.state_in : p.state_out;
     if (len == 0) {  // no tokens: the final state is the initial one (or zeros)
-        constexpr int64_t head_elems = (int64_t)kHeadDim * N;  // a multiple of 4 * kSThreads
+        constexpr int64_t head_bytes = (int64_t)kHeadDim * N * (SB ? 2 : 4);  // a multiple of 16 * kSThreads
         for (int h = h_begin; h < h_end; ++h) {
-            const float *src = state_src + (slot * p.H + h) * head_elems;
-            float *dst = p.state_out + (slot * p.H + h) * head_elems;
+            const char *src = static_cast<const char *>(state_src) + (slot * p.H + h) * head_bytes;
+            char *dst = static_cast<char *>(p.state_out) + (slot * p.H + h) * head_bytes;
             if (init && src == dst) continue;  // in place: already there
-            for (int64_t e = 4 * (int64_t)threadIdx.x; e < head_elems; e += 4 * kSThreads)
-                *reinterpret_cast<f32x4 *>(dst + e) = init ? *reinterpret_cast<const f32x4 *>(src + e) : f32x4{};
+            for (int64_t e = 16 * (int64_t)threadIdx.x; e < head_bytes; e += 16 * kSThreads)
+                *reinterpret_cast<u32x4 *>(dst + e) = init ? *reinterpret_cast<const u32x4 *>(src + e) : u32x4{};
         }
         return;
     }
@@ -268,9 +270,9 @@ __global__ __launch_bounds__(kSThreads) void ssd_short_kernel(Params p) {
             if (p.dt_bias != nullptr) bnx = p.dt_bias[h];
         }
         if (owner && init) {  // both uniform over the wavefront
-            const float *src = state_src + ((slot * p.H + h) * kHeadDim + 32 * pts + l32) * N + 32 * nt + 4 * hl;
+            const int64_t idx = ((slot * p.H + h) * kHeadDim + 32 * pts + l32) * N + 32 * nt + 4 * hl;
 #pragma unroll
-            for (int a = 0; a < 4; ++a) hn[a] = *reinterpret_cast<const f32x4 *>(src + 8 * a);
+            for (int a = 0; a < 4; ++a) hn[a] = load_state4<SB>(state_src, idx + 8 * a);
         }
     };
     // maxima and decay table of the loaded head h into buffer nb
@@ -525,13 +527,13 @@ __global__ __launch_bounds__(kSThreads) void ssd_short_kernel(Params p) {
         if (owner) {
             const float dec = fast_exp2(cs_last);
             const float us = ldexpf(1.0f, kw - sb - xe);
-            float *dst = p.state_out + ((slot * p.H + h) * kHeadDim + 32 * pts + l32) * N + 32 * nt + 4 * hl;
+            const int64_t idx = ((slot * p.H + h) * kHeadDim + 32 * pts + l32) * N + 32 * nt + 4 * hl;
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
                 f32x4 o;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) o[e] = dec * hc[a][e] + sacc[4 * a + e] * us;
-                *reinterpret_cast<f32x4 *>(dst + 8 * a) = o;
+                store_state4<SB>(p.state_out, idx + 8 * a, o);
             }
         }
         // y back to unit scale, bf16; lanes l and l+32 trade groups so each
@@ -554,18 +556,17 @@ __global__ __launch_bounds__(kSThreads) void ssd_short_kernel(Params p) {
 }
 
 hipError_t launch_short(const Params &p, const Launch &l) {
-    // split a group's heads over workgroups while the grid is small for the
-    // GPU (not every sequence of the batch need be short: workgroups of the
-    // others leave at once)
-    const int hg = p.H / p.G;
-    int hz = 1;
-    while ((int64_t)p.batch * p.G * hz < 2 * (int64_t)p.num_cus && hg % (2 * hz) == 0) hz *= 2;
-    const dim3 grid((unsigned)p.batch, (unsigned)p.G, (unsigned)hz);
+    const dim3 grid((unsigned)p.batch, (unsigned)p.G, (unsigned)short_head_slices(p));
+    const dim3 block(kSThreads);
     switch (p.N) {
-    case 64: return launch_kernel(ssd_short_kernel<64>, grid, dim3(kSThreads), l, p);
-    case 128: return launch_kernel(ssd_short_kernel<128>, grid, dim3(kSThreads), l, p);
+    case 64:
+        return p.state_bf16 ? launch_kernel(ssd_short_kernel<64, true>, grid, block, l, p)
+                            : launch_kernel(ssd_short_kernel<64, false>, grid, block, l, p);
+    case 128:
+        return p.state_bf16 ? launch_kernel(ssd_short_kernel<128, true>, grid, block, l, p)
+                            : launch_kernel(ssd_short_kernel<128, false>, grid, block, l, p);
     default:  // no sequence is short at other dstates (not launched there); a one-workgroup no-op
-        return launch_kernel(ssd_short_kernel<128>, dim3(1, 1, 1), dim3(kSThreads), l, p);  // p.N != 128: exits
+        return launch_kernel(ssd_short_kernel<128, false>, dim3(1, 1, 1), block, l, p);  // p.N != 128: exits
     }
 }
 

@@ -4,7 +4,7 @@
 // For sequence b, head h and every state element (p, n), walking the
 // sequence's chunks k in order (slot = cache_indices[b] for the in-place
 // operation, b for the other one):
-//   h_in[first]  = initial ? state_in[slot][h][p][n] : 0
+//   h_in[first]  = initial ? state_in[slot][h][p][n] : 0    (fp32 or bf16 storage)
 //   h_in[k + 1]  = exp(cs_last(k)) * h_in[k] + S[k]
 //   final        = exp(cs_last(K-1)) * h_in[K-1] + S[K-1]
 //   state_out[slot][h][p][n] = final
@@ -56,7 +56,8 @@ __device__ __forceinline__ float row_max(float m) {
 
 // LIST: the grid's x walks the sequence list prep wrote (the short path is
 // on: only sequences longer than its limit are there), else the batch.
-template <int N, bool LIST>
+// SB: states stored as bf16 (read widened to fp32, final state rounded once).
+template <int N, bool LIST, bool SB>
 __global__ __launch_bounds__(256) void ssd_state_passing_kernel(Params p) {
     int b = blockIdx.x;
     if constexpr (LIST) {
@@ -75,15 +76,14 @@ __global__ __launch_bounds__(256) void ssd_state_passing_kernel(Params p) {
     const bool init = p.init_all != 0 || (p.has_init != nullptr && p.has_init[b] != 0);
     const int64_t off = (slot * p.H + h) * head_elems + e0;
     // state_in is null only when no sequence reads it
-    const float4 *in4 = reinterpret_cast<const float4 *>((p.state_in != nullptr ? p.state_in : p.state_out) + off);
-    float4 *out4 = reinterpret_cast<float4 *>(p.state_out + off);
+    const void *src = p.state_in != nullptr ? p.state_in : p.state_out;
 
     float st[kPer];
-    {
-        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-        const float4 lo = init ? in4[0] : z, hi = init ? in4[1] : z;
-        st[0] = lo.x; st[1] = lo.y; st[2] = lo.z; st[3] = lo.w;
-        st[4] = hi.x; st[5] = hi.y; st[6] = hi.z; st[7] = hi.w;
+    if (init) {
+        load_state8<SB>(src, off, st);
+    } else {
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) st[e] = 0.f;
     }
     const int64_t stride = (int64_t)p.H * head_elems;  // one chunk of states
     const uint16_t *S = p.states + ((int64_t)k0 * p.H + h) * head_elems + e0;
@@ -153,8 +153,7 @@ __global__ __launch_bounds__(256) void ssd_state_passing_kernel(Params p) {
         fetch(kb, sv, sev, dv);
         link(kb, sv, sev, dv);
     }
-    out4[0] = make_float4(st[0], st[1], st[2], st[3]);
-    out4[1] = make_float4(st[4], st[5], st[6], st[7]);
+    store_state8<SB>(p.state_out, off, st);
 }
 
 hipError_t launch_state_passing(const Params &p, const Launch &l) {
@@ -162,15 +161,29 @@ hipError_t launch_state_passing(const Params &p, const Launch &l) {
     const unsigned zb = (unsigned)((head_elems / kPer + 255) / 256);
     const bool list = p.short_max > 0;
     dim3 grid((unsigned)(list ? p.nseq_grid : p.batch), (unsigned)p.H, zb);
+    const dim3 block(256);
+    if (p.state_bf16) {
+        switch (p.N) {
+        case 64:
+            return list ? launch_kernel(ssd_state_passing_kernel<64, true, true>, grid, block, l, p)
+                        : launch_kernel(ssd_state_passing_kernel<64, false, true>, grid, block, l, p);
+        case 128:
+            return list ? launch_kernel(ssd_state_passing_kernel<128, true, true>, grid, block, l, p)
+                        : launch_kernel(ssd_state_passing_kernel<128, false, true>, grid, block, l, p);
+        case 256:  // the short path does not serve dstate 256
+            return launch_kernel(ssd_state_passing_kernel<256, false, true>, grid, block, l, p);
+        default: return hipErrorInvalidValue;
+        }
+    }
     switch (p.N) {
     case 64:
-        return list ? launch_kernel(ssd_state_passing_kernel<64, true>, grid, dim3(256), l, p)
-                    : launch_kernel(ssd_state_passing_kernel<64, false>, grid, dim3(256), l, p);
+        return list ? launch_kernel(ssd_state_passing_kernel<64, true, false>, grid, block, l, p)
+                    : launch_kernel(ssd_state_passing_kernel<64, false, false>, grid, block, l, p);
     case 128:
-        return list ? launch_kernel(ssd_state_passing_kernel<128, true>, grid, dim3(256), l, p)
-                    : launch_kernel(ssd_state_passing_kernel<128, false>, grid, dim3(256), l, p);
-    case 256:  // the short path does not serve dstate 256
-        return launch_kernel(ssd_state_passing_kernel<256, false>, grid, dim3(256), l, p);
+        return list ? launch_kernel(ssd_state_passing_kernel<128, true, false>, grid, block, l, p)
+                    : launch_kernel(ssd_state_passing_kernel<128, false, false>, grid, block, l, p);
+    case 256:
+        return launch_kernel(ssd_state_passing_kernel<256, false, false>, grid, block, l, p);
     default: return hipErrorInvalidValue;
     }
 }

@@ -27,7 +27,8 @@ def upload(prob: dict, device="cuda"):
         C=t(prob["C"].reshape(T, G, N)).view(torch.bfloat16),
         D=t(prob.get("D")),
         dt_bias=t(prob.get("dt_bias")),
-        pool=t(prob["pool"]),
+        pool=(t(prob["pool"]).view(torch.bfloat16) if prob.get("state_dtype", "f32") == "bf16"
+              else t(prob["pool"])),
         query_start_loc=t(prob["query_start_loc"].astype(np.int32)),
         has_initial_state=t(prob.get("has_initial_state")),
         cache_indices=t(prob["cache_indices"].astype(np.int32)),
@@ -56,5 +57,8 @@ def run_fwd(d: dict, initial_states, final_states, workspace=None, stream=None):
 def problem_struct(d: dict):
     T, H, P = d["x"].shape
     G, N = d["B"].shape[1], d["B"].shape[2]
+    import torch
     return binding.make_problem(T, d["query_start_loc"].numel() - 1, H, P, G, N,
-                                d["pool"].shape[0], d["dt_softplus"])
+                                d["pool"].shape[0], d["dt_softplus"],
+                                state_dtype=(binding.STATE_BF16 if d["pool"].dtype == torch.bfloat16
+                                             else binding.STATE_F32))

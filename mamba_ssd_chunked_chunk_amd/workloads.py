@@ -62,13 +62,15 @@ def _normal_bf16(rng, shape, std=1.0):
 
 def make_problem(seqlens, *, nheads, head_dim, ngroups, dstate, max_slots, seed,
                  init="none", pool_std=0.1, dt_softplus=True, with_D=True,
-                 with_dt_bias=True, with_has_init=True, name="custom"):
+                 with_dt_bias=True, with_has_init=True, name="custom", state_dtype="f32"):
     """Draw a problem.
 
     ``seqlens``: list of ints, or a callable rng -> list (drawn first).
     ``init``: "none" (has_initial_state all 0, pool zeros), "all",
     "half" (exactly half the sequences, chosen by a permutation),
     "bernoulli" (p = 0.5 each), or an explicit 0/1 list.
+    ``state_dtype``: "f32", or "bf16" for a pool stored as bf16 (the same
+    draw, rounded to bf16 bit patterns; see ``with_bf16_states``).
     """
     rng = np.random.Generator(np.random.PCG64(seed))
     lens = seqlens(rng) if callable(seqlens) else list(seqlens)
@@ -112,14 +114,26 @@ def make_problem(seqlens, *, nheads, head_dim, ngroups, dstate, max_slots, seed,
         for s in range(max_slots):
             pool[s] = rng.standard_normal((H, P, N), dtype=np.float32) * np.float32(pool_std)
 
-    return dict(
+    out = dict(
         name=name, seqlens=lens, total_len=T, batch=batch,
         nheads=H, head_dim=P, ngroups=G, dstate=N, chunk_size=CHUNK,
         max_slots=max_slots, dt_softplus=bool(dt_softplus),
         query_start_loc=qsl, x=x, dt=dt, A=A, B=B, C=C,
         D=D if with_D else None, dt_bias=dt_bias if with_dt_bias else None,
         pool=pool, has_initial_state=hi if with_has_init else None,
-        cache_indices=ci, seed=seed)
+        cache_indices=ci, seed=seed, state_dtype="f32")
+    return with_bf16_states(out) if state_dtype == "bf16" else out
+
+
+def with_bf16_states(prob: dict) -> dict:
+    """The problem with its pool stored as bf16 (uint16 bit patterns,
+    rounded to nearest even from the fp32 draw); everything else shared."""
+    if prob.get("state_dtype", "f32") == "bf16":
+        return prob
+    q = dict(prob)
+    q["pool"] = f32_to_bf16_bits(prob["pool"])
+    q["state_dtype"] = "bf16"
+    return q
 
 
 def _loguniform_lengths(rng):

@@ -108,7 +108,10 @@ def recurrence(prob: dict, *, seqs: tuple[int, int] | None = None,
     A = np.ascontiguousarray(prob["A"], dtype=np.float32)
     D = None if prob.get("D") is None else np.ascontiguousarray(prob["D"], dtype=np.float32)
     bias = None if prob.get("dt_bias") is None else np.ascontiguousarray(prob["dt_bias"], dtype=np.float32)
-    pool = np.ascontiguousarray(prob["pool"], dtype=np.float32)
+    pool = prob["pool"]
+    if prob.get("state_dtype", "f32") == "bf16":  # bf16 bit patterns: their exact values
+        pool = (np.ascontiguousarray(pool, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    pool = np.ascontiguousarray(pool, dtype=np.float32)
     max_slots = pool.shape[0]
     hi = prob.get("has_initial_state")
     hi = None if hi is None else np.ascontiguousarray(hi, dtype=np.uint8)

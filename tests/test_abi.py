@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert binding.ssd_abi_version() == binding.ABI_VERSION == 9
+    assert binding.ssd_abi_version() == binding.ABI_VERSION == 12
     for code, name in binding.STATUS_NAMES.items():
         assert lib.ssd_status_string(code).decode().startswith(name)
     assert b"unknown" in lib.ssd_status_string(99)
@@ -56,7 +56,7 @@ def test_workspace_layout_arithmetic(lib):
     assert L["nchunks_max"] == ncm
     assert L["total_bytes"] == binding.ssd_workspace_size(p)
     offs = [L[k] for k in ("meta", "chunk_off", "desc", "dts", "cs2", "cbt", "gexp", "states", "sexp", "hin", "hexp",
-                           "xexp", "seq_list")]
+                           "xexp", "seq_list", "recur_list")]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert L["cbt"] - L["cs2"] >= ncm * 16 * 256 * 4
     assert L["gexp"] - L["cbt"] >= ncm * 1 * 36 * 64 * 16 * 2
@@ -66,14 +66,15 @@ def test_workspace_layout_arithmetic(lib):
     assert L["hexp"] - L["hin"] >= ncm * 16 * 64 * 256 * 2
     assert L["xexp"] - L["hexp"] >= ncm * 16 * 64 * 4
     assert L["seq_list"] - L["xexp"] >= ncm * 16 * 4
-    assert L["total_bytes"] - L["seq_list"] >= 4 * 4
+    assert L["recur_list"] - L["seq_list"] >= 4 * 4
+    assert L["total_bytes"] - L["recur_list"] >= 4 * 4
     assert L["cs2"] - L["dts"] >= ncm * 16 * 256 * 4
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(batch=0), 2), (dict(nheads=6, ngroups=4), 2), (dict(total_len=-1), 2),
     (dict(max_slots=0), 2), (dict(dstate=512), 3), (dict(dstate=96), 3),
-    (dict(head_dim=128), 3), (dict(chunk_size=128), 3),
+    (dict(head_dim=128), 3), (dict(chunk_size=128), 3), (dict(state_dtype=2), 3), (dict(state_dtype=-1), 3),
 ])
 def test_bad_problems_rejected(lib, kw, status):
     n = ctypes.c_size_t(0)
@@ -147,6 +148,14 @@ def test_validate_inputs_host_errors(lib):
     assert lib.ssd_validate_inputs(ctypes.byref(_prob(batch=0)), None, None, None) == 2
 
 
+def test_state_dtype_accepted_and_layout_unchanged(lib):
+    """bf16 state storage is a valid problem and does not change the
+    workspace (the intermediates are the same either way)."""
+    a = binding.ssd_workspace_get_layout(_prob())
+    b = binding.ssd_workspace_get_layout(_prob(state_dtype=binding.STATE_BF16))
+    assert a == b
+
+
 def test_short_path_setting_host_only(lib):
     """The routing knob is host state: it returns the previous value, rejects
     values outside 0..SSD_SHORT_PATH_LIMIT without changing anything, and the
@@ -163,4 +172,4 @@ def test_short_path_setting_host_only(lib):
     finally:
         binding.ssd_set_short_path_max(prev)
     names = [lib.ssd_kernel_name(i).decode() for i in range(lib.ssd_kernel_count())]
-    assert names == ["ssd_prep", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan", "ssd_short"]
+    assert names == ["ssd_prep", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan", "ssd_short", "ssd_recur"]

@@ -26,6 +26,10 @@ pytestmark = pytest.mark.gpu
 
 Y_RTOL = 2e-2
 FINAL_TOL = 1e-3
+# bf16 state storage: the final state is rounded once to bf16 (8 significant
+# bits, nearest even: each element moves by at most half a unit in the last
+# place, 2^-8 of its magnitude), so the bound grows by 2^-8
+FINAL_TOL_BF16 = FINAL_TOL + 2.0 ** -8
 
 
 @contextlib.contextmanager
@@ -59,13 +63,13 @@ def assert_y(y_gpu, y_ref, what=""):
     return worst
 
 
-def assert_final(pool_slot, ref, what=""):
+def assert_final(pool_slot, ref, what="", tol=FINAL_TOL):
     nref = np.linalg.norm(ref)
     if nref == 0:
         assert np.all(pool_slot == 0), f"{what}: expected zeros"
         return 0.0
     r = frob_rel(pool_slot, ref)
-    assert r <= FINAL_TOL, f"{what}: final-state rel err {r:.2e}"
+    assert r <= tol, f"{what}: final-state rel err {r:.2e}"
     return r
 
 
@@ -75,9 +79,15 @@ def assert_untouched(pool_after, pool_before, written):
             assert np.array_equal(pool_after[s].view(np.uint32), pool_before[s].view(np.uint32)), f"slot {s} modified"
 
 
+def bits(t):
+    """The tensor's bit patterns (for bitwise comparisons that NaNs survive)."""
+    return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32)
+
+
 def full_check(prob, seqs=None):
     """Run on GPU, compare with the oracle (optionally only sequences
     seqs=(lo, hi)), check slot bookkeeping.  Returns (y worst ratio, final worst)."""
+    tol = FINAL_TOL_BF16 if prob.get("state_dtype", "f32") == "bf16" else FINAL_TOL
     d = torch_io.upload(prob, "cuda")
     before = d["pool"].clone()
     torch_io.run(d)
@@ -92,13 +102,13 @@ def full_check(prob, seqs=None):
     wf = 0.0
     for b in range(lo, hi):
         slot = int(ci[b])
-        wf = max(wf, assert_final(d["pool"][slot].cpu().numpy(), ref["final"][b], f"seq {b}"))
+        wf = max(wf, assert_final(d["pool"][slot].float().cpu().numpy(), ref["final"][b], f"seq {b}", tol))
     # slots outside cache_indices: bit-identical (compared on the device)
     written = torch.zeros(prob["pool"].shape[0], dtype=torch.bool, device="cuda")
     written[torch.from_numpy(ci.astype(np.int64)).cuda()] = True
     keep = (~written).nonzero().flatten()
-    assert torch.equal(d["pool"].index_select(0, keep).view(torch.int32),
-                       before.index_select(0, keep).view(torch.int32)), "an untouched slot changed"
+    assert torch.equal(bits(d["pool"].index_select(0, keep)),
+                       bits(before.index_select(0, keep))), "an untouched slot changed"
     assert bool(torch.isfinite(d["y"]).all()), "non-finite y"
     return wy, wf
 
@@ -427,3 +437,100 @@ def test_workloads_full_size_sampled(name, seqs):
     print(f"\n{name}: T={prob['total_len']} batch={prob['batch']} checking sequences {seqs}", flush=True)
     wy, wf = full_check(prob, seqs=seqs)
     print(f"{name}: y worst/bound {wy:.3f}  final rel {wf:.2e}", flush=True)
+
+
+# ------------------------------------------------- bf16 state storage
+
+@pytest.mark.parametrize("name", ["n256_chunked", "n128_mixed_short", "n64_edges"])
+def test_bf16_states_match_oracle(name):
+    """bf16 pool: initial states read as their bf16 values, final states
+    within FINAL_TOL_BF16 of the fp64 oracle, untouched slots bitwise."""
+    spec = {
+        "n256_chunked": dict(seqlens=[1000, 5, 0], H=2, G=1, N=256, init="half"),
+        "n128_mixed_short": dict(seqlens=MIXED_LENS, H=8, G=4, N=128, init="all"),
+        "n64_edges": dict(seqlens=[0, 1, 255, 256, 257, 511], H=4, G=2, N=64, init="bernoulli"),
+    }[name]
+    lens = spec.pop("seqlens")
+    prob = small_problem(lens, P=64, seed=300 + len(name), state_dtype="bf16", **spec)
+    with short_path(binding.SHORT_PATH_LIMIT):
+        full_check(prob)
+
+
+@pytest.mark.parametrize("route", ["default", "chunked"])
+def test_bf16_states_are_rounded_fp32_results(route):
+    """With the same (bf16-representable) initial states, the bf16-storage
+    run's final states are the fp32-storage run's, rounded to nearest even,
+    bit for bit: the arithmetic is the same, only the store differs."""
+    from mamba_ssd_chunked_chunk_amd.workloads import with_bf16_states
+    prob = small_problem([300, 40, 0, 96, 700], H=4, P=64, G=2, N=128, seed=310, init="bernoulli")
+    pb = with_bf16_states(prob)
+    pf = clone(prob)
+    pf["pool"] = bf16_to_f64(pb["pool"]).astype(np.float32)  # exactly the bf16 values
+    with short_path(binding.SHORT_PATH_LIMIT if route == "default" else 0):
+        df, _ = gpu_run(pf)
+        db, _ = gpu_run(pb)
+    assert torch.equal(bits(db["y"]), bits(df["y"]))
+    assert torch.equal(bits(db["pool"]), bits(df["pool"].to(torch.bfloat16)))
+
+
+def test_bf16_states_separate_entry():
+    prob = small_problem([300, 0, 513, 17], H=4, P=64, G=2, N=128, seed=320, init="none")
+    init = random_states(prob, 321)
+    init_b = torch.from_numpy(init).to(torch.bfloat16)
+    init_exact = init_b.float().numpy()
+    d = torch_io.upload(prob, "cuda")
+    fin = torch.full(init_b.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    with short_path(binding.SHORT_PATH_LIMIT):
+        torch_io.run_fwd(d, init_b.cuda(), fin)
+    torch.cuda.synchronize()
+    ref = oracle.recurrence_separate(prob, init_exact)
+    assert_y(y_host(d), ref["y"], "bf16 separate")
+    fh = fin.float().cpu().numpy()
+    for b in range(4):
+        assert_final(fh[b], ref["final"][b], f"seq {b}", FINAL_TOL_BF16)
+    assert torch.equal(bits(fin[1].cpu()), bits(init_b[1]))  # zero-length: the initial state
+
+
+def test_bf16_states_short_workload_sampled():
+    from mamba_ssd_chunked_chunk_amd.workloads import with_bf16_states
+    prob = with_bf16_states(make_workload("short_512_h128_g8_n128"))
+    wy, wf = full_check(prob, seqs=(200, 240))
+    print(f"short workload, bf16 states: y worst/bound {wy:.3f}  final rel {wf:.2e}", flush=True)
+
+
+# ------------------------------------------- token recurrence (decode steps)
+
+@pytest.mark.parametrize("N,state_dtype", [(64, "f32"), (128, "f32"), (128, "bf16")])
+def test_recur_path_lengths(N, state_dtype):
+    """Sequences of 1..4 tokens take the token recurrence, 5 and more the
+    MFMA short kernel: lengths on both sides of that boundary, with and
+    without initial states, against the oracle."""
+    lens = [1, 2, 3, 4, 5, 6, 9, 0, 1, 4]
+    prob = small_problem(lens, H=4, P=64, G=2, N=N, seed=400 + N, init="bernoulli", state_dtype=state_dtype)
+    with short_path(binding.SHORT_PATH_LIMIT):
+        full_check(prob)
+
+
+def test_recur_limit_follows_short_limit():
+    """With the short path limited to 2 tokens, the recurrence takes 1..2 and
+    the chunked steps the rest (the chunk count checked)."""
+    lens = [1, 2, 3, 8, 30]
+    prob = small_problem(lens, H=4, P=64, G=1, N=128, seed=410, init="all")
+    with short_path(2):
+        d, ws = gpu_run(prob)
+    ref = oracle.recurrence(prob, want_pool=False)
+    assert_y(y_host(d), ref["y"], "limit 2")
+    for b, slot in enumerate(prob["cache_indices"]):
+        assert_final(d["pool"][int(slot)].cpu().numpy(), ref["final"][b], f"seq {b}")
+    L = binding.ssd_workspace_get_layout(torch_io.problem_struct(d))
+    assert int(ws.cpu().numpy()[L["meta"]:L["meta"] + 4].view(np.int32)[0]) == 3
+
+
+@pytest.mark.parametrize("state_dtype", ["f32", "bf16"])
+def test_decode_workload_sampled(state_dtype):
+    from mamba_ssd_chunked_chunk_amd.workloads import with_bf16_states
+    prob = make_workload("decode_512_h128_g8_n128")
+    if state_dtype == "bf16":
+        prob = with_bf16_states(prob)
+    wy, wf = full_check(prob, seqs=(100, 164))
+    print(f"decode workload ({state_dtype} states): y worst/bound {wy:.3f}  final rel {wf:.2e}", flush=True)
