@@ -1,7 +1,8 @@
-// Short sequences in one pass ("short path"): every sequence of 1 ..
-// short_max tokens (at most 128; dstate 64 or 128) is scanned whole by one
+// Short sequences in one pass ("short path"): every sequence of recur_max+1
+// .. short_max tokens (at most 128; dstate 64 or 128) is scanned whole by one
 // kernel, instead of going through the chunk table, the chunk-state and
-// state-passing steps and their fp16 intermediates in the workspace.  With
+// state-passing steps and their fp16 intermediates in the workspace (the
+// shortest, 1 .. recur_max tokens, take the token-recurrence kernel).  With
 // the path on, zero-length sequences are also finished here (their final
 // state is the initial one, or zeros).
 //
