@@ -93,8 +93,9 @@ class Hip:
 # ------------------------------------------------------- algorithmic figures
 
 def is_short(L, N, short_max):
-    """Whether the library routes a sequence of L tokens to the short path."""
-    return N <= 128 and 1 <= L <= short_max
+    """Whether the library routes a sequence of L tokens to the short path
+    (with the path on, zero-length sequences are finished there too)."""
+    return N <= 128 and short_max > 0 and L <= short_max
 
 
 def algorithmic(prob, short_max=SHORT_MAX):
@@ -125,8 +126,8 @@ def algorithmic(prob, short_max=SHORT_MAX):
         return bx, bbc, bdt, (n_init + len(seqs)) * slot, f
 
     recur_max = min(short_max, RECUR_MAX)
-    recur = [b for b in range(len(lens)) if is_short(lens[b], N, short_max) and lens[b] <= recur_max]
-    short = [b for b in range(len(lens)) if is_short(lens[b], N, short_max) and lens[b] > recur_max]
+    recur = [b for b in range(len(lens)) if is_short(lens[b], N, short_max) and 1 <= lens[b] <= recur_max]
+    short = [b for b in range(len(lens)) if is_short(lens[b], N, short_max) and not 1 <= lens[b] <= recur_max]
     chunked = [b for b in range(len(lens)) if not is_short(lens[b], N, short_max)]
     bx, bbc, bdt, pool_rw, f = part(chunked)
     sx, sbc, sdt, spool, sf = part(short)

@@ -1,0 +1,82 @@
+"""Host-side logic of bench.py (no GPU): the algorithmic bytes and flops
+that the roofline divides by, the routing it mirrors, and the multi-GPU
+refusal.  The reference figures are the per-token byte count and the
+chunked method's flop formula applied by hand to the workload shapes."""
+
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+from mamba_ssd_chunked_chunk_amd.workloads import make_workload, with_bf16_states  # noqa: E402
+
+
+def _flops_by_hand(lens, H, P, G, N, L=256):
+    f = 0
+    for n in lens:
+        full, rem = divmod(n, L)
+        for l in [L] * full + ([rem] if rem else []):
+            f += 2 * l * N * P * H + 2 * l * N * P * H + l * (l + 1) * P * H + l * (l + 1) * N * G
+    return f
+
+
+def test_algorithmic_fixed_workload():
+    """16 heads x 64, one group, dstate 256, 4 x 4096 tokens, zero initial
+    states: 5184 bytes per token (x and y 2*16*64*2, B and C 2*256*2, dt
+    16*4) plus each sequence's final state written (16*64*256*4)."""
+    prob = make_workload("fixed_4x4096_h16_n256")
+    a = bench.algorithmic(prob)
+    T = 4 * 4096
+    assert a["whole"]["bytes"] == T * 5184 + 4 * 16 * 64 * 256 * 4
+    assert a["whole"]["flops"] == _flops_by_hand([4096] * 4, 16, 64, 1, 256)
+    assert abs(a["whole"]["bytes"] / 1e6 - 89.1) < 0.1   # the figure quoted for this workload
+    assert abs(a["whole"]["flops"] / 1e9 - 22.6) < 0.1
+    # per kernel: chunk_scan moves x, y, B, C, dt; state_passing the pool
+    assert a["ssd_chunk_scan"]["bytes"] == T * (2 * 16 * 64 * 2 + 2 * 256 * 2 + 16 * 4)
+    assert a["ssd_state_passing"]["bytes"] == 4 * 16 * 64 * 256 * 4
+    assert a["ssd_short"]["bytes"] == 0 and a["ssd_recur"]["bytes"] == 0
+
+
+def test_algorithmic_short_routing_and_bf16_pool():
+    """Short sequences count for the short-path kernels (1..4 tokens for the
+    recurrence, 5..128 and zero-length ones for the MFMA kernel), the others
+    for the chunked steps, and bf16 storage halves the pool bytes."""
+    import numpy as np
+    lens = [int(v) for v in np.random.default_rng(5).integers(0, 140, 512)]
+    prob = dict(seqlens=lens, nheads=128, head_dim=64, ngroups=8, dstate=128,
+                has_initial_state=np.ones(512, np.uint8), pool=np.zeros((1, 1), np.float32))
+    a = bench.algorithmic(prob)
+    slot = 128 * 64 * 128 * 4
+    n_recur = sum(1 for n in lens if 1 <= n <= 4)
+    n_short = sum(1 for n in lens if n == 0 or 5 <= n <= 128)
+    tok = lambda seqs: sum(seqs) * (2 * 128 * 64 * 2 + 2 * 8 * 128 * 2 + 128 * 4)
+    assert a["ssd_recur"]["bytes"] == tok([n for n in lens if 1 <= n <= 4]) + 2 * n_recur * slot
+    # (a zero-length sequence with an initial state reads and writes its slot)
+    assert a["ssd_short"]["bytes"] == tok([n for n in lens if 5 <= n <= 128]) + 2 * n_short * slot
+    n_long = sum(1 for n in lens if n > 128)
+    assert a["ssd_state_passing"]["bytes"] == 2 * n_long * slot
+    off = bench.algorithmic(prob, short_max=0)  # every sequence through the chunked steps
+    assert off["ssd_short"]["bytes"] == 0 and off["whole"]["bytes"] == a["whole"]["bytes"]
+    b = bench.algorithmic(with_bf16_states(prob))
+    assert a["whole"]["bytes"] - b["whole"]["bytes"] == 512 * 2 * slot // 2
+
+
+def test_dstate_256_never_short():
+    prob = make_workload("tiny_1x512_h4_n64")
+    assert bench.is_short(96, 64, 128) and not bench.is_short(96, 256, 128)
+    assert bench.is_short(0, 64, 128) and not bench.is_short(129, 64, 128)
+    assert not bench.is_short(5, 64, 0)
+    a = bench.algorithmic(prob)
+    assert a["ssd_short"]["bytes"] == 0  # its one sequence is 512 tokens
+
+
+def test_multi_gpu_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "single-GPU" in json.loads(r.stdout.strip().splitlines()[-1])["error"]

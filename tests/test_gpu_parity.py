@@ -534,3 +534,41 @@ def test_decode_workload_sampled(state_dtype):
         prob = with_bf16_states(prob)
     wy, wf = full_check(prob, seqs=(100, 164))
     print(f"decode workload ({state_dtype} states): y worst/bound {wy:.3f}  final rel {wf:.2e}", flush=True)
+
+
+# ------------------------------------------------------- HIP graph capture
+
+@pytest.mark.parametrize("N,lens", [(128, MIXED_LENS), (256, [700, 300, 0, 45])])
+def test_graph_capture_replays_match_eager(N, lens):
+    """The call enqueues kernels only (no allocation, no memset, no host
+    synchronisation), so it can be captured into a HIP graph.  Each replay
+    (after the pool is restored by eager work) must equal the eager call,
+    bit for bit, under the chunked and the short paths."""
+    prob = small_problem(lens, H=4, P=64, G=2, N=N, seed=500 + N, init="bernoulli")
+    d = torch_io.upload(prob, "cuda")
+    pool0 = d["pool"].clone()
+    ws = torch.empty(binding.ssd_workspace_size(torch_io.problem_struct(d)), dtype=torch.uint8, device="cuda")
+    with short_path(binding.SHORT_PATH_LIMIT):
+        torch_io.run(d, ws)
+        torch.cuda.synchronize()
+        y_ref, pool_ref = d["y"].clone(), d["pool"].clone()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):  # warm-up on the capture stream
+            d["pool"].copy_(pool0)
+            torch_io.run(d, ws)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        d["pool"].copy_(pool0)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            torch_io.run(d, ws)
+        for rep in range(3):
+            d["y"].zero_()
+            d["pool"].copy_(pool0)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(bits(d["y"]), bits(y_ref)), f"replay {rep}: y differs"
+            assert torch.equal(bits(d["pool"]), bits(pool_ref)), f"replay {rep}: pool differs"
