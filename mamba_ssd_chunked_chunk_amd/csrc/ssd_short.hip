@@ -70,6 +70,45 @@ struct __attribute__((aligned(16))) ShortSmem {
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+// A 32x32 state tile in the MFMA accumulator layout holds, in lane (l, h =
+// l/32), the elements n = 8a + 4h + 0..3 (a = 0..3) of row l%32.  With bf16
+// storage each lane instead loads or stores 16 bytes, n = 16h + 8c + 0..7
+// (c = 0, 1): dword d of group c is (n = 16h + 8c + 2d, +1).  Lane h = 0
+// keeps its own n 0..3 and 8..11 and takes n 16..19 and 24..27 from lane
+// l+32; lane h = 1 the mirror image: one v_permlane32_swap per dword pair.
+__device__ __forceinline__ void to_acc_layout(const u32x4 &q0, const u32x4 &q1, f32x4 (&hn)[4]) {
+    uint32_t w[4][2];  // [a][pair of e]
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+        const auto s0 = __builtin_amdgcn_permlane32_swap(q0[d], q0[d + 2], false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(q1[d], q1[d + 2], false, false);
+        w[0][d] = s0[0];
+        w[2][d] = s0[1];
+        w[1][d] = s1[0];
+        w[3][d] = s1[1];
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+        hn[a] = f32x4{bf16x2_lo(w[a][0]), bf16x2_hi(w[a][0]), bf16x2_lo(w[a][1]), bf16x2_hi(w[a][1])};
+}
+__device__ __forceinline__ void from_acc_layout(const f32x4 (&o)[4], u32x4 &q0, u32x4 &q1) {
+    uint32_t w[4][2];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        w[a][0] = pack_bf16x2(o[a][0], o[a][1]);
+        w[a][1] = pack_bf16x2(o[a][2], o[a][3]);
+    }
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+        const auto s0 = __builtin_amdgcn_permlane32_swap(w[0][d], w[2][d], false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(w[1][d], w[3][d], false, false);
+        q0[d] = s0[0];
+        q0[d + 2] = s0[1];
+        q1[d] = s1[0];
+        q1[d + 2] = s1[1];
+    }
+}
+
 // running maximum of bf16 magnitudes (as bit patterns) over a dword's two halves
 __device__ __forceinline__ uint32_t bf16_absmax2(uint32_t m, uint32_t w) {
     return max(m, max(w & 0x7FFFu, (w >> 16) & 0x7FFFu));
@@ -271,9 +310,18 @@ __global__ __launch_bounds__(kSThreads) void ssd_short_kernel(Params p) {
             if (p.dt_bias != nullptr) bnx = p.dt_bias[h];
         }
         if (owner && init) {  // both uniform over the wavefront
-            const int64_t idx = ((slot * p.H + h) * kHeadDim + 32 * pts + l32) * N + 32 * nt + 4 * hl;
+            const int64_t row = ((slot * p.H + h) * kHeadDim + 32 * pts + l32) * N + 32 * nt;
+            if constexpr (SB) {
+                // bf16: 16 bytes per lane (n = 32 nt + 16 hl + 8c .. +7), then
+                // lanes l and l+32 trade halves into the accumulator layout
+                const uint16_t *src = static_cast<const uint16_t *>(state_src) + row + 16 * hl;
+                const u32x4 q0 = *reinterpret_cast<const u32x4 *>(src);
+                const u32x4 q1 = *reinterpret_cast<const u32x4 *>(src + 8);
+                to_acc_layout(q0, q1, hn);
+            } else {
 #pragma unroll
-            for (int a = 0; a < 4; ++a) hn[a] = load_state4<SB>(state_src, idx + 8 * a);
+                for (int a = 0; a < 4; ++a) hn[a] = load_state4<SB>(state_src, row + 4 * hl + 8 * a);
+            }
         }
     };
     // maxima and decay table of the loaded head h into buffer nb
@@ -528,13 +576,21 @@ __global__ __launch_bounds__(kSThreads) void ssd_short_kernel(Params p) {
         if (owner) {
             const float dec = fast_exp2(cs_last);
             const float us = ldexpf(1.0f, kw - sb - xe);
-            const int64_t idx = ((slot * p.H + h) * kHeadDim + 32 * pts + l32) * N + 32 * nt + 4 * hl;
+            const int64_t row = ((slot * p.H + h) * kHeadDim + 32 * pts + l32) * N + 32 * nt;
+            f32x4 o[4];
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                f32x4 o;
+            for (int a = 0; a < 4; ++a)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = dec * hc[a][e] + sacc[4 * a + e] * us;
-                store_state4<SB>(p.state_out, idx + 8 * a, o);
+                for (int e = 0; e < 4; ++e) o[a][e] = dec * hc[a][e] + sacc[4 * a + e] * us;
+            if constexpr (SB) {  // the load's trade in reverse: 16 bytes per lane
+                u32x4 q0, q1;
+                from_acc_layout(o, q0, q1);
+                uint16_t *dst = static_cast<uint16_t *>(p.state_out) + row + 16 * hl;
+                *reinterpret_cast<u32x4 *>(dst) = q0;
+                *reinterpret_cast<u32x4 *>(dst + 8) = q1;
+            } else {
+#pragma unroll
+                for (int a = 0; a < 4; ++a) store_state4<SB>(p.state_out, row + 4 * hl + 8 * a, o[a]);
             }
         }
         // y back to unit scale, bf16; lanes l and l+32 trade groups so each
