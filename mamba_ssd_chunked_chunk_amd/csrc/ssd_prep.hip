@@ -8,7 +8,12 @@
 // query_start_loc boundary: "mamba2_ssd_scan", section "Per-token
 // recurrence").  Every workgroup computes the prefix itself, so no separate
 // launch is needed; workgroup (0, 0) also publishes it (chunk_off, nchunks)
-// for the state-passing step.
+// for the state-passing step.  Sequences the short path takes (short_max > 0:
+// 0 .. short_max tokens) own no chunks; workgroup (0, 0) then also writes
+// the list of the sequences the state chain walks (the others) and the list
+// of those of 1 .. recur_max tokens for the token-recurrence kernel, with
+// their counts (meta[1], meta[2]).  The grid is sized to the host's bound on
+// the chunks that can reach it.
 //
 // Cumulative decay (blockIdx.y == 0): for each head h and token j of the chunk,
 //   dts_j = softplus(dt[t,h] + dt_bias[h])   (or dt + dt_bias without softplus)

@@ -20,20 +20,25 @@
 //
 // Work split: one workgroup of eight wavefronts per (sequence, group, slice
 // of the group's heads), walking its heads.  Wavefront w owns
-//   - y rows 32*(w/2) .. +31 (row block rb; blocks past the end skip their
-//     products), p columns 32*(w%2) .. +31, with its row block's C.B^T tiles
-//     (bf16 MFMA on the exact inputs, kept as fp16 under a power of two in
-//     registers for all heads);
+//   - y rows 32 rb .. +31 with rb = 0, 0, 1, 1, 3, 3, 2, 2 for w = 0..7 (the
+//     two wavefronts on a SIMD, w and w+4, hold 5 causal tiles between them;
+//     blocks past the end skip their products), p columns 32 (w%2) .. +31,
+//     with its row block's C.B^T tiles (bf16 MFMA on the exact inputs, kept as
+//     fp16 under a power of two in registers for all heads);
 //   - the 32x32 tile (p tile w%2, n tile w/2) of the final state, when
 //     w/2 < dstate/32, whose h0 elements it holds in registers.
-// B^T and C are staged once in LDS as fp16.  Per head, two barriers: before the
-// first, x^T (fp16 under one power of two) and h0 (fp16 under a power of two
-// per row p) are staged from registers loaded during the previous head, and
-// the next head's x, dt and h0 loads are issued; between them come the
-// products (final = exp2(cs2_last) h0 + B^T (w x) for the state tile, h0 C^T
-// and the causal tiles for y) and, once the next head's loads have landed,
-// its maxima and decay table (cs2, dts, w = exp2(cs2_last - cs2_j) dts_j)
-// go to the other half of a double buffer.
+// B^T and C are staged once in LDS as fp16.  Per head, two barriers: before
+// the first, x^T and (w x)^T (fp16 under one power of two) and h0 (fp16
+// under a power of two per row p) are staged from registers loaded during the
+// previous head, and the next head's x, dt, h0 and scalars are loaded
+// (unconditionally: after the last head it loads itself again, so no wait
+// depends on a branch).  Between the barriers: the state tile's S = B^T (w x),
+// the off-diagonal part h0 C^T, the causal tiles (below the diagonal as a
+// column-factor table times one row factor; the diagonal tile with its decay
+// per element); then, once the next head's loads have landed, its maxima and
+// decay tables go to the other half of a double buffer, and only then are
+// this head's y and final state (exp2(cs2_last) h0 + S, straight into the
+// slot) stored: a vector-memory wait also waits for the stores before it.
 #include <type_traits>
 
 #include "ssd_common.hpp"
@@ -65,11 +70,9 @@ struct __attribute__((aligned(16))) ShortSmem {
     float xmx[2][kSWaves];          // max |x| of each wavefront's share
     float hdr[2][4];                // {cs2_last, kw, max dts, unused}
     float hs[kHeadDim];             // 2^-hx[p]
-    float red[kSWaves];
+    float red[kSWaves];             // max |B| of each wavefront's share (prologue)
 };
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 // A 32x32 state tile in the MFMA accumulator layout holds, in lane (l, h =
 // l/32), the elements n = 8a + 4h + 0..3 (a = 0..3) of row l%32.  With bf16
 // storage each lane instead loads or stores 16 bytes, n = 16h + 8c + 0..7
@@ -255,7 +258,7 @@ __global__ __launch_bounds__(kSThreads) void ssd_short_kernel(Params p) {
             for (int k = 0; k < KN; ++k) {
                 u32x4 o;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) o[q] = pack_f16x2(bf16_lo(cq[k][q]) * cs, bf16_hi(cq[k][q]) * cs);
+                for (int q = 0; q < 4; ++q) o[q] = pack_f16x2(bf16x2_lo(cq[k][q]) * cs, bf16x2_hi(cq[k][q]) * cs);
                 *reinterpret_cast<u32x4 *>(sm.ct + i_l * HS + 8 * k + 4 * hl) = o;
             }
         }
@@ -274,8 +277,8 @@ __global__ __launch_bounds__(kSThreads) void ssd_short_kernel(Params p) {
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 const uint32_t a = braw[q][0][k >> 1], c = braw[q][1][k >> 1];
-                const float lo = (k & 1) ? bf16_hi(a) : bf16_lo(a);
-                const float hi = (k & 1) ? bf16_hi(c) : bf16_lo(c);
+                const float lo = (k & 1) ? bf16x2_hi(a) : bf16x2_lo(a);
+                const float hi = (k & 1) ? bf16x2_hi(c) : bf16x2_lo(c);
                 sm.bt[(n0 + k) * BS + lane] = pack_f16x2(lo * bs, hi * bs);
             }
         }
@@ -404,8 +407,8 @@ __global__ __launch_bounds__(kSThreads) void ssd_short_kernel(Params p) {
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 const uint32_t a = xr[0][k >> 1], c = xr[1][k >> 1];
-                const float lo = ((k & 1) ? bf16_hi(a) : bf16_lo(a)) * s0;
-                const float hi = ((k & 1) ? bf16_hi(c) : bf16_lo(c)) * s0;
+                const float lo = ((k & 1) ? bf16x2_hi(a) : bf16x2_lo(a)) * s0;
+                const float hi = ((k & 1) ? bf16x2_hi(c) : bf16x2_lo(c)) * s0;
                 sm.xt[(8 * xg8 + k) * XS + xm8] = pack_f16x2(lo, hi);
                 sm.wxt[(8 * xg8 + k) * XS + xm8] = pack_f16x2(lo * w2.x, hi * w2.y);
             }
