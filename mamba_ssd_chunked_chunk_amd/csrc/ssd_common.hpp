@@ -318,8 +318,8 @@ inline hipError_t launch_kernel(K kernel, dim3 grid, dim3 block, const Launch &l
     return hipGetLastError();
 }
 
-// Slices a group's heads are split into by the short-path kernels, whose
-// grid is (sequence, group, slice): more while the grid is small for the GPU
+// Slices a group's heads are split into by the short-sequence kernel, whose
+// workgroups are (sequence, group, slice): more while the grid is small for the GPU
 // (not every sequence of the batch need be short; workgroups of the others
 // leave at once).
 inline int short_head_slices(const Params &p) {

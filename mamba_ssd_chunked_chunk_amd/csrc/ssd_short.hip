@@ -19,7 +19,9 @@
 // goes straight to its slot (the pool in place, or final_states).
 //
 // Work split: one workgroup of eight wavefronts per (sequence, group, slice
-// of the group's heads), walking its heads.  Wavefront w owns
+// of the group's heads), walking its heads; workgroup ids run over the
+// sequences slowest, so a sequence's workgroups spread over the XCDs.
+// Wavefront w owns
 //   - y rows 32 rb .. +31 with rb = 0, 0, 1, 1, 3, 3, 2, 2 for w = 0..7 (the
 //     two wavefronts on a SIMD, w and w+4, hold 5 causal tiles between them;
 //     blocks past the end skip their products), p columns 32 (w%2) .. +31,
@@ -127,17 +129,26 @@ __global__ __launch_bounds__(kSThreads) void ssd_short_kernel(Params p) {
     constexpr int HS = ShortSmem<N>::HS;
     __shared__ ShortSmem<N> sm;
 
-    const int b = blockIdx.x;
-    const int g = blockIdx.y;
+    if (p.N != N) return;
+    // workgroup id -> (sequence, group, slice of the group's heads), the
+    // sequence slowest: ids are dealt to the eight XCDs round-robin, so the
+    // workgroups of one sequence spread over several XCDs (with the sequence
+    // fastest, all of them would share one, and a batch's few short sequences
+    // could crowd a single XCD)
+    const int per_seq = (int)(gridDim.x / (unsigned)p.batch);  // groups * slices
+    const int hz = per_seq / p.G;
+    const int b = (int)(blockIdx.x / (unsigned)per_seq);
+    const int rem = (int)blockIdx.x - b * per_seq;
+    const int g = rem / hz;
     const int64_t t0 = p.qsl[b];
     const int len = p.qsl[b + 1] - (int)t0;
-    if (p.N != N || !is_short_sequence(len, p.short_max)) return;  // the chunked path takes it
+    if (!is_short_sequence(len, p.short_max)) return;  // the chunked path takes it
     if (len >= 1 && len <= p.recur_max) return;                      // the token-recurrence kernel takes it
     const int64_t slot = p.cache_idx != nullptr ? (int64_t)p.cache_idx[b] : (int64_t)b;
     const bool init = p.init_all != 0 || (p.has_init != nullptr && p.has_init[b] != 0);
     const int hg = p.H / p.G;
-    const int hpw = hg / (int)gridDim.z;
-    const int h_begin = g * hg + (int)blockIdx.z * hpw;
+    const int hpw = hg / hz;
+    const int h_begin = g * hg + (rem - g * hz) * hpw;
     const int h_end = h_begin + hpw;
     const void *state_src = p.state_in != nullptr ? p.state_in : p.state_out;
     if (len == 0) {  // no tokens: the final state is the initial one (or zeros)
@@ -616,7 +627,7 @@ __global__ __launch_bounds__(kSThreads) void ssd_short_kernel(Params p) {
 }
 
 hipError_t launch_short(const Params &p, const Launch &l) {
-    const dim3 grid((unsigned)p.batch, (unsigned)p.G, (unsigned)short_head_slices(p));
+    const dim3 grid((unsigned)((int64_t)p.batch * p.G * short_head_slices(p)));
     const dim3 block(kSThreads);
     switch (p.N) {
     case 64:

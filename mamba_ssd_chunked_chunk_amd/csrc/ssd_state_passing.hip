@@ -31,6 +31,8 @@
 // kDepth chunks ahead of their use, so that many loads per thread are in
 // flight while the chain advances.  A row p spans N/8 lanes; its maximum is
 // taken with DPP within rows of 16 lanes and a v_permlane16_swap across them.
+#include <algorithm>
+
 #include "ssd_common.hpp"
 
 namespace ssd {
@@ -54,20 +56,11 @@ __device__ __forceinline__ float row_max(float m) {
 }
 }  // namespace
 
-// LIST: the grid's x walks the sequence list prep wrote (the short path is
-// on: only sequences longer than its limit are there), else the batch.
-// SB: states stored as bf16 (read widened to fp32, final state rounded once).
-template <int N, bool LIST, bool SB>
-__global__ __launch_bounds__(256) void ssd_state_passing_kernel(Params p) {
-    int b = blockIdx.x;
-    if constexpr (LIST) {
-        if (b >= p.meta[1]) return;
-        b = p.seq_list[b];
-    }
-    const int h = blockIdx.y;
-    constexpr int64_t head_elems = (int64_t)kHeadDim * N;  // a multiple of 256 * kPer
-    const int64_t e0 = ((int64_t)blockIdx.z * 256 + threadIdx.x) * kPer;
-    if (e0 >= head_elems) return;  // whole workgroups only
+// the chain of one item: sequence b, head h, this thread's kPer state
+// elements from e0 of the head
+template <int N, bool SB>
+__device__ __forceinline__ void walk_chain(const Params &p, int b, int h, int e0) {
+    constexpr int64_t head_elems = (int64_t)kHeadDim * N;
 
     // clamped to the table so malformed query_start_loc cannot index past it
     const int k1 = (int)min((int64_t)p.chunk_off[b + 1], p.nchunks_max);
@@ -156,11 +149,40 @@ __global__ __launch_bounds__(256) void ssd_state_passing_kernel(Params p) {
     store_state8<SB>(p.state_out, off, st);
 }
 
+// An item is (sequence, slice of 256 * kPer state elements, head), the
+// sequence slowest and the head fastest; each workgroup walks every
+// gridDim.x-th item.  Workgroup ids are dealt to the eight XCDs round-robin,
+// so the heads of one sequence land on different XCDs and every XCD gets a
+// share of every sequence.  With the sequence as the fast index a sequence's
+// whole chain runs on one XCD, and ragged lengths leave most XCDs idle while
+// a few walk the long chains (the ragged 32-sequence workload: 421 us, 145 us
+// in this order).
+// LIST: the sequences are those of the list prep wrote (the short path is on:
+// only sequences longer than its limit are there), else the batch.
+// SB: states stored as bf16 (read widened to fp32, final state rounded once).
+template <int N, bool LIST, bool SB>
+__global__ __launch_bounds__(256) void ssd_state_passing_kernel(Params p) {
+    constexpr int ZB = kHeadDim * N / (256 * kPer);  // slices per head
+    const int64_t per_seq = (int64_t)p.H * ZB;
+    const int64_t items = (LIST ? (int64_t)p.meta[1] : (int64_t)p.batch) * per_seq;
+#pragma unroll 1
+    for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
+        const int64_t bi = item / per_seq;
+        const int rem = (int)(item - bi * per_seq);
+        const int z = rem / p.H;
+        const int h = rem - z * p.H;
+        const int b = LIST ? p.seq_list[bi] : (int)bi;
+        walk_chain<N, SB>(p, b, h, (z * 256 + (int)threadIdx.x) * kPer);
+    }
+}
+
 hipError_t launch_state_passing(const Params &p, const Launch &l) {
-    const int64_t head_elems = (int64_t)kHeadDim * p.N;
-    const unsigned zb = (unsigned)((head_elems / kPer + 255) / 256);
+    // items: (sequence, slice, head); the sequences are at most nseq_grid
+    // (the list) or batch.  Up to 32 workgroups per compute unit; past that,
+    // workgroups take several items.
+    const int64_t items = (int64_t)(p.short_max > 0 ? p.nseq_grid : p.batch) * p.H * (kHeadDim * p.N / (256 * kPer));
     const bool list = p.short_max > 0;
-    dim3 grid((unsigned)(list ? p.nseq_grid : p.batch), (unsigned)p.H, zb);
+    const dim3 grid((unsigned)std::max<int64_t>(1, std::min<int64_t>(items, (int64_t)p.num_cus * 32)));
     const dim3 block(256);
     if (p.state_bf16) {
         switch (p.N) {
