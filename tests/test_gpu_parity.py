@@ -85,24 +85,26 @@ def bits(t):
 
 
 def full_check(prob, seqs=None):
-    """Run on GPU, compare with the oracle (optionally only sequences
-    seqs=(lo, hi)), check slot bookkeeping.  Returns (y worst ratio, final worst)."""
+    """Run on GPU, compare with the oracle (optionally only the sequences of
+    seqs: a range (lo, hi) or a list of ranges), check slot bookkeeping.
+    Returns (y worst ratio, final worst)."""
     tol = FINAL_TOL_BF16 if prob.get("state_dtype", "f32") == "bf16" else FINAL_TOL
     d = torch_io.upload(prob, "cuda")
     before = d["pool"].clone()
     torch_io.run(d)
     torch.cuda.synchronize()
-    ref = oracle.recurrence(prob, seqs=seqs, want_pool=False)
     qsl = prob["query_start_loc"]
-    lo, hi = (0, len(qsl) - 1) if seqs is None else seqs
-    s, e = int(qsl[lo]), int(qsl[hi])
-    yg = d["y"][s:e].float().cpu().numpy().astype(np.float64)
-    wy = assert_y(yg, ref["y"][s:e], prob.get("name", ""))
     ci = prob["cache_indices"]
-    wf = 0.0
-    for b in range(lo, hi):
-        slot = int(ci[b])
-        wf = max(wf, assert_final(d["pool"][slot].float().cpu().numpy(), ref["final"][b], f"seq {b}", tol))
+    wy = wf = 0.0
+    for rng in ([None] if seqs is None else seqs if isinstance(seqs, list) else [seqs]):
+        ref = oracle.recurrence(prob, seqs=rng, want_pool=False)
+        lo, hi = (0, len(qsl) - 1) if rng is None else rng
+        s, e = int(qsl[lo]), int(qsl[hi])
+        yg = d["y"][s:e].float().cpu().numpy().astype(np.float64)
+        wy = max(wy, assert_y(yg, ref["y"][s:e], prob.get("name", "")))
+        for b in range(lo, hi):
+            slot = int(ci[b])
+            wf = max(wf, assert_final(d["pool"][slot].float().cpu().numpy(), ref["final"][b], f"seq {b}", tol))
     # slots outside cache_indices: bit-identical (compared on the device)
     written = torch.zeros(prob["pool"].shape[0], dtype=torch.bool, device="cuda")
     written[torch.from_numpy(ci.astype(np.int64)).cuda()] = True
@@ -429,7 +431,10 @@ def test_separate_states_aliased_buffer():
 @pytest.mark.parametrize("name,seqs", [
     ("fixed_4x4096_h16_n256", (1, 2)),
     ("long_8x16384_h16_n256", (2, 4)),
-    ("ragged_32_h128_g8_n128", (0, 6)),
+    # 24..29: walked by the state chain's workgroups as their second item (the
+    # ragged workload has more chain items than the grid has workgroups), and
+    # one short sequence
+    ("ragged_32_h128_g8_n128", [(0, 6), (24, 30)]),
     ("short_512_h128_g8_n128", (100, 164)),
 ])
 def test_workloads_full_size_sampled(name, seqs):
