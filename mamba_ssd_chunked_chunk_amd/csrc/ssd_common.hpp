@@ -319,13 +319,15 @@ inline hipError_t launch_kernel(K kernel, dim3 grid, dim3 block, const Launch &l
 }
 
 // Slices a group's heads are split into by the short-sequence kernel, whose
-// workgroups are (sequence, group, slice): more while the grid is small for the GPU
-// (not every sequence of the batch need be short; workgroups of the others
-// leave at once).
+// workgroups are (sequence, group, slice): more while the grid is under four
+// workgroups per compute unit (not every sequence of the batch need be
+// short; workgroups of the others leave at once).  Each slice repeats the
+// sequence's prologue, so a larger target costs more than it gains (the
+// ragged 32-sequence workload: 2 per CU 56 us, 4: 39 us, 8: 51 us, 16: 74 us).
 inline int short_head_slices(const Params &p) {
     const int hg = p.H / p.G;
     int hz = 1;
-    while ((int64_t)p.batch * p.G * hz < 2 * (int64_t)p.num_cus && hg % (2 * hz) == 0) hz *= 2;
+    while ((int64_t)p.batch * p.G * hz < 4 * (int64_t)p.num_cus && hg % (2 * hz) == 0) hz *= 2;
     return hz;
 }
 
