@@ -252,19 +252,42 @@ __global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(Params p) {
         const int half = tid >> 8;
         const int wq = wave & 3;  // wavefront within the half
         const bool valid = j < len;
+        constexpr int K = kHeadBlock / 2;
+        // this thread's raw inputs of a head block (dt of its token, dt_bias and
+        // A of its 8 heads), loaded one head block ahead so the loop waits for
+        // memory once; the loads are unconditional (rows past the chunk end read
+        // its last row, heads past H the last head, the last block itself again
+        // past the end), their values discarded below where they do not apply
+        const float *dt_row = p.dt + (t0 + min(j, len - 1)) * p.H;
+        const float *bias = p.dt_bias ? p.dt_bias : p.A;  // a valid address either way
+        const int last_hb = (p.H - 1) / kHeadBlock * kHeadBlock;
+        float r_dt[K], r_bias[K], r_a[K];
+        auto load_block = [&](int hb) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const int h = min(hb + half * K + k, p.H - 1);
+                r_dt[k] = dt_row[h];
+                r_bias[k] = bias[h];
+                r_a[k] = p.A[h];
+            }
+        };
+        load_block(0);
         for (int hb = 0; hb < p.H; hb += kHeadBlock) {
-            constexpr int K = kHeadBlock / 2;
+            float v_dt[K], v_bias[K], v_a[K];
+#pragma unroll
+            for (int k = 0; k < K; ++k) { v_dt[k] = r_dt[k]; v_bias[k] = r_bias[k]; v_a[k] = r_a[k]; }
+            load_block(min(hb + kHeadBlock, last_hb));
             float d[K], a[K];
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 const int h = hb + half * K + k;
                 float ds = 0.0f;
                 if (valid && h < p.H) {
-                    const float v = p.dt[(t0 + j) * p.H + h] + (p.dt_bias ? p.dt_bias[h] : 0.0f);
+                    const float v = v_dt[k] + (p.dt_bias ? v_bias[k] : 0.0f);
                     ds = p.dt_softplus ? softplus_f(v) : v;
                 }
                 d[k] = ds;
-                a[k] = h < p.H ? p.A[h] * ds : 0.0f;
+                a[k] = h < p.H ? v_a[k] * ds : 0.0f;
             }
             // inclusive scan over the tokens, per head
 #pragma unroll
