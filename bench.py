@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--summarize-profile", metavar="DIR",
                     help="no GPU run: summarise the rocprofv3 output under DIR (kt/, fetch/, write/) "
                          "for --workload, print it as markdown and write profiles/traffic.json")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="no GPU run: print the shader-counter table of the two rocprofv3 --pmc passes "
+                         "under DIR (p1/, p2/: the counters of COUNTER_PASSES)")
     return ap.parse_args()
 
 
@@ -224,6 +227,52 @@ def _per_dispatch(csv_path):
     return out
 
 
+def _per_dispatch_counters(csv_path):
+    """{dispatch id: (kernel name, {counter: value summed over instances})}."""
+    import csv
+    out = {}
+    for r in csv.DictReader(open(csv_path)):
+        d = int(r["Dispatch_Id"])
+        name, vals = out.setdefault(d, (r["Kernel_Name"], {}))
+        vals[r["Counter_Name"]] = vals.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return out
+
+
+COUNTER_PASSES = {
+    "p1": "SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_INST_ANY SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS "
+          "SQ_LDS_BANK_CONFLICT",
+    "p2": "SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_WAIT_ANY SQ_INSTS_VMEM_RD "
+          "SQ_INSTS_VMEM_WR SQ_INSTS_SALU GRBM_GUI_ACTIVE",
+}
+
+
+def summarize_counters(root):
+    """Markdown table of the libssd kernels' shader counters from the two
+    rocprofv3 --pmc passes under root/p1 and root/p2 (COUNTER_PASSES), the
+    median over each kernel's dispatches."""
+    vals = {}
+    for pas in COUNTER_PASSES:
+        for name, cs in _per_dispatch_counters(os.path.join(root, pas, "run_counter_collection.csv")).values():
+            k = _short(name)
+            if k.startswith("ssd_"):
+                for c, v in cs.items():
+                    vals.setdefault(k, {}).setdefault(c, []).append(v)
+    lines = ["| kernel | waves | VALU / wave | MFMA / wave | LDS / wave | VMEM rd / wave | VMEM wr / wave "
+             "| SALU / wave | SQ_WAIT_ANY / SQ_WAVE_CYCLES | SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS "
+             "| SQ_VALU_MFMA_BUSY_CYCLES / SQ_INSTS_MFMA |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for k in sorted(vals, key=lambda k: -statistics.median(vals[k]["SQ_WAVE_CYCLES"])):
+        m = {c: statistics.median(v) for c, v in vals[k].items()}
+        w = m["SQ_WAVES"]
+        per = lambda c: f"{m[c] / w:.0f}"
+        ratio = lambda a, b: "" if m[b] == 0 else f"{m[a] / m[b]:.2f}"
+        lines.append(f"| {k} | {w:.0f} | {per('SQ_INSTS_VALU')} | {per('SQ_INSTS_MFMA')} | {per('SQ_INSTS_LDS')} "
+                     f"| {per('SQ_INSTS_VMEM_RD')} | {per('SQ_INSTS_VMEM_WR')} | {per('SQ_INSTS_SALU')} "
+                     f"| {ratio('SQ_WAIT_ANY', 'SQ_WAVE_CYCLES')} | {ratio('SQ_LDS_BANK_CONFLICT', 'SQ_INSTS_LDS')} "
+                     f"| {ratio('SQ_VALU_MFMA_BUSY_CYCLES', 'SQ_INSTS_MFMA')} |")
+    print("\n".join(lines))
+
+
 def _short(name):
     k = name.split("(")[0].replace("void ", "").split("<")[0].split("::")[-1]
     return k[:-len("_kernel")] if k.startswith("ssd_") and k.endswith("_kernel") else k
@@ -328,6 +377,9 @@ def main():
     args = parse()
     if args.summarize_profile:
         summarize_profile(args.summarize_profile, args.workload, args.short_max)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "libssd is a single-GPU library; this benchmark runs on exactly one "

@@ -80,3 +80,34 @@ def test_multi_gpu_refused():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "single-GPU" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
+
+
+def test_counter_summary_ratios(tmp_path):
+    """bench.py --summarize-counters: per-wavefront counts and the three
+    ratios from two synthetic counter passes (two dispatches of one kernel,
+    counters split over two instances; the median over dispatches)."""
+    import csv
+    vals = {"SQ_WAVES": 8, "SQ_WAVE_CYCLES": 1000, "SQ_BUSY_CYCLES": 1, "SQ_WAIT_INST_ANY": 1,
+            "SQ_INSTS_VALU": 800, "SQ_INSTS_MFMA": 40, "SQ_INSTS_LDS": 80, "SQ_LDS_BANK_CONFLICT": 20,
+            "SQ_VALU_MFMA_BUSY_CYCLES": 1280, "SQ_ACTIVE_INST_VALU": 1, "SQ_ACTIVE_INST_LDS": 1,
+            "SQ_WAIT_ANY": 250, "SQ_INSTS_VMEM_RD": 16, "SQ_INSTS_VMEM_WR": 8, "SQ_INSTS_SALU": 24,
+            "GRBM_GUI_ACTIVE": 1}
+    for pas, names in bench.COUNTER_PASSES.items():
+        d = tmp_path / pas
+        d.mkdir()
+        with open(d / "run_counter_collection.csv", "w", newline="") as fh:
+            w = csv.DictWriter(fh, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+            w.writeheader()
+            for disp, scale in ((1, 1), (2, 3)):
+                for c in names.split():
+                    for inst in range(2):  # two instances of half the value each
+                        w.writerow(dict(Dispatch_Id=disp, Kernel_Name="void ssd::ssd_chunk_scan_kernel<256, 4>(ssd::Params)",
+                                        Counter_Name=c, Counter_Value=vals[c] * scale / 2))
+    import contextlib, io
+    out = io.StringIO()
+    with contextlib.redirect_stdout(out):
+        bench.summarize_counters(str(tmp_path))
+    row = [r for r in out.getvalue().splitlines() if r.startswith("| ssd_chunk_scan")][0]
+    cells = [c.strip() for c in row.strip("|").split("|")]
+    # median of dispatches (scale 1 and 3) = scale 2: 16 waves; per-wave counts unchanged
+    assert cells == ["ssd_chunk_scan", "16", "100", "5", "10", "2", "1", "3", "0.25", "0.25", "32.00"]
