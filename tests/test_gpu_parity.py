@@ -444,6 +444,16 @@ def test_workloads_full_size_sampled(name, seqs):
     print(f"{name}: y worst/bound {wy:.3f}  final rel {wf:.2e}", flush=True)
 
 
+def test_ragged_chunked_route_second_items():
+    """With the short path off, the state chain walks the whole batch (not a
+    list): on the ragged workload it has more items than workgroups, and
+    sequences 24..29 are second items of theirs."""
+    prob = make_workload("ragged_32_h128_g8_n128")
+    with short_path(0):
+        wy, wf = full_check(prob, seqs=(24, 30))
+    print(f"ragged, every sequence chunked: y worst/bound {wy:.3f}  final rel {wf:.2e}", flush=True)
+
+
 # ------------------------------------------------- bf16 state storage
 
 @pytest.mark.parametrize("name", ["n256_chunked", "n128_mixed_short", "n64_edges"])
