@@ -295,14 +295,14 @@ __global__ __launch_bounds__(StateShape<N>::THREADS) void ssd_chunk_state_kernel
     }
 }
 
-// Heads per workgroup: the largest of 8, 4, 2, 1 that divides the heads of a
-// group and still gives at least one workgroup per compute unit (a workgroup
+// Heads per workgroup: the largest of 16, 8, 4, 2, 1 that divides the heads of
+// a group and still gives at least one workgroup per compute unit (a workgroup
 // fills a compute unit; more heads per workgroup amortise its shared
 // operands).
 static int state_heads_per_block(const Params &p) {
     const int hg = p.H / p.G;
     const int64_t chunks = (p.nchunks_grid + 7) / 8 * 8;
-    for (int hb = 8; hb > 1; hb /= 2)
+    for (int hb = 16; hb > 1; hb /= 2)
         if (hg % hb == 0 && chunks * (p.H / hb) >= (int64_t)p.num_cus) return hb;
     return 1;
 }
@@ -317,6 +317,7 @@ static hipError_t launch_nh(const Params &p, const Launch &l) {
 template <int N>
 static hipError_t launch_n(const Params &p, const Launch &l) {
     switch (state_heads_per_block(p)) {
+    case 16: return launch_nh<N, 16>(p, l);
     case 8: return launch_nh<N, 8>(p, l);
     case 4: return launch_nh<N, 4>(p, l);
     case 2: return launch_nh<N, 2>(p, l);
