@@ -46,13 +46,17 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="skip the per-workload lines (every workload of PER_CONFIG, timed after the headline)")
+    ap.add_argument("--config-steps", type=int, default=10,
+                    help="timed calls per workload of the per-workload lines")
     ap.add_argument("--entry", choices=("inplace", "separate"), default="inplace",
                     help="entry point to time: the in-place pool operation (default) or the one with "
                          "separate initial_states / final_states (sequences without an initial state "
                          "start from zero rows; none at all passes NULL)")
     ap.add_argument("--short-max", type=int, default=SHORT_MAX,
-                    help="longest sequence routed to the fused short-sequence kernel (dstate <= 128; "
-                         "0 sends every sequence through the chunked steps)")
+                    help="ssd_problem.short_path_max of every call: longest sequence routed to the fused "
+                         "short-sequence kernel (dstate <= 128; 0 sends every sequence through the chunked steps)")
     ap.add_argument("--state-dtype", choices=("f32", "bf16"), default="f32",
                     help="storage type of the pool / states (bf16: rounded once per final state; the "
                          "arithmetic stays fp32)")
@@ -136,13 +140,16 @@ def algorithmic(prob, short_max=SHORT_MAX):
     sx, sbc, sdt, spool, sf = part(short)
     rx, rbc, rdt, rpool, _ = part(recur)  # VALU recurrence: no MFMA flops
     fl = sum(f.values()) + sum(sf.values())
+    # per kernel: the caller's buffers that kernel itself reads or writes (a
+    # buffer that two kernels read counts for both, so the shares can sum to
+    # more than the call; the whole call counts every buffer once)
     return dict(
         whole=dict(bytes=2 * (bx + sx + rx) + 2 * (bbc + sbc + rbc) + bdt + sdt + rdt + pool_rw + spool + rpool,
                    flops=fl),
-        ssd_chunk_scan=dict(bytes=2 * bx + 2 * bbc + bdt, flops=f["off"] + f["diag"] + f["cb"]),
-        ssd_chunk_state=dict(bytes=bx + bbc + bdt, flops=f["state"]),
+        ssd_prep=dict(bytes=bdt + 2 * bbc, flops=f["cb"]),
+        ssd_chunk_state=dict(bytes=bx + bbc, flops=f["state"]),
         ssd_state_passing=dict(bytes=pool_rw, flops=0),
-        ssd_prep=dict(bytes=bdt + bbc, flops=0),
+        ssd_chunk_scan=dict(bytes=2 * bx + bbc, flops=f["off"] + f["diag"]),
         ssd_short=dict(bytes=2 * sx + 2 * sbc + sdt + spool, flops=sum(sf.values())),
         ssd_recur=dict(bytes=2 * rx + 2 * rbc + rdt + rpool, flops=0),
     )
@@ -352,6 +359,17 @@ def summarize_profile(root, workload, short_max=SHORT_MAX):
 
 # ------------------------------------------------------------------ CPU leg
 
+def cpu_model():
+    """The host CPU's model name (first entry of /proc/cpuinfo), or None."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(prob, min_seconds, entry="inplace"):
     import oracle
     T = prob["total_len"]
@@ -366,15 +384,133 @@ def cpu_baseline(prob, min_seconds, entry="inplace"):
         if time.perf_counter() - t0 >= min_seconds:
             break
     el = time.perf_counter() - t0
-    return dict(value=round(reps * T / el, 1), unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+    # the oracle runs one OpenMP thread per (sequence, head) pair at a time
+    pairs = prob["batch"] * prob["nheads"]
+    return dict(value=round(reps * T / el, 1), unit="tokens/s", cores=min(oracle.num_threads(), pairs),
+                kind="oracle", cpu=cpu_model(), host_cpus=len(os.sched_getaffinity(0)),
                 sample=f"whole workload ({T} tokens, all heads), fp64 per-token recurrence, "
                        f"{reps} run(s) in {el:.1f} s")
 
 
 # -------------------------------------------------------------------- main
 
+# the five workloads the scan is measured on: the tiny case, the two
+# 16-head / dstate-256 workloads, the ragged 128-head batch and the batch of
+# short sequences; the headline is the 4 x 4096 one
+PER_CONFIG = ["tiny_1x512_h4_n64", "fixed_4x4096_h16_n256", "long_8x16384_h16_n256",
+              "ragged_32_h128_g8_n128", "short_512_h128_g8_n128"]
+
+
+class Runner:
+    """One uploaded problem and the library calls that time it."""
+
+    def __init__(self, torch, lib, hip, dev, prob, short_max, entry="inplace"):
+        import numpy as np
+
+        from mamba_ssd_chunked_chunk_amd import binding, torch_io
+        self.torch, self.lib, self.hip, self.prob = torch, lib, hip, prob
+        self.short_max = short_max
+        d = torch_io.upload(prob, dev)
+        self.d = d
+        self.ps = torch_io.problem_struct(d, short_path_max=short_max)
+        self.ws = torch.empty(binding.ssd_workspace_size(self.ps), dtype=torch.uint8, device=dev)
+        self.stream = torch.cuda.current_stream(dev)
+        self.nk = lib.ssd_kernel_count()
+        knames = [lib.ssd_kernel_name(i).decode() for i in range(self.nk)]
+        # the short path's kernels (the last two) are not launched where no
+        # sequence can take it (dstate 256, or the path off): their events are
+        # then only markers on the stream, left out of the call time and the list
+        assert knames[-2:] == ["ssd_short", "ssd_recur"]
+        n_run = self.nk if (prob["dstate"] <= 128 and short_max != 0) else self.nk - 2
+        self.n_run = n_run
+        self.knames_run = knames[:n_run]
+
+        def P(t):
+            return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+        tail = [P(self.ws), ctypes.c_size_t(self.ws.numel()), ctypes.c_void_p(self.stream.cuda_stream)]
+        if entry == "inplace":
+            self.args = [P(d["y"]), P(d["x"]), P(d["dt"]), P(d["A"]), P(d["B"]), P(d["C"]), P(d["D"]),
+                         P(d["dt_bias"]), P(d["pool"]), P(d["query_start_loc"]), P(d["has_initial_state"]),
+                         P(d["cache_indices"])] + tail
+            self.f_plain, self.f_prof = (lib.ssd_chunk_scan_varlen_fwd_inplace,
+                                         lib.ssd_chunk_scan_varlen_fwd_inplace_profiled)
+        else:
+            # the same sequences' initial states as rows of their own tensor
+            init_t = None
+            hi = prob.get("has_initial_state")
+            if hi is not None and np.any(hi):
+                rows = d["pool"].index_select(0, d["cache_indices"].long())
+                init_t = torch.where(d["has_initial_state"].bool()[:, None, None, None], rows,
+                                     torch.zeros_like(rows)).contiguous()
+            self.final_t = torch.empty((prob["batch"],) + tuple(d["pool"].shape[1:]), dtype=d["pool"].dtype,
+                                       device=dev)
+            self.init_t = init_t
+            self.args = [P(d["y"]), P(d["x"]), P(d["dt"]), P(d["A"]), P(d["B"]), P(d["C"]), P(d["D"]),
+                         P(d["dt_bias"]), P(init_t), P(self.final_t), P(d["query_start_loc"])] + tail
+            self.f_plain, self.f_prof = lib.ssd_chunk_scan_varlen_fwd, lib.ssd_chunk_scan_varlen_fwd_profiled
+
+    def call(self, events=None):
+        if events is None:
+            st = self.f_plain(ctypes.byref(self.ps), *self.args)
+        else:
+            arr = (ctypes.c_void_p * (self.nk + 1))(*[e.value for e in events])
+            st = self.f_prof(ctypes.byref(self.ps), *self.args, arr, self.nk + 1)
+        if st != 0:
+            raise RuntimeError(self.lib.ssd_status_string(st).decode())
+
+    def measure(self, steps, warmup, flush, warm=True):
+        """warmup untimed calls, then steps calls each preceded by a cache
+        eviction (untimed) and bracketed by the kernels' own events."""
+        import numpy as np
+        torch, hip = self.torch, self.hip
+        ev_sets = [[hip.event() for _ in range(self.nk + 1)] for _ in range(steps)]
+        for _ in range(warmup):
+            self.call()
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        for k in range(steps):
+            flush.fill_(k & 0xFF)
+            self.call(ev_sets[k])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        per_call, per_kernel = [], {n: [] for n in self.knames_run}
+        for evs in ev_sets:
+            per_call.append(hip.elapsed_ms(evs[0], evs[self.n_run]))
+            for i, n in enumerate(self.knames_run):
+                per_kernel[n].append(hip.elapsed_ms(evs[i], evs[i + 1]))
+        ms = statistics.fmean(per_call)
+        out = dict(ms=ms, wall=wall, kern_us={n: statistics.fmean(v) * 1e3 for n, v in per_kernel.items()},
+                   us_per_call={"mean": round(ms * 1e3, 2), "median": round(statistics.median(per_call) * 1e3, 2),
+                                "p10": round(float(np.percentile(per_call, 10)) * 1e3, 2),
+                                "p90": round(float(np.percentile(per_call, 90)) * 1e3, 2)})
+        if warm:  # back-to-back, caches not evicted, for reference
+            w0, w1 = hip.event(), hip.event()
+            hip.lib.hipEventRecord(w0, ctypes.c_void_p(self.stream.cuda_stream))
+            for _ in range(steps):
+                self.call()
+            hip.lib.hipEventRecord(w1, ctypes.c_void_p(self.stream.cuda_stream))
+            hip.lib.hipEventSynchronize(w1)
+            out["us_per_call"]["warm_back_to_back"] = round(hip.elapsed_ms(w0, w1) / steps * 1e3, 2)
+        return out
+
+
+def config_line(prob, m, alg):
+    """The per-workload summary: µs per call, tokens/s, the whole call and
+    the longest kernel against their rooflines."""
+    kern = m["kern_us"]
+    dom = max(kern, key=kern.get)
+    return {"tokens": prob["total_len"], "batch": prob["batch"], "us_per_call": m["us_per_call"],
+            "tokens_per_s": round(prob["total_len"] / (m["ms"] * 1e-3), 1),
+            "kernels_us": {n: round(v, 2) for n, v in kern.items()},
+            "roofline_whole_call": roofline_entry("whole", alg, m["ms"] * 1e3),
+            "roofline_dominant_kernel": roofline_entry(dom, alg, kern[dom])}
+
+
 def main():
     args = parse()
+    if args.short_max < 0:  # as in the library: a negative limit selects the default
+        args.short_max = SHORT_MAX
     if args.summarize_profile:
         summarize_profile(args.summarize_profile, args.workload, args.short_max)
         return
@@ -386,107 +522,36 @@ def main():
                                    "GPU (--gpus 1); sharding over GPUs is not built."}))
         sys.exit(2)
 
-    import numpy as np
     import torch
 
-    from mamba_ssd_chunked_chunk_amd import binding, torch_io
+    from mamba_ssd_chunked_chunk_amd import binding
     from mamba_ssd_chunked_chunk_amd.workloads import make_workload, with_bf16_states
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    prob = make_workload(args.workload)
-    if args.state_dtype == "bf16":
-        prob = with_bf16_states(prob)
-    T = prob["total_len"]
-    d = torch_io.upload(prob, dev)
-    ps = torch_io.problem_struct(d)
-    ws = torch.empty(binding.ssd_workspace_size(ps), dtype=torch.uint8, device=dev)
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     lib = binding.load_library()
-    binding.ssd_set_short_path_max(args.short_max)
     hip = Hip()
-    nk = lib.ssd_kernel_count()
-    knames = [lib.ssd_kernel_name(i).decode() for i in range(nk)]
-    # the short path's kernels (the last two) are not launched where no
-    # sequence can take it (dstate 256, or the path off): their events are
-    # then only markers on the stream, left out of the call time and the list
-    assert knames[-2:] == ["ssd_short", "ssd_recur"]
-    n_run = nk if (prob["dstate"] <= 128 and args.short_max > 0) else nk - 2
-    knames_run = knames[:n_run]
-    stream = torch.cuda.current_stream(dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
 
-    def P(t):
-        return None if t is None else ctypes.c_void_p(t.data_ptr())
+    def load(name):
+        p = make_workload(name)
+        return with_bf16_states(p) if args.state_dtype == "bf16" else p
 
-    tail = [P(ws), ctypes.c_size_t(ws.numel()), ctypes.c_void_p(stream.cuda_stream)]
-    if args.entry == "inplace":
-        args_ptrs = [P(d["y"]), P(d["x"]), P(d["dt"]), P(d["A"]), P(d["B"]), P(d["C"]), P(d["D"]),
-                     P(d["dt_bias"]), P(d["pool"]), P(d["query_start_loc"]), P(d["has_initial_state"]),
-                     P(d["cache_indices"])] + tail
-        f_plain, f_prof = lib.ssd_chunk_scan_varlen_fwd_inplace, lib.ssd_chunk_scan_varlen_fwd_inplace_profiled
-    else:
-        # the same sequences' initial states as rows of their own tensor
-        init_t = None
-        hi = prob.get("has_initial_state")
-        if hi is not None and np.any(hi):
-            rows = d["pool"].index_select(0, d["cache_indices"].long())
-            init_t = torch.where(d["has_initial_state"].bool()[:, None, None, None], rows,
-                                 torch.zeros_like(rows)).contiguous()
-        final_t = torch.empty((prob["batch"],) + tuple(d["pool"].shape[1:]), dtype=d["pool"].dtype, device=dev)
-        args_ptrs = [P(d["y"]), P(d["x"]), P(d["dt"]), P(d["A"]), P(d["B"]), P(d["C"]), P(d["D"]),
-                     P(d["dt_bias"]), P(init_t), P(final_t), P(d["query_start_loc"])] + tail
-        f_plain, f_prof = lib.ssd_chunk_scan_varlen_fwd, lib.ssd_chunk_scan_varlen_fwd_profiled
+    prob = load(args.workload)
+    T = prob["total_len"]
+    run = Runner(torch, lib, hip, dev, prob, args.short_max, args.entry)
+    m = run.measure(args.steps, args.warmup, flush)
+    ms, kern_us = m["ms"], m["kern_us"]
 
-    ev_sets = [[hip.event() for _ in range(nk + 1)] for _ in range(args.steps)]
-
-    def call(events=None):
-        if events is None:
-            st = f_plain(ctypes.byref(ps), *args_ptrs)
-        else:
-            arr = (ctypes.c_void_p * (nk + 1))(*[e.value for e in events])
-            st = f_prof(ctypes.byref(ps), *args_ptrs, arr, nk + 1)
-        if st != 0:
-            raise RuntimeError(lib.ssd_status_string(st).decode())
-
-    for _ in range(args.warmup):
-        call()
-    torch.cuda.synchronize()
-
-    # timed region: K steps, each = cache eviction (untimed) + one call (events)
-    wall0 = time.perf_counter()
-    for k in range(args.steps):
-        flush.fill_(k & 0xFF)
-        call(ev_sets[k])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-
-    per_call = []
-    per_kernel = {n: [] for n in knames_run}
-    for evs in ev_sets:
-        per_call.append(hip.elapsed_ms(evs[0], evs[n_run]))
-        for i, n in enumerate(knames_run):
-            per_kernel[n].append(hip.elapsed_ms(evs[i], evs[i + 1]))
-    ms = statistics.fmean(per_call)
-
-    # warm (back-to-back, caches not evicted) for reference
-    w0, w1 = hip.event(), hip.event()
-    hip.lib.hipEventRecord(w0, ctypes.c_void_p(stream.cuda_stream))
-    for _ in range(args.steps):
-        call()
-    hip.lib.hipEventRecord(w1, ctypes.c_void_p(stream.cuda_stream))
-    hip.lib.hipEventSynchronize(w1)
-    warm_ms = hip.elapsed_ms(w0, w1) / args.steps
-
-    copy_gbs = copy_probe(torch, dev, hip, stream)
+    copy_gbs = copy_probe(torch, dev, hip, run.stream)
 
     alg = algorithmic(prob, args.short_max)
-    kern_us = {n: statistics.fmean(v) * 1e3 for n, v in per_kernel.items()}
     dom = max(kern_us, key=kern_us.get)
     roof = roofline_entry(dom, alg, kern_us[dom],
                           traffic_for(dom, args.workload) if args.short_max == SHORT_MAX and args.state_dtype == "f32" else None)
     whole = roofline_entry("whole", alg, ms * 1e3)
-    per_kernel_roof = {n: roofline_entry(n, alg, kern_us[n]) for n in knames_run if alg[n]["bytes"] or alg[n]["flops"]}
+    per_kernel_roof = {n: roofline_entry(n, alg, kern_us[n]) for n in run.knames_run if alg[n]["bytes"] or alg[n]["flops"]}
 
     out = {
         "metric": METRIC,
@@ -508,17 +573,28 @@ def main():
                    **({} if args.entry == "inplace" else {"entry": "separate initial/final states"}),
                    **({} if args.short_max == SHORT_MAX else {"short_path_max": args.short_max}),
                    **({} if args.state_dtype == "f32" else {"state_dtype": "bf16 (storage)"})},
-        "us_per_call": {"mean": round(ms * 1e3, 2), "median": round(statistics.median(per_call) * 1e3, 2),
-                        "p10": round(float(np.percentile(per_call, 10)) * 1e3, 2),
-                        "p90": round(float(np.percentile(per_call, 90)) * 1e3, 2),
-                        "warm_back_to_back": round(warm_ms * 1e3, 2)},
+        "us_per_call": m["us_per_call"],
         "kernels_us": {n: round(v, 2) for n, v in kern_us.items()},
         "roofline": roof,
         "roofline_whole_call": whole,
         "roofline_per_kernel": per_kernel_roof,
         "achievable_copy_GBps": copy_gbs,
-        "wall_s_timed_region": round(wall, 3),
+        "wall_s_timed_region": round(m["wall"], 3),
     }
+    del run
+    if not args.no_per_config:
+        per = {}
+        for name in PER_CONFIG:
+            p = prob if name == args.workload else load(name)
+            if name == args.workload:
+                pm = m
+            else:
+                r = Runner(torch, lib, hip, dev, p, args.short_max, args.entry)
+                pm = r.measure(args.config_steps, 2, flush, warm=False)
+                del r
+                torch.cuda.empty_cache()
+            per[name] = config_line(p, pm, algorithmic(p, args.short_max))
+        out["per_config"] = per
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(prob, args.cpu_seconds, args.entry)
     print(json.dumps(out))

@@ -33,6 +33,18 @@
  *     host synchronisation); ssd_validate_inputs checks them on demand.
  *     Violating them is undefined behaviour.
  *   - y must not alias any input; ssm_pool is the only read-write buffer.
+ *   - Alignment: y, x, B, C and the state tensors (ssm_pool,
+ *     initial_states, final_states) must start on a 16-byte boundary (the
+ *     kernels move them 16 bytes per lane); dt, A, D, dt_bias,
+ *     query_start_loc and cache_indices on a 4-byte boundary; the workspace
+ *     on a 256-byte boundary.  Buffers from hipMalloc, or whole torch
+ *     tensors, satisfy this; a view that starts mid-row (x[1:] of a tensor
+ *     whose rows are not a multiple of 16 bytes, ...) may not.  A misaligned
+ *     tensor gives SSD_ERR_MISALIGNED, a misaligned workspace
+ *     SSD_ERR_WORKSPACE, before any launch.
+ *   - Every option is passed per call in ssd_problem: the library keeps no
+ *     mutable state, so concurrent calls (other host threads, other
+ *     streams) and captured graphs see exactly the options they were given.
  *   - A call that fails while kernels run (SSD_ERR_HIP from a later status
  *     query) may leave the pool partially written.
  */
@@ -46,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 12
+#define SSD_ABI_VERSION 13
 #define SSD_MAX_DSTATE 256  /* largest dstate, as in "mamba2_ssd_scan", comptime MAX_DSTATE */
 #define SSD_SHORT_PATH_LIMIT 128  /* longest sequence the short path can take */
 #define SSD_RECUR_LIMIT 4         /* of those, the longest the token recurrence takes */
@@ -61,7 +73,8 @@ typedef enum ssd_status {
     SSD_ERR_UNSUPPORTED = 3,  /* a size this build has no kernel for            */
     SSD_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than required         */
     SSD_ERR_BAD_INPUT = 5,    /* ssd_validate_inputs found a violated precondition */
-    SSD_ERR_HIP = 6           /* a HIP runtime call or kernel launch failed       */
+    SSD_ERR_HIP = 6,          /* a HIP runtime call or kernel launch failed       */
+    SSD_ERR_MISALIGNED = 7    /* a tensor pointer breaks the alignment rule above */
 } ssd_status;
 
 /* Problem sizes.  Dense row-major tensors:
@@ -91,14 +104,20 @@ typedef struct ssd_problem {
                           * from bf16, the state chain and all arithmetic stay fp32, and
                           * each final state is rounded to bf16 (nearest even) once, when
                           * it is written */
+    int32_t short_path_max; /* longest sequence the short path takes (see below):
+                          * 0 = none (every sequence through the chunked steps),
+                          * 1 .. SSD_SHORT_PATH_LIMIT, or any negative value for
+                          * the default SSD_SHORT_PATH_LIMIT; larger values give
+                          * SSD_ERR_UNSUPPORTED.  Only dstate 64 and 128 have a
+                          * short path; at dstate 256 the field is ignored. */
 } ssd_problem;
 
 /* Offsets (bytes from the workspace base) and sizes of the intermediates the
  * compute entry point leaves in the workspace, so tests can compare each
  * step with the oracle.  nchunks_max = floor(total_len / 256) + batch bounds
  * the number of chunks; chunk c of the call occupies row c of each table.
- * Sequences taken by the short path (see ssd_set_short_path_max; there a
- * zero-length sequence is taken as well) have no chunks: chunk_off[b] ==
+ * Sequences taken by the short path (see ssd_problem.short_path_max; there
+ * a zero-length sequence is taken as well) have no chunks: chunk_off[b] ==
  * chunk_off[b+1] and no row of any table is theirs.
  *   meta      int32[4]                    {nchunks, nseq, nrecur, 0}: chunks,
  *                                         sequences the state chain walks,
@@ -177,6 +196,10 @@ ssd_status ssd_workspace_get_layout(const ssd_problem *prob, ssd_workspace_layou
  *   workspace         scratch of at least ssd_workspace_size() bytes, 256-byte
  *                     aligned; its contents on return are the intermediates
  *                     described by ssd_workspace_layout.
+ * Errors (all before any launch; nothing is modified): SSD_ERR_NULL_ARG for
+ * a NULL problem or required pointer (y, x, dt, B, C may be NULL only when
+ * total_len is 0), SSD_ERR_BAD_SHAPE / SSD_ERR_UNSUPPORTED for the sizes,
+ * SSD_ERR_MISALIGNED, SSD_ERR_WORKSPACE; SSD_ERR_HIP if a launch fails.
  * Precision: y is rounded to bf16 (nearest even); the inter-chunk state chain
  * and the pool are fp32.  Results are deterministic (bitwise run to run).  */
 ssd_status ssd_chunk_scan_varlen_fwd_inplace(
@@ -191,28 +214,25 @@ ssd_status ssd_chunk_scan_varlen_fwd_inplace(
  * (0 <= i < ssd_kernel_count(), launch order; NULL otherwise).  The last
  * two, "ssd_short" and "ssd_recur", serve the short path and are not
  * launched when no sequence can take it (dstate 256, or
- * ssd_set_short_path_max(0)).                                              */
+ * short_path_max = 0).                                                      */
 int ssd_kernel_count(void);
 const char *ssd_kernel_name(int i);
 
-/* Short-sequence path.  At dstate 64 and 128, every sequence of 1 .. tokens
- * tokens is scanned whole by one fused kernel instead of the chunked steps,
- * with the final state written straight to its slot: sequences of up to
- * SSD_RECUR_LIMIT tokens (decode steps) by the token recurrence of
- * "mamba2_ssd_scan" ("Per-token recurrence") with the state split over the
- * threads along dstate ("ssd_recur"), longer ones by the single-chunk case
- * of the segment-sum form of "Mamba chunk scan with segsum" (description),
- * on MFMA ("ssd_short").  Zero-length sequences are finished there too.  The route depends on the sequence's own length
- * only (a sequence's results do not depend on the rest of the batch).
- * Results agree with the chunked path within the documented tolerances, not
- * bitwise.  tokens = 0 sends every sequence through the chunked steps (the
- * faster choice for batches of mostly long sequences with a few short
- * ones, where the short kernel runs after the chunked ones).  Process-wide
- * setting, read when a compute call is enqueued (atomic; default
- * SSD_SHORT_PATH_LIMIT).  Returns the previous value, or -1 (nothing
- * changed) when tokens is outside 0 .. SSD_SHORT_PATH_LIMIT.  Host only;
- * enqueues nothing.                                                         */
-int ssd_set_short_path_max(int tokens);
+/* Short-sequence path (ssd_problem.short_path_max).  At dstate 64 and 128,
+ * every sequence of 1 .. short_path_max tokens is scanned whole by one fused
+ * kernel instead of the chunked steps, with the final state written straight
+ * to its slot: sequences of up to SSD_RECUR_LIMIT tokens (decode steps) by
+ * the token recurrence of "mamba2_ssd_scan" ("Per-token recurrence") with the
+ * state split over the threads along dstate ("ssd_recur"), longer ones by the
+ * single-chunk case of the segment-sum form of "Mamba chunk scan with segsum"
+ * (description), on MFMA ("ssd_short").  Zero-length sequences are finished
+ * there too.  The route depends on the sequence's own length only (a
+ * sequence's results do not depend on the rest of the batch).  Results agree
+ * with the chunked path within the documented tolerances, not bitwise.
+ * short_path_max = 0 sends every sequence through the chunked steps (the
+ * faster choice for batches of mostly long sequences with a few short ones,
+ * where the short kernel runs after the chunked ones).  The limit is read
+ * from the problem of each call; nothing is remembered between calls. */
 
 /* Same computation as ssd_chunk_scan_varlen_fwd_inplace; additionally
  * records events (each a hipEvent_t created by the caller, passed as void*)

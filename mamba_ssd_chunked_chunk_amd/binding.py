@@ -18,14 +18,13 @@ LIB_PATH = os.path.join(_PKG, "libssd.so")
 
 SSD_OK = 0
 STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_NULL_ARG", 2: "SSD_ERR_BAD_SHAPE", 3: "SSD_ERR_UNSUPPORTED",
-                4: "SSD_ERR_WORKSPACE", 5: "SSD_ERR_BAD_INPUT", 6: "SSD_ERR_HIP"}
+                4: "SSD_ERR_WORKSPACE", 5: "SSD_ERR_BAD_INPUT", 6: "SSD_ERR_HIP", 7: "SSD_ERR_MISALIGNED"}
 
 # every symbol include/ssd.h declares
 EXPORTED = ("ssd_abi_version", "ssd_status_string", "ssd_workspace_size",
             "ssd_workspace_get_layout", "ssd_chunk_scan_varlen_fwd_inplace",
             "ssd_kernel_count", "ssd_kernel_name", "ssd_chunk_scan_varlen_fwd_inplace_profiled",
-            "ssd_chunk_scan_varlen_fwd", "ssd_chunk_scan_varlen_fwd_profiled", "ssd_validate_inputs",
-            "ssd_set_short_path_max")
+            "ssd_chunk_scan_varlen_fwd", "ssd_chunk_scan_varlen_fwd_profiled", "ssd_validate_inputs")
 
 
 class SsdError(RuntimeError):
@@ -39,7 +38,8 @@ class ssd_problem(ctypes.Structure):
                 ("nheads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("ngroups", ctypes.c_int32), ("dstate", ctypes.c_int32),
                 ("max_slots", ctypes.c_int32), ("chunk_size", ctypes.c_int32),
-                ("dt_softplus", ctypes.c_int32), ("state_dtype", ctypes.c_int32)]
+                ("dt_softplus", ctypes.c_int32), ("state_dtype", ctypes.c_int32),
+                ("short_path_max", ctypes.c_int32)]
 
 
 class ssd_workspace_layout(ctypes.Structure):
@@ -55,9 +55,10 @@ _lock = threading.Lock()
 _lib = None
 
 # SSD_ABI_VERSION of include/ssd.h that the ctypes structures below mirror
-ABI_VERSION = 12
+ABI_VERSION = 13
 STATE_F32, STATE_BF16 = 0, 1  # SSD_STATE_F32, SSD_STATE_BF16
 SHORT_PATH_LIMIT = 128  # SSD_SHORT_PATH_LIMIT
+SHORT_PATH_DEFAULT = -1  # ssd_problem.short_path_max: any negative value selects SHORT_PATH_LIMIT
 
 
 def load_library():
@@ -99,8 +100,6 @@ def load_library():
                 [PP] + [V] * 12 + [ctypes.c_size_t, V, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int])
             lib.ssd_validate_inputs.restype = ctypes.c_int
             lib.ssd_validate_inputs.argtypes = [PP, V, V, V]
-            lib.ssd_set_short_path_max.restype = ctypes.c_int
-            lib.ssd_set_short_path_max.argtypes = [ctypes.c_int]
             _lib = lib
     return _lib
 
@@ -113,10 +112,11 @@ def _check(status: int, what: str):
 
 
 def make_problem(total_len, batch, nheads, head_dim, ngroups, dstate, max_slots,
-                 dt_softplus=True, chunk_size=0, state_dtype=STATE_F32) -> ssd_problem:
+                 dt_softplus=True, chunk_size=0, state_dtype=STATE_F32,
+                 short_path_max=SHORT_PATH_DEFAULT) -> ssd_problem:
     return ssd_problem(int(total_len), int(batch), int(nheads), int(head_dim), int(ngroups),
                        int(dstate), int(max_slots), int(chunk_size), 1 if dt_softplus else 0,
-                       int(state_dtype))
+                       int(state_dtype), int(short_path_max))
 
 
 def _state_dtype(t, name):
@@ -127,15 +127,6 @@ def _state_dtype(t, name):
     if t.dtype == torch.bfloat16:
         return STATE_BF16
     raise TypeError(f"{name}: expected float32 or bfloat16 states, got {t.dtype}")
-
-
-def ssd_set_short_path_max(tokens: int) -> int:
-    """Longest sequence the fused short-sequence kernel takes (0: none);
-    returns the previous setting."""
-    prev = load_library().ssd_set_short_path_max(int(tokens))
-    if prev < 0:
-        raise ValueError(f"short path maximum must be in 0..{SHORT_PATH_LIMIT}, got {tokens}")
-    return prev
 
 
 def ssd_abi_version() -> int:
@@ -181,16 +172,17 @@ def _opt(t, name, dtype, shape, device):
     return t
 
 
-def problem_from_tensors(x, B, ssm_pool, query_start_loc, dt_softplus=True) -> ssd_problem:
+def problem_from_tensors(x, B, ssm_pool, query_start_loc, dt_softplus=True,
+                         short_path_max=SHORT_PATH_DEFAULT) -> ssd_problem:
     T, H, P = x.shape
     _, G, N = B.shape
     return make_problem(T, query_start_loc.numel() - 1, H, P, G, N, ssm_pool.shape[0], dt_softplus,
-                        state_dtype=_state_dtype(ssm_pool, "ssm_pool"))
+                        state_dtype=_state_dtype(ssm_pool, "ssm_pool"), short_path_max=short_path_max)
 
 
 def ssd_chunk_scan_varlen_fwd_inplace(y, x, dt, A, B, C, D, dt_bias, ssm_pool, query_start_loc,
                                       has_initial_state, cache_indices, *, dt_softplus=True,
-                                      workspace=None, stream=None):
+                                      short_path_max=SHORT_PATH_DEFAULT, workspace=None, stream=None):
     """In-place varlen SSD forward (see include/ssd.h for the semantics).
 
     Tensors (torch, on one HIP device, contiguous): y, x bf16 [T,H,P];
@@ -202,6 +194,8 @@ def ssd_chunk_scan_varlen_fwd_inplace(y, x, dt, A, B, C, D, dt_bias, ssm_pool, q
     None to allocate one.  Runs on ``stream`` (a torch.cuda.Stream) or the
     current stream; asynchronous.  Returns the workspace tensor.  A bf16
     ssm_pool selects bf16 state storage (arithmetic stays fp32).
+    ``short_path_max``: longest sequence the short path takes (dstate <= 128;
+    0: none, negative: the library default SHORT_PATH_LIMIT).
     """
     import torch
     dev = x.device
@@ -234,7 +228,7 @@ def ssd_chunk_scan_varlen_fwd_inplace(y, x, dt, A, B, C, D, dt_bias, ssm_pool, q
         raise TypeError("cache_indices must be int32 or uint32")
     if tuple(cache_indices.shape) != (batch,) or not cache_indices.is_contiguous() or cache_indices.device != dev:
         raise ValueError("cache_indices must be a contiguous [batch] tensor on the same device")
-    prob = make_problem(T, batch, H, P, G, N, S, dt_softplus, state_dtype=sd)
+    prob = make_problem(T, batch, H, P, G, N, S, dt_softplus, state_dtype=sd, short_path_max=short_path_max)
     need = ssd_workspace_size(prob)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -251,7 +245,8 @@ def ssd_chunk_scan_varlen_fwd_inplace(y, x, dt, A, B, C, D, dt_bias, ssm_pool, q
 
 
 def ssd_chunk_scan_varlen_fwd(y, x, dt, A, B, C, D, dt_bias, initial_states, final_states,
-                              query_start_loc, *, dt_softplus=True, workspace=None, stream=None):
+                              query_start_loc, *, dt_softplus=True, short_path_max=SHORT_PATH_DEFAULT,
+                              workspace=None, stream=None):
     """Varlen SSD forward with separate initial and final states (see
     include/ssd.h): sequence b starts from ``initial_states[b]`` ([batch,H,P,N],
     or None/empty for zero) and its final state is written to
@@ -282,7 +277,8 @@ def ssd_chunk_scan_varlen_fwd(y, x, dt, A, B, C, D, dt_bias, initial_states, fin
     initial_states = _opt(initial_states, "initial_states", final_states.dtype, (batch, H, P, N), dev)
     _need(final_states, "final_states", final_states.dtype, (batch, H, P, N), dev)
     _need(query_start_loc, "query_start_loc", torch.int32, (batch + 1,), dev)
-    prob = make_problem(T, batch, H, P, G, N, max(batch, 1), dt_softplus, state_dtype=sd)
+    prob = make_problem(T, batch, H, P, G, N, max(batch, 1), dt_softplus, state_dtype=sd,
+                        short_path_max=short_path_max)
     need = ssd_workspace_size(prob)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)

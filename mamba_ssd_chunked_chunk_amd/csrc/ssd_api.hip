@@ -9,7 +9,6 @@
 #include <string.h>
 
 #include <algorithm>
-#include <atomic>
 #include <vector>
 
 #include "ssd.h"
@@ -18,9 +17,6 @@
 namespace {
 
 constexpr size_t kAlign = 256;
-
-// Longest sequence routed to the short-path kernel (dstate 64 and 128).
-std::atomic<int> g_short_max{ssd::kShortMax};
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -38,6 +34,7 @@ ssd_status check_problem(const ssd_problem *p) {
     if (p->dstate != 64 && p->dstate != 128 && p->dstate != 256) return SSD_ERR_UNSUPPORTED;
     if (p->head_dim != ssd::kHeadDim) return SSD_ERR_UNSUPPORTED;
     if (p->chunk_size != 0 && p->chunk_size != ssd::kChunk) return SSD_ERR_UNSUPPORTED;
+    if (p->short_path_max > SSD_SHORT_PATH_LIMIT) return SSD_ERR_UNSUPPORTED;
     if (p->nheads > 65535) return SSD_ERR_UNSUPPORTED;  // grid y limit
     const int64_t ncm = p->total_len / ssd::kChunk + p->batch;
     if (ncm > INT32_MAX) return SSD_ERR_UNSUPPORTED;
@@ -83,6 +80,9 @@ const char *ssd_status_string(int s) {
     case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE: workspace missing, misaligned or too small";
     case SSD_ERR_BAD_INPUT: return "SSD_ERR_BAD_INPUT: query_start_loc or cache_indices violate a precondition";
     case SSD_ERR_HIP: return "SSD_ERR_HIP: a HIP runtime call failed";
+    case SSD_ERR_MISALIGNED:
+        return "SSD_ERR_MISALIGNED: y, x, B, C or a state tensor is not 16-byte aligned, or dt, A, D, dt_bias, "
+               "query_start_loc or cache_indices not 4-byte aligned";
     default: return "unknown ssd_status";
     }
 }
@@ -109,11 +109,6 @@ static const char *const kKernelNames[] = {"ssd_prep",       "ssd_chunk_state", 
                                            "ssd_chunk_scan", "ssd_short",       "ssd_recur"};
 static constexpr int kNumKernels = 6;
 static constexpr int kFirstShortKernel = 4;  // this and the later ones serve the short path
-
-int ssd_set_short_path_max(int tokens) {
-    if (tokens < 0 || tokens > SSD_SHORT_PATH_LIMIT) return -1;
-    return g_short_max.exchange(tokens);
-}
 
 int ssd_kernel_count(void) { return kNumKernels; }
 
@@ -143,7 +138,7 @@ static ssd_status run_scan(
     if (!aligned(y, 16) || !aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) ||
         !aligned(sio.out, 16) || !aligned(sio.in, 16) || !aligned(dt, 4) || !aligned(A, 4) ||
         !aligned(D, 4) || !aligned(dt_bias, 4) || !aligned(query_start_loc, 4) || !aligned(sio.cache_idx, 4))
-        return SSD_ERR_BAD_SHAPE;
+        return SSD_ERR_MISALIGNED;
     ssd_workspace_layout L;
     layout_of(prob, &L);
     if (workspace == nullptr || workspace_bytes < L.total_bytes || !aligned(workspace, kAlign))
@@ -185,7 +180,7 @@ static ssd_status run_scan(
     // the short path serves dstate 64 and 128; the route of a sequence
     // depends on its own length only, so its results do not depend on the
     // rest of the batch
-    p.short_max = p.N <= 128 ? g_short_max.load() : 0;
+    p.short_max = p.N <= 128 ? (prob->short_path_max < 0 ? ssd::kShortMax : prob->short_path_max) : 0;
     p.recur_max = std::min(p.short_max, ssd::kRecurMax);
     // with the short path on, only sequences longer than its limit reach the
     // chunked steps: at most T / (short_max + 1) of them, with at most

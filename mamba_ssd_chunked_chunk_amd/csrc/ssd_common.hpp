@@ -118,9 +118,14 @@ __device__ __forceinline__ float f16_bits_to_float(uint32_t bits16) {
 }
 
 // Exponent s that puts a positive maximum m in [2^14, 2^15) after scaling by
-// 2^s (0 when m is 0), so scaled values stay well inside fp16's range.
+// 2^s (0 when m is 0 or NaN), so scaled values stay well inside fp16's range.
+// s is capped at 126 so that 2^s and 2^-s are both finite, normal floats:
+// below 2^-112 (subnormal m included, whose exponent field reads as -127) the
+// scaled maximum lands under 2^14 instead, which fp16 still holds.
 __device__ __forceinline__ int f16_scale_exponent(float m) {
-    return m > 0.0f ? 14 - ((int)((__float_as_uint(m) >> 23) & 0xFF) - 127) : 0;
+    if (!(m > 0.0f)) return 0;
+    const int s = 14 - ((int)((__float_as_uint(m) >> 23) & 0xFF) - 127);
+    return s < 126 ? s : 126;
 }
 
 __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {

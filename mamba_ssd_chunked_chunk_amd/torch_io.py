@@ -38,27 +38,29 @@ def upload(prob: dict, device="cuda"):
     return d
 
 
-def run(d: dict, workspace=None, stream=None):
+def run(d: dict, workspace=None, stream=None, short_path_max=binding.SHORT_PATH_DEFAULT):
     """One call of the in-place scan on an uploaded problem (asynchronous)."""
     return binding.ssd_chunk_scan_varlen_fwd_inplace(
         d["y"], d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["dt_bias"], d["pool"],
         d["query_start_loc"], d["has_initial_state"], d["cache_indices"],
-        dt_softplus=d["dt_softplus"], workspace=workspace, stream=stream)
+        dt_softplus=d["dt_softplus"], short_path_max=short_path_max, workspace=workspace, stream=stream)
 
 
-def run_fwd(d: dict, initial_states, final_states, workspace=None, stream=None):
+def run_fwd(d: dict, initial_states, final_states, workspace=None, stream=None,
+            short_path_max=binding.SHORT_PATH_DEFAULT):
     """One call of the scan with separate initial/final states (asynchronous)."""
     return binding.ssd_chunk_scan_varlen_fwd(
         d["y"], d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["dt_bias"], initial_states,
-        final_states, d["query_start_loc"], dt_softplus=d["dt_softplus"], workspace=workspace,
-        stream=stream)
+        final_states, d["query_start_loc"], dt_softplus=d["dt_softplus"], short_path_max=short_path_max,
+        workspace=workspace, stream=stream)
 
 
-def problem_struct(d: dict):
+def problem_struct(d: dict, short_path_max=binding.SHORT_PATH_DEFAULT):
     T, H, P = d["x"].shape
     G, N = d["B"].shape[1], d["B"].shape[2]
     import torch
     return binding.make_problem(T, d["query_start_loc"].numel() - 1, H, P, G, N,
                                 d["pool"].shape[0], d["dt_softplus"],
                                 state_dtype=(binding.STATE_BF16 if d["pool"].dtype == torch.bfloat16
-                                             else binding.STATE_F32))
+                                             else binding.STATE_F32),
+                                short_path_max=short_path_max)

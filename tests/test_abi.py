@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert binding.ssd_abi_version() == binding.ABI_VERSION == 12
+    assert binding.ssd_abi_version() == binding.ABI_VERSION == 13
     for code, name in binding.STATUS_NAMES.items():
         assert lib.ssd_status_string(code).decode().startswith(name)
     assert b"unknown" in lib.ssd_status_string(99)
@@ -75,6 +75,7 @@ def test_workspace_layout_arithmetic(lib):
     (dict(batch=0), 2), (dict(nheads=6, ngroups=4), 2), (dict(total_len=-1), 2),
     (dict(max_slots=0), 2), (dict(dstate=512), 3), (dict(dstate=96), 3),
     (dict(head_dim=128), 3), (dict(chunk_size=128), 3), (dict(state_dtype=2), 3), (dict(state_dtype=-1), 3),
+    (dict(short_path_max=129), 3), (dict(short_path_max=1 << 20), 3),
 ])
 def test_bad_problems_rejected(lib, kw, status):
     n = ctypes.c_size_t(0)
@@ -105,7 +106,7 @@ def test_null_and_workspace_errors_before_launch(lib):
     # misaligned bf16 tensor
     a = list(args)
     a[1] = ctypes.c_void_p((1 << 20) + 2)
-    assert f(ctypes.byref(p), *a, need, None) == 2
+    assert f(ctypes.byref(p), *a, need, None) == 7
     # optional D / dt_bias / has_initial_state may be NULL: the call then only
     # fails on the (deliberately too small) workspace
     a = list(args)
@@ -129,7 +130,7 @@ def test_separate_states_errors_before_launch(lib):
     for idx in (8, 9):
         a = list(args)
         a[idx] = ctypes.c_void_p((1 << 20) + 8)
-        assert f(ctypes.byref(p), *a, need, None) == 2, idx
+        assert f(ctypes.byref(p), *a, need, None) == 7, idx
     # workspace too small; optional D, dt_bias and initial_states may be NULL
     a = list(args)
     a[6] = a[7] = a[8] = None
@@ -156,20 +157,41 @@ def test_state_dtype_accepted_and_layout_unchanged(lib):
     assert a == b
 
 
-def test_short_path_setting_host_only(lib):
-    """The routing knob is host state: it returns the previous value, rejects
-    values outside 0..SSD_SHORT_PATH_LIMIT without changing anything, and the
-    kernel list names the fused short-sequence kernel last."""
-    prev = binding.ssd_set_short_path_max(binding.SHORT_PATH_LIMIT)
-    try:
-        assert binding.ssd_set_short_path_max(0) == binding.SHORT_PATH_LIMIT
-        assert binding.ssd_set_short_path_max(64) == 0
-        assert lib.ssd_set_short_path_max(-1) == -1
-        assert lib.ssd_set_short_path_max(binding.SHORT_PATH_LIMIT + 1) == -1
-        assert binding.ssd_set_short_path_max(binding.SHORT_PATH_LIMIT) == 64
-        with pytest.raises(ValueError):
-            binding.ssd_set_short_path_max(1000)
-    finally:
-        binding.ssd_set_short_path_max(prev)
+@pytest.mark.parametrize("idx,misalign", [
+    # y, x, B, C, ssm_pool: 16 bytes (offsets 2 and 8 both break it)
+    (0, 2), (1, 8), (4, 2), (5, 8), (8, 8), (8, 4),
+    # dt, A, D, dt_bias, query_start_loc, cache_indices: 4 bytes
+    (2, 2), (3, 1), (6, 2), (7, 2), (9, 2), (11, 1),
+])
+def test_alignment_status(lib, idx, misalign):
+    """Each tensor pointer that breaks the documented alignment gives
+    SSD_ERR_MISALIGNED before anything is launched; aligned pointers reach
+    the (deliberately too small) workspace check instead."""
+    p = _prob()
+    f = lib.ssd_chunk_scan_varlen_fwd_inplace
+    base = 1 << 20  # never dereferenced: every call below fails its host checks
+    args = [ctypes.c_void_p(base)] * 13
+    need = binding.ssd_workspace_size(p)
+    a = list(args)
+    a[idx] = ctypes.c_void_p(base + misalign)
+    assert f(ctypes.byref(p), *a, need, None) == 7
+    assert lib.ssd_status_string(7).decode().startswith("SSD_ERR_MISALIGNED")
+    # has_initial_state is bytes: any address is aligned
+    a = list(args)
+    a[10] = ctypes.c_void_p(base + 1)
+    assert f(ctypes.byref(p), *a, need - 1, None) == 4
+
+
+def test_short_path_limit_is_a_problem_field(lib):
+    """The short-path limit is part of each call's problem (no library
+    state): negative selects the default, 0..SSD_SHORT_PATH_LIMIT are valid,
+    larger values are rejected; the layout does not depend on it; the kernel
+    list names the two short-path kernels last."""
+    for v in (-1, -100, 0, 1, 4, 64, binding.SHORT_PATH_LIMIT):
+        assert binding.ssd_workspace_get_layout(_prob(short_path_max=v)) == binding.ssd_workspace_get_layout(_prob())
+    n = ctypes.c_size_t(0)
+    assert lib.ssd_workspace_size(ctypes.byref(_prob(short_path_max=binding.SHORT_PATH_LIMIT + 1)),
+                                  ctypes.byref(n)) == 3
+    assert not hasattr(binding, "ssd_set_short_path_max")
     names = [lib.ssd_kernel_name(i).decode() for i in range(lib.ssd_kernel_count())]
     assert names == ["ssd_prep", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan", "ssd_short", "ssd_recur"]

@@ -8,7 +8,6 @@ Intermediates left in the workspace are compared step by step with the
 chunked oracle (oracle.chunked) on small problems.
 """
 
-import contextlib
 import math
 
 import numpy as np
@@ -32,20 +31,14 @@ FINAL_TOL = 1e-3
 FINAL_TOL_BF16 = FINAL_TOL + 2.0 ** -8
 
 
-@contextlib.contextmanager
-def short_path(tokens):
-    """Route sequences of 1..tokens tokens (dstate <= 128) to the fused short
-    kernel for the duration (0: every sequence through the chunked steps)."""
-    prev = binding.ssd_set_short_path_max(tokens)
-    try:
-        yield
-    finally:
-        binding.ssd_set_short_path_max(prev)
+# ssd_problem.short_path_max: the library default (128), or every sequence chunked
+DEFAULT = binding.SHORT_PATH_DEFAULT
+CHUNKED = 0
 
 
-def gpu_run(prob, **kw):
+def gpu_run(prob, short_max=DEFAULT, **kw):
     d = torch_io.upload(prob, "cuda")
-    ws = torch_io.run(d, **kw)
+    ws = torch_io.run(d, short_path_max=short_max, **kw)
     torch.cuda.synchronize()
     return d, ws
 
@@ -84,27 +77,22 @@ def bits(t):
     return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32)
 
 
-def full_check(prob, seqs=None):
-    """Run on GPU, compare with the oracle (optionally only the sequences of
-    seqs: a range (lo, hi) or a list of ranges), check slot bookkeeping.
-    Returns (y worst ratio, final worst)."""
+def full_check(prob, short_max=DEFAULT):
+    """Run on GPU, compare every sequence with the oracle, check slot
+    bookkeeping.  Returns (y worst ratio, final worst)."""
     tol = FINAL_TOL_BF16 if prob.get("state_dtype", "f32") == "bf16" else FINAL_TOL
     d = torch_io.upload(prob, "cuda")
     before = d["pool"].clone()
-    torch_io.run(d)
+    torch_io.run(d, short_path_max=short_max)
     torch.cuda.synchronize()
-    qsl = prob["query_start_loc"]
     ci = prob["cache_indices"]
-    wy = wf = 0.0
-    for rng in ([None] if seqs is None else seqs if isinstance(seqs, list) else [seqs]):
-        ref = oracle.recurrence(prob, seqs=rng, want_pool=False)
-        lo, hi = (0, len(qsl) - 1) if rng is None else rng
-        s, e = int(qsl[lo]), int(qsl[hi])
-        yg = d["y"][s:e].float().cpu().numpy().astype(np.float64)
-        wy = max(wy, assert_y(yg, ref["y"][s:e], prob.get("name", "")))
-        for b in range(lo, hi):
-            slot = int(ci[b])
-            wf = max(wf, assert_final(d["pool"][slot].float().cpu().numpy(), ref["final"][b], f"seq {b}", tol))
+    ref = oracle.recurrence(prob, want_pool=False)
+    wy = assert_y(y_host(d), ref["y"], prob.get("name", ""))
+    wf = 0.0
+    # the written slots, gathered on the device and copied back together
+    fin = d["pool"].index_select(0, torch.from_numpy(ci.astype(np.int64)).cuda()).float().cpu().numpy()
+    for b in range(len(ci)):
+        wf = max(wf, assert_final(fin[b], ref["final"][b], f"seq {b}", tol))
     # slots outside cache_indices: bit-identical (compared on the device)
     written = torch.zeros(prob["pool"].shape[0], dtype=torch.bool, device="cuda")
     written[torch.from_numpy(ci.astype(np.int64)).cuda()] = True
@@ -136,8 +124,7 @@ def test_small_cases(name, route):
     spec = dict(SMALL[name])
     lens = spec.pop("seqlens")
     prob = small_problem(lens, seed=100 + len(name), **spec)
-    with short_path(binding.SHORT_PATH_LIMIT if route == "default" else 0):
-        full_check(prob)
+    full_check(prob, DEFAULT if route == "default" else CHUNKED)
 
 
 # lengths around the short-path limit and the fused kernel's 16-token K-steps
@@ -148,8 +135,7 @@ MIXED_LENS = [1, 2, 15, 16, 17, 31, 32, 33, 0, 64, 95, 96, 97, 127, 128, 129, 25
 @pytest.mark.parametrize("N,G,init", [(64, 2, "bernoulli"), (128, 4, "all"), (128, 1, "none")])
 def test_short_path_mixed_lengths(N, G, init):
     prob = small_problem(MIXED_LENS, H=8, P=64, G=G, N=N, seed=90 + N + G, init=init)
-    with short_path(binding.SHORT_PATH_LIMIT):
-        full_check(prob)
+    full_check(prob, binding.SHORT_PATH_LIMIT)
 
 
 @pytest.mark.parametrize("limit", [1, 33, 96])
@@ -157,8 +143,7 @@ def test_short_path_limit_respected(limit):
     """A lower limit moves the longer short sequences back to the chunked
     steps: the chunk table holds exactly the sequences above the limit."""
     prob = small_problem(MIXED_LENS, H=4, P=64, G=2, N=128, seed=95, init="bernoulli")
-    with short_path(limit):
-        d, ws = gpu_run(prob)
+    d, ws = gpu_run(prob, limit)
     ref = oracle.recurrence(prob, want_pool=False)
     assert_y(y_host(d), ref["y"], f"limit {limit}")
     for b, slot in enumerate(prob["cache_indices"]):
@@ -194,8 +179,7 @@ def test_short_nan_slot_not_read():
     ci = prob["cache_indices"]
     prob["pool"][ci[0]] = np.nan
     prob["pool"][ci[2]] = np.nan
-    with short_path(binding.SHORT_PATH_LIMIT):
-        full_check(prob)
+    full_check(prob, binding.SHORT_PATH_LIMIT)
 
 
 @pytest.mark.parametrize("opt", ["no_D", "no_dt_bias", "no_has_init", "no_softplus"])
@@ -231,23 +215,25 @@ def test_intermediates_match_chunked_oracle():
     ncm = L["nchunks_max"]
     H, P, N = 4, 64, 128
     nch = int(w[L["meta"]:L["meta"] + 4].view(np.int32)[0])
-    assert nch == 3 + 0 + 1 + 1
+    assert nch == 3 + 0 + 1 + 1 <= ncm
     chunk_off = w[L["chunk_off"]:L["chunk_off"] + 5 * 4].view(np.int32)
     assert list(chunk_off) == [0, 3, 3, 4, 5]
-    desc = w[L["desc"]:L["desc"] + ncm * 16].view(np.int32).reshape(ncm, 4)
-    dts = w[L["dts"]:L["dts"] + ncm * H * 256 * 4].view(np.float32).reshape(ncm, H, 256)
-    cs2 = w[L["cs2"]:L["cs2"] + ncm * H * 256 * 4].view(np.float32).reshape(ncm, H, 256)
-    S16 = w[L["states"]:L["states"] + ncm * H * P * N * 2].view(np.float16).reshape(ncm, H, P, N)
-    sexp = w[L["sexp"]:L["sexp"] + ncm * H * 2 * (N // 32) * 4].view(np.int32).reshape(ncm, H, 2, N // 32)
+    # only the call's nch rows of each table were written: rows past them are
+    # left as the workspace held them and are not decoded
+    desc = w[L["desc"]:L["desc"] + ncm * 16].view(np.int32).reshape(ncm, 4)[:nch]
+    dts = w[L["dts"]:L["dts"] + ncm * H * 256 * 4].view(np.float32).reshape(ncm, H, 256)[:nch]
+    cs2 = w[L["cs2"]:L["cs2"] + ncm * H * 256 * 4].view(np.float32).reshape(ncm, H, 256)[:nch]
+    S16 = w[L["states"]:L["states"] + ncm * H * P * N * 2].view(np.float16).reshape(ncm, H, P, N)[:nch]
+    sexp = w[L["sexp"]:L["sexp"] + ncm * H * 2 * (N // 32) * 4].view(np.int32).reshape(ncm, H, 2, N // 32)[:nch]
     sfac = np.exp2(-sexp.astype(np.float64)).repeat(32, axis=2).repeat(32, axis=3)  # per element (p, n)
     S = S16.astype(np.float64) * sfac
-    hin16 = w[L["hin"]:L["hin"] + ncm * H * P * N * 2].view(np.float16).reshape(ncm, H, P, N)
-    hexp = w[L["hexp"]:L["hexp"] + ncm * H * P * 4].view(np.int32).reshape(ncm, H, P)
+    hin16 = w[L["hin"]:L["hin"] + ncm * H * P * N * 2].view(np.float16).reshape(ncm, H, P, N)[:nch]
+    hexp = w[L["hexp"]:L["hexp"] + ncm * H * P * 4].view(np.int32).reshape(ncm, H, P)[:nch]
     hin = hin16.astype(np.float64) * np.exp2(-hexp.astype(np.float64))[..., None]
-    cbt16 = w[L["cbt"]:L["cbt"] + ncm * 2 * 36 * 1024 * 2].view(np.float16).reshape(ncm, 2, 36, 64, 16)
-    gexp = w[L["gexp"]:L["gexp"] + ncm * 2 * 4].view(np.int32).reshape(ncm, 2)
+    cbt16 = w[L["cbt"]:L["cbt"] + ncm * 2 * 36 * 1024 * 2].view(np.float16).reshape(ncm, 2, 36, 64, 16)[:nch]
+    gexp = w[L["gexp"]:L["gexp"] + ncm * 2 * 4].view(np.int32).reshape(ncm, 2)[:nch]
     cbt = cbt16.astype(np.float64) * np.exp2(-gexp.astype(np.float64))[..., None, None, None]
-    xexp = w[L["xexp"]:L["xexp"] + ncm * H * 4].view(np.int32).reshape(ncm, H)
+    xexp = w[L["xexp"]:L["xexp"] + ncm * H * 4].view(np.int32).reshape(ncm, H)[:nch]
     ref = chunked_scan(prob, 256, keep_intermediates=True)["chunks"]
     qsl = prob["query_start_loc"]
     for rec in ref:
@@ -347,6 +333,97 @@ def test_split_carry_through_pool():
     assert_final(d2["pool"][slot].cpu().numpy(), full["final"][0], "split final")
 
 
+def test_short_limit_is_per_call():
+    """The short-path limit travels in each call's problem: two calls back to
+    back on one stream with different limits each route by their own limit
+    (the chunk count in the workspace) and each matches the oracle."""
+    prob = small_problem(MIXED_LENS, H=4, P=64, G=2, N=128, seed=96, init="bernoulli")
+    ref = oracle.recurrence(prob, want_pool=False)
+    d1 = torch_io.upload(prob, "cuda")
+    d2 = torch_io.upload(prob, "cuda")
+    ws1 = torch_io.run(d1, short_path_max=CHUNKED)
+    ws2 = torch_io.run(d2, short_path_max=40)  # enqueued right behind the first, no sync between
+    torch.cuda.synchronize()
+    for d, ws, limit in ((d1, ws1, 0), (d2, ws2, 40)):
+        assert_y(y_host(d), ref["y"], f"limit {limit}")
+        for b, slot in enumerate(prob["cache_indices"]):
+            assert_final(d["pool"][int(slot)].cpu().numpy(), ref["final"][b], f"limit {limit} seq {b}")
+        L = binding.ssd_workspace_get_layout(torch_io.problem_struct(d))
+        nch = int(ws.cpu().numpy()[L["meta"]:L["meta"] + 4].view(np.int32)[0])
+        assert nch == sum(-(-n // 256) for n in MIXED_LENS if n > limit), limit
+
+
+def test_canaries_around_outputs():
+    """y and the pool placed inside larger buffers whose margins hold a
+    canary pattern: no store of the call lands outside y's rows or the pool's
+    slots (the margins are compared bitwise after the call)."""
+    prob = small_problem([300, 0, 513, 17, 128], H=4, P=64, G=2, N=128, max_slots=7, seed=47, init="bernoulli")
+    d = torch_io.upload(prob, "cuda")
+    T, H, P = d["y"].shape
+    pad = 16  # tokens / slots of margin on each side
+    ybuf = torch.full((T + 2 * pad, H, P), -12345.0, dtype=torch.bfloat16, device="cuda")
+    d["y"] = ybuf[pad:pad + T]
+    S = d["pool"].shape[0]
+    pbuf = torch.full((S + 2,) + tuple(d["pool"].shape[1:]), 777.0, dtype=torch.float32, device="cuda")
+    pbuf[1:S + 1].copy_(d["pool"])
+    d["pool"] = pbuf[1:S + 1]
+    ycan, pcan = ybuf.clone(), pbuf.clone()
+    pool0 = d["pool"].clone()
+    ref = oracle.recurrence(prob, want_pool=False)
+    for sm in (DEFAULT, CHUNKED):
+        d["pool"].copy_(pool0)  # the call updates the pool in place: each run starts from the same states
+        torch_io.run(d, short_path_max=sm)
+        torch.cuda.synchronize()
+        assert torch.equal(bits(ybuf[:pad]), bits(ycan[:pad])) and torch.equal(bits(ybuf[pad + T:]),
+                                                                           bits(ycan[pad + T:])), sm
+        assert torch.equal(bits(pbuf[0]), bits(pcan[0])) and torch.equal(bits(pbuf[S + 1]), bits(pcan[S + 1])), sm
+        assert_y(y_host(d), ref["y"], f"canary run, short_path_max {sm}")
+
+
+@pytest.mark.parametrize("short_max", [DEFAULT, CHUNKED])
+def test_batch_permutation_bitwise(short_max):
+    """Permuting the sequences together with their cache_indices and
+    has_initial_state permutes the y rows and moves nothing else: each
+    sequence's y rows and final state are bit-identical in both orders."""
+    prob = small_problem([300, 45, 0, 513, 96, 1], H=4, P=64, G=2, N=128, max_slots=9, seed=48, init="bernoulli")
+    perm = [3, 0, 5, 2, 4, 1]
+    q = sub_batch(prob, perm)
+    d1, _ = gpu_run(prob, short_max)
+    d2, _ = gpu_run(q, short_max)
+    qa, qb = prob["query_start_loc"], q["query_start_loc"]
+    for i, b in enumerate(perm):
+        assert torch.equal(bits(d1["y"][qa[b]:qa[b + 1]]), bits(d2["y"][qb[i]:qb[i + 1]])), b
+    assert torch.equal(bits(d1["pool"]), bits(d2["pool"]))
+
+
+def test_subnormal_initial_states():
+    """Initial states whose rows are fp32 subnormals (1e-40), and a chunk of
+    zero x after strong decay: the power-of-two scalings of the state rows
+    must stay finite, and y and the final states match the oracle (the final
+    states may carry the subnormal range's coarser rounding: a few units of
+    2^-149 on top of the relative bar)."""
+    for N, sm in ((128, DEFAULT), (128, CHUNKED), (256, DEFAULT)):
+        prob = small_problem([700, 40, 300], H=2, P=64, G=1, N=N, max_slots=4, seed=49, init="all")
+        ci = prob["cache_indices"]
+        prob["pool"][ci[0]] = np.float32(1e-40)
+        prob["pool"][ci[1]] = np.float32(-3e-41)
+        # the third sequence: x zero on its second half, A strongly negative
+        T = prob["total_len"]
+        x = bf16_to_f64(prob["x"]).reshape(T, 2, 64)
+        x[740 + 150:] = 0.0
+        prob["x"] = bf16(x)
+        prob["A"] = np.array([-16.0, -1.0], np.float32)
+        d, _ = gpu_run(prob, sm)
+        ref = oracle.recurrence(prob, want_pool=False)
+        assert_y(y_host(d), ref["y"], f"N {N} short_max {sm}")
+        for b, slot in enumerate(ci):
+            got = d["pool"][int(slot)].cpu().numpy().astype(np.float64)
+            want = ref["final"][b]
+            err = np.linalg.norm(got - want)
+            assert np.all(np.isfinite(got))
+            assert err <= 1e-3 * np.linalg.norm(want) + 8 * 2.0 ** -149 * math.sqrt(got.size), (N, sm, b, err)
+
+
 def test_validate_inputs_on_device():
     prob = small_problem([10, 20], H=2, P=64, G=1, N=64, max_slots=4, seed=45)
     d = torch_io.upload(prob, "cuda")
@@ -428,30 +505,23 @@ def test_separate_states_aliased_buffer():
     assert torch.equal(fin.view(torch.int32), fin2.view(torch.int32))
 
 
-@pytest.mark.parametrize("name,seqs", [
-    ("fixed_4x4096_h16_n256", (1, 2)),
-    ("long_8x16384_h16_n256", (2, 4)),
-    # 24..29: walked by the state chain's workgroups as their second item (the
-    # ragged workload has more chain items than the grid has workgroups), and
-    # one short sequence
-    ("ragged_32_h128_g8_n128", [(0, 6), (24, 30)]),
-    ("short_512_h128_g8_n128", (100, 164)),
+@pytest.mark.parametrize("name,short_max", [
+    ("fixed_4x4096_h16_n256", DEFAULT),
+    ("long_8x16384_h16_n256", DEFAULT),
+    ("ragged_32_h128_g8_n128", DEFAULT),
+    # the same batch with every sequence through the chunked steps: the
+    # state chain then walks the whole batch, short sequences included
+    ("ragged_32_h128_g8_n128", CHUNKED),
+    ("short_512_h128_g8_n128", DEFAULT),
+    ("decode_512_h128_g8_n128", DEFAULT),
 ])
-def test_workloads_full_size_sampled(name, seqs):
+def test_workloads_full_size(name, short_max):
+    """Every sequence of the full-size workloads against the fp64 oracle (y
+    elementwise, every written slot, every other slot bitwise)."""
     prob = make_workload(name)
-    print(f"\n{name}: T={prob['total_len']} batch={prob['batch']} checking sequences {seqs}", flush=True)
-    wy, wf = full_check(prob, seqs=seqs)
-    print(f"{name}: y worst/bound {wy:.3f}  final rel {wf:.2e}", flush=True)
-
-
-def test_ragged_chunked_route_second_items():
-    """With the short path off, the state chain walks the whole batch (not a
-    list): on the ragged workload it has more items than workgroups, and
-    sequences 24..29 are second items of theirs."""
-    prob = make_workload("ragged_32_h128_g8_n128")
-    with short_path(0):
-        wy, wf = full_check(prob, seqs=(24, 30))
-    print(f"ragged, every sequence chunked: y worst/bound {wy:.3f}  final rel {wf:.2e}", flush=True)
+    print(f"\n{name} (short_path_max {short_max}): T={prob['total_len']} batch={prob['batch']}", flush=True)
+    wy, wf = full_check(prob, short_max)
+    print(f"{name}: every sequence: y worst/bound {wy:.3f}  final rel {wf:.2e}", flush=True)
 
 
 # ------------------------------------------------- bf16 state storage
@@ -467,8 +537,7 @@ def test_bf16_states_match_oracle(name):
     }[name]
     lens = spec.pop("seqlens")
     prob = small_problem(lens, P=64, seed=300 + len(name), state_dtype="bf16", **spec)
-    with short_path(binding.SHORT_PATH_LIMIT):
-        full_check(prob)
+    full_check(prob, binding.SHORT_PATH_LIMIT)
 
 
 @pytest.mark.parametrize("route", ["default", "chunked"])
@@ -481,9 +550,9 @@ def test_bf16_states_are_rounded_fp32_results(route):
     pb = with_bf16_states(prob)
     pf = clone(prob)
     pf["pool"] = bf16_to_f64(pb["pool"]).astype(np.float32)  # exactly the bf16 values
-    with short_path(binding.SHORT_PATH_LIMIT if route == "default" else 0):
-        df, _ = gpu_run(pf)
-        db, _ = gpu_run(pb)
+    sm = DEFAULT if route == "default" else CHUNKED
+    df, _ = gpu_run(pf, sm)
+    db, _ = gpu_run(pb, sm)
     assert torch.equal(bits(db["y"]), bits(df["y"]))
     assert torch.equal(bits(db["pool"]), bits(df["pool"].to(torch.bfloat16)))
 
@@ -495,8 +564,7 @@ def test_bf16_states_separate_entry():
     init_exact = init_b.float().numpy()
     d = torch_io.upload(prob, "cuda")
     fin = torch.full(init_b.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
-    with short_path(binding.SHORT_PATH_LIMIT):
-        torch_io.run_fwd(d, init_b.cuda(), fin)
+    torch_io.run_fwd(d, init_b.cuda(), fin, short_path_max=binding.SHORT_PATH_LIMIT)
     torch.cuda.synchronize()
     ref = oracle.recurrence_separate(prob, init_exact)
     assert_y(y_host(d), ref["y"], "bf16 separate")
@@ -506,11 +574,12 @@ def test_bf16_states_separate_entry():
     assert torch.equal(bits(fin[1].cpu()), bits(init_b[1]))  # zero-length: the initial state
 
 
-def test_bf16_states_short_workload_sampled():
+@pytest.mark.parametrize("name", ["short_512_h128_g8_n128", "decode_512_h128_g8_n128"])
+def test_bf16_states_workloads_full_size(name):
     from mamba_ssd_chunked_chunk_amd.workloads import with_bf16_states
-    prob = with_bf16_states(make_workload("short_512_h128_g8_n128"))
-    wy, wf = full_check(prob, seqs=(200, 240))
-    print(f"short workload, bf16 states: y worst/bound {wy:.3f}  final rel {wf:.2e}", flush=True)
+    prob = with_bf16_states(make_workload(name))
+    wy, wf = full_check(prob)
+    print(f"{name}, bf16 states, every sequence: y worst/bound {wy:.3f}  final rel {wf:.2e}", flush=True)
 
 
 # ------------------------------------------- token recurrence (decode steps)
@@ -522,8 +591,7 @@ def test_recur_path_lengths(N, state_dtype):
     without initial states, against the oracle."""
     lens = [1, 2, 3, 4, 5, 6, 9, 0, 1, 4]
     prob = small_problem(lens, H=4, P=64, G=2, N=N, seed=400 + N, init="bernoulli", state_dtype=state_dtype)
-    with short_path(binding.SHORT_PATH_LIMIT):
-        full_check(prob)
+    full_check(prob, binding.SHORT_PATH_LIMIT)
 
 
 def test_recur_limit_follows_short_limit():
@@ -531,24 +599,13 @@ def test_recur_limit_follows_short_limit():
     the chunked steps the rest (the chunk count checked)."""
     lens = [1, 2, 3, 8, 30]
     prob = small_problem(lens, H=4, P=64, G=1, N=128, seed=410, init="all")
-    with short_path(2):
-        d, ws = gpu_run(prob)
+    d, ws = gpu_run(prob, 2)
     ref = oracle.recurrence(prob, want_pool=False)
     assert_y(y_host(d), ref["y"], "limit 2")
     for b, slot in enumerate(prob["cache_indices"]):
         assert_final(d["pool"][int(slot)].cpu().numpy(), ref["final"][b], f"seq {b}")
     L = binding.ssd_workspace_get_layout(torch_io.problem_struct(d))
     assert int(ws.cpu().numpy()[L["meta"]:L["meta"] + 4].view(np.int32)[0]) == 3
-
-
-@pytest.mark.parametrize("state_dtype", ["f32", "bf16"])
-def test_decode_workload_sampled(state_dtype):
-    from mamba_ssd_chunked_chunk_amd.workloads import with_bf16_states
-    prob = make_workload("decode_512_h128_g8_n128")
-    if state_dtype == "bf16":
-        prob = with_bf16_states(prob)
-    wy, wf = full_check(prob, seqs=(100, 164))
-    print(f"decode workload ({state_dtype} states): y worst/bound {wy:.3f}  final rel {wf:.2e}", flush=True)
 
 
 # ------------------------------------------------------- HIP graph capture
@@ -563,27 +620,55 @@ def test_graph_capture_replays_match_eager(N, lens):
     d = torch_io.upload(prob, "cuda")
     pool0 = d["pool"].clone()
     ws = torch.empty(binding.ssd_workspace_size(torch_io.problem_struct(d)), dtype=torch.uint8, device="cuda")
-    with short_path(binding.SHORT_PATH_LIMIT):
-        torch_io.run(d, ws)
-        torch.cuda.synchronize()
-        y_ref, pool_ref = d["y"].clone(), d["pool"].clone()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):  # warm-up on the capture stream
-            d["pool"].copy_(pool0)
-            torch_io.run(d, ws)
-        torch.cuda.current_stream().wait_stream(s)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
+    sm = binding.SHORT_PATH_LIMIT
+    torch_io.run(d, ws, short_path_max=sm)
+    torch.cuda.synchronize()
+    y_ref, pool_ref = d["y"].clone(), d["pool"].clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm-up on the capture stream
+        d["pool"].copy_(pool0)
+        torch_io.run(d, ws, short_path_max=sm)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    d["pool"].copy_(pool0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        torch_io.run(d, ws, short_path_max=sm)
+    for rep in range(3):
+        d["y"].zero_()
         d["pool"].copy_(pool0)
         torch.cuda.synchronize()
-        with torch.cuda.graph(g):
-            torch_io.run(d, ws)
-        for rep in range(3):
-            d["y"].zero_()
-            d["pool"].copy_(pool0)
-            torch.cuda.synchronize()
-            g.replay()
-            torch.cuda.synchronize()
-            assert torch.equal(bits(d["y"]), bits(y_ref)), f"replay {rep}: y differs"
-            assert torch.equal(bits(d["pool"]), bits(pool_ref)), f"replay {rep}: pool differs"
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bits(d["y"]), bits(y_ref)), f"replay {rep}: y differs"
+        assert torch.equal(bits(d["pool"]), bits(pool_ref)), f"replay {rep}: pool differs"
+
+
+# ------------------------------------- random tiny shapes (property test, GPU)
+
+try:
+    from hypothesis import given, settings, strategies as st
+    HAVE_HYPOTHESIS = True
+except ImportError:  # pragma: no cover
+    HAVE_HYPOTHESIS = False
+
+if HAVE_HYPOTHESIS:
+    @settings(max_examples=24, deadline=None, derandomize=True, database=None)
+    @given(lens=st.lists(st.one_of(st.integers(0, 8), st.integers(0, 700)), min_size=1, max_size=5),
+           shape=st.sampled_from([(2, 1, 64), (4, 2, 64), (4, 4, 128), (8, 2, 128), (2, 1, 256), (4, 1, 256)]),
+           init=st.sampled_from(["none", "all", "bernoulli"]),
+           short_max=st.sampled_from([DEFAULT, CHUNKED, 1, 4, 33, 128]),
+           state_dtype=st.sampled_from(["f32", "f32", "bf16"]),
+           seed=st.integers(0, 2 ** 31 - 1))
+    def test_random_tiny_shapes(lens, shape, init, short_max, state_dtype, seed):
+        """A bounded number of random small problems (ragged lengths with
+        empty and single-token sequences, every supported dstate, groups,
+        initial states, short-path limits, state storage types) through the
+        C ABI against the fp64 oracle."""
+        H, G, N = shape
+        prob = small_problem(lens, H=H, P=64, G=G, N=N, seed=seed, init=init, state_dtype=state_dtype)
+        print(f"random case: lens={lens} H={H} G={G} N={N} init={init} short_max={short_max} "
+              f"states={state_dtype} seed={seed}", flush=True)
+        full_check(prob, short_max)

@@ -406,3 +406,77 @@ def test_chunked_intermediates_chain():
     rec = oracle.recurrence(prob)
     np.testing.assert_allclose(math.exp(ch[2]["cs"][-1]) * ch[2]["h_in"] + ch[2]["S"],
                                rec["final"][0, 0], rtol=1e-10)
+
+
+# ------------------------------------------------- bf16 state storage (widening)
+
+def test_bf16_pool_widening_by_hand():
+    """A pool stored as bf16 bit patterns is read as the exact values those
+    patterns encode: 0x3FC0 is 1.5 and 0xBFC0 is -1.5 (sign, exponent 127,
+    one fraction bit), 0x0001 is the smallest bf16 subnormal 2^-133.  With
+    B = 0 and one token, the final state is exp(A dts) h0 and y = C.h1 + D x,
+    worked out here from those values."""
+    prob = small_problem([1], H=1, P=2, G=1, N=3, max_slots=2, seed=63, init="all", state_dtype="bf16")
+    slot = int(prob["cache_indices"][0])
+    pool = np.zeros((2, 1, 2, 3), np.uint16)
+    pool[slot, 0] = [[0x3FC0, 0xBFC0, 0x0001], [0x0000, 0x4040, 0xC000]]   # 1.5 -1.5 2^-133 / 0 3 -2
+    prob["pool"] = pool
+    prob["B"] = bf16(np.zeros((1, 1, 3)))
+    h0 = np.array([[1.5, -1.5, 2.0 ** -133], [0.0, 3.0, -2.0]])
+    dts = softplus(np.float64(prob["dt"][0, 0]) + np.float64(prob["dt_bias"][0]))
+    h1 = math.exp(float(prob["A"][0]) * dts) * h0
+    x = bf16_to_f64(prob["x"]).reshape(2)
+    Cv = bf16_to_f64(prob["C"]).reshape(3)
+    out = oracle.recurrence(prob, want_pool=False)
+    np.testing.assert_allclose(out["final"][0, 0], h1, rtol=1e-14, atol=0)
+    np.testing.assert_allclose(out["y"].reshape(2), h1 @ Cv + float(prob["D"][0]) * x, rtol=1e-13)
+
+
+def test_bf16_pool_equals_its_fp32_values():
+    """The bf16-storage problem gives the same y and final states as the fp32
+    problem whose pool holds exactly the bf16 values (widened here by
+    placing the 16 bits above 16 zero bits of an fp32 word), bitwise."""
+    prob = small_problem([40, 0, 300], H=2, P=4, G=1, N=8, max_slots=5, seed=64, init="bernoulli",
+                         state_dtype="bf16")
+    pf = clone(prob)
+    pf["pool"] = (prob["pool"].astype(np.uint32) << np.uint32(16)).view(np.float32)
+    pf["state_dtype"] = "f32"
+    a = oracle.recurrence(prob, want_pool=False)
+    b = oracle.recurrence(pf, want_pool=False)
+    assert np.array_equal(a["y"], b["y"]) and np.array_equal(a["final"], b["final"])
+
+
+# ----------------------------------------- random tiny shapes (property test)
+
+try:
+    from hypothesis import given, settings, strategies as st
+    HAVE_HYPOTHESIS = True
+except ImportError:  # pragma: no cover
+    HAVE_HYPOTHESIS = False
+
+
+if HAVE_HYPOTHESIS:
+    @settings(max_examples=60, deadline=None, derandomize=True, database=None)
+    @given(lens=st.lists(st.integers(0, 40), min_size=1, max_size=4),
+           hg=st.sampled_from([(1, 1), (2, 1), (2, 2), (4, 2)]),
+           P=st.integers(1, 3), N=st.integers(1, 5), chunk=st.integers(1, 50),
+           init=st.sampled_from(["none", "all", "bernoulli"]), softplus_on=st.booleans(),
+           seed=st.integers(0, 2 ** 31 - 1))
+    def test_random_tiny_shapes_chunked_equals_recurrence(lens, hg, P, N, chunk, init, softplus_on, seed):
+        """On random tiny shapes (ragged lengths with empty sequences, random
+        chunk sizes, groups, initial states, both dt settings) the chunked
+        formulation agrees with the per-token recurrence to fp64 rounding,
+        and every pool slot outside cache_indices keeps its bits."""
+        H, G = hg
+        prob = small_problem(lens, H=H, P=P, G=G, N=N, seed=seed, init=init, dt_softplus=softplus_on)
+        if not softplus_on:  # keep dts >= 0 so the decays stay decays
+            prob["dt"] = np.abs(prob["dt"]) * np.float32(0.1)
+            prob["dt_bias"] = np.full_like(prob["dt_bias"], 0.01)
+        rec = oracle.recurrence(prob)
+        ch = chunked_scan(prob, chunk)
+        assert max_rel(ch["y"], rec["y"]) <= 1e-10
+        assert max_rel(ch["final"], rec["final"]) <= 1e-10
+        written = set(int(c) for c in prob["cache_indices"])
+        for s in range(prob["pool"].shape[0]):
+            if s not in written:
+                assert np.array_equal(rec["pool"][s].view(np.uint32), prob["pool"][s].view(np.uint32))
