@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 13
+#define SSD_ABI_VERSION 14
 #define SSD_MAX_DSTATE 256  /* largest dstate, as in "mamba2_ssd_scan", comptime MAX_DSTATE */
 #define SSD_SHORT_PATH_LIMIT 128  /* longest sequence the short path can take */
 #define SSD_RECUR_LIMIT 4         /* of those, the longest the token recurrence takes */
@@ -74,7 +74,10 @@ typedef enum ssd_status {
     SSD_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than required         */
     SSD_ERR_BAD_INPUT = 5,    /* ssd_validate_inputs found a violated precondition */
     SSD_ERR_HIP = 6,          /* a HIP runtime call or kernel launch failed       */
-    SSD_ERR_MISALIGNED = 7    /* a tensor pointer breaks the alignment rule above */
+    SSD_ERR_MISALIGNED = 7,   /* a tensor pointer breaks the alignment rule above */
+    SSD_ERR_SCRATCH = 8       /* the problem needs more scratch than the
+                               * no-allocation entry point holds
+                               * (SSD_NOALLOC_SCRATCH_BYTES)                  */
 } ssd_status;
 
 /* Problem sizes.  Dense row-major tensors:
@@ -293,6 +296,29 @@ ssd_status ssd_chunk_scan_varlen_fwd_profiled(
     const int32_t *query_start_loc,
     void *workspace, size_t workspace_bytes, void *stream,
     void *const *events, int n_events);
+
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * operation as ssd_chunk_scan_varlen_fwd_inplace (same arguments, minus the
+ * workspace), whose intermediates go to a scratch array that the library
+ * holds in device memory instead: SSD_NOALLOC_SCRATCH_BYTES per GPU it runs
+ * on, kept until the process ends.  The call allocates nothing (no hipMalloc,
+ * no allocating library routine); its first call on a device looks up that
+ * device's copy of the array once.  It runs on the current device; `stream`
+ * must belong to it.  Problems whose ssd_workspace_size() exceeds
+ * SSD_NOALLOC_SCRATCH_BYTES give SSD_ERR_SCRATCH before any launch (other
+ * errors as for the in-place entry point).  Every call on one GPU shares
+ * that GPU's array and leaves its intermediates there: calls on one stream
+ * are ordered, but calls that can overlap on one GPU (other streams, other
+ * host threads without ordering) race on it and must not be issued.       */
+#define SSD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+ssd_status ssd_chunk_scan_varlen_fwd_inplace_noalloc(
+    const ssd_problem *prob,
+    void *y, const void *x, const float *dt, const float *A,
+    const void *B, const void *C, const float *D, const float *dt_bias,
+    void *ssm_pool, const int32_t *query_start_loc,
+    const uint8_t *has_initial_state, const uint32_t *cache_indices,
+    void *stream);
 
 /* Synchronous debug check of the device-side preconditions: copies
  * query_start_loc and cache_indices to the host (after synchronising

@@ -18,13 +18,15 @@ LIB_PATH = os.path.join(_PKG, "libssd.so")
 
 SSD_OK = 0
 STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_NULL_ARG", 2: "SSD_ERR_BAD_SHAPE", 3: "SSD_ERR_UNSUPPORTED",
-                4: "SSD_ERR_WORKSPACE", 5: "SSD_ERR_BAD_INPUT", 6: "SSD_ERR_HIP", 7: "SSD_ERR_MISALIGNED"}
+                4: "SSD_ERR_WORKSPACE", 5: "SSD_ERR_BAD_INPUT", 6: "SSD_ERR_HIP", 7: "SSD_ERR_MISALIGNED",
+                8: "SSD_ERR_SCRATCH"}
 
 # every symbol include/ssd.h declares
 EXPORTED = ("ssd_abi_version", "ssd_status_string", "ssd_workspace_size",
             "ssd_workspace_get_layout", "ssd_chunk_scan_varlen_fwd_inplace",
             "ssd_kernel_count", "ssd_kernel_name", "ssd_chunk_scan_varlen_fwd_inplace_profiled",
-            "ssd_chunk_scan_varlen_fwd", "ssd_chunk_scan_varlen_fwd_profiled", "ssd_validate_inputs")
+            "ssd_chunk_scan_varlen_fwd", "ssd_chunk_scan_varlen_fwd_profiled", "ssd_validate_inputs",
+            "ssd_chunk_scan_varlen_fwd_inplace_noalloc")
 
 
 class SsdError(RuntimeError):
@@ -55,7 +57,8 @@ _lock = threading.Lock()
 _lib = None
 
 # SSD_ABI_VERSION of include/ssd.h that the ctypes structures below mirror
-ABI_VERSION = 13
+ABI_VERSION = 14
+NOALLOC_SCRATCH_BYTES = 64 << 20  # SSD_NOALLOC_SCRATCH_BYTES
 STATE_F32, STATE_BF16 = 0, 1  # SSD_STATE_F32, SSD_STATE_BF16
 SHORT_PATH_LIMIT = 128  # SSD_SHORT_PATH_LIMIT
 SHORT_PATH_DEFAULT = -1  # ssd_problem.short_path_max: any negative value selects SHORT_PATH_LIMIT
@@ -98,6 +101,8 @@ def load_library():
             lib.ssd_chunk_scan_varlen_fwd_profiled.restype = ctypes.c_int
             lib.ssd_chunk_scan_varlen_fwd_profiled.argtypes = (
                 [PP] + [V] * 12 + [ctypes.c_size_t, V, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int])
+            lib.ssd_chunk_scan_varlen_fwd_inplace_noalloc.restype = ctypes.c_int
+            lib.ssd_chunk_scan_varlen_fwd_inplace_noalloc.argtypes = [PP] + [V] * 12 + [V]
             lib.ssd_validate_inputs.restype = ctypes.c_int
             lib.ssd_validate_inputs.argtypes = [PP, V, V, V]
             _lib = lib
@@ -242,6 +247,54 @@ def ssd_chunk_scan_varlen_fwd_inplace(y, x, dt, A, B, C, D, dt_bias, ssm_pool, q
         ctypes.c_void_p(st.cuda_stream))
     _check(status, "ssd_chunk_scan_varlen_fwd_inplace")
     return workspace
+
+
+def ssd_chunk_scan_varlen_fwd_inplace_noalloc(y, x, dt, A, B, C, D, dt_bias, ssm_pool, query_start_loc,
+                                              has_initial_state, cache_indices, *, dt_softplus=True,
+                                              short_path_max=SHORT_PATH_DEFAULT, stream=None):
+    """The in-place operation without a workspace argument: the library's
+    own scratch array (NOALLOC_SCRATCH_BYTES per GPU) holds the
+    intermediates, and nothing is allocated.  Same tensors and checks as
+    ssd_chunk_scan_varlen_fwd_inplace; calls that can overlap on one GPU race
+    on the shared scratch (one stream orders them)."""
+    import torch
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("libssd runs on a HIP device; got tensors on " + str(dev))
+    T, H, P = x.shape
+    if B.dim() != 3:
+        raise ValueError("B must be [T, G, N]")
+    G, N = B.shape[1], B.shape[2]
+    batch = query_start_loc.numel() - 1
+    S = ssm_pool.shape[0]
+    _need(y, "y", torch.bfloat16, (T, H, P), dev)
+    _need(x, "x", torch.bfloat16, (T, H, P), dev)
+    _need(dt, "dt", torch.float32, (T, H), dev)
+    _need(A, "A", torch.float32, (H,), dev)
+    _need(B, "B", torch.bfloat16, (T, G, N), dev)
+    _need(C, "C", torch.bfloat16, (T, G, N), dev)
+    D = _opt(D, "D", torch.float32, (H,), dev)
+    dt_bias = _opt(dt_bias, "dt_bias", torch.float32, (H,), dev)
+    sd = _state_dtype(ssm_pool, "ssm_pool")
+    _need(ssm_pool, "ssm_pool", ssm_pool.dtype, (S, H, P, N), dev)
+    _need(query_start_loc, "query_start_loc", torch.int32, (batch + 1,), dev)
+    if has_initial_state is not None and has_initial_state.numel() > 0:
+        if has_initial_state.dtype == torch.bool:
+            has_initial_state = has_initial_state.view(torch.uint8)
+        _need(has_initial_state, "has_initial_state", torch.uint8, (batch,), dev)
+    else:
+        has_initial_state = None
+    if cache_indices.dtype not in (torch.int32, torch.uint32):
+        raise TypeError("cache_indices must be int32 or uint32")
+    if tuple(cache_indices.shape) != (batch,) or not cache_indices.is_contiguous() or cache_indices.device != dev:
+        raise ValueError("cache_indices must be a contiguous [batch] tensor on the same device")
+    prob = make_problem(T, batch, H, P, G, N, S, dt_softplus, state_dtype=sd, short_path_max=short_path_max)
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    status = load_library().ssd_chunk_scan_varlen_fwd_inplace_noalloc(
+        ctypes.byref(prob), _ptr(y), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+        _ptr(dt_bias), _ptr(ssm_pool), _ptr(query_start_loc), _ptr(has_initial_state),
+        _ptr(cache_indices), ctypes.c_void_p(st.cuda_stream))
+    _check(status, "ssd_chunk_scan_varlen_fwd_inplace_noalloc")
 
 
 def ssd_chunk_scan_varlen_fwd(y, x, dt, A, B, C, D, dt_bias, initial_states, final_states,

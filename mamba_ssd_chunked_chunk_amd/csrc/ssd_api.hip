@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "ssd.h"
@@ -17,6 +18,16 @@
 namespace {
 
 constexpr size_t kAlign = 256;
+
+// Scratch of the no-allocation entry point: one copy per GPU, in device
+// memory for the life of the process.  Host code never uses this name as an
+// address (on the host it is a stand-in, not the device location): the
+// device address of the current GPU's copy comes from hipGetSymbolAddress,
+// once per device, and is kept in g_scratch.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[SSD_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -80,6 +91,9 @@ const char *ssd_status_string(int s) {
     case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE: workspace missing, misaligned or too small";
     case SSD_ERR_BAD_INPUT: return "SSD_ERR_BAD_INPUT: query_start_loc or cache_indices violate a precondition";
     case SSD_ERR_HIP: return "SSD_ERR_HIP: a HIP runtime call failed";
+    case SSD_ERR_SCRATCH:
+        return "SSD_ERR_SCRATCH: the problem needs more scratch than the no-allocation entry point holds "
+               "(SSD_NOALLOC_SCRATCH_BYTES)";
     case SSD_ERR_MISALIGNED:
         return "SSD_ERR_MISALIGNED: y, x, B, C or a state tensor is not 16-byte aligned, or dt, A, D, dt_bias, "
                "query_start_loc or cache_indices not 4-byte aligned";
@@ -123,11 +137,11 @@ struct StateIO {
     bool init_all;
 };
 
-static ssd_status run_scan(
-    const ssd_problem *prob, void *y, const void *x, const float *dt, const float *A,
-    const void *B, const void *C, const float *D, const float *dt_bias,
-    const int32_t *query_start_loc, const StateIO &sio, void *workspace, size_t workspace_bytes,
-    void *stream, void *const *events) {
+// Host checks of a compute call's problem and tensor pointers (everything but
+// the workspace): nothing here touches the device.
+static ssd_status check_call(const ssd_problem *prob, const void *y, const void *x, const float *dt,
+                             const float *A, const void *B, const void *C, const float *D, const float *dt_bias,
+                             const int32_t *query_start_loc, const StateIO &sio) {
     ssd_status st = check_problem(prob);
     if (st != SSD_OK) return st;
     const bool has_tokens = prob->total_len > 0;
@@ -139,6 +153,16 @@ static ssd_status run_scan(
         !aligned(sio.out, 16) || !aligned(sio.in, 16) || !aligned(dt, 4) || !aligned(A, 4) ||
         !aligned(D, 4) || !aligned(dt_bias, 4) || !aligned(query_start_loc, 4) || !aligned(sio.cache_idx, 4))
         return SSD_ERR_MISALIGNED;
+    return SSD_OK;
+}
+
+static ssd_status run_scan(
+    const ssd_problem *prob, void *y, const void *x, const float *dt, const float *A,
+    const void *B, const void *C, const float *D, const float *dt_bias,
+    const int32_t *query_start_loc, const StateIO &sio, void *workspace, size_t workspace_bytes,
+    void *stream, void *const *events) {
+    ssd_status st = check_call(prob, y, x, dt, A, B, C, D, dt_bias, query_start_loc, sio);
+    if (st != SSD_OK) return st;
     ssd_workspace_layout L;
     layout_of(prob, &L);
     if (workspace == nullptr || workspace_bytes < L.total_bytes || !aligned(workspace, kAlign))
@@ -239,6 +263,21 @@ static ssd_status inplace(const ssd_problem *prob, void *y, const void *x, const
                     stream, events);
 }
 
+// The current device's copy of the scratch array (looked up on its first use).
+static ssd_status scratch_address(void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SSD_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return SSD_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch[dev] == nullptr) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return SSD_ERR_HIP;
+        g_scratch[dev] = ptr;
+    }
+    *out = g_scratch[dev];
+    return SSD_OK;
+}
+
 static ssd_status separate(const ssd_problem *prob, void *y, const void *x, const float *dt, const float *A,
                            const void *B, const void *C, const float *D, const float *dt_bias,
                            const void *initial_states, void *final_states, const int32_t *query_start_loc,
@@ -266,6 +305,27 @@ ssd_status ssd_chunk_scan_varlen_fwd_inplace(
     const uint32_t *cache_indices, void *workspace, size_t workspace_bytes, void *stream) {
     return inplace(prob, y, x, dt, A, B, C, D, dt_bias, ssm_pool, query_start_loc, has_initial_state,
                    cache_indices, workspace, workspace_bytes, stream, nullptr);
+}
+
+ssd_status ssd_chunk_scan_varlen_fwd_inplace_noalloc(
+    const ssd_problem *prob, void *y, const void *x, const float *dt, const float *A,
+    const void *B, const void *C, const float *D, const float *dt_bias, void *ssm_pool,
+    const int32_t *query_start_loc, const uint8_t *has_initial_state,
+    const uint32_t *cache_indices, void *stream) {
+    // every host check first, so a rejected call touches no device state
+    if (ssm_pool == nullptr || cache_indices == nullptr) return SSD_ERR_NULL_ARG;
+    const StateIO sio{ssm_pool, ssm_pool, has_initial_state, cache_indices, false};
+    ssd_status st = check_call(prob, y, x, dt, A, B, C, D, dt_bias, query_start_loc, sio);
+    if (st != SSD_OK) return st;
+    size_t need = 0;
+    st = ssd_workspace_size(prob, &need);
+    if (st != SSD_OK) return st;
+    if (need > SSD_NOALLOC_SCRATCH_BYTES) return SSD_ERR_SCRATCH;
+    void *ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != SSD_OK) return st;
+    return inplace(prob, y, x, dt, A, B, C, D, dt_bias, ssm_pool, query_start_loc, has_initial_state,
+                   cache_indices, ws, SSD_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 ssd_status ssd_chunk_scan_varlen_fwd_inplace_profiled(

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert binding.ssd_abi_version() == binding.ABI_VERSION == 13
+    assert binding.ssd_abi_version() == binding.ABI_VERSION == 14
     for code, name in binding.STATUS_NAMES.items():
         assert lib.ssd_status_string(code).decode().startswith(name)
     assert b"unknown" in lib.ssd_status_string(99)
@@ -195,3 +195,23 @@ def test_short_path_limit_is_a_problem_field(lib):
     assert not hasattr(binding, "ssd_set_short_path_max")
     names = [lib.ssd_kernel_name(i).decode() for i in range(lib.ssd_kernel_count())]
     assert names == ["ssd_prep", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan", "ssd_short", "ssd_recur"]
+
+
+def test_noalloc_entry_host_errors(lib):
+    """The no-allocation entry point runs every host check before it looks up
+    its scratch: a problem whose workspace exceeds SSD_NOALLOC_SCRATCH_BYTES
+    gives SSD_ERR_SCRATCH, NULL and misaligned pointers their own statuses."""
+    f = lib.ssd_chunk_scan_varlen_fwd_inplace_noalloc
+    base = 1 << 20  # never dereferenced: every call below fails its host checks
+    args = [ctypes.c_void_p(base)] * 12
+    big = _prob(total_len=16384)  # the 4 x 4096, 16-head, dstate-256 problem
+    assert binding.ssd_workspace_size(big) > binding.NOALLOC_SCRATCH_BYTES
+    assert f(ctypes.byref(big), *args, None) == 8
+    assert lib.ssd_status_string(8).decode().startswith("SSD_ERR_SCRATCH")
+    assert f(None, *args, None) == 1
+    a = list(args)
+    a[8] = None  # ssm_pool
+    assert f(ctypes.byref(_prob()), *a, None) == 1
+    a = list(args)
+    a[1] = ctypes.c_void_p(base + 2)  # x
+    assert f(ctypes.byref(_prob()), *a, None) == 7
