@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 14
+#define SSD_ABI_VERSION 15
 #define SSD_MAX_DSTATE 256  /* largest dstate, as in "mamba2_ssd_scan", comptime MAX_DSTATE */
 #define SSD_SHORT_PATH_LIMIT 128  /* longest sequence the short path can take */
 #define SSD_RECUR_LIMIT 4         /* of those, the longest the token recurrence takes */
@@ -117,10 +117,12 @@ typedef struct ssd_problem {
 
 /* Offsets (bytes from the workspace base) and sizes of the intermediates the
  * compute entry point leaves in the workspace, so tests can compare each
- * step with the oracle.  nchunks_max = floor(total_len / 256) + batch bounds
- * the number of chunks; chunk c of the call occupies row c of each table.
- * Sequences taken by the short path (see ssd_problem.short_path_max; there
- * a zero-length sequence is taken as well) have no chunks: chunk_off[b] ==
+ * step with the oracle.  nchunks_max bounds the number of chunks the call can
+ * hold: floor(total_len / 256) plus the sequences the chunked steps can see
+ * (batch, or with the short path on at most total_len / (short_path_max + 1)
+ * of them); chunk c of the call occupies row c of each table.  Sequences
+ * taken by the short path (see ssd_problem.short_path_max; there a
+ * zero-length sequence is taken as well) have no chunks: chunk_off[b] ==
  * chunk_off[b+1] and no row of any table is theirs.
  *   meta      int32[4]                    {nchunks, nseq, nrecur, 0}: chunks,
  *                                         sequences the state chain walks,
@@ -137,20 +139,27 @@ typedef struct ssd_problem {
  *                                         each in MFMA accumulator order: lane
  *                                         l, element e holds j = 32t + 8(e/4)
  *                                         + 4(l/32) + e%4, i = 32rb + l%32;
- *                                         scaled by 2^gexp[c][g]; the
- *                                         diagonal tiles (t = rb) hold 0
- *                                         where j > i
- *   gexp      int32[nchunks_max][G]       exponent of each cbt block
- *   states    fp16[nchunks_max][H][P][N]  chunk's own state contribution,
- *                                         element (p, n) scaled by
- *                                         2^sexp[c][h][p/32][n/32]
- *   sexp      int32[nchunks_max][H][2][N/32]  exponent of each 32x32 tile
- *   hin       fp16[nchunks_max][H][P][N]  state entering the chunk, row p
- *                                         scaled by 2^hexp[c][h][p]
- *   hexp      int32[nchunks_max][H][P]    exponent of each hin row
- *   xexp      int32[nchunks_max][H]       2^xexp puts the chunk's largest |x|
- *                                         of the head in [2^14, 2^15) (0 if
- *                                         all zero)
+ *                                         scaled by 2^gexp[c][g][min(rb,
+ *                                         7-rb)]; the diagonal tiles (t = rb)
+ *                                         hold 0 where j > i
+ *   gexp      int32[nchunks_max][G][4]    exponent of the cbt tiles of row
+ *                                         blocks q and 7-q
+ *   bfrag     fp16[nchunks_max][G][N/32][16][64][8]  B^T of the chunk as MFMA
+ *                                         A operands: n tile nt, K-step s,
+ *                                         lane l holds B[t0 + 16s + 8(l/32)
+ *                                         + 0..7][g][32nt + l%32] (0 past the
+ *                                         chunk end), scaled by
+ *                                         2^bexp[c][g][nt]
+ *   bexp      int32[nchunks_max][G][N/32] exponent of each bfrag n tile
+ *   hin       fp16[nchunks_max][H][P][N]  state entering the chunk, element
+ *                                         (p, n) scaled by
+ *                                         2^hexp[c][h][n/32][p/32]
+ *   hexp      int16[nchunks_max][H][N/32][2]  exponent of each 32x32 tile
+ *                                         (126 for an all-zero tile)
+ *   xexp      int32[nchunks_max][H][2]    2^xexp[c][h][i] puts the chunk's
+ *                                         largest |x| over p = 32i .. 32i+31
+ *                                         of the head in [2^14, 2^15) (1000
+ *                                         if all zero)
  *   seq_list  int32[batch]                the nseq sequences the state chain
  *                                         walks, in order (all of them when
  *                                         no sequence can take the short
@@ -162,7 +171,7 @@ typedef struct ssd_problem {
 typedef struct ssd_workspace_layout {
     size_t total_bytes;
     int64_t nchunks_max;
-    size_t meta, chunk_off, desc, dts, cs2, cbt, gexp, states, sexp, hin, hexp, xexp, seq_list, recur_list;
+    size_t meta, chunk_off, desc, dts, cs2, cbt, gexp, bfrag, bexp, hin, hexp, xexp, seq_list, recur_list;
 } ssd_workspace_layout;
 
 /* ABI version of the loaded library (SSD_ABI_VERSION it was built with). */

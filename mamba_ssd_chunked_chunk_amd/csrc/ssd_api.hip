@@ -47,13 +47,34 @@ ssd_status check_problem(const ssd_problem *p) {
     if (p->chunk_size != 0 && p->chunk_size != ssd::kChunk) return SSD_ERR_UNSUPPORTED;
     if (p->short_path_max > SSD_SHORT_PATH_LIMIT) return SSD_ERR_UNSUPPORTED;
     if (p->nheads > 65535) return SSD_ERR_UNSUPPORTED;  // grid y limit
-    const int64_t ncm = p->total_len / ssd::kChunk + p->batch;
+    const int64_t ncm = p->total_len / ssd::kChunk + p->batch;  // bounds every routing's chunk count
     if (ncm > INT32_MAX) return SSD_ERR_UNSUPPORTED;
     return SSD_OK;
 }
 
+// Longest sequence the short path takes in this call (0: none; the path
+// serves dstate 64 and 128 only).
+int short_max_of(const ssd_problem *p) {
+    if (p->dstate > 128) return 0;
+    return p->short_path_max < 0 ? ssd::kShortMax : p->short_path_max;
+}
+
+// Sequences the chunked steps can see at most, and chunks they can hold: with
+// the short path on, only sequences longer than its limit reach them, at most
+// T / (limit + 1) of them, each with at most one partial chunk beyond
+// floor(T / 256) full ones (at least 1 each: a grid dimension cannot be 0,
+// and prep's first workgroup publishes the chunk count and the lists).
+void routed_bounds(const ssd_problem *p, int *nseq, int64_t *nchunks) {
+    const int sm = short_max_of(p);
+    const int64_t T = p->total_len;
+    *nseq = sm > 0 ? (int)std::max<int64_t>(1, std::min<int64_t>(p->batch, T / (sm + 1))) : p->batch;
+    *nchunks = std::max<int64_t>(1, T / ssd::kChunk + *nseq);
+}
+
 void layout_of(const ssd_problem *p, ssd_workspace_layout *L) {
-    const int64_t ncm = p->total_len / ssd::kChunk + p->batch;
+    int nseq;
+    int64_t ncm;
+    routed_bounds(p, &nseq, &ncm);
     const size_t H = (size_t)p->nheads, G = (size_t)p->ngroups;
     const size_t PN = (size_t)p->head_dim * (size_t)p->dstate;
     size_t off = 0;
@@ -65,12 +86,12 @@ void layout_of(const ssd_problem *p, ssd_workspace_layout *L) {
     L->dts = off;       off = align_up(off + (size_t)ncm * H * ssd::kChunk * sizeof(float));
     L->cs2 = off;       off = align_up(off + (size_t)ncm * H * ssd::kChunk * sizeof(float));
     L->cbt = off;       off = align_up(off + (size_t)ncm * G * 36 * 64 * 16 * sizeof(uint16_t));
-    L->gexp = off;      off = align_up(off + (size_t)ncm * G * sizeof(int32_t));
-    L->states = off;    off = align_up(off + (size_t)ncm * H * PN * sizeof(uint16_t));
-    L->sexp = off;      off = align_up(off + (size_t)ncm * H * 2 * ((size_t)p->dstate / 32) * sizeof(int32_t));
+    L->gexp = off;      off = align_up(off + (size_t)ncm * G * 4 * sizeof(int32_t));
+    L->bfrag = off;     off = align_up(off + (size_t)ncm * G * (size_t)p->dstate * ssd::kChunk * sizeof(uint16_t));
+    L->bexp = off;      off = align_up(off + (size_t)ncm * G * ((size_t)p->dstate / 32) * sizeof(int32_t));
     L->hin = off;       off = align_up(off + (size_t)ncm * H * PN * sizeof(uint16_t));
-    L->hexp = off;      off = align_up(off + (size_t)ncm * H * (size_t)p->head_dim * sizeof(int32_t));
-    L->xexp = off;      off = align_up(off + (size_t)ncm * H * sizeof(int32_t));
+    L->hexp = off;      off = align_up(off + (size_t)ncm * H * 2 * ((size_t)p->dstate / 32) * sizeof(int16_t));
+    L->xexp = off;      off = align_up(off + (size_t)ncm * H * 2 * sizeof(int32_t));
     L->seq_list = off;  off = align_up(off + (size_t)p->batch * sizeof(int32_t));
     L->recur_list = off; off = align_up(off + (size_t)p->batch * sizeof(int32_t));
     L->total_bytes = off;
@@ -119,10 +140,10 @@ ssd_status ssd_workspace_get_layout(const ssd_problem *prob, ssd_workspace_layou
     return SSD_OK;
 }
 
-static const char *const kKernelNames[] = {"ssd_prep",       "ssd_chunk_state", "ssd_state_passing",
-                                           "ssd_chunk_scan", "ssd_short",       "ssd_recur"};
-static constexpr int kNumKernels = 6;
-static constexpr int kFirstShortKernel = 4;  // this and the later ones serve the short path
+static const char *const kKernelNames[] = {"ssd_prep", "ssd_state_chain", "ssd_chunk_scan", "ssd_short",
+                                           "ssd_recur"};
+static constexpr int kNumKernels = 5;
+static constexpr int kFirstShortKernel = 3;  // this and the later ones serve the short path
 
 int ssd_kernel_count(void) { return kNumKernels; }
 
@@ -204,37 +225,29 @@ static ssd_status run_scan(
     // the short path serves dstate 64 and 128; the route of a sequence
     // depends on its own length only, so its results do not depend on the
     // rest of the batch
-    p.short_max = p.N <= 128 ? (prob->short_path_max < 0 ? ssd::kShortMax : prob->short_path_max) : 0;
+    p.short_max = short_max_of(prob);
     p.recur_max = std::min(p.short_max, ssd::kRecurMax);
-    // with the short path on, only sequences longer than its limit reach the
-    // chunked steps: at most T / (short_max + 1) of them, with at most
-    // T / 256 + that many chunks; the launches are sized to these bounds
-    // (at least 1 each: a grid dimension cannot be 0, and prep's first
-    // workgroup publishes the chunk count and the sequence list)
-    p.nseq_grid = p.short_max > 0 ? (int)std::max<int64_t>(1, std::min<int64_t>(p.batch, p.T / (p.short_max + 1)))
-                                  : p.batch;
-    p.nchunks_grid = p.short_max > 0
-                         ? std::max<int64_t>(1, std::min<int64_t>(L.nchunks_max, p.T / ssd::kChunk + p.nseq_grid))
-                         : L.nchunks_max;
+    // the launches are sized to the bounds on what the routing lets reach the
+    // chunked steps (the workspace tables have that many rows)
+    routed_bounds(prob, &p.nseq_grid, &p.nchunks_grid);
     p.meta = reinterpret_cast<int32_t *>(ws + L.meta);
     p.chunk_off = reinterpret_cast<int32_t *>(ws + L.chunk_off);
     p.desc = reinterpret_cast<int4 *>(ws + L.desc);
     p.dts = reinterpret_cast<float *>(ws + L.dts);
     p.cs2 = reinterpret_cast<float *>(ws + L.cs2);
-    p.hexp = reinterpret_cast<int32_t *>(ws + L.hexp);
+    p.hexp = reinterpret_cast<int16_t *>(ws + L.hexp);
     p.xexp = reinterpret_cast<int32_t *>(ws + L.xexp);
     p.seq_list = reinterpret_cast<int32_t *>(ws + L.seq_list);
     p.recur_list = reinterpret_cast<int32_t *>(ws + L.recur_list);
     p.cbt = reinterpret_cast<uint16_t *>(ws + L.cbt);
     p.gexp = reinterpret_cast<int32_t *>(ws + L.gexp);
-    p.states = reinterpret_cast<uint16_t *>(ws + L.states);
-    p.sexp = reinterpret_cast<int32_t *>(ws + L.sexp);
+    p.bfrag = reinterpret_cast<uint16_t *>(ws + L.bfrag);
+    p.bexp = reinterpret_cast<int32_t *>(ws + L.bexp);
     p.hin = reinterpret_cast<uint16_t *>(ws + L.hin);
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t (*const launchers[kNumKernels])(const ssd::Params &, const ssd::Launch &) = {
-        ssd::launch_prep, ssd::launch_chunk_state, ssd::launch_state_passing, ssd::launch_chunk_scan,
-        ssd::launch_short, ssd::launch_recur};
+        ssd::launch_prep, ssd::launch_state_chain, ssd::launch_chunk_scan, ssd::launch_short, ssd::launch_recur};
     for (int k = 0; k < kNumKernels; ++k) {
         // no sequence can take the short path: its kernels would have nothing
         // to do, so they are not launched (their completion events, if any,

@@ -23,6 +23,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kShortMax = 128;   // longest sequence the short-path kernel takes
 constexpr int kRecurMax = 4;     // longest sequence the token-recurrence kernel takes
+constexpr int kNoExponent = 1000;  // stored scale exponent of an all-zero block of x
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -68,19 +69,19 @@ struct Params {
     // of the short sequences, those of 1 .. recur_max tokens go to the
     // token-recurrence kernel (0: none)
     int recur_max;
-    // workspace carve (device)
+    // workspace carve (device); nchunks_max rows per table
     int32_t *meta;       // [4]: nchunks
     int32_t *chunk_off;  // [batch+1]
     int4 *desc;          // [nchunks_max]: {seq, t0, len, 0}
-    float *dts;          // [nchunks_max][H][256]
-    float *cs2;          // [nchunks_max][H][256]
+    float *dts;          // [nchunks_max][H][256]: dts per token, 0 past the chunk end
+    float *cs2;          // [nchunks_max][H][256]: log2(e) * inclusive cumsum of A dts
     uint16_t *cbt;       // [nchunks_max][G][36][64][16] fp16 C.B^T tiles * 2^gexp, accumulator order
-    int32_t *gexp;       // [nchunks_max][G]
-    uint16_t *states;    // [nchunks_max][H][P][N] fp16, scaled by 2^sexp
-    int32_t *sexp;       // [nchunks_max][H][2][N/32]: per 32x32 tile (p tile, n tile)
-    uint16_t *hin;       // [nchunks_max][H][P][N] fp16, row p scaled by 2^hexp
-    int32_t *hexp;       // [nchunks_max][H][P]
-    int32_t *xexp;       // [nchunks_max][H]: 2^xexp puts the chunk's max |x| of the head in [2^14, 2^15)
+    int32_t *gexp;       // [nchunks_max][G][4]: tiles of row blocks q and 7-q
+    uint16_t *bfrag;     // [nchunks_max][G][N/32][16][64][8] fp16 B^T MFMA A operands * 2^bexp
+    int32_t *bexp;       // [nchunks_max][G][N/32]
+    uint16_t *hin;       // [nchunks_max][H][P][N] fp16, 32x32 tile (p/32, n/32) scaled by 2^hexp
+    int16_t *hexp;       // [nchunks_max][H][N/32][2]: per 32x32 tile (n tile, p tile)
+    int32_t *xexp;       // [nchunks_max][H][2]: 2^xexp puts the chunk's max |x| over p half of the head in [2^14, 2^15)
     int32_t *seq_list;   // [batch]: the meta[1] sequences the state chain walks
     int32_t *recur_list; // [batch]: the meta[2] sequences the token recurrence takes
 };
@@ -208,6 +209,12 @@ __device__ __forceinline__ float wave_max(float v) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+__device__ __forceinline__ int wave_min_i32(int v) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v = min(v, __shfl_xor(v, d, 64));
+    return v;
+}
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) {
@@ -294,6 +301,36 @@ __device__ __forceinline__ void store_state8(void *base, int64_t idx, const floa
     }
 }
 
+// Cumulative decay of one chunk and head ("chunk_cumsum"), by one wavefront
+// whose lane l holds tokens 4l .. 4l+3 of the chunk:
+//   dts_j = softplus(dt_j + dt_bias)  (dt_j + dt_bias without softplus), 0 for j >= len
+//   cs2_j = log2(e) * sum_{k <= j} A dts_k                  (constant past the chunk end)
+// ("mamba2_ssd_scan", "Per-token recurrence": dA = exp(A dts); the segment
+// sums of "Mamba chunk scan with segsum", description).  Every kernel that
+// needs these values calls this with the same inputs, so they agree bit for
+// bit.  Returns cs2 of token 255, the chunk's total, in every lane.
+__device__ __forceinline__ float chunk_cumsum4(const float (&dtv)[4], float bias, float A, bool softplus_on,
+                                               int len, float (&dts)[4], float (&cs2)[4]) {
+    const int lane = threadIdx.x & 63;
+    float a[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float v = dtv[e] + bias;
+        const float d = 4 * lane + e < len ? (softplus_on ? softplus_f(v) : v) : 0.0f;
+        dts[e] = d;
+        a[e] = A * d;
+    }
+    a[1] += a[0];
+    a[2] += a[1];
+    a[3] += a[2];
+    const float incl = wave_incl_scan(a[3]);
+    float excl = __shfl_up(incl, 1, 64);
+    if (lane == 0) excl = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) cs2[e] = (excl + a[e]) * kLog2e;
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs2[3]), 63));
+}
+
 // Whether a sequence of len tokens goes to the short-path kernel (with the
 // path on, zero-length sequences go there too).
 __host__ __device__ __forceinline__ bool is_short_sequence(int len, int short_max) {
@@ -337,8 +374,7 @@ inline int short_head_slices(const Params &p) {
 }
 
 hipError_t launch_prep(const Params &p, const Launch &l);
-hipError_t launch_chunk_state(const Params &p, const Launch &l);
-hipError_t launch_state_passing(const Params &p, const Launch &l);
+hipError_t launch_state_chain(const Params &p, const Launch &l);
 hipError_t launch_chunk_scan(const Params &p, const Launch &l);
 hipError_t launch_short(const Params &p, const Launch &l);
 hipError_t launch_recur(const Params &p, const Launch &l);

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert binding.ssd_abi_version() == binding.ABI_VERSION == 14
+    assert binding.ssd_abi_version() == binding.ABI_VERSION == 15
     for code, name in binding.STATUS_NAMES.items():
         assert lib.ssd_status_string(code).decode().startswith(name)
     assert b"unknown" in lib.ssd_status_string(99)
@@ -50,25 +50,37 @@ def _prob(**kw):
 
 
 def test_workspace_layout_arithmetic(lib):
+    """Offsets ascend, 256-byte aligned, each region holds its table; the
+    tables have floor(T / 256) + (sequences the chunked steps can see) rows."""
     p = _prob()
     L = binding.ssd_workspace_get_layout(p)
-    ncm = 1024 // 256 + 4
+    ncm = 1024 // 256 + 4  # dstate 256: no short path, all 4 sequences chunked
     assert L["nchunks_max"] == ncm
     assert L["total_bytes"] == binding.ssd_workspace_size(p)
-    offs = [L[k] for k in ("meta", "chunk_off", "desc", "dts", "cs2", "cbt", "gexp", "states", "sexp", "hin", "hexp",
-                           "xexp", "seq_list", "recur_list")]
+    keys = ("meta", "chunk_off", "desc", "dts", "cs2", "cbt", "gexp", "bfrag", "bexp", "hin", "hexp", "xexp",
+            "seq_list", "recur_list")
+    offs = [L[k] for k in keys]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
-    assert L["cbt"] - L["cs2"] >= ncm * 16 * 256 * 4
-    assert L["gexp"] - L["cbt"] >= ncm * 1 * 36 * 64 * 16 * 2
-    assert L["states"] - L["gexp"] >= ncm * 1 * 4
-    assert L["sexp"] - L["states"] >= ncm * 16 * 64 * 256 * 2
-    assert L["hin"] - L["sexp"] >= ncm * 16 * 2 * 8 * 4
-    assert L["hexp"] - L["hin"] >= ncm * 16 * 64 * 256 * 2
-    assert L["xexp"] - L["hexp"] >= ncm * 16 * 64 * 4
-    assert L["seq_list"] - L["xexp"] >= ncm * 16 * 4
-    assert L["recur_list"] - L["seq_list"] >= 4 * 4
-    assert L["total_bytes"] - L["recur_list"] >= 4 * 4
-    assert L["cs2"] - L["dts"] >= ncm * 16 * 256 * 4
+    need = dict(meta=16, chunk_off=5 * 4, desc=ncm * 16, dts=ncm * 16 * 256 * 4, cs2=ncm * 16 * 256 * 4,
+                cbt=ncm * 1 * 36 * 64 * 16 * 2, gexp=ncm * 1 * 4 * 4, bfrag=ncm * 1 * 8 * 16 * 64 * 8 * 2,
+                bexp=ncm * 1 * 8 * 4, hin=ncm * 16 * 64 * 256 * 2, hexp=ncm * 16 * 8 * 2 * 2,
+                xexp=ncm * 16 * 2 * 4, seq_list=4 * 4, recur_list=4 * 4)
+    ends = offs[1:] + [L["total_bytes"]]
+    for k, o, e in zip(keys, offs, ends):
+        assert e - o >= need[k], k
+
+
+def test_workspace_rows_follow_the_routing(lib):
+    """With the short path on (dstate <= 128) only sequences longer than its
+    limit reach the chunked steps, at most T / (limit + 1) of them: the
+    tables get floor(T / 256) + that many rows."""
+    kw = dict(total_len=512, batch=512, nheads=128, dstate=128, ngroups=8, max_slots=1024)
+    assert binding.ssd_workspace_get_layout(_prob(**kw))["nchunks_max"] == 2 + 512 // 129
+    assert binding.ssd_workspace_get_layout(_prob(short_path_max=4, **kw))["nchunks_max"] == 2 + 512 // 5
+    assert binding.ssd_workspace_get_layout(_prob(short_path_max=0, **kw))["nchunks_max"] == 2 + 512
+    # at dstate 256 the limit is ignored
+    assert (binding.ssd_workspace_get_layout(_prob(short_path_max=0)) ==
+            binding.ssd_workspace_get_layout(_prob(short_path_max=128)))
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -185,16 +197,20 @@ def test_alignment_status(lib, idx, misalign):
 def test_short_path_limit_is_a_problem_field(lib):
     """The short-path limit is part of each call's problem (no library
     state): negative selects the default, 0..SSD_SHORT_PATH_LIMIT are valid,
-    larger values are rejected; the layout does not depend on it; the kernel
-    list names the two short-path kernels last."""
-    for v in (-1, -100, 0, 1, 4, 64, binding.SHORT_PATH_LIMIT):
-        assert binding.ssd_workspace_get_layout(_prob(short_path_max=v)) == binding.ssd_workspace_get_layout(_prob())
+    larger values are rejected; the kernel list names the two short-path
+    kernels last."""
+    n128 = dict(dstate=128, nheads=16)
+    for v in (-1, -100):
+        assert (binding.ssd_workspace_get_layout(_prob(short_path_max=v, **n128)) ==
+                binding.ssd_workspace_get_layout(_prob(short_path_max=binding.SHORT_PATH_LIMIT, **n128)))
+    for v in (0, 1, 4, 64, binding.SHORT_PATH_LIMIT):
+        assert binding.ssd_workspace_size(_prob(short_path_max=v, **n128)) > 0
     n = ctypes.c_size_t(0)
     assert lib.ssd_workspace_size(ctypes.byref(_prob(short_path_max=binding.SHORT_PATH_LIMIT + 1)),
                                   ctypes.byref(n)) == 3
     assert not hasattr(binding, "ssd_set_short_path_max")
     names = [lib.ssd_kernel_name(i).decode() for i in range(lib.ssd_kernel_count())]
-    assert names == ["ssd_prep", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan", "ssd_short", "ssd_recur"]
+    assert names == ["ssd_prep", "ssd_state_chain", "ssd_chunk_scan", "ssd_short", "ssd_recur"]
 
 
 def test_noalloc_entry_host_errors(lib):
@@ -204,7 +220,7 @@ def test_noalloc_entry_host_errors(lib):
     f = lib.ssd_chunk_scan_varlen_fwd_inplace_noalloc
     base = 1 << 20  # never dereferenced: every call below fails its host checks
     args = [ctypes.c_void_p(base)] * 12
-    big = _prob(total_len=16384)  # the 4 x 4096, 16-head, dstate-256 problem
+    big = _prob(total_len=8 * 4096, batch=8)  # 8 x 4096 tokens, 16 heads, dstate 256
     assert binding.ssd_workspace_size(big) > binding.NOALLOC_SCRATCH_BYTES
     assert f(ctypes.byref(big), *args, None) == 8
     assert lib.ssd_status_string(8).decode().startswith("SSD_ERR_SCRATCH")

@@ -223,17 +223,21 @@ def test_intermediates_match_chunked_oracle():
     desc = w[L["desc"]:L["desc"] + ncm * 16].view(np.int32).reshape(ncm, 4)[:nch]
     dts = w[L["dts"]:L["dts"] + ncm * H * 256 * 4].view(np.float32).reshape(ncm, H, 256)[:nch]
     cs2 = w[L["cs2"]:L["cs2"] + ncm * H * 256 * 4].view(np.float32).reshape(ncm, H, 256)[:nch]
-    S16 = w[L["states"]:L["states"] + ncm * H * P * N * 2].view(np.float16).reshape(ncm, H, P, N)[:nch]
-    sexp = w[L["sexp"]:L["sexp"] + ncm * H * 2 * (N // 32) * 4].view(np.int32).reshape(ncm, H, 2, N // 32)[:nch]
-    sfac = np.exp2(-sexp.astype(np.float64)).repeat(32, axis=2).repeat(32, axis=3)  # per element (p, n)
-    S = S16.astype(np.float64) * sfac
     hin16 = w[L["hin"]:L["hin"] + ncm * H * P * N * 2].view(np.float16).reshape(ncm, H, P, N)[:nch]
-    hexp = w[L["hexp"]:L["hexp"] + ncm * H * P * 4].view(np.int32).reshape(ncm, H, P)[:nch]
-    hin = hin16.astype(np.float64) * np.exp2(-hexp.astype(np.float64))[..., None]
+    hexp = w[L["hexp"]:L["hexp"] + ncm * H * (N // 32) * 2 * 2].view(np.int16).reshape(ncm, H, N // 32, 2)[:nch]
+    # element (p, n) of a chunk and head is scaled by 2^hexp[n / 32][p / 32]
+    hfac = np.exp2(-hexp.astype(np.float64)).transpose(0, 1, 3, 2).repeat(32, axis=2).repeat(32, axis=3)
+    hin = hin16.astype(np.float64) * hfac
     cbt16 = w[L["cbt"]:L["cbt"] + ncm * 2 * 36 * 1024 * 2].view(np.float16).reshape(ncm, 2, 36, 64, 16)[:nch]
-    gexp = w[L["gexp"]:L["gexp"] + ncm * 2 * 4].view(np.int32).reshape(ncm, 2)[:nch]
-    cbt = cbt16.astype(np.float64) * np.exp2(-gexp.astype(np.float64))[..., None, None, None]
-    xexp = w[L["xexp"]:L["xexp"] + ncm * H * 4].view(np.int32).reshape(ncm, H)[:nch]
+    # one exponent per row-block pair (q, 7 - q) of each chunk and group
+    gexp = w[L["gexp"]:L["gexp"] + ncm * 2 * 4 * 4].view(np.int32).reshape(ncm, 2, 4)[:nch]
+    pair_of_tile = np.array([min(rb, 7 - rb) for rb in range(8) for _ in range(rb + 1)])
+    cbt = cbt16.astype(np.float64) * np.exp2(-gexp[:, :, pair_of_tile].astype(np.float64))[..., None, None]
+    xexp = w[L["xexp"]:L["xexp"] + ncm * H * 2 * 4].view(np.int32).reshape(ncm, H, 2)[:nch]
+    NT = N // 32
+    bfrag = w[L["bfrag"]:L["bfrag"] + ncm * 2 * NT * 16 * 64 * 8 * 2].view(np.float16)
+    bfrag = bfrag.reshape(ncm, 2, NT, 16, 64, 8)[:nch]
+    bexp = w[L["bexp"]:L["bexp"] + ncm * 2 * NT * 4].view(np.int32).reshape(ncm, 2, NT)[:nch]
     ref = chunked_scan(prob, 256, keep_intermediates=True)["chunks"]
     qsl = prob["query_start_loc"]
     for rec in ref:
@@ -245,8 +249,15 @@ def test_intermediates_match_chunked_oracle():
         cs2_ref = rec["cs"] * math.log2(math.e)
         tol = 3e-5 * (abs(cs2_ref[-1]) + 1.0)
         assert np.max(np.abs(cs2[c, h, :l] - cs2_ref)) <= tol
-        assert frob_rel(S[c, h], rec["S"]) <= 1e-3
         assert frob_rel(hin[c, h], rec["h_in"]) <= 1e-3
+        # each 32x32 tile's exponent keeps its largest magnitude in [2^14, 2^15)
+        for ntile in range(N // 32):
+            for ptile in range(2):
+                tile = np.abs(hin16[c, h, 32 * ptile:32 * ptile + 32, 32 * ntile:32 * ntile + 32].astype(np.float64))
+                if tile.max() > 0:
+                    assert 2.0 ** 14 <= tile.max() < 2.0 ** 15 or hexp[c, h, ntile, ptile] == 126
+                else:
+                    assert hexp[c, h, ntile, ptile] == 126
         # C.B^T tiles (stored transposed, in MFMA accumulator order) against the plain product
         T = prob["total_len"]
         g = h // 2
@@ -254,15 +265,34 @@ def test_intermediates_match_chunked_oracle():
         Cc = bf16_to_f64(prob["C"]).reshape(T, 2, N)[t0:t0 + l, g]
         GT = np.zeros((256, 256))
         GT[:l, :l] = Bc @ Cc.T  # G^T[j][i] = B_j . C_i
-        # x exponent of the chunk and head: 2^xexp puts the largest |x| in [2^14, 2^15)
-        xm = np.abs(bf16_to_f64(prob["x"]).reshape(T, H, P)[t0:t0 + l, h]).max()
-        if xm > 0:
-            assert 2.0 ** 14 <= xm * 2.0 ** xexp[c, h] < 2.0 ** 15
-        else:
-            assert xexp[c, h] == 0
+        rows = np.minimum(np.arange(256), l - 1)
+        GTe = Bc[rows] @ Cc[rows].T
+        # x exponent of the chunk, head and half of p: 2^xexp puts the
+        # half's largest |x| in [2^14, 2^15) (1000 marks an all-zero half)
+        for ph in range(2):
+            xm = np.abs(bf16_to_f64(prob["x"]).reshape(T, H, P)[t0:t0 + l, h, 32 * ph:32 * ph + 32]).max()
+            if xm > 0:
+                assert 2.0 ** 14 <= xm * 2.0 ** xexp[c, h, ph] < 2.0 ** 15
+            else:
+                assert xexp[c, h, ph] == 1000
+        # B^T operands of the chunk and group: K-step s, lane ln holds
+        # B[t0 + 16 s + 8 (ln / 32) + 0..7][32 nt + ln % 32] 2^bexp, 0 past the chunk end
+        s_ = np.arange(16)[:, None, None]
+        ln = np.arange(64)[None, :, None]
+        e8 = np.arange(8)[None, None, :]
+        jj = 16 * s_ + 8 * (ln // 32) + e8
+        for nt in range(NT):
+            Bt = np.zeros((256, 32))
+            Bt[:l] = Bc[:, 32 * nt:32 * nt + 32]
+            want = np.where(jj < l, Bt[np.minimum(jj, 255), ln % 32], 0.0)
+            got = bfrag[c, g, nt].astype(np.float64) * 2.0 ** -bexp[c, g, nt]
+            assert np.all(np.abs(got - want) <= 2.0 ** -11 * np.abs(want) + 2.0 ** (-24.0 - bexp[c, g, nt]))
+            bm = np.abs(Bt).max()
+            if bm > 0:
+                assert 2.0 ** 14 <= bm * 2.0 ** bexp[c, g, nt] < 2.0 ** 15
         lane = np.arange(64)[:, None]
         e = np.arange(16)[None, :]
-        gm = 0.0
+        gm = np.zeros(4)
         for rb in range(8):
             for t in range(rb + 1):
                 jj = 32 * t + 8 * (e // 4) + 4 * (lane // 32) + e % 4
@@ -271,11 +301,15 @@ def test_intermediates_match_chunked_oracle():
                 want = np.where(jj <= ii, GT[jj, ii], 0.0)  # the diagonal tile is zero above its diagonal
                 np.testing.assert_allclose(cbt[c, g, rb * (rb + 1) // 2 + t][inside], want[inside],
                                            rtol=2.0 ** -11, atol=np.abs(GT).max() * 2.0 ** -24)
-                gm = max(gm, np.abs(GT[jj, ii]).max())
-        # the tiles' exponent keeps their largest magnitude below 2^15, and the
-        # chunk's own entries reach at least 2^13 (rows past the end repeat rows)
-        if gm > 0:
-            assert 2.0 ** 13 <= gm * 2.0 ** gexp[c, g] < 2.0 ** 15
+                # the stored tile's entries, rows past the chunk end included
+                # (those repeat the chunk's last row of B and of C)
+                q = min(rb, 7 - rb)
+                gm[q] = max(gm[q], np.abs(np.where(jj <= ii, GTe[jj, ii], 0.0)).max())
+        # each pair's exponent puts its tiles' largest magnitude in [2^14,
+        # 2^15), up to the rounding of the fp32 products (2^13 allows for it)
+        for q in range(4):
+            if gm[q] > 0:
+                assert 2.0 ** 13 <= gm[q] * 2.0 ** gexp[c, g, q] < 2.0 ** 15
 
 
 # --------------------------------------------------------------- invariants

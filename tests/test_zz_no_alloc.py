@@ -55,8 +55,8 @@ def test_noalloc_equals_workspace_entry_on_consecutive_calls(short_max):
 def test_noalloc_rejects_problems_beyond_its_scratch():
     """A problem whose workspace exceeds the scratch array is refused before
     anything is launched: the outputs and the pool keep their bits."""
-    prob = small_problem([4096] * 4, H=16, P=64, G=1, N=256, max_slots=5, seed=803, init="none")
-    ps = binding.make_problem(prob["total_len"], 4, 16, 64, 1, 256, 5)
+    prob = small_problem([4096] * 8, H=16, P=64, G=1, N=256, max_slots=9, seed=803, init="none")
+    ps = binding.make_problem(prob["total_len"], 8, 16, 64, 1, 256, 9)
     assert binding.ssd_workspace_size(ps) > binding.NOALLOC_SCRATCH_BYTES
     d = torch_io.upload(prob, "cuda")
     d["y"].fill_(3.0)
