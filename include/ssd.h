@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 15
+#define SSD_ABI_VERSION 16
 #define SSD_MAX_DSTATE 256  /* largest dstate, as in "mamba2_ssd_scan", comptime MAX_DSTATE */
 #define SSD_SHORT_PATH_LIMIT 128  /* longest sequence the short path can take */
 #define SSD_RECUR_LIMIT 4         /* of those, the longest the token recurrence takes */
@@ -125,7 +125,7 @@ typedef struct ssd_problem {
  * zero-length sequence is taken as well) have no chunks: chunk_off[b] ==
  * chunk_off[b+1] and no row of any table is theirs.
  *   meta      int32[4]                    {nchunks, nseq, nrecur, 0}: chunks,
- *                                         sequences the state chain walks,
+ *                                         sequences the state passing walks,
  *                                         sequences the token recurrence
  *                                         takes
  *   chunk_off int32[batch + 1]            first chunk of each sequence
@@ -151,16 +151,18 @@ typedef struct ssd_problem {
  *                                         chunk end), scaled by
  *                                         2^bexp[c][g][nt]
  *   bexp      int32[nchunks_max][G][N/32] exponent of each bfrag n tile
- *   hin       fp16[nchunks_max][H][P][N]  state entering the chunk, element
- *                                         (p, n) scaled by
- *                                         2^hexp[c][h][n/32][p/32]
- *   hexp      int16[nchunks_max][H][N/32][2]  exponent of each 32x32 tile
- *                                         (126 for an all-zero tile)
+ *   states    fp16[nchunks_max][H][P][N]  chunk's own state contribution,
+ *                                         element (p, n) scaled by
+ *                                         2^sexp[c][h][p/32][n/32]
+ *   sexp      int32[nchunks_max][H][2][N/32]  exponent of each 32x32 tile
+ *   hin       fp16[nchunks_max][H][P][N]  state entering the chunk, row p
+ *                                         scaled by 2^hexp[c][h][p]
+ *   hexp      int32[nchunks_max][H][P]    exponent of each hin row
  *   xexp      int32[nchunks_max][H][2]    2^xexp[c][h][i] puts the chunk's
  *                                         largest |x| over p = 32i .. 32i+31
  *                                         of the head in [2^14, 2^15) (1000
  *                                         if all zero)
- *   seq_list  int32[batch]                the nseq sequences the state chain
+ *   seq_list  int32[batch]                the nseq sequences the state passing
  *                                         walks, in order (all of them when
  *                                         no sequence can take the short
  *                                         path; else those longer than its
@@ -171,7 +173,8 @@ typedef struct ssd_problem {
 typedef struct ssd_workspace_layout {
     size_t total_bytes;
     int64_t nchunks_max;
-    size_t meta, chunk_off, desc, dts, cs2, cbt, gexp, bfrag, bexp, hin, hexp, xexp, seq_list, recur_list;
+    size_t meta, chunk_off, desc, dts, cs2, cbt, gexp, bfrag, bexp, states, sexp, hin, hexp, xexp, seq_list,
+        recur_list;
 } ssd_workspace_layout;
 
 /* ABI version of the loaded library (SSD_ABI_VERSION it was built with). */

@@ -89,8 +89,10 @@ void layout_of(const ssd_problem *p, ssd_workspace_layout *L) {
     L->gexp = off;      off = align_up(off + (size_t)ncm * G * 4 * sizeof(int32_t));
     L->bfrag = off;     off = align_up(off + (size_t)ncm * G * (size_t)p->dstate * ssd::kChunk * sizeof(uint16_t));
     L->bexp = off;      off = align_up(off + (size_t)ncm * G * ((size_t)p->dstate / 32) * sizeof(int32_t));
+    L->states = off;    off = align_up(off + (size_t)ncm * H * PN * sizeof(uint16_t));
+    L->sexp = off;      off = align_up(off + (size_t)ncm * H * 2 * ((size_t)p->dstate / 32) * sizeof(int32_t));
     L->hin = off;       off = align_up(off + (size_t)ncm * H * PN * sizeof(uint16_t));
-    L->hexp = off;      off = align_up(off + (size_t)ncm * H * 2 * ((size_t)p->dstate / 32) * sizeof(int16_t));
+    L->hexp = off;      off = align_up(off + (size_t)ncm * H * (size_t)p->head_dim * sizeof(int32_t));
     L->xexp = off;      off = align_up(off + (size_t)ncm * H * 2 * sizeof(int32_t));
     L->seq_list = off;  off = align_up(off + (size_t)p->batch * sizeof(int32_t));
     L->recur_list = off; off = align_up(off + (size_t)p->batch * sizeof(int32_t));
@@ -140,10 +142,10 @@ ssd_status ssd_workspace_get_layout(const ssd_problem *prob, ssd_workspace_layou
     return SSD_OK;
 }
 
-static const char *const kKernelNames[] = {"ssd_prep", "ssd_state_chain", "ssd_chunk_scan", "ssd_short",
-                                           "ssd_recur"};
-static constexpr int kNumKernels = 5;
-static constexpr int kFirstShortKernel = 3;  // this and the later ones serve the short path
+static const char *const kKernelNames[] = {"ssd_prep",       "ssd_chunk_state", "ssd_state_passing",
+                                           "ssd_chunk_scan", "ssd_short",       "ssd_recur"};
+static constexpr int kNumKernels = 6;
+static constexpr int kFirstShortKernel = 4;  // this and the later ones serve the short path
 
 int ssd_kernel_count(void) { return kNumKernels; }
 
@@ -235,7 +237,7 @@ static ssd_status run_scan(
     p.desc = reinterpret_cast<int4 *>(ws + L.desc);
     p.dts = reinterpret_cast<float *>(ws + L.dts);
     p.cs2 = reinterpret_cast<float *>(ws + L.cs2);
-    p.hexp = reinterpret_cast<int16_t *>(ws + L.hexp);
+    p.hexp = reinterpret_cast<int32_t *>(ws + L.hexp);
     p.xexp = reinterpret_cast<int32_t *>(ws + L.xexp);
     p.seq_list = reinterpret_cast<int32_t *>(ws + L.seq_list);
     p.recur_list = reinterpret_cast<int32_t *>(ws + L.recur_list);
@@ -244,10 +246,13 @@ static ssd_status run_scan(
     p.bfrag = reinterpret_cast<uint16_t *>(ws + L.bfrag);
     p.bexp = reinterpret_cast<int32_t *>(ws + L.bexp);
     p.hin = reinterpret_cast<uint16_t *>(ws + L.hin);
+    p.states = reinterpret_cast<uint16_t *>(ws + L.states);
+    p.sexp = reinterpret_cast<int32_t *>(ws + L.sexp);
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t (*const launchers[kNumKernels])(const ssd::Params &, const ssd::Launch &) = {
-        ssd::launch_prep, ssd::launch_state_chain, ssd::launch_chunk_scan, ssd::launch_short, ssd::launch_recur};
+        ssd::launch_prep,       ssd::launch_chunk_state, ssd::launch_state_passing,
+        ssd::launch_chunk_scan, ssd::launch_short,       ssd::launch_recur};
     for (int k = 0; k < kNumKernels; ++k) {
         // no sequence can take the short path: its kernels would have nothing
         // to do, so they are not launched (their completion events, if any,

@@ -236,30 +236,22 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
     // wait counts never assume a later load is missing and wait for all.
     const int pq = tid & 3;     // x staging: quarter of p
     const int pair = tid >> 2;  // x staging: token pair
-    constexpr int NT = N / 32;  // n tiles of h_in
     u32x4 hreg[HVEC];
-    uint32_t hxp = 0;           // exponents of h_in tiles (0, nt_t) (low half) and (1, nt_t) (high half)
     u32x4 xr[2][2];
     float tab_cs = 0.f, tab_dt = 0.f, tab_dh = 0.f;
-    int tab_xe = 0;
+    int tab_hx = 0, tab_xe = 0;
     const float *dsrc = p.D ? p.D : p.A;  // a valid address either way; D = 0 when absent
     auto load_tabs = [&](int h) {
         const int64_t r = ((int64_t)cc * p.H + h) * kChunk + (tid & (kChunk - 1));
         tab_cs = p.cs2[r];
         tab_dt = p.dts[r];
+        tab_hx = p.hexp[((int64_t)cc * p.H + h) * kHeadDim + (tid & (kHeadDim - 1))];
         tab_dh = dsrc[h];
         // one exponent per half of p (kNoExponent for an all-zero half): the
         // head's is the smaller, that of the larger maximum (0 if all zero)
         const int2 xe2 = *reinterpret_cast<const int2 *>(p.xexp + ((int64_t)cc * p.H + h) * 2);
         tab_xe = min(xe2.x, xe2.y);
         tab_xe = tab_xe == kNoExponent ? 0 : tab_xe;
-        // every h_in vector of this thread lies in n tile nt_t (the vectors are
-        // kThreads apart, a multiple of a row's N / 8), in p tile 0 or 1; the
-        // index is recomputed here rather than held across the head loop
-        int t = threadIdx.x;
-        asm volatile("" : "+v"(t));
-        const int nt_t = (t % (N / 8)) >> 2;
-        hxp = *reinterpret_cast<const uint32_t *>(p.hexp + (((int64_t)cc * p.H + h) * NT + nt_t) * 2);
         const uint16_t *hin_head = p.hin + ((int64_t)cc * p.H + h) * kHeadDim * N;
 #pragma unroll
         for (int it = 0; it < HVEC; ++it)
@@ -278,42 +270,22 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
     };
     const bool has_d = p.D != nullptr;
     auto stage_tabs = [&](int b) {
-        // h_in arrives with one exponent per 32x32 tile; each 32-row block is
-        // brought to one exponent, the smallest of its tiles (the tile with
-        // the largest values), so that the off-diagonal product can undo it per
-        // row: the other tiles are multiplied by 2^(E - e) <= 1 in fp16 (exact
-        // but where values fall below fp16's normal range, as a per-row scale
-        // would leave them; factors below 2^-24 flush those tiles to zero)
-        // every wavefront holds each tile's exponent in some lane (nt_t runs
-        // over all n tiles within its lanes), so the block minimum is a
-        // wavefront minimum
-        const int hx0 = (int)(int16_t)(hxp & 0xFFFFu), hx1 = (int)(int16_t)(hxp >> 16);
-        const int E0 = wave_min_i32(hx0), E1 = wave_min_i32(hx1);
         if (tid < kChunk) {  // four whole wavefronts
             sm.cs2[b][tid] = tab_cs;
             sm.dts[b][tid] = tab_dt;
             const float m = wave_max(fabsf(tab_dt));
             if ((tid & 63) == 0) sm.dmx[b][tid >> 6] = m;
-        } else if (tid >= kChunk && tid < kChunk + kHeadDim) {
-            sm.hs[b][tid - kChunk] = ldexpf(1.0f, -((tid - kChunk) < 32 ? E0 : E1));
+        } else if (tid < kChunk + kHeadDim) {
+            sm.hs[b][tid - kChunk] = ldexpf(1.0f, -tab_hx);
         } else if (tid == kChunk + kHeadDim) {
             sm.dd[b] = has_d ? tab_dh : 0.0f;
             sm.xexp[b] = tab_xe;
         }
-        const int d0 = E0 - hx0, d1 = E1 - hx1;
-        const _Float16 f0 = d0 < -24 ? (_Float16)0.0f : (_Float16)ldexpf(1.0f, d0);
-        const _Float16 f1 = d1 < -24 ? (_Float16)0.0f : (_Float16)ldexpf(1.0f, d1);
-        const uint32_t f20 = __builtin_bit_cast(uint32_t, f16x2{f0, f0});
-        const uint32_t f21 = __builtin_bit_cast(uint32_t, f16x2{f1, f1});
 #pragma unroll
         for (int it = 0; it < HVEC; ++it) {
             const int idx = tid + it * kThreads;
             const int row = idx / (N / 8), v = idx - row * (N / 8);
-            const uint32_t f2 = row < 32 ? f20 : f21;
-            u32x4 hv = hreg[it];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) hv[w] = hmul2(hv[w], f2);
-            *reinterpret_cast<u32x4 *>(sm.h + row * H_STRIDE + v * 4) = hv;
+            *reinterpret_cast<u32x4 *>(sm.h + row * H_STRIDE + v * 4) = hreg[it];
         }
     };
     const int h_last = h_first + HB - 1;

@@ -79,10 +79,12 @@ struct Params {
     int32_t *gexp;       // [nchunks_max][G][4]: tiles of row blocks q and 7-q
     uint16_t *bfrag;     // [nchunks_max][G][N/32][16][64][8] fp16 B^T MFMA A operands * 2^bexp
     int32_t *bexp;       // [nchunks_max][G][N/32]
-    uint16_t *hin;       // [nchunks_max][H][P][N] fp16, 32x32 tile (p/32, n/32) scaled by 2^hexp
-    int16_t *hexp;       // [nchunks_max][H][N/32][2]: per 32x32 tile (n tile, p tile)
+    uint16_t *states;    // [nchunks_max][H][P][N] fp16 chunk contributions, 32x32 tile scaled by 2^sexp
+    int32_t *sexp;       // [nchunks_max][H][2][N/32]: per 32x32 tile (p tile, n tile)
+    uint16_t *hin;       // [nchunks_max][H][P][N] fp16, row p scaled by 2^hexp
+    int32_t *hexp;       // [nchunks_max][H][P]: per row
     int32_t *xexp;       // [nchunks_max][H][2]: 2^xexp puts the chunk's max |x| over p half of the head in [2^14, 2^15)
-    int32_t *seq_list;   // [batch]: the meta[1] sequences the state chain walks
+    int32_t *seq_list;   // [batch]: the meta[1] sequences the state passing walks
     int32_t *recur_list; // [batch]: the meta[2] sequences the token recurrence takes
 };
 
@@ -374,7 +376,8 @@ inline int short_head_slices(const Params &p) {
 }
 
 hipError_t launch_prep(const Params &p, const Launch &l);
-hipError_t launch_state_chain(const Params &p, const Launch &l);
+hipError_t launch_chunk_state(const Params &p, const Launch &l);
+hipError_t launch_state_passing(const Params &p, const Launch &l);
 hipError_t launch_chunk_scan(const Params &p, const Launch &l);
 hipError_t launch_short(const Params &p, const Launch &l);
 hipError_t launch_recur(const Params &p, const Launch &l);

@@ -223,11 +223,14 @@ def test_intermediates_match_chunked_oracle():
     desc = w[L["desc"]:L["desc"] + ncm * 16].view(np.int32).reshape(ncm, 4)[:nch]
     dts = w[L["dts"]:L["dts"] + ncm * H * 256 * 4].view(np.float32).reshape(ncm, H, 256)[:nch]
     cs2 = w[L["cs2"]:L["cs2"] + ncm * H * 256 * 4].view(np.float32).reshape(ncm, H, 256)[:nch]
+    S16 = w[L["states"]:L["states"] + ncm * H * P * N * 2].view(np.float16).reshape(ncm, H, P, N)[:nch]
+    sexp = w[L["sexp"]:L["sexp"] + ncm * H * 2 * (N // 32) * 4].view(np.int32).reshape(ncm, H, 2, N // 32)[:nch]
+    # element (p, n) of a chunk's contribution is scaled by 2^sexp[p / 32][n / 32]
+    S = S16.astype(np.float64) * np.exp2(-sexp.astype(np.float64)).repeat(32, axis=2).repeat(32, axis=3)
     hin16 = w[L["hin"]:L["hin"] + ncm * H * P * N * 2].view(np.float16).reshape(ncm, H, P, N)[:nch]
-    hexp = w[L["hexp"]:L["hexp"] + ncm * H * (N // 32) * 2 * 2].view(np.int16).reshape(ncm, H, N // 32, 2)[:nch]
-    # element (p, n) of a chunk and head is scaled by 2^hexp[n / 32][p / 32]
-    hfac = np.exp2(-hexp.astype(np.float64)).transpose(0, 1, 3, 2).repeat(32, axis=2).repeat(32, axis=3)
-    hin = hin16.astype(np.float64) * hfac
+    hexp = w[L["hexp"]:L["hexp"] + ncm * H * P * 4].view(np.int32).reshape(ncm, H, P)[:nch]
+    # row p of a chunk and head is scaled by 2^hexp[p]
+    hin = hin16.astype(np.float64) * np.exp2(-hexp.astype(np.float64))[..., None]
     cbt16 = w[L["cbt"]:L["cbt"] + ncm * 2 * 36 * 1024 * 2].view(np.float16).reshape(ncm, 2, 36, 64, 16)[:nch]
     # one exponent per row-block pair (q, 7 - q) of each chunk and group
     gexp = w[L["gexp"]:L["gexp"] + ncm * 2 * 4 * 4].view(np.int32).reshape(ncm, 2, 4)[:nch]
@@ -249,15 +252,17 @@ def test_intermediates_match_chunked_oracle():
         cs2_ref = rec["cs"] * math.log2(math.e)
         tol = 3e-5 * (abs(cs2_ref[-1]) + 1.0)
         assert np.max(np.abs(cs2[c, h, :l] - cs2_ref)) <= tol
+        assert frob_rel(S[c, h], rec["S"]) <= 1e-3
         assert frob_rel(hin[c, h], rec["h_in"]) <= 1e-3
-        # each 32x32 tile's exponent keeps its largest magnitude in [2^14, 2^15)
-        for ntile in range(N // 32):
-            for ptile in range(2):
-                tile = np.abs(hin16[c, h, 32 * ptile:32 * ptile + 32, 32 * ntile:32 * ntile + 32].astype(np.float64))
-                if tile.max() > 0:
-                    assert 2.0 ** 14 <= tile.max() < 2.0 ** 15 or hexp[c, h, ntile, ptile] == 126
-                else:
-                    assert hexp[c, h, ntile, ptile] == 126
+        # each 32x32 tile of S is scaled so that its largest magnitude lies in
+        # [2^14, 2^15) before the rounding to fp16, which can carry it to 2^15
+        for ptile in range(2):
+            for ntile in range(N // 32):
+                tile = np.abs(S16[c, h, 32 * ptile:32 * ptile + 32, 32 * ntile:32 * ntile + 32].astype(np.float64))
+                assert tile.max() == 0 or 2.0 ** 14 <= tile.max() <= 2.0 ** 15
+        # each nonzero row of h_in likewise
+        rows = np.abs(hin16[c, h].astype(np.float64)).max(axis=1)
+        assert np.all((rows == 0) | ((rows >= 2.0 ** 14) & (rows <= 2.0 ** 15)))
         # C.B^T tiles (stored transposed, in MFMA accumulator order) against the plain product
         T = prob["total_len"]
         g = h // 2
