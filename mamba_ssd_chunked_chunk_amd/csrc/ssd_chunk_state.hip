@@ -10,14 +10,14 @@
 // each chunk's x for the chunk-scan step (xexp) is written here too.
 //
 // Work split.  One workgroup per (chunk, block of HB heads of one group); no
-// chunk waits for another.  Twelve wavefronts in two roles:
+// chunk waits for another.  Sixteen wavefronts in two roles:
 //   - consumers (wavefronts 0-7): wavefront w owns n tile w (dstate 256), or
 //     n tile w/2 and p tile w%2 (dstate 128, 64; at 64 only wavefronts 0-3).
 //     Its B^T operands, formed once per chunk and group by the prep step,
 //     are loaded into registers once and serve all HB heads.  Per head, each
 //     S^T tile is 16 v_mfma_f32_32x32x16_f16 over the chunk's 256 tokens
 //     (fp32 accumulate), stored as fp16.
-//   - producers (wavefronts 8-11): load each head's x and the dts and cs2 of
+//   - producers (wavefronts 8-15): load each head's x and the dts and cs2 of
 //     its tokens two heads ahead, form the token weights
 //     w_j = exp2(cs2_last - cs2_j) dts_j and the maxima of |w| and |x| one
 //     head ahead, and stage (w x)^T into one of two LDS buffers as fp16 under
@@ -36,7 +36,8 @@ namespace ssd {
 
 namespace {
 constexpr int kConsumers = 8;
-constexpr int kThreads = 64 * (kConsumers + 4);
+constexpr int kProducers = 8;
+constexpr int kThreads = 64 * (kConsumers + kProducers);
 // dwords per staged row: 128 token pairs + pad.  LDS serves 4-byte accesses
 // 32 lanes at a time over 32 banks and 8-byte accesses 32 lanes at a time
 // over 64 banks.  At this stride the MFMA operand reads (8 bytes, rows 0..31
@@ -47,16 +48,16 @@ constexpr int XT_STRIDE = 130;
 
 struct __attribute__((aligned(16))) StateSmem {
     uint32_t xt[2][kHeadDim * XT_STRIDE];  // (w x)^T 2^sx: row p, fp16 token pairs; head k in buffer k & 1
-    float red[2][3][4];                    // per producer wavefront: max |w|, max |x| over p < 32, over p >= 32
+    float red[2][3][kProducers];           // per producer wavefront: max |w|, max |x| over p < 32, over p >= 32
     int sx[2];                             // scale exponent of the head in buffer b
 };
 
-// A producer thread's inputs of one head: x at token pairs pq + 32 it (two
+// A producer thread's inputs of one head: x at token pairs pq + 64 it (two
 // tokens each, 8 p), the chunk's cs2 and dts at those tokens and its last
 // cs2; once analysed, the tokens' weights
 struct HeadIn {
-    u32x4 x[4][2];
-    float2 cs[4], dt[4], w[4];
+    u32x4 x[2][2];
+    float2 cs[2], dt[2], w[2];
     float clast;
 };
 
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_state_kernel(Params p) {
     // barriers (one per phase, after a prologue barrier).
     if (producer) {
         const int pw = wave - kConsumers;  // producer wavefront 0 .. 3
-        // thread t: p = 8 pv .. 8 pv + 7 of token pairs pq + 32 it, so that
+        // thread t: p = 8 pv .. 8 pv + 7 of token pairs pq + 64 it, so that
         // each 32-lane half of a wavefront stages 16 consecutive pairs of two
         // rows 8 apart (distinct banks, see XT_STRIDE)
         auto coords = [&](int &pv, int &pq) {
@@ -118,14 +119,14 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_state_kernel(Params p) {
             const uint32_t xrow = (uint32_t)p.H * kHeadDim * 2;  // bytes between tokens of x
             const char *xb = reinterpret_cast<const char *>(p.x + (t0 * p.H + h) * kHeadDim + 8 * pv);
 #pragma unroll
-            for (int it = 0; it < 4; ++it) {
+            for (int it = 0; it < 2; ++it) {
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
-                    const uint32_t j = (uint32_t)min(2 * (pq + 32 * it) + e, len - 1);
+                    const uint32_t j = (uint32_t)min(2 * (pq + 64 * it) + e, len - 1);
                     o.x[it][e] = *reinterpret_cast<const u32x4 *>(xb + j * xrow);
                 }
-                o.cs[it] = *reinterpret_cast<const float2 *>(p.cs2 + r + 2 * (pq + 32 * it));
-                o.dt[it] = *reinterpret_cast<const float2 *>(p.dts + r + 2 * (pq + 32 * it));
+                o.cs[it] = *reinterpret_cast<const float2 *>(p.cs2 + r + 2 * (pq + 64 * it));
+                o.dt[it] = *reinterpret_cast<const float2 *>(p.dts + r + 2 * (pq + 64 * it));
             }
             o.clast = p.cs2[r + kChunk - 1 + min(opaque_tid(), 0)];  // a vector load (in-order waits)
         };
@@ -135,14 +136,14 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_state_kernel(Params p) {
             coords(pv, pq);
             float wm = 0.0f;
 #pragma unroll
-            for (int it = 0; it < 4; ++it) {
+            for (int it = 0; it < 2; ++it) {
                 o.w[it].x = fast_exp2(o.clast - o.cs[it].x) * o.dt[it].x;
                 o.w[it].y = fast_exp2(o.clast - o.cs[it].y) * o.dt[it].y;
                 wm = fmaxf(wm, fmaxf(fabsf(o.w[it].x), fabsf(o.w[it].y)));
             }
             u16x2 mx2 = u16x2{0, 0};
 #pragma unroll
-            for (int it = 0; it < 4; ++it)
+            for (int it = 0; it < 2; ++it)
 #pragma unroll
                 for (int e = 0; e < 2; ++e)
 #pragma unroll
@@ -159,9 +160,13 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_state_kernel(Params p) {
         // head hh (analysed into slot s2) staged into buffer s2
         auto stage = [&](int hh, int s2, const HeadIn &o) {
             const int h = h_first + min(hh, HB - 1);
-            const float wmax = fmaxf(fmaxf(sm.red[s2][0][0], sm.red[s2][0][1]), fmaxf(sm.red[s2][0][2], sm.red[s2][0][3]));
-            const float xm0 = fmaxf(fmaxf(sm.red[s2][1][0], sm.red[s2][1][1]), fmaxf(sm.red[s2][1][2], sm.red[s2][1][3]));
-            const float xm1 = fmaxf(fmaxf(sm.red[s2][2][0], sm.red[s2][2][1]), fmaxf(sm.red[s2][2][2], sm.red[s2][2][3]));
+            float wmax = 0.0f, xm0 = 0.0f, xm1 = 0.0f;
+#pragma unroll
+            for (int v = 0; v < kProducers; ++v) {
+                wmax = fmaxf(wmax, sm.red[s2][0][v]);
+                xm0 = fmaxf(xm0, sm.red[s2][1][v]);
+                xm1 = fmaxf(xm1, sm.red[s2][2][v]);
+            }
             // the chunk-scan step stages x under the power of two of the
             // chunk's max |x| over each half of p (kNoExponent for an all-zero
             // half); every lane stores one of the two (the same value per
@@ -178,17 +183,17 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_state_kernel(Params p) {
             const float xs = ldexpf(1.0f, sx);
             int pv, pq;
             coords(pv, pq);
-            // rows 8 pv + i, pairs pq + 32 it: every store is this thread's
+            // rows 8 pv + i, pairs pq + 64 it: every store is this thread's
             // base plus a constant
             uint32_t *xt = sm.xt[s2] + 8 * pv * XT_STRIDE + pq;
 #pragma unroll
-            for (int it = 0; it < 4; ++it) {
+            for (int it = 0; it < 2; ++it) {
                 const float wx0 = o.w[it].x * xs, wx1 = o.w[it].y * xs;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const uint32_t a0 = o.x[it][0][i >> 1], a1 = o.x[it][1][i >> 1];
                     const bool hi = i & 1;
-                    xt[i * XT_STRIDE + 32 * it] = pack_f16x2((hi ? bf16x2_hi(a0) : bf16x2_lo(a0)) * wx0,
+                    xt[i * XT_STRIDE + 64 * it] = pack_f16x2((hi ? bf16x2_hi(a0) : bf16x2_lo(a0)) * wx0,
                                                              (hi ? bf16x2_hi(a1) : bf16x2_lo(a1)) * wx1);
                 }
             }
