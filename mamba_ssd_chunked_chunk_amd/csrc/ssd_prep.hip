@@ -196,9 +196,17 @@ __device__ __forceinline__ void gram_tiles(const Params &p, int c, int g, int q,
 
 template <int N>
 __global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(Params p) {
-    const int c = blockIdx.x;
-    const int g = blockIdx.y;
-    const int q = blockIdx.z;
+    // XCD-aware decode: workgroup ids go to the eight XCDs round-robin; every
+    // workgroup (group, pair) of chunk c gets an id congruent to c mod 8, so
+    // they all run on one XCD and read the chunk's B and C into one L2
+    const int xcd = blockIdx.x & 7;
+    const int slot = blockIdx.x >> 3;
+    const int per = 4 * p.G;  // workgroups per chunk
+    const int c = (slot / per) * 8 + xcd;
+    const int rem = slot - (slot / per) * per;
+    const int g = rem >> 2;
+    const int q = rem & 3;
+    if (c >= p.nchunks_grid) return;  // the grid's padding to a multiple of 8 chunks (uniform)
     const bool lead = g == 0 && q == 0;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -313,7 +321,7 @@ __global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(Params p) {
 }
 
 hipError_t launch_prep(const Params &p, const Launch &l) {
-    const dim3 grid((unsigned)p.nchunks_grid, (unsigned)p.G, 4);
+    const dim3 grid((unsigned)((p.nchunks_grid + 7) / 8 * 8 * 4 * p.G));
     switch (p.N) {
     case 64: return launch_kernel(ssd_prep_kernel<64>, grid, dim3(kPrepThreads), l, p);
     case 128: return launch_kernel(ssd_prep_kernel<128>, grid, dim3(kPrepThreads), l, p);

@@ -127,6 +127,18 @@ def test_small_cases(name, route):
     full_check(prob, DEFAULT if route == "default" else CHUNKED)
 
 
+@pytest.mark.parametrize("nseq", [2, 4])
+def test_head_blocks_dstate64(nseq):
+    """dstate 64 with 16 heads in one group and 128 or 256 chunks: the
+    chunked kernels pick 8 or 16 heads per workgroup (one workgroup per
+    compute unit), a block size no other dstate-64 case reaches.  Every
+    sequence is compared with the oracle."""
+    prob = small_problem([16384] * nseq, H=16, P=64, G=1, N=64, max_slots=nseq + 2, seed=120 + nseq,
+                         init="bernoulli")
+    wy, wf = full_check(prob)
+    print(f"dstate 64, {nseq} x 16384: worst y ratio {wy:.3f}, worst final {wf:.2e}")
+
+
 # lengths around the short-path limit and the fused kernel's 16-token K-steps
 # and 32-token row blocks, with empty and chunked neighbours
 MIXED_LENS = [1, 2, 15, 16, 17, 31, 32, 33, 0, 64, 95, 96, 97, 127, 128, 129, 255, 300]
