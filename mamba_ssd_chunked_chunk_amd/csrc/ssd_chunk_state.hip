@@ -23,13 +23,17 @@
 //     head ahead, and stage (w x)^T into one of two LDS buffers as fp16 under
 //     the power of two that puts max|w| max|x| in [2^14, 2^15).
 // One barrier per head: while the consumers multiply head k-1 out of one
-// buffer, the producers stage head k into the other, so the vector work of
-// the staging and the matrix products overlap.
+// buffer (and store head k-2), the producers stage head k into the other, so
+// the vector work of the staging and the matrix products overlap.
 // Workgroups are numbered so that all head blocks of a chunk land on one XCD
 // (dispatch is round-robin over the 8 XCDs) and share the chunk's B operands
 // in its L2.
 // Output: S as fp16 in [chunk][head][p][n], each 32x32 tile under the power
-// of two that puts its max |S| in [2^14, 2^15) (sexp).
+// of two that puts its max |S| in [2^14, 2^15) (sexp).  The tiles go through
+// a double-buffered LDS area and are stored one phase later as whole rows
+// (16 bytes per lane, N/8 lanes per row): stores of a tile's 32 rows x 64
+// bytes straight from the MFMA layout touch 32 cache lines per instruction
+// and took about twice as long for the same bytes.
 #include "ssd_common.hpp"
 
 namespace ssd {
@@ -46,10 +50,20 @@ constexpr int kThreads = 64 * (kConsumers + kProducers);
 // two rows 16 banks apart).
 constexpr int XT_STRIDE = 130;
 
+// dwords per row of the S staging area: N/2 (N fp16) + 2.  The consumers'
+// 8-byte writes (rows 0..31 of one column per 32 lanes) then fall on distinct
+// bank pairs, and the 16-byte reads for the stores are contiguous in a row.
+template <int N>
+struct SStride {
+    static constexpr int value = N / 2 + 2;
+};
+
+template <int N>
 struct __attribute__((aligned(16))) StateSmem {
-    uint32_t xt[2][kHeadDim * XT_STRIDE];  // (w x)^T 2^sx: row p, fp16 token pairs; head k in buffer k & 1
-    float red[2][3][kProducers];           // per producer wavefront: max |w|, max |x| over p < 32, over p >= 32
-    int sx[2];                             // scale exponent of the head in buffer b
+    uint32_t xt[2][kHeadDim * XT_STRIDE];             // (w x)^T 2^sx: row p, fp16 token pairs; head k in buffer k & 1
+    uint32_t sbuf[2][kHeadDim * SStride<N>::value];   // S of head k (fp16, per-tile scales), row p, in buffer k & 1
+    float red[2][3][kProducers];                      // per producer wavefront: max |w|, max |x| over p < 32, over p >= 32
+    int sx[2];                                        // scale exponent of the head in buffer b
 };
 
 // A producer thread's inputs of one head: x at token pairs pq + 64 it (two
@@ -74,7 +88,7 @@ template <int N, int HB>
 __global__ __launch_bounds__(kThreads) void ssd_chunk_state_kernel(Params p) {
     constexpr int NT = N / 32;
     constexpr int TPW = N == 256 ? 2 : 1;  // p tiles per consumer wavefront
-    __shared__ StateSmem sm;
+    __shared__ StateSmem<N> sm;
 
     // ---- XCD-aware decode: all head blocks of chunk c share one XCD
     const int nhb = p.H / HB;
@@ -93,14 +107,17 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_state_kernel(Params p) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool producer = wave >= kConsumers;  // wavefront-uniform
+    // phases 0 .. HB+1 (products of head j-1 and stores of head j-2 in phase
+    // j), rounded up to pairs
+    constexpr int kPhases = (HB + 3) & ~1;
 
-    // Phase j (j = 0 .. HB, and one more when HB is odd, so that phases come
-    // in pairs and the two register sets of each role alternate at compile
-    // time): producers stage head j into buffer j & 1 and analyse head j+1;
-    // consumers multiply head j-1.  Each role runs its own loop with the same
-    // barriers (one per phase, after a prologue barrier).
+    // Phase j (j = 0 .. kPhases-1, in pairs so that the two register sets of
+    // each role alternate at compile time): producers stage head j into
+    // buffer j & 1 and analyse head j+1 (past the last head they repeat it);
+    // consumers store head j-2 and multiply head j-1.  Each role runs its own
+    // loop with the same barriers (one per phase, after a prologue barrier).
     if (producer) {
-        const int pw = wave - kConsumers;  // producer wavefront 0 .. 3
+        const int pw = wave - kConsumers;  // producer wavefront 0 .. 7
         // thread t: p = 8 pv .. 8 pv + 7 of token pairs pq + 64 it, so that
         // each 32-lane half of a wavefront stages 16 consecutive pairs of two
         // rows 8 apart (distinct banks, see XT_STRIDE)
@@ -208,7 +225,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_state_kernel(Params p) {
         analyze(r0, 0);
         __syncthreads();
 #pragma unroll 1
-        for (int j = 0; j <= HB; j += 2) {
+        for (int j = 0; j < kPhases; j += 2) {
             stage(j, 0, r0);
             __builtin_amdgcn_sched_barrier(0);
             load_head(j + 2, r0);
@@ -280,29 +297,46 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_state_kernel(Params p) {
                 // every lane: the same value
                 p.sexp[(((int64_t)c * p.H + h) * 2 + pt) * NT + nt] = ea + sx + sb;
                 const float as = ldexpf(1.0f, ea);
-                // lane l holds n = 8a + 4(l/32) + 0..3 of row p; per pair of
-                // groups (a, a+1) a v_permlane32_swap per dword gives lanes l
-                // and l+32 8 consecutive n each: one 16-byte store, 32
-                // contiguous bytes per row
-                uint16_t *row = p.states + (((int64_t)c * p.H + h) * kHeadDim + r) * N + 32 * nt + 8 * hl;
+                // into the staging area: lane l holds n = 32 nt + 8a + 4(l/32)
+                // + 0..3 of row p, one 8-byte write per a
+                uint32_t *srow = sm.sbuf[b] + r * SStride<N>::value + 16 * nt + 2 * hl;
 #pragma unroll
-                for (int a = 0; a < 4; a += 2) {
-                    const uint32_t a0 = pack_f16x2(acc[4 * a] * as, acc[4 * a + 1] * as);
-                    const uint32_t a1 = pack_f16x2(acc[4 * a + 2] * as, acc[4 * a + 3] * as);
-                    const uint32_t b0 = pack_f16x2(acc[4 * a + 4] * as, acc[4 * a + 5] * as);
-                    const uint32_t b1 = pack_f16x2(acc[4 * a + 6] * as, acc[4 * a + 7] * as);
-                    const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
-                    const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
-                    *reinterpret_cast<u32x4 *>(row + 8 * a) = u32x4{s0[0], s1[0], s0[1], s1[1]};
-                }
+                for (int a = 0; a < 4; ++a)
+                    *reinterpret_cast<u32x2 *>(srow + 4 * a) =
+                        u32x2{pack_f16x2(acc[4 * a] * as, acc[4 * a + 1] * as),
+                              pack_f16x2(acc[4 * a + 2] * as, acc[4 * a + 3] * as)};
             }
+        };
+        // head hh's S out of staging buffer hh & 1 into [chunk][head][p][n]:
+        // N/8 lanes per row, 16 bytes each, so every store instruction writes
+        // whole rows (8 rows per wavefront)
+        auto store_s = [&](int hh) {
+            constexpr int LPR = N / 8;            // lanes per row
+            constexpr int RPI = 64 / LPR;         // rows per instruction
+            const int h = h_first + hh;
+            const int t = opaque_tid();
+            const int l = t & 63;
+            const int rr = l / LPR, ch = l % LPR;
+#pragma unroll
+            for (int i = 0; i < 8 / RPI; ++i) {
+                const int row = 8 * wave + RPI * i + rr;
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(sm.sbuf[hh & 1] + row * SStride<N>::value + 4 * ch);
+                *reinterpret_cast<u32x4 *>(p.states + (((int64_t)c * p.H + h) * kHeadDim + row) * N + 8 * ch) = v;
+            }
+        };
+        // phase j: the stores of head j-2, then the products of head j-1
+        // (their staging buffer is the other one); the stores of the last head
+        // run in phase HB+1
+        auto phase = [&](int j) {
+            if (j >= 2 && j - 2 < HB) store_s(j - 2);
+            if (mma && j >= 1 && j - 1 < HB) multiply(j - 1);
         };
         __syncthreads();
 #pragma unroll 1
-        for (int j = 0; j <= HB; j += 2) {
-            if (mma && j >= 1) multiply(j - 1);
+        for (int j = 0; j < kPhases; j += 2) {
+            phase(j);
             __syncthreads();
-            if (mma && j + 1 <= HB) multiply(j);
+            phase(j + 1);
             __syncthreads();
         }
     }
