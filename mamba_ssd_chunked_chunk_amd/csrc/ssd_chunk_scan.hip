@@ -546,27 +546,72 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(Params p) {
                     for (int e = 0; e < 16; ++e) acc[pt][e] *= rs;
             }
             diag_tile(sm, cs2, dts, acc, lane, rb, ci, cap + lmg, ldexpf(dh, smx - xe));
-            // ---- back to unit scale, store bf16.  Lane l holds p = 8a + 4(l/32)
-            // + 0..3 of token i_l for a = 0..3; for each pair of groups (a, a+1)
-            // one v_permlane32_swap per dword trades the upper half-wavefront's
-            // group a for the lower one's group a+1, so lanes l and l+32 (same
-            // token) each hold 8 consecutive p: one 16-byte store, 32
-            // contiguous bytes per token.
-            if (i_l < len) {  // the same for lanes l and l+32
+            // ---- back to unit scale, store bf16.  Lane l holds p = 32 pt + 8a +
+            // 4(l/32) + 0..3 of token i_l (a = 0..3).  Stores that write whole
+            // 128-byte lines (8 tokens x 64 p per instruction) run at about twice
+            // the rate of 32-byte pieces of 32 lines, so three exchanges first
+            // move the p bits above 2 into lane bits and token bits into the
+            // register index: a 32-lane swap trades p bit 2 (lane bit 5) for p
+            // bit 3, a 16-lane swap p bit 4 for token bit 4 (lane bit 4), and a
+            // quad exchange p bit 5 for token bit 0 (lane bit 0).  Lane l then
+            // holds the 16-byte piece 4(l & 1) + 2((l >> 4) & 1) + (l >> 5) of
+            // the tokens 32 rb + 16 t4 + (l & 14) + b (t4, b = 0, 1), one store
+            // each.
+            // The buffer store's range check (the chunk's rows of y) drops the
+            // tokens past the chunk end without a branch.
+            {
                 const float inv = ldexpf(1.0f, -smx);
-                uint16_t *dst = p.y + ((t0 + i_l) * p.H + h) * kHeadDim + 8 * hl;
+                uint32_t e[2][2][2][2];  // [p bit 5][p bit 4][p bit 2][p bit 1]
 #pragma unroll
-                for (int pt = 0; pt < 2; ++pt) {
+                for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
-                    for (int a = 0; a < 4; a += 2) {
-                        const uint32_t a0 = pack_bf16x2(acc[pt][4 * a] * inv, acc[pt][4 * a + 1] * inv);
-                        const uint32_t a1 = pack_bf16x2(acc[pt][4 * a + 2] * inv, acc[pt][4 * a + 3] * inv);
-                        const uint32_t b0 = pack_bf16x2(acc[pt][4 * a + 4] * inv, acc[pt][4 * a + 5] * inv);
-                        const uint32_t b1 = pack_bf16x2(acc[pt][4 * a + 6] * inv, acc[pt][4 * a + 7] * inv);
-                        const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
-                        const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
-                        *reinterpret_cast<u32x4 *>(dst + 32 * pt + 8 * a) = u32x4{s0[0], s1[0], s0[1], s1[1]};
-                    }
+                    for (int a = 0; a < 4; a += 2)
+#pragma unroll
+                        for (int q = 0; q < 2; ++q) {
+                            const uint32_t lo = pack_bf16x2(acc[pt][4 * a + 2 * q] * inv, acc[pt][4 * a + 2 * q + 1] * inv);
+                            const uint32_t hi = pack_bf16x2(acc[pt][4 * a + 4 + 2 * q] * inv, acc[pt][4 * a + 5 + 2 * q] * inv);
+                            const auto sw = __builtin_amdgcn_permlane32_swap(lo, hi, false, false);
+                            e[pt][a >> 1][0][q] = sw[0];
+                            e[pt][a >> 1][1][q] = sw[1];
+                        }
+                uint32_t f[2][2][2][2];  // [p bit 5][token bit 4][p bit 2][p bit 1]
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+#pragma unroll
+                        for (int q = 0; q < 2; ++q) {
+                            const auto sw = __builtin_amdgcn_permlane16_swap(e[pt][0][u][q], e[pt][1][u][q], false, false);
+                            f[pt][0][u][q] = sw[0];
+                            f[pt][1][u][q] = sw[1];
+                        }
+                const bool odd = lane & 1;
+                const uint64_t ybase = reinterpret_cast<uint64_t>(p.y + t0 * p.H * kHeadDim);
+                // readfirstlane returns int: widen each word through uint32_t
+                // (a direct cast would sign-extend the low word into the high one)
+                const uint64_t yb = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)ybase) |
+                                    ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(ybase >> 32)) << 32);
+                const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
+                    reinterpret_cast<void *>(yb), 0, len * p.H * kHeadDim * 2, kBufferFormat32);
+                const int piece = 4 * (lane & 1) + 2 * ((lane >> 4) & 1) + (lane >> 5);
+                const int tok = 32 * rb + (lane & 14);
+#pragma unroll
+                for (int t4 = 0; t4 < 2; ++t4) {
+                    uint32_t g[2][2][2];  // [token bit 0][p bit 2][p bit 1]
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+#pragma unroll
+                        for (int q = 0; q < 2; ++q) {
+                            const uint32_t send = odd ? f[0][t4][u][q] : f[1][t4][u][q];
+                            const uint32_t got = __builtin_amdgcn_update_dpp(0u, send, kQuadSwap01, 0xF, 0xF, false);
+                            g[0][u][q] = odd ? got : f[0][t4][u][q];
+                            g[1][u][q] = odd ? f[1][t4][u][q] : got;
+                        }
+#pragma unroll
+                    for (int t0b = 0; t0b < 2; ++t0b)
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            u32x4{g[t0b][0][0], g[t0b][0][1], g[t0b][1][0], g[t0b][1][1]}, yr,
+                            ((tok + 16 * t4 + t0b) * p.H + h) * (kHeadDim * 2) + 16 * piece, 0, 0);
                 }
             }
         }

@@ -24,6 +24,11 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kShortMax = 128;   // longest sequence the short-path kernel takes
 constexpr int kRecurMax = 4;     // longest sequence the token-recurrence kernel takes
 constexpr int kNoExponent = 1000;  // stored scale exponent of an all-zero block of x
+// Word 3 of a raw buffer resource: 32-bit data format, no swizzle; accesses at
+// offsets past the resource's byte count are dropped by the range check.
+constexpr int kBufferFormat32 = 0x00020000;
+// DPP quad permutation [1, 0, 3, 2]: each lane reads its neighbour (lane ^ 1).
+constexpr int kQuadSwap01 = 0xB1;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
