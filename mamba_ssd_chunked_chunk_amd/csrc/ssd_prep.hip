@@ -42,22 +42,23 @@
 namespace ssd {
 
 namespace {
-constexpr int kPrepThreads = 256;
+constexpr int kPrepThreads = 512;
 constexpr int kPrepWaves = kPrepThreads / 64;
 constexpr int R_STRIDE = 20;  // dwords per staged row of 32 bf16 + pad
 }  // namespace
 
 // Tile i (0..8) of row-block pair q: row block q for i <= q (column blocks
 // 0..q), else row block 7-q (column blocks 0..7-q).  Wavefront W of the
-// workgroup takes tiles W, W+4, W+8.
+// workgroup takes tiles W and W+8.
 __host__ __device__ constexpr int pair_rb(int q, int i) { return i <= q ? q : 7 - q; }
 __host__ __device__ constexpr int pair_t(int q, int i) { return i <= q ? i : i - q - 1; }
-__host__ __device__ constexpr int wave_ntiles(int W) { return W == 0 ? 3 : 2; }
+__host__ __device__ constexpr int wave_ntiles(int W) { return W == 0 ? 2 : 1; }
 
 // The C.B^T tiles of wavefront W for chunk c, group g, row-block pair q, and
-// the B^T operand slices of the pair.  W is a template parameter so that the
-// number of tiles, and with it every MFMA, is fixed at compile time.
-template <int N, int W>
+// the B^T operand slices of the pair, PD0 slices in flight in registers.  W
+// is a template parameter so that the number of tiles, and with it every
+// MFMA, is fixed at compile time.
+template <int N, int W, int PD0>
 __device__ __forceinline__ void gram_tiles(const Params &p, int c, int g, int q, int64_t t0, int len, uint32_t *s_b,
                                            uint32_t *s_c, float *s_red, float (*s_bmax)[kPrepWaves]) {
     constexpr int KS = N / 32;
@@ -66,12 +67,14 @@ __device__ __forceinline__ void gram_tiles(const Params &p, int c, int g, int q,
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int hl = lane >> 5;
-    constexpr int PD = KS < 3 ? KS : 3;  // slices in flight
+    constexpr int PD = KS < PD0 ? KS : PD0;  // slices in flight
     constexpr int BV = kChunk * 4 / kPrepThreads;  // 16-byte pieces of B per thread and slice
-    // this thread's pieces: B row (tid + 256 it) / 4, C local row tid / 4
-    // (rows 0..31: row block q, 32..63: row block 7-q), piece tid % 4
+    // this thread's pieces: B row (tid + kPrepThreads it) / 4, C local row
+    // (tid % 256) / 4 (rows 0..31: row block q, 32..63: row block 7-q; the
+    // threads from 256 on load the same pieces again and do not store them),
+    // piece tid % 4
     const int v = tid & 3;
-    const int cr = tid >> 2;
+    const int cr = (tid & 255) >> 2;
     const int crow = cr < 32 ? 32 * q + cr : 32 * (7 - q) + cr - 32;
     u32x4 rbv[PD][BV], rcv[PD];
     auto load_slice = [&](int ks, int d) {
@@ -98,7 +101,7 @@ __device__ __forceinline__ void gram_tiles(const Params &p, int c, int g, int q,
             const int j = (tid + it * kPrepThreads) >> 2;
             *reinterpret_cast<u32x4 *>(s_b + j * R_STRIDE + v * 4) = rbv[ks % PD][it];
         }
-        *reinterpret_cast<u32x4 *>(s_c + cr * R_STRIDE + v * 4) = rcv[ks % PD];
+        if (tid < 256) *reinterpret_cast<u32x4 *>(s_c + cr * R_STRIDE + v * 4) = rcv[ks % PD];
         const bool frag = (ks & 3) == q;  // uniform: this workgroup writes slice ks's B^T operands
         if (frag) {
             // max |B| of this thread's share of the slice (rows past the chunk
@@ -117,7 +120,7 @@ __device__ __forceinline__ void gram_tiles(const Params &p, int c, int g, int q,
         for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
             for (int i = 0; i < NTW; ++i) {
-                const int ti = W + 4 * i;
+                const int ti = W + kPrepWaves * i;
                 const int rb = pair_rb(q, ti), t = pair_t(q, ti);
                 const int lr = rb == q ? 0 : 32;  // local C row block
                 const bf16x8 cb = __builtin_bit_cast(
@@ -160,7 +163,7 @@ __device__ __forceinline__ void gram_tiles(const Params &p, int c, int g, int q,
     // 8(e/4) + 4(l/32) + e%4, i - 32 rb = l%32), so readers need no mask
 #pragma unroll
     for (int i = 0; i < NTW; ++i)
-        if (pair_rb(q, W + 4 * i) == pair_t(q, W + 4 * i))
+        if (pair_rb(q, W + kPrepWaves * i) == pair_t(q, W + kPrepWaves * i))
 #pragma unroll
             for (int e = 0; e < 16; ++e)
                 if (8 * (e >> 2) + 4 * hl + (e & 3) > l32) accg[i][e] = 0.f;
@@ -183,7 +186,7 @@ __device__ __forceinline__ void gram_tiles(const Params &p, int c, int g, int q,
     uint16_t *dst = p.cbt + ((int64_t)c * p.G + g) * 36 * 1024;
 #pragma unroll
     for (int i = 0; i < NTW; ++i) {
-        const int rb = pair_rb(q, W + 4 * i), t = pair_t(q, W + 4 * i);
+        const int rb = pair_rb(q, W + kPrepWaves * i), t = pair_t(q, W + kPrepWaves * i);
         u32x4 *o = reinterpret_cast<u32x4 *>(dst + (rb * (rb + 1) / 2 + t) * 1024 + lane * 16);
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
@@ -194,7 +197,7 @@ __device__ __forceinline__ void gram_tiles(const Params &p, int c, int g, int q,
     }
 }
 
-template <int N>
+template <int N, int PD>
 __global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(Params p) {
     // XCD-aware decode: workgroup ids go to the eight XCDs round-robin; every
     // workgroup (group, pair) of chunk c gets an id congruent to c mod 8, so
@@ -313,21 +316,36 @@ __global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(Params p) {
 
     // ---- C.B^T tiles of row blocks q and 7-q, B^T operands of slices q, q+4, ...
     switch (__builtin_amdgcn_readfirstlane(wave)) {
-    case 0: gram_tiles<N, 0>(p, c, g, q, t0, len, s_b, s_c, s_red, s_bmax); break;
-    case 1: gram_tiles<N, 1>(p, c, g, q, t0, len, s_b, s_c, s_red, s_bmax); break;
-    case 2: gram_tiles<N, 2>(p, c, g, q, t0, len, s_b, s_c, s_red, s_bmax); break;
-    default: gram_tiles<N, 3>(p, c, g, q, t0, len, s_b, s_c, s_red, s_bmax); break;
+    case 0: gram_tiles<N, 0, PD>(p, c, g, q, t0, len, s_b, s_c, s_red, s_bmax); break;
+    case 1: gram_tiles<N, 1, PD>(p, c, g, q, t0, len, s_b, s_c, s_red, s_bmax); break;
+    case 2: gram_tiles<N, 2, PD>(p, c, g, q, t0, len, s_b, s_c, s_red, s_bmax); break;
+    case 3: gram_tiles<N, 3, PD>(p, c, g, q, t0, len, s_b, s_c, s_red, s_bmax); break;
+    case 4: gram_tiles<N, 4, PD>(p, c, g, q, t0, len, s_b, s_c, s_red, s_bmax); break;
+    case 5: gram_tiles<N, 5, PD>(p, c, g, q, t0, len, s_b, s_c, s_red, s_bmax); break;
+    case 6: gram_tiles<N, 6, PD>(p, c, g, q, t0, len, s_b, s_c, s_red, s_bmax); break;
+    default: gram_tiles<N, 7, PD>(p, c, g, q, t0, len, s_b, s_c, s_red, s_bmax); break;
     }
 }
 
-hipError_t launch_prep(const Params &p, const Launch &l) {
-    const dim3 grid((unsigned)((p.nchunks_grid + 7) / 8 * 8 * 4 * p.G));
+template <int PD>
+static hipError_t launch_pd(const Params &p, const Launch &l, dim3 grid) {
     switch (p.N) {
-    case 64: return launch_kernel(ssd_prep_kernel<64>, grid, dim3(kPrepThreads), l, p);
-    case 128: return launch_kernel(ssd_prep_kernel<128>, grid, dim3(kPrepThreads), l, p);
-    case 256: return launch_kernel(ssd_prep_kernel<256>, grid, dim3(kPrepThreads), l, p);
+    case 64: return launch_kernel(ssd_prep_kernel<64, PD>, grid, dim3(kPrepThreads), l, p);
+    case 128: return launch_kernel(ssd_prep_kernel<128, PD>, grid, dim3(kPrepThreads), l, p);
+    case 256: return launch_kernel(ssd_prep_kernel<256, PD>, grid, dim3(kPrepThreads), l, p);
     default: return hipErrorInvalidValue;
     }
+}
+
+// Slices in flight: all of them at dstate 64 and 128 (76 and 100 registers);
+// at 256, all eight while the full chunks fit one workgroup per compute unit
+// (the workgroup's latency is then the kernel's; 148 registers, one workgroup
+// per CU), else three (120 registers, two workgroups per CU, which hide each
+// other's latency).
+hipError_t launch_prep(const Params &p, const Launch &l) {
+    const dim3 grid((unsigned)((p.nchunks_grid + 7) / 8 * 8 * 4 * p.G));
+    const bool all = p.N < 256 || p.T / kChunk * 4 * p.G <= p.num_cus;
+    return all ? launch_pd<8>(p, l, grid) : launch_pd<3>(p, l, grid);
 }
 
 }  // namespace ssd
