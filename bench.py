@@ -146,8 +146,7 @@ def algorithmic(prob, short_max=SHORT_MAX):
     return dict(
         whole=dict(bytes=2 * (bx + sx + rx) + 2 * (bbc + sbc + rbc) + bdt + sdt + rdt + pool_rw + spool + rpool,
                    flops=fl),
-        ssd_prep=dict(bytes=2 * bbc + bdt, flops=f["cb"]),
-        ssd_chunk_state=dict(bytes=bx, flops=f["state"]),
+        ssd_chunk_state=dict(bytes=bx + 2 * bbc + bdt, flops=f["state"] + f["cb"]),
         ssd_state_passing=dict(bytes=pool_rw, flops=0),
         ssd_chunk_scan=dict(bytes=2 * bx + bbc, flops=f["off"] + f["diag"]),
         ssd_short=dict(bytes=2 * sx + 2 * sbc + sdt + spool, flops=sum(sf.values())),

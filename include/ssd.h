@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 16
+#define SSD_ABI_VERSION 17
 #define SSD_MAX_DSTATE 256  /* largest dstate, as in "mamba2_ssd_scan", comptime MAX_DSTATE */
 #define SSD_SHORT_PATH_LIMIT 128  /* longest sequence the short path can take */
 #define SSD_RECUR_LIMIT 4         /* of those, the longest the token recurrence takes */
@@ -144,13 +144,6 @@ typedef struct ssd_problem {
  *                                         hold 0 where j > i
  *   gexp      int32[nchunks_max][G][4]    exponent of the cbt tiles of row
  *                                         blocks q and 7-q
- *   bfrag     fp16[nchunks_max][G][N/32][16][64][8]  B^T of the chunk as MFMA
- *                                         A operands: n tile nt, K-step s,
- *                                         lane l holds B[t0 + 16s + 8(l/32)
- *                                         + 0..7][g][32nt + l%32] (0 past the
- *                                         chunk end), scaled by
- *                                         2^bexp[c][g][nt]
- *   bexp      int32[nchunks_max][G][N/32] exponent of each bfrag n tile
  *   states    fp16[nchunks_max][H][P][N]  chunk's own state contribution,
  *                                         element (p, n) scaled by
  *                                         2^sexp[c][h][p/32][n/32]
@@ -173,8 +166,7 @@ typedef struct ssd_problem {
 typedef struct ssd_workspace_layout {
     size_t total_bytes;
     int64_t nchunks_max;
-    size_t meta, chunk_off, desc, dts, cs2, cbt, gexp, bfrag, bexp, states, sexp, hin, hexp, xexp, seq_list,
-        recur_list;
+    size_t meta, chunk_off, desc, dts, cs2, cbt, gexp, states, sexp, hin, hexp, xexp, seq_list, recur_list;
 } ssd_workspace_layout;
 
 /* ABI version of the loaded library (SSD_ABI_VERSION it was built with). */

@@ -48,8 +48,8 @@ class ssd_workspace_layout(ctypes.Structure):
     _fields_ = [("total_bytes", ctypes.c_size_t), ("nchunks_max", ctypes.c_int64),
                 ("meta", ctypes.c_size_t), ("chunk_off", ctypes.c_size_t),
                 ("desc", ctypes.c_size_t), ("dts", ctypes.c_size_t), ("cs2", ctypes.c_size_t),
-                ("cbt", ctypes.c_size_t), ("gexp", ctypes.c_size_t), ("bfrag", ctypes.c_size_t),
-                ("bexp", ctypes.c_size_t), ("states", ctypes.c_size_t), ("sexp", ctypes.c_size_t),
+                ("cbt", ctypes.c_size_t), ("gexp", ctypes.c_size_t),
+                ("states", ctypes.c_size_t), ("sexp", ctypes.c_size_t),
                 ("hin", ctypes.c_size_t), ("hexp", ctypes.c_size_t), ("xexp", ctypes.c_size_t),
                 ("seq_list", ctypes.c_size_t), ("recur_list", ctypes.c_size_t)]
 
@@ -58,7 +58,7 @@ _lock = threading.Lock()
 _lib = None
 
 # SSD_ABI_VERSION of include/ssd.h that the ctypes structures below mirror
-ABI_VERSION = 16
+ABI_VERSION = 17
 NOALLOC_SCRATCH_BYTES = 64 << 20  # SSD_NOALLOC_SCRATCH_BYTES
 STATE_F32, STATE_BF16 = 0, 1  # SSD_STATE_F32, SSD_STATE_BF16
 SHORT_PATH_LIMIT = 128  # SSD_SHORT_PATH_LIMIT

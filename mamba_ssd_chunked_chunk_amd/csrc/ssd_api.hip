@@ -63,7 +63,8 @@ int short_max_of(const ssd_problem *p) {
 // the short path on, only sequences longer than its limit reach them, at most
 // T / (limit + 1) of them, each with at most one partial chunk beyond
 // floor(T / 256) full ones (at least 1 each: a grid dimension cannot be 0,
-// and prep's first workgroup publishes the chunk count and the lists).
+// and the first workgroup of chunk_state publishes the chunk count and the
+// lists).
 void routed_bounds(const ssd_problem *p, int *nseq, int64_t *nchunks) {
     const int sm = short_max_of(p);
     const int64_t T = p->total_len;
@@ -87,8 +88,6 @@ void layout_of(const ssd_problem *p, ssd_workspace_layout *L) {
     L->cs2 = off;       off = align_up(off + (size_t)ncm * H * ssd::kChunk * sizeof(float));
     L->cbt = off;       off = align_up(off + (size_t)ncm * G * 36 * 64 * 16 * sizeof(uint16_t));
     L->gexp = off;      off = align_up(off + (size_t)ncm * G * 4 * sizeof(int32_t));
-    L->bfrag = off;     off = align_up(off + (size_t)ncm * G * (size_t)p->dstate * ssd::kChunk * sizeof(uint16_t));
-    L->bexp = off;      off = align_up(off + (size_t)ncm * G * ((size_t)p->dstate / 32) * sizeof(int32_t));
     L->states = off;    off = align_up(off + (size_t)ncm * H * PN * sizeof(uint16_t));
     L->sexp = off;      off = align_up(off + (size_t)ncm * H * 2 * ((size_t)p->dstate / 32) * sizeof(int32_t));
     L->hin = off;       off = align_up(off + (size_t)ncm * H * PN * sizeof(uint16_t));
@@ -142,10 +141,10 @@ ssd_status ssd_workspace_get_layout(const ssd_problem *prob, ssd_workspace_layou
     return SSD_OK;
 }
 
-static const char *const kKernelNames[] = {"ssd_prep",       "ssd_chunk_state", "ssd_state_passing",
-                                           "ssd_chunk_scan", "ssd_short",       "ssd_recur"};
-static constexpr int kNumKernels = 6;
-static constexpr int kFirstShortKernel = 4;  // this and the later ones serve the short path
+static const char *const kKernelNames[] = {"ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan", "ssd_short",
+                                           "ssd_recur"};
+static constexpr int kNumKernels = 5;
+static constexpr int kFirstShortKernel = 3;  // this and the later ones serve the short path
 
 int ssd_kernel_count(void) { return kNumKernels; }
 
@@ -243,16 +242,14 @@ static ssd_status run_scan(
     p.recur_list = reinterpret_cast<int32_t *>(ws + L.recur_list);
     p.cbt = reinterpret_cast<uint16_t *>(ws + L.cbt);
     p.gexp = reinterpret_cast<int32_t *>(ws + L.gexp);
-    p.bfrag = reinterpret_cast<uint16_t *>(ws + L.bfrag);
-    p.bexp = reinterpret_cast<int32_t *>(ws + L.bexp);
     p.hin = reinterpret_cast<uint16_t *>(ws + L.hin);
     p.states = reinterpret_cast<uint16_t *>(ws + L.states);
     p.sexp = reinterpret_cast<int32_t *>(ws + L.sexp);
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t (*const launchers[kNumKernels])(const ssd::Params &, const ssd::Launch &) = {
-        ssd::launch_prep,       ssd::launch_chunk_state, ssd::launch_state_passing,
-        ssd::launch_chunk_scan, ssd::launch_short,       ssd::launch_recur};
+        ssd::launch_chunk_state, ssd::launch_state_passing, ssd::launch_chunk_scan, ssd::launch_short,
+        ssd::launch_recur};
     for (int k = 0; k < kNumKernels; ++k) {
         // no sequence can take the short path: its kernels would have nothing
         // to do, so they are not launched (their completion events, if any,

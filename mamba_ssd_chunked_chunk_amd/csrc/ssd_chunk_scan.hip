@@ -2,7 +2,7 @@
 //
 // For chunk c of sequence b, head h (group g), and rows i, j of the chunk
 // (cs2 = log2(e) * cumulative A*dts, h_in = state entering the chunk):
-//   G[i][j]   = sum_n C[i,g,n] * B[j,g,n]                  (formed by the prep step)
+//   G[i][j]   = sum_n C[i,g,n] * B[j,g,n]            (formed by the chunk-state step)
 //   M[i][j]   = G[i][j] * exp2(cs2_i - cs2_j) * dts_j     for j <= i, else 0
 //   y[i][p]   = sum_j M[i][j] * x[j,h,p]                              (diagonal block)
 //             + exp2(cs2_i) * sum_n C[i,g,n] * h_in[p][n]             (off-diagonal part)
@@ -17,8 +17,8 @@
 // SIMD own row blocks k and 7-k, so each SIMD handles 9 of the 36
 // lower-triangular 32x32 tiles.  The operands the heads of a group share,
 // the wavefront's C rows (registers, converted here to fp16 under a
-// per-wavefront power of two) and its C.B^T tiles (from the prep step, LDS),
-// are loaded once and stay on chip while the workgroup walks its heads; each
+// per-wavefront power of two) and its C.B^T tiles (from the chunk-state
+// step, LDS), are loaded once and stay on chip while the workgroup walks its heads; each
 // head's x and h_in are loaded into registers during the previous head's
 // products.  Workgroups
 // are numbered so that all head blocks of a chunk land on one XCD (dispatch

@@ -82,8 +82,6 @@ struct Params {
     float *cs2;          // [nchunks_max][H][256]: log2(e) * inclusive cumsum of A dts
     uint16_t *cbt;       // [nchunks_max][G][36][64][16] fp16 C.B^T tiles * 2^gexp, accumulator order
     int32_t *gexp;       // [nchunks_max][G][4]: tiles of row blocks q and 7-q
-    uint16_t *bfrag;     // [nchunks_max][G][N/32][16][64][8] fp16 B^T MFMA A operands * 2^bexp
-    int32_t *bexp;       // [nchunks_max][G][N/32]
     uint16_t *states;    // [nchunks_max][H][P][N] fp16 chunk contributions, 32x32 tile scaled by 2^sexp
     int32_t *sexp;       // [nchunks_max][H][2][N/32]: per 32x32 tile (p tile, n tile)
     uint16_t *hin;       // [nchunks_max][H][P][N] fp16, row p scaled by 2^hexp
@@ -380,7 +378,6 @@ inline int short_head_slices(const Params &p) {
     return hz;
 }
 
-hipError_t launch_prep(const Params &p, const Launch &l);
 hipError_t launch_chunk_state(const Params &p, const Launch &l);
 hipError_t launch_state_passing(const Params &p, const Launch &l);
 hipError_t launch_chunk_scan(const Params &p, const Launch &l);

@@ -14,8 +14,8 @@
 // the same but whose per-token arithmetic is not.
 //
 // A grid of at most 16384 workgroups of 512 threads walks the (sequence,
-// head) items of the sequences prep listed for it (recur_list), each
-// workgroup a block of consecutive items, so a batch with few of them costs
+// head) items of the sequences listed for it (recur_list, written by the
+// chunk-state step), each workgroup a block of consecutive items, so a batch with few of them costs
 // few live workgroups.  Per item, every load the head needs (its
 // state rows, x and dt of its tokens, the tokens' B and C rows, staged in
 // LDS) is issued before any arithmetic, so the item waits for memory once; at

@@ -18,7 +18,7 @@
 // "Mamba2SSDChunkScanVarlenFwdInplace" (struct description).  A sequence with
 // no tokens writes its initial state (or zeros) back.  With the short path
 // on, the sequences it takes (zero-length ones included) are not walked: the
-// grid runs over the list of the others that prep writes.
+// grid runs over the list of the others that the chunk-state step writes.
 //
 // Chunk contributions arrive as fp16 under one power-of-two exponent per
 // 32x32 tile of (chunk, head).  The chain is fp32.  h_in only feeds the
@@ -157,8 +157,9 @@ __device__ __forceinline__ void walk_chain(const Params &p, int b, int h, int e0
 // whole chain runs on one XCD, and ragged lengths leave most XCDs idle while
 // a few walk the long chains (the ragged 32-sequence workload: 421 us, 145 us
 // in this order).
-// LIST: the sequences are those of the list prep wrote (the short path is on:
-// only sequences longer than its limit are there), else the batch.
+// LIST: the sequences are those of the list the chunk-state step wrote (the
+// short path is on: only sequences longer than its limit are there), else the
+// batch.
 // SB: states stored as bf16 (read widened to fp32, final state rounded once).
 template <int N, bool LIST, bool SB>
 __global__ __launch_bounds__(256) void ssd_state_passing_kernel(Params p) {

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert binding.ssd_abi_version() == binding.ABI_VERSION == 16
+    assert binding.ssd_abi_version() == binding.ABI_VERSION == 17
     for code, name in binding.STATUS_NAMES.items():
         assert lib.ssd_status_string(code).decode().startswith(name)
     assert b"unknown" in lib.ssd_status_string(99)
@@ -57,13 +57,13 @@ def test_workspace_layout_arithmetic(lib):
     ncm = 1024 // 256 + 4  # dstate 256: no short path, all 4 sequences chunked
     assert L["nchunks_max"] == ncm
     assert L["total_bytes"] == binding.ssd_workspace_size(p)
-    keys = ("meta", "chunk_off", "desc", "dts", "cs2", "cbt", "gexp", "bfrag", "bexp", "states", "sexp", "hin",
+    keys = ("meta", "chunk_off", "desc", "dts", "cs2", "cbt", "gexp", "states", "sexp", "hin",
             "hexp", "xexp", "seq_list", "recur_list")
     offs = [L[k] for k in keys]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     need = dict(meta=16, chunk_off=5 * 4, desc=ncm * 16, dts=ncm * 16 * 256 * 4, cs2=ncm * 16 * 256 * 4,
-                cbt=ncm * 1 * 36 * 64 * 16 * 2, gexp=ncm * 1 * 4 * 4, bfrag=ncm * 1 * 8 * 16 * 64 * 8 * 2,
-                bexp=ncm * 1 * 8 * 4, states=ncm * 16 * 64 * 256 * 2, sexp=ncm * 16 * 2 * 8 * 4,
+                cbt=ncm * 1 * 36 * 64 * 16 * 2, gexp=ncm * 1 * 4 * 4,
+                states=ncm * 16 * 64 * 256 * 2, sexp=ncm * 16 * 2 * 8 * 4,
                 hin=ncm * 16 * 64 * 256 * 2, hexp=ncm * 16 * 64 * 4,
                 xexp=ncm * 16 * 2 * 4, seq_list=4 * 4, recur_list=4 * 4)
     ends = offs[1:] + [L["total_bytes"]]
@@ -211,7 +211,7 @@ def test_short_path_limit_is_a_problem_field(lib):
                                   ctypes.byref(n)) == 3
     assert not hasattr(binding, "ssd_set_short_path_max")
     names = [lib.ssd_kernel_name(i).decode() for i in range(lib.ssd_kernel_count())]
-    assert names == ["ssd_prep", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan", "ssd_short", "ssd_recur"]
+    assert names == ["ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan", "ssd_short", "ssd_recur"]
 
 
 def test_noalloc_entry_host_errors(lib):
