@@ -139,6 +139,31 @@ def test_head_blocks_dstate64(nseq):
     print(f"dstate 64, {nseq} x 16384: worst y ratio {wy:.3f}, worst final {wf:.2e}")
 
 
+# (heads, groups, dstate, sequence lengths) that make the chunked kernels split
+# each (chunk, group) over nwg workgroups of HB heads, and so split the four
+# row-block pairs of its C.B^T tiles differently (on a 256-CU device): nwg 16
+# (workgroups 4..15 form no tile), 3 (pairs 0 and 3, 1, 2), 2 at dstate 256,
+# and 8 at dstate 128 with the short path on
+GRAM_SPLITS = {
+    "nwg16_n256": (16, 1, 256, [300, 300]),
+    "nwg3_n256": (12, 1, 256, [6800, 6800, 6800]),
+    "nwg2_n256": (16, 1, 256, [8250] * 4),
+    "nwg8_n128": (8, 1, 128, [700, 700]),
+}
+
+
+@pytest.mark.parametrize("name", list(GRAM_SPLITS))
+def test_gram_tiles_split_over_head_blocks(name):
+    """The workgroups of a chunk and group share its C.B^T tiles (each forms
+    the tiles of its row-block pairs) and read them all back: every sequence
+    is compared with the oracle."""
+    H, G, N, lens = GRAM_SPLITS[name]
+    prob = small_problem(lens, H=H, P=64, G=G, N=N, max_slots=len(lens) + 1, seed=140 + H + N,
+                         init="bernoulli")
+    wy, wf = full_check(prob)
+    print(f"{name}: worst y ratio {wy:.3f}, worst final {wf:.2e}")
+
+
 # lengths around the short-path limit and the fused kernel's 16-token K-steps
 # and 32-token row blocks, with empty and chunked neighbours
 MIXED_LENS = [1, 2, 15, 16, 17, 31, 32, 33, 0, 64, 95, 96, 97, 127, 128, 129, 255, 300]
