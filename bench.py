@@ -304,26 +304,35 @@ def summarize_profile(root, workload, short_max=SHORT_MAX):
             if k.startswith("ssd_"):
                 per[which]["raw"].setdefault(k, []).append(v)
     stats = list(csv.DictReader(open(os.path.join(root, "kt", "run_kernel_stats.csv"))))
-    # the calls bench.py times are the ones that follow its cache-evicting fill
-    # (a call's kernels run in order; a name seen again starts the next call)
-    timed, after_fill, seen = {}, False, set()
+    # the calls bench.py times are the ones that follow its cache-evicting
+    # read (a sum over the flush buffer); the comparison pass, later, follows
+    # fills of it (fills before the first read set up inputs).  A call's
+    # kernels run in order; a name seen again starts the next call.
+    timed = {"read": {}, "write": {}}
+    after, seen, any_read = None, set(), False
     trace = sorted(csv.DictReader(open(os.path.join(root, "kt", "run_kernel_trace.csv"))),
                    key=lambda r: int(r["Start_Timestamp"]))
     for r in trace:
         k = _short(r["Kernel_Name"])
-        if "FillFunctor" in r["Kernel_Name"]:
-            after_fill, seen = True, set()
+        if "reduce_kernel" in r["Kernel_Name"]:
+            after, seen, any_read = "read", set(), True
+        elif "FillFunctor" in r["Kernel_Name"]:
+            after, seen = ("write" if any_read else None), set()
         elif k.startswith("ssd_"):
             if k in seen:
-                after_fill = False
+                after = None
             seen.add(k)
-            if after_fill:
-                timed.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+            if after is not None:
+                timed[after].setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
         else:
-            after_fill = False
-    lines = ["| kernel | calls | avg µs | min µs | max µs | avg µs, timed calls | FETCH KiB/launch "
-             "| WRITE KiB/launch | HBM MB/launch (calibrated) | algorithmic MB/launch |",
-             "|---|---|---|---|---|---|---|---|---|---|"]
+            after = None
+
+    def avg(which, k):
+        v = timed[which].get(k)
+        return "" if not v else f"{statistics.mean(v):.2f} ({len(v)})"
+    lines = ["| kernel | calls | avg µs | min µs | max µs | avg µs, timed calls | avg µs, calls after a write "
+             "flush | FETCH KiB/launch | WRITE KiB/launch | HBM MB/launch (calibrated) | algorithmic MB/launch |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
     traffic = {}
     for r in stats:
         k = _short(r["Name"])
@@ -335,7 +344,7 @@ def summarize_profile(root, workload, short_max=SHORT_MAX):
         a = alg.get(k, {}).get("bytes")
         lines.append(f"| {k} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} "
                      f"| {float(r['MaxNs']) / 1e3:.2f} "
-                     f"| {'' if k not in timed else f'{statistics.mean(timed[k]):.2f} ({len(timed[k])})'} "
+                     f"| {avg('read', k)} | {avg('write', k)} "
                      f"| {'' if f is None else f'{f:.0f}'} "
                      f"| {'' if w is None else f'{w:.0f}'} "
                      f"| {'' if k not in traffic else f'{traffic[k] / 1e6:.1f}'} "
@@ -400,6 +409,28 @@ PER_CONFIG = ["tiny_1x512_h4_n64", "fixed_4x4096_h16_n256", "long_8x16384_h16_n2
               "ragged_32_h128_g8_n128", "short_512_h128_g8_n128"]
 
 
+class CacheFlush:
+    """A 512 MiB buffer, twice the memory-side cache, passed through before
+    each timed call so that the call's inputs come from HBM.  read() sums it:
+    every line the call touches is evicted and the caches hold only clean
+    lines.  write(k) fills it, which also evicts the inputs but leaves up to
+    the whole memory-side cache dirty with the buffer, and the timed call then
+    pays for writing that back: the flush's cost, not the call's."""
+
+    def __init__(self, torch, dev):
+        self.buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        self.buf.fill_(1)
+        self.words = self.buf.view(torch.int64)
+        self.out = torch.empty((), dtype=torch.int64, device=dev)
+        self.torch = torch
+
+    def read(self):
+        self.torch.sum(self.words, dim=0, out=self.out)
+
+    def write(self, k):
+        self.buf.fill_(k & 0xFF)
+
+
 class Runner:
     """One uploaded problem and the library calls that time it."""
 
@@ -458,9 +489,11 @@ class Runner:
         if st != 0:
             raise RuntimeError(self.lib.ssd_status_string(st).decode())
 
-    def measure(self, steps, warmup, flush, warm=True):
+    def measure(self, steps, warmup, flush, warm=True, write_flush=False):
         """warmup untimed calls, then steps calls each preceded by a cache
-        eviction (untimed) and bracketed by the kernels' own events."""
+        eviction (untimed) and bracketed by the kernels' own events.  The
+        eviction reads a 512 MiB buffer; with write_flush it writes it (see
+        CacheFlush)."""
         import numpy as np
         torch, hip = self.torch, self.hip
         ev_sets = [[hip.event() for _ in range(self.nk + 1)] for _ in range(steps)]
@@ -469,7 +502,10 @@ class Runner:
         torch.cuda.synchronize()
         wall0 = time.perf_counter()
         for k in range(steps):
-            flush.fill_(k & 0xFF)
+            if write_flush:
+                flush.write(k)
+            else:
+                flush.read()
             self.call(ev_sets[k])
         torch.cuda.synchronize()
         wall = time.perf_counter() - wall0
@@ -531,7 +567,7 @@ def main():
     torch.cuda.set_device(dev)
     lib = binding.load_library()
     hip = Hip()
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = CacheFlush(torch, dev)
 
     def load(name):
         p = make_workload(name)
@@ -542,6 +578,9 @@ def main():
     run = Runner(torch, lib, hip, dev, prob, args.short_max, args.entry)
     m = run.measure(args.steps, args.warmup, flush)
     ms, kern_us = m["ms"], m["kern_us"]
+    # the same calls after a flush that writes its buffer, for comparison
+    mw = run.measure(args.steps, 2, flush, warm=False, write_flush=True)
+    m["us_per_call"]["mean_after_write_flush"] = mw["us_per_call"]["mean"]
 
     copy_gbs = copy_probe(torch, dev, hip, run.stream)
 

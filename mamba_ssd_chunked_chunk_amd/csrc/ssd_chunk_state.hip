@@ -24,8 +24,8 @@
 //
 // One workgroup per (chunk, block of HB heads of one group); no chunk waits
 // for another.  Sixteen wavefronts.  Prologue, once per workgroup:
-//   - chunk_cumsum of the block's heads (wavefronts 0-7, one wavefront per
-//     head): dts = softplus(dt + dt_bias) (0 past the chunk end) and
+//   - chunk_cumsum of the block's heads (wavefronts 0-7, wavefront w taking
+//     heads w and w + 8): dts = softplus(dt + dt_bias) (0 past the chunk end) and
 //     cs2 = log2(e) * cumsum(A dts), the segment sums of "Mamba chunk scan
 //     with segsum" (description) in base 2, stored for the later steps;
 //   - the chunk's B (256 rows, zero past the chunk end) is staged in LDS

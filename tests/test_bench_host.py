@@ -117,3 +117,72 @@ def test_counter_summary_ratios(tmp_path):
     cells = [c.strip() for c in row.strip("|").split("|")]
     # median of dispatches (scale 1 and 3) = scale 2: 16 waves; per-wave counts unchanged
     assert cells == ["ssd_chunk_scan", "16", "100", "5", "10", "2", "1", "3", "0.25", "0.25", "32.00"]
+
+
+def test_profile_summary_splits_read_and_write_flush_calls(tmp_path, monkeypatch):
+    """bench.py --summarize-profile: the calls after the cache-evicting read
+    (a reduce kernel) are the timed ones, those after a fill the comparison
+    pass, and back-to-back calls count for neither; counters are calibrated
+    by the copy kernel (synthetic rocprofv3 CSVs)."""
+    import contextlib, csv, io
+    root = tmp_path / "prof"
+    names = {k: f"void ssd::{k}_kernel<256, 4>(ssd::Params)" for k in
+             ("ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan")}
+    copy = "void at::native::vectorized_elementwise_kernel<4, at::native::MulFunctor<float>>(int)"
+    for which, per_kernel in (("fetch", 100.0), ("write", 50.0)):
+        (root / which).mkdir(parents=True)
+        with open(root / which / "run_counter_collection.csv", "w", newline="") as fh:
+            w = csv.DictWriter(fh, fieldnames=["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name",
+                                               "Counter_Value"])
+            w.writeheader()
+            # the copy reads and writes 256 MiB: counters read half of that, so the factor is 2
+            w.writerow(dict(Dispatch_Id=1, Kernel_Name=copy, Grid_Size=1, Counter_Name="X",
+                            Counter_Value=bench.COPY_MIB * 1024 / 2))
+            for i, n in enumerate(names.values()):
+                w.writerow(dict(Dispatch_Id=2 + i, Kernel_Name=n, Grid_Size=1, Counter_Name="X",
+                                Counter_Value=per_kernel))
+    (root / "kt").mkdir()
+    rows, t = [], 0
+
+    def launch(name, us):
+        nonlocal t
+        rows.append(dict(Kernel_Name=name, Start_Timestamp=t, End_Timestamp=t + int(us * 1000)))
+        t += int(us * 1000) + 500
+
+    # a fill that sets up inputs, then a warm-up call: neither
+    launch("void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<unsigned char>>(int)", 70)
+    for n in names.values():
+        launch(n, 77)
+    for call in range(2):  # timed: after the read
+        launch("void at::native::reduce_kernel<512, 1, at::native::ReduceOp<long>>(int)", 50)
+        for k, n in names.items():
+            launch(n, 10 + call)
+    launch("void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<unsigned char>>(int)", 70)
+    for n in names.values():
+        launch(n, 20)
+    for n in names.values():  # back to back: neither
+        launch(n, 99)
+    with open(root / "kt" / "run_kernel_trace.csv", "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        w.writerows(rows)
+    with open(root / "kt" / "run_kernel_stats.csv", "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Name", "Calls", "AverageNs", "MinNs", "MaxNs"])
+        w.writeheader()
+        for n in names.values():
+            w.writerow(dict(Name=n, Calls=4, AverageNs=1000, MinNs=1000, MaxNs=1000))
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_sources_hash", lambda: "0123456789abcdef")
+    out = io.StringIO()
+    with contextlib.redirect_stdout(out):
+        bench.summarize_profile(str(root), "fixed_4x4096_h16_n256")
+    rows = {r.split("|")[1].strip(): [c.strip() for c in r.strip("|").split("|")]
+            for r in out.getvalue().splitlines() if r.startswith("| ssd_")}
+    assert rows["ssd_chunk_state"][5] == "10.50 (2)"   # after the read: 10 and 11 us
+    assert rows["ssd_chunk_state"][6] == "20.00 (1)"   # after the fill
+    d = json.load(open(tmp_path / "profiles" / "traffic.json"))
+    assert d["sources_sha256_16"] == "0123456789abcdef"
+    assert d["calibration"]["fetch"] == pytest.approx(2.0)
+    # (100 + 50 KiB) x 2 per launch
+    assert d["fixed_4x4096_h16_n256"]["ssd_chunk_scan"] == 300 * 1024
