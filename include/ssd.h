@@ -58,8 +58,9 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 17
+#define SSD_ABI_VERSION 18
 #define SSD_MAX_DSTATE 256  /* largest dstate, as in "mamba2_ssd_scan", comptime MAX_DSTATE */
+#define SSD_MAX_HEAD_DIM 1024  /* largest head_dim this build takes (the pages fix none) */
 #define SSD_SHORT_PATH_LIMIT 128  /* longest sequence the short path can take */
 #define SSD_RECUR_LIMIT 4         /* of those, the longest the token recurrence takes */
 /* element types of the state tensors (ssd_problem.state_dtype) */
@@ -70,7 +71,7 @@ typedef enum ssd_status {
     SSD_OK = 0,
     SSD_ERR_NULL_ARG = 1,     /* a required pointer is NULL                     */
     SSD_ERR_BAD_SHAPE = 2,    /* negative/zero sizes, nheads % ngroups != 0 ...  */
-    SSD_ERR_UNSUPPORTED = 3,  /* a size this build has no kernel for            */
+    SSD_ERR_UNSUPPORTED = 3,  /* a size beyond this build's limits              */
     SSD_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than required         */
     SSD_ERR_BAD_INPUT = 5,    /* ssd_validate_inputs found a violated precondition */
     SSD_ERR_HIP = 6,          /* a HIP runtime call or kernel launch failed       */
@@ -94,9 +95,9 @@ typedef struct ssd_problem {
     int64_t total_len;   /* T == query_start_loc[batch]; >= 0                */
     int32_t batch;       /* number of sequences; >= 1                         */
     int32_t nheads;      /* H; multiple of ngroups                            */
-    int32_t head_dim;    /* P; this build supports 64                         */
+    int32_t head_dim;    /* P; 1 .. SSD_MAX_HEAD_DIM (see "Sizes" below)       */
     int32_t ngroups;     /* G                                                 */
-    int32_t dstate;      /* N; this build supports 64, 128, 256               */
+    int32_t dstate;      /* N; 1 .. SSD_MAX_DSTATE (see "Sizes" below)        */
     int32_t max_slots;   /* leading dimension of ssm_pool; >= 1               */
     int32_t chunk_size;  /* 0 selects 256; this build supports 256 only       */
     int32_t dt_softplus; /* nonzero: dts = softplus(dt + dt_bias); zero: dt + dt_bias */
@@ -111,9 +112,21 @@ typedef struct ssd_problem {
                           * 0 = none (every sequence through the chunked steps),
                           * 1 .. SSD_SHORT_PATH_LIMIT, or any negative value for
                           * the default SSD_SHORT_PATH_LIMIT; larger values give
-                          * SSD_ERR_UNSUPPORTED.  Only dstate 64 and 128 have a
-                          * short path; at dstate 256 the field is ignored. */
+                          * SSD_ERR_UNSUPPORTED.  Only dstate up to 128 has a
+                          * short path; above 128 the field is ignored. */
 } ssd_problem;
+
+/* Sizes.  The scan kernels take head_dim 64 and dstate 64, 128 or 256.  Other
+ * sizes run on them through copies in the workspace (ssd_workspace_layout's
+ * x_pad .. state_pad): dstate is rounded up to the next of 64, 128, 256 (B and
+ * C copied with zero columns), head_dim up to a multiple of 64 (x copied with
+ * zero channels, y cropped back), each 64-channel block of a head runs as a
+ * head of its own (dt, A, D and dt_bias repeated per block; no copy of x, y
+ * or the states when head_dim is a multiple of 64), and when either size is
+ * padded the states pass through a zero-padded area of one slot per sequence
+ * (copied in from the slots read, copied back into the slots written).  The
+ * results are those of the same recurrence; only the time and the workspace
+ * grow.  nheads * ceil(head_dim / 64) must not exceed 65535.            */
 
 /* Offsets (bytes from the workspace base) and sizes of the intermediates the
  * compute entry point leaves in the workspace, so tests can compare each
@@ -167,6 +180,19 @@ typedef struct ssd_workspace_layout {
     size_t total_bytes;
     int64_t nchunks_max;
     size_t meta, chunk_off, desc, dts, cs2, cbt, gexp, states, sexp, hin, hexp, xexp, seq_list, recur_list;
+    /* The tables above are those of the problem the kernels run (see
+     * "Sizes"): core_nheads heads of head_dim 64 and dstate core_dstate
+     * (nheads and dstate for head_dim 64 and dstate 64, 128 or 256).  The
+     * copies the other sizes need (SIZE_MAX where a size needs none):
+     *   x_pad, y_pad  bf16 [T][H][64 ceil(P/64)]   x and y, zero-padded channels
+     *   bc_pad        bf16 [T][G][core_dstate] B, then (at the next 256-byte
+     *                 boundary) the same for C, zero-padded columns
+     *   head_wide     fp32 dt [T][core_nheads], then A, D, dt_bias
+     *                 [core_nheads], each from a 256-byte boundary
+     *   state_pad     [batch][H][64 ceil(P/64)][core_dstate] in the state dtype:
+     *                 each sequence's state, zero-padded                   */
+    int32_t core_nheads, core_dstate;
+    size_t x_pad, y_pad, bc_pad, head_wide, state_pad;
 } ssd_workspace_layout;
 
 /* ABI version of the loaded library (SSD_ABI_VERSION it was built with). */
@@ -250,7 +276,8 @@ const char *ssd_kernel_name(int i);
  * time (with the gap before it, for i > 0) and (events[0],
  * events[ssd_kernel_count()]) the whole call.  n_events must equal
  * ssd_kernel_count()+1 (SSD_ERR_NULL_ARG / SSD_ERR_BAD_SHAPE otherwise,
- * before any launch).                                                      */
+ * before any launch).  For sizes that need the copies of "Sizes", the events
+ * cover the scan's kernels only (the copies run before and after them).    */
 ssd_status ssd_chunk_scan_varlen_fwd_inplace_profiled(
     const ssd_problem *prob,
     void *y, const void *x, const float *dt, const float *A,

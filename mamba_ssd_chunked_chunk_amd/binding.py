@@ -51,17 +51,21 @@ class ssd_workspace_layout(ctypes.Structure):
                 ("cbt", ctypes.c_size_t), ("gexp", ctypes.c_size_t),
                 ("states", ctypes.c_size_t), ("sexp", ctypes.c_size_t),
                 ("hin", ctypes.c_size_t), ("hexp", ctypes.c_size_t), ("xexp", ctypes.c_size_t),
-                ("seq_list", ctypes.c_size_t), ("recur_list", ctypes.c_size_t)]
+                ("seq_list", ctypes.c_size_t), ("recur_list", ctypes.c_size_t),
+                ("core_nheads", ctypes.c_int32), ("core_dstate", ctypes.c_int32),
+                ("x_pad", ctypes.c_size_t), ("y_pad", ctypes.c_size_t), ("bc_pad", ctypes.c_size_t),
+                ("head_wide", ctypes.c_size_t), ("state_pad", ctypes.c_size_t)]
 
 
 _lock = threading.Lock()
 _lib = None
 
 # SSD_ABI_VERSION of include/ssd.h that the ctypes structures below mirror
-ABI_VERSION = 17
+ABI_VERSION = 18
 NOALLOC_SCRATCH_BYTES = 64 << 20  # SSD_NOALLOC_SCRATCH_BYTES
 STATE_F32, STATE_BF16 = 0, 1  # SSD_STATE_F32, SSD_STATE_BF16
 SHORT_PATH_LIMIT = 128  # SSD_SHORT_PATH_LIMIT
+MAX_DSTATE, MAX_HEAD_DIM = 256, 1024  # SSD_MAX_DSTATE, SSD_MAX_HEAD_DIM
 SHORT_PATH_DEFAULT = -1  # ssd_problem.short_path_max: any negative value selects SHORT_PATH_LIMIT
 
 

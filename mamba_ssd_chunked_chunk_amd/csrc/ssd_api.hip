@@ -42,15 +42,53 @@ ssd_status check_problem(const ssd_problem *p) {
     if (p->state_dtype != SSD_STATE_F32 && p->state_dtype != SSD_STATE_BF16) return SSD_ERR_UNSUPPORTED;
     if (p->total_len > INT32_MAX) return SSD_ERR_BAD_SHAPE;  // query_start_loc is int32
     if (p->dstate > SSD_MAX_DSTATE) return SSD_ERR_UNSUPPORTED;
-    if (p->dstate != 64 && p->dstate != 128 && p->dstate != 256) return SSD_ERR_UNSUPPORTED;
-    if (p->head_dim != ssd::kHeadDim) return SSD_ERR_UNSUPPORTED;
+    if (p->head_dim > SSD_MAX_HEAD_DIM) return SSD_ERR_UNSUPPORTED;
     if (p->chunk_size != 0 && p->chunk_size != ssd::kChunk) return SSD_ERR_UNSUPPORTED;
     if (p->short_path_max > SSD_SHORT_PATH_LIMIT) return SSD_ERR_UNSUPPORTED;
-    if (p->nheads > 65535) return SSD_ERR_UNSUPPORTED;  // grid y limit
+    // the kernels see head_dim / 64 (rounded up) heads per head
+    const int64_t hk = (int64_t)p->nheads * ((p->head_dim + ssd::kHeadDim - 1) / ssd::kHeadDim);
+    if (hk > 65535) return SSD_ERR_UNSUPPORTED;  // grid y limit
     const int64_t ncm = p->total_len / ssd::kChunk + p->batch;  // bounds every routing's chunk count
     if (ncm > INT32_MAX) return SSD_ERR_UNSUPPORTED;
     return SSD_OK;
 }
+
+// How a problem maps onto the sizes the scan kernels take (head_dim 64;
+// dstate 64, 128 or 256), through the copies of ssd_adapt.hip.
+struct Shape {
+    int m;            // heads of 64 channels per head: head_dim rounded up to 64 m
+    int pp, np;       // head_dim and dstate as the kernels see them
+    bool pad_x;       // head_dim not a multiple of 64: x and y through padded copies
+    bool pad_bc;      // dstate not 64, 128 or 256: B and C through padded copies
+    bool wide;        // m > 1: dt, A, D and dt_bias repeated per 64-channel block
+    bool pad_states;  // either size padded: the states through a padded area
+    bool adapted() const { return pad_x || pad_bc || wide || pad_states; }
+};
+
+Shape shape_of(const ssd_problem *p) {
+    Shape s;
+    s.m = (p->head_dim + ssd::kHeadDim - 1) / ssd::kHeadDim;
+    s.pp = s.m * ssd::kHeadDim;
+    s.np = p->dstate <= 64 ? 64 : p->dstate <= 128 ? 128 : 256;
+    s.pad_x = s.pp != p->head_dim;
+    s.pad_bc = s.np != p->dstate;
+    s.wide = s.m > 1;
+    s.pad_states = s.pad_x || s.pad_bc;
+    return s;
+}
+
+// The problem the kernels run: m H heads of 64 channels, dstate np; with
+// padded states, one slot per sequence (the padded area).
+ssd_problem core_of(const ssd_problem *p, const Shape &s) {
+    ssd_problem q = *p;
+    q.nheads = p->nheads * s.m;
+    q.head_dim = ssd::kHeadDim;
+    q.dstate = s.np;
+    if (s.pad_states) q.max_slots = p->batch;
+    return q;
+}
+
+size_t state_elem_bytes(const ssd_problem *p) { return p->state_dtype == SSD_STATE_BF16 ? 2 : 4; }
 
 // Longest sequence the short path takes in this call (0: none; the path
 // serves dstate 64 and 128 only).
@@ -72,7 +110,8 @@ void routed_bounds(const ssd_problem *p, int *nseq, int64_t *nchunks) {
     *nchunks = std::max<int64_t>(1, T / ssd::kChunk + *nseq);
 }
 
-void layout_of(const ssd_problem *p, ssd_workspace_layout *L) {
+// The kernels' part of the workspace (a problem of kernel sizes).
+void core_layout_of(const ssd_problem *p, ssd_workspace_layout *L) {
     int nseq;
     int64_t ncm;
     routed_bounds(p, &nseq, &ncm);
@@ -95,6 +134,35 @@ void layout_of(const ssd_problem *p, ssd_workspace_layout *L) {
     L->xexp = off;      off = align_up(off + (size_t)ncm * H * 2 * sizeof(int32_t));
     L->seq_list = off;  off = align_up(off + (size_t)p->batch * sizeof(int32_t));
     L->recur_list = off; off = align_up(off + (size_t)p->batch * sizeof(int32_t));
+    L->total_bytes = off;
+}
+
+// The whole workspace: the kernels' part for the mapped problem, then the
+// copies the mapping needs (SIZE_MAX where not needed).
+void layout_of(const ssd_problem *p, ssd_workspace_layout *L) {
+    const Shape s = shape_of(p);
+    const ssd_problem q = core_of(p, s);
+    core_layout_of(&q, L);
+    L->core_nheads = q.nheads;
+    L->core_dstate = q.dstate;
+    L->x_pad = L->y_pad = L->bc_pad = L->head_wide = L->state_pad = SIZE_MAX;
+    size_t off = L->total_bytes;
+    const size_t T = (size_t)p->total_len, H = (size_t)p->nheads, G = (size_t)p->ngroups;
+    if (s.pad_x) {
+        L->x_pad = off; off = align_up(off + T * H * (size_t)s.pp * sizeof(uint16_t));
+        L->y_pad = off; off = align_up(off + T * H * (size_t)s.pp * sizeof(uint16_t));
+    }
+    if (s.pad_bc) {  // B, then C
+        L->bc_pad = off; off = align_up(off + 2 * align_up(T * G * (size_t)s.np * sizeof(uint16_t)));
+    }
+    if (s.wide) {  // dt [T][m H], then A, D, dt_bias [m H]
+        L->head_wide = off;
+        off = align_up(off + align_up(T * H * s.m * sizeof(float)) + 3 * align_up(H * s.m * sizeof(float)));
+    }
+    if (s.pad_states) {
+        L->state_pad = off;
+        off = align_up(off + (size_t)p->batch * H * (size_t)s.pp * (size_t)s.np * state_elem_bytes(p));
+    }
     L->total_bytes = off;
 }
 
@@ -178,19 +246,13 @@ static ssd_status check_call(const ssd_problem *prob, const void *y, const void 
     return SSD_OK;
 }
 
-static ssd_status run_scan(
+// The scan kernels on a problem of their sizes (head_dim 64; dstate 64, 128
+// or 256), with the workspace carved as L.
+static ssd_status run_core(
     const ssd_problem *prob, void *y, const void *x, const float *dt, const float *A,
     const void *B, const void *C, const float *D, const float *dt_bias,
-    const int32_t *query_start_loc, const StateIO &sio, void *workspace, size_t workspace_bytes,
+    const int32_t *query_start_loc, const StateIO &sio, char *ws, const ssd_workspace_layout &L,
     void *stream, void *const *events) {
-    ssd_status st = check_call(prob, y, x, dt, A, B, C, D, dt_bias, query_start_loc, sio);
-    if (st != SSD_OK) return st;
-    ssd_workspace_layout L;
-    layout_of(prob, &L);
-    if (workspace == nullptr || workspace_bytes < L.total_bytes || !aligned(workspace, kAlign))
-        return SSD_ERR_WORKSPACE;
-
-    char *ws = static_cast<char *>(workspace);
     ssd::Params p;
     p.T = prob->total_len;
     p.batch = prob->batch;
@@ -264,6 +326,87 @@ static ssd_status run_scan(
                             events ? static_cast<hipEvent_t>(events[k + 1]) : nullptr};
         if (launchers[k](p, l) != hipSuccess) return SSD_ERR_HIP;
     }
+    return SSD_OK;
+}
+
+static ssd_status run_scan(
+    const ssd_problem *prob, void *y, const void *x, const float *dt, const float *A,
+    const void *B, const void *C, const float *D, const float *dt_bias,
+    const int32_t *query_start_loc, const StateIO &sio, void *workspace, size_t workspace_bytes,
+    void *stream, void *const *events) {
+    ssd_status st = check_call(prob, y, x, dt, A, B, C, D, dt_bias, query_start_loc, sio);
+    if (st != SSD_OK) return st;
+    ssd_workspace_layout L;
+    layout_of(prob, &L);
+    if (workspace == nullptr || workspace_bytes < L.total_bytes || !aligned(workspace, kAlign))
+        return SSD_ERR_WORKSPACE;
+    char *ws = static_cast<char *>(workspace);
+    const Shape sh = shape_of(prob);
+    if (!sh.adapted())
+        return run_core(prob, y, x, dt, A, B, C, D, dt_bias, query_start_loc, sio, ws, L, stream, events);
+
+    // Other sizes: copies into the kernels' sizes, the scan, copies back
+    // (ssd_adapt.hip).  Only the scan's kernels carry the events.
+    const ssd_problem q = core_of(prob, sh);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t T = prob->total_len;
+    const int H = prob->nheads, G = prob->ngroups, P = prob->head_dim, N = prob->dstate;
+    const int es = (int)state_elem_bytes(prob);
+    const void *xk = x, *Bk = B, *Ck = C;
+    void *yk = y;
+    const float *dtk = dt, *Ak = A, *Dk = D, *biask = dt_bias;
+    StateIO sk = sio;
+    auto ok = [](hipError_t e) { return e == hipSuccess; };
+    if (sh.pad_x && T > 0) {
+        xk = ws + L.x_pad;
+        yk = ws + L.y_pad;
+        if (!ok(ssd::adapt_resize_rows(x, ws + L.x_pad, T * H, P, sh.pp, 2, s))) return SSD_ERR_HIP;
+    }
+    if (sh.pad_bc && T > 0) {
+        char *bp = ws + L.bc_pad;
+        char *cp = bp + align_up((size_t)T * G * sh.np * sizeof(uint16_t));
+        Bk = bp;
+        Ck = cp;
+        if (!ok(ssd::adapt_resize_rows(B, bp, T * G, N, sh.np, 2, s)) ||
+            !ok(ssd::adapt_resize_rows(C, cp, T * G, N, sh.np, 2, s)))
+            return SSD_ERR_HIP;
+    }
+    if (sh.wide) {
+        float *w = reinterpret_cast<float *>(ws + L.head_wide);
+        const size_t hs = align_up((size_t)H * sh.m * sizeof(float)) / sizeof(float);
+        float *dtw = w, *aw = w + align_up((size_t)T * H * sh.m * sizeof(float)) / sizeof(float);
+        float *dw = aw + hs, *bw = dw + hs;
+        if (T > 0) {
+            if (!ok(ssd::adapt_repeat(dt, dtw, T * H * sh.m, sh.m, s))) return SSD_ERR_HIP;
+            dtk = dtw;
+        }
+        if (!ok(ssd::adapt_repeat(A, aw, (int64_t)H * sh.m, sh.m, s))) return SSD_ERR_HIP;
+        Ak = aw;
+        if (D != nullptr) {
+            if (!ok(ssd::adapt_repeat(D, dw, (int64_t)H * sh.m, sh.m, s))) return SSD_ERR_HIP;
+            Dk = dw;
+        }
+        if (dt_bias != nullptr) {
+            if (!ok(ssd::adapt_repeat(dt_bias, bw, (int64_t)H * sh.m, sh.m, s))) return SSD_ERR_HIP;
+            biask = bw;
+        }
+    }
+    if (sh.pad_states) {
+        // every sequence's initial state (zeros without one) into the padded
+        // area, which is then each sequence's initial and final state
+        void *area = ws + L.state_pad;
+        if (!ok(ssd::adapt_gather_states(sio.in, area, sio.cache_idx, sio.has_init, sio.init_all, prob->batch, H,
+                                         P, N, sh.pp, sh.np, es, s)))
+            return SSD_ERR_HIP;
+        sk = StateIO{area, area, nullptr, nullptr, true};
+    }
+    st = run_core(&q, yk, xk, dtk, Ak, Bk, Ck, Dk, biask, query_start_loc, sk, ws, L, stream, events);
+    if (st != SSD_OK) return st;
+    if (sh.pad_x && T > 0 && !ok(ssd::adapt_resize_rows(ws + L.y_pad, y, T * H, sh.pp, P, 2, s)))
+        return SSD_ERR_HIP;
+    if (sh.pad_states && !ok(ssd::adapt_scatter_states(ws + L.state_pad, sio.out, sio.cache_idx, prob->batch, H,
+                                                        P, N, sh.pp, sh.np, es, s)))
+        return SSD_ERR_HIP;
     return SSD_OK;
 }
 

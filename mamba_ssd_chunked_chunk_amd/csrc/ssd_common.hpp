@@ -15,6 +15,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 namespace ssd {
 
 constexpr int kChunk = 256;      // chunk length (tokens)
@@ -383,4 +385,14 @@ hipError_t launch_state_passing(const Params &p, const Launch &l);
 hipError_t launch_chunk_scan(const Params &p, const Launch &l);
 hipError_t launch_short(const Params &p, const Launch &l);
 hipError_t launch_recur(const Params &p, const Launch &l);
+
+// Copies of the size adapter (ssd_adapt.hip), launched on stream s.
+hipError_t adapt_resize_rows(const void *src, void *dst, int64_t rows, int nin, int nout, int elem_bytes,
+                             hipStream_t s);
+hipError_t adapt_repeat(const float *src, float *dst, int64_t n_out, int m, hipStream_t s);
+hipError_t adapt_gather_states(const void *src, void *area, const uint32_t *cache_idx, const uint8_t *has_init,
+                               bool init_all, int batch, int H, int P, int N, int Pp, int Np, int elem_bytes,
+                               hipStream_t s);
+hipError_t adapt_scatter_states(const void *area, void *dst, const uint32_t *cache_idx, int batch, int H, int P,
+                                int N, int Pp, int Np, int elem_bytes, hipStream_t s);
 }  // namespace ssd

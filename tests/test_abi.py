@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert binding.ssd_abi_version() == binding.ABI_VERSION == 17
+    assert binding.ssd_abi_version() == binding.ABI_VERSION == 18
     for code, name in binding.STATUS_NAMES.items():
         assert lib.ssd_status_string(code).decode().startswith(name)
     assert b"unknown" in lib.ssd_status_string(99)
@@ -69,6 +69,52 @@ def test_workspace_layout_arithmetic(lib):
     ends = offs[1:] + [L["total_bytes"]]
     for k, o, e in zip(keys, offs, ends):
         assert e - o >= need[k], k
+    # kernel sizes: no copies
+    assert (L["core_nheads"], L["core_dstate"]) == (16, 256)
+    for k in ("x_pad", "y_pad", "bc_pad", "head_wide", "state_pad"):
+        assert L[k] == SIZE_MAX, k
+
+
+SIZE_MAX = 2 ** (8 * ctypes.sizeof(ctypes.c_size_t)) - 1
+
+
+def _up(v):
+    return (v + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("P,N,state_dtype", [(96, 100, 0), (128, 256, 0), (64, 16, 1), (200, 64, 0), (32, 256, 1)])
+def test_adapted_layout(lib, P, N, state_dtype):
+    """Sizes the kernels do not take: the tables are the mapped problem's
+    (ceil(P / 64) heads of 64 per head, dstate rounded up to 64 / 128 / 256),
+    followed by the copies each size needs, 256-byte aligned and large
+    enough, and the workspace ends with the last of them."""
+    T, batch, H, G = 1000, 3, 8, 2
+    kw = dict(total_len=T, batch=batch, nheads=H, head_dim=P, ngroups=G, dstate=N, max_slots=5,
+              state_dtype=state_dtype)
+    L = binding.ssd_workspace_get_layout(_prob(**kw))
+    m = (P + 63) // 64
+    Np = 64 if N <= 64 else 128 if N <= 128 else 256
+    assert (L["core_nheads"], L["core_dstate"]) == (H * m, Np)
+    # the tables: those of the mapped problem (one slot per sequence when states are padded)
+    core = binding.ssd_workspace_get_layout(_prob(**dict(kw, nheads=H * m, head_dim=64, dstate=Np,
+                                                         max_slots=batch if (P % 64 or N != Np) else 5)))
+    for k in ("nchunks_max", "meta", "chunk_off", "desc", "dts", "cs2", "cbt", "gexp", "states", "sexp",
+              "hin", "hexp", "xexp", "seq_list", "recur_list"):
+        assert L[k] == core[k], k
+    es = 2 if state_dtype == 1 else 4
+    need = dict(x_pad=T * H * 64 * m * 2 if P % 64 else None,
+                y_pad=T * H * 64 * m * 2 if P % 64 else None,
+                bc_pad=2 * _up(T * G * Np * 2) if N != Np else None,
+                head_wide=_up(T * H * m * 4) + 3 * _up(H * m * 4) if m > 1 else None,
+                state_pad=batch * H * 64 * m * Np * es if (P % 64 or N != Np) else None)
+    prev_end = core["total_bytes"]
+    for k in ("x_pad", "y_pad", "bc_pad", "head_wide", "state_pad"):
+        if need[k] is None:
+            assert L[k] == SIZE_MAX, k
+            continue
+        assert L[k] % 256 == 0 and L[k] >= prev_end, k
+        prev_end = L[k] + need[k]
+    assert L["total_bytes"] == _up(prev_end) == binding.ssd_workspace_size(_prob(**kw))
 
 
 def test_workspace_rows_follow_the_routing(lib):
@@ -86,8 +132,9 @@ def test_workspace_rows_follow_the_routing(lib):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(batch=0), 2), (dict(nheads=6, ngroups=4), 2), (dict(total_len=-1), 2),
-    (dict(max_slots=0), 2), (dict(dstate=512), 3), (dict(dstate=96), 3),
-    (dict(head_dim=128), 3), (dict(chunk_size=128), 3), (dict(state_dtype=2), 3), (dict(state_dtype=-1), 3),
+    (dict(max_slots=0), 2), (dict(dstate=0), 2), (dict(head_dim=0), 2), (dict(dstate=257), 3),
+    (dict(dstate=512), 3), (dict(head_dim=1025), 3), (dict(nheads=32768, head_dim=65), 3),
+    (dict(chunk_size=128), 3), (dict(state_dtype=2), 3), (dict(state_dtype=-1), 3),
     (dict(short_path_max=129), 3), (dict(short_path_max=1 << 20), 3),
 ])
 def test_bad_problems_rejected(lib, kw, status):
