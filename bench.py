@@ -409,6 +409,16 @@ PER_CONFIG = ["tiny_1x512_h4_n64", "fixed_4x4096_h16_n256", "long_8x16384_h16_n2
               "ragged_32_h128_g8_n128", "short_512_h128_g8_n128"]
 
 
+def launches_short_path(prob, short_max):
+    """Whether the library launches the short path's kernels for this call:
+    some sequence may take it (dstate <= 128, the path on, and not a single
+    sequence longer than the limit)."""
+    limit = SHORT_MAX if short_max < 0 else short_max
+    if prob["dstate"] > 128 or limit == 0:
+        return False
+    return not (len(prob["query_start_loc"]) == 2 and prob["total_len"] > limit)
+
+
 class CacheFlush:
     """A 512 MiB buffer, twice the memory-side cache, passed through before
     each timed call so that the call's inputs come from HBM.  read() sums it:
@@ -448,10 +458,11 @@ class Runner:
         self.nk = lib.ssd_kernel_count()
         knames = [lib.ssd_kernel_name(i).decode() for i in range(self.nk)]
         # the short path's kernels (the last two) are not launched where no
-        # sequence can take it (dstate 256, or the path off): their events are
-        # then only markers on the stream, left out of the call time and the list
+        # sequence can take it (dstate above 128, the path off, or one sequence
+        # longer than its limit): their events are then only markers on the
+        # stream, left out of the call time and the list
         assert knames[-2:] == ["ssd_short", "ssd_recur"]
-        n_run = self.nk if (prob["dstate"] <= 128 and short_max != 0) else self.nk - 2
+        n_run = self.nk if launches_short_path(prob, short_max) else self.nk - 2
         self.n_run = n_run
         self.knames_run = knames[:n_run]
 

@@ -312,11 +312,13 @@ static ssd_status run_core(
     hipError_t (*const launchers[kNumKernels])(const ssd::Params &, const ssd::Launch &) = {
         ssd::launch_chunk_state, ssd::launch_state_passing, ssd::launch_chunk_scan, ssd::launch_short,
         ssd::launch_recur};
+    // no sequence can take the short path (it is off, or the call's one
+    // sequence is longer than its limit): its kernels would have nothing to
+    // do, so they are not launched (their completion events, if any, are
+    // recorded on the stream where they would have run)
+    const bool no_short = p.short_max == 0 || (prob->batch == 1 && prob->total_len > p.short_max);
     for (int k = 0; k < kNumKernels; ++k) {
-        // no sequence can take the short path: its kernels would have nothing
-        // to do, so they are not launched (their completion events, if any,
-        // are recorded on the stream where they would have run)
-        if (k >= kFirstShortKernel && p.short_max == 0) {
+        if (k >= kFirstShortKernel && no_short) {
             if (events && hipEventRecord(static_cast<hipEvent_t>(events[k + 1]), s) != hipSuccess) return SSD_ERR_HIP;
             continue;
         }

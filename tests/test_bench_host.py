@@ -8,6 +8,7 @@ import os
 import subprocess
 import sys
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -186,3 +187,19 @@ def test_profile_summary_splits_read_and_write_flush_calls(tmp_path, monkeypatch
     assert d["calibration"]["fetch"] == pytest.approx(2.0)
     # (100 + 50 KiB) x 2 per launch
     assert d["fixed_4x4096_h16_n256"]["ssd_chunk_scan"] == 300 * 1024
+
+
+def test_short_path_launch_rule():
+    """bench.py times the short path's kernels only where the library
+    launches them: dstate <= 128, the path on, and not a single sequence
+    longer than the limit."""
+    def prob(lens, N):
+        q = np.zeros(len(lens) + 1, np.int32)
+        q[1:] = np.cumsum(lens)
+        return dict(dstate=N, query_start_loc=q, total_len=int(q[-1]))
+    f = bench.launches_short_path
+    assert not f(prob([100, 50], 256), -1)
+    assert not f(prob([100, 50], 128), 0)
+    assert not f(prob([129], 64), -1) and f(prob([128], 64), -1)
+    assert not f(prob([200], 128), 100) and f(prob([100], 128), 100)
+    assert f(prob([300, 300], 128), -1) and f(prob([0], 64), -1)

@@ -127,6 +127,16 @@ def test_small_cases(name, route):
     full_check(prob, DEFAULT if route == "default" else CHUNKED)
 
 
+@pytest.mark.parametrize("N,T,short_max", [(64, 129, DEFAULT), (128, 700, DEFAULT), (128, 128, DEFAULT),
+                                           (64, 4, DEFAULT), (128, 200, 100), (64, 300, CHUNKED)])
+def test_single_sequence_routing(N, T, short_max):
+    """One sequence: the host knows its length, and launches the short path's
+    kernels only when that length is within the limit; the result is the
+    oracle's either way."""
+    prob = small_problem([T], H=4, P=64, G=2, N=N, seed=90 + T, init="all")
+    full_check(prob, short_max)
+
+
 @pytest.mark.parametrize("nseq", [2, 4])
 def test_head_blocks_dstate64(nseq):
     """dstate 64 with 16 heads in one group and 128 or 256 chunks: the
