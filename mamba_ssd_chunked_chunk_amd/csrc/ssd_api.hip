@@ -91,7 +91,7 @@ ssd_problem core_of(const ssd_problem *p, const Shape &s) {
 size_t state_elem_bytes(const ssd_problem *p) { return p->state_dtype == SSD_STATE_BF16 ? 2 : 4; }
 
 // Longest sequence the short path takes in this call (0: none; the path
-// serves dstate 64 and 128 only).
+// serves dstate up to 128 only).
 int short_max_of(const ssd_problem *p) {
     if (p->dstate > 128) return 0;
     return p->short_path_max < 0 ? ssd::kShortMax : p->short_path_max;
