@@ -31,6 +31,8 @@ SIZES = {
     "n64_p96": dict(seqlens=[90, 400, 1], H=2, P=96, G=1, N=64, init="bernoulli"),
     "n48_p200": dict(seqlens=[260, 70], H=2, P=200, G=1, N=48, init="all"),
     "n1_p1": dict(seqlens=[5, 300], H=2, P=1, G=1, N=1, init="all"),
+    # the largest head_dim: sixteen heads of 64 per head
+    "n32_p1024": dict(seqlens=[300, 9], H=1, P=1024, G=1, N=32, init="all"),
     # bf16 state storage through the padded area
     "n100_p64_bf16": dict(seqlens=[300, 20, 0, 64], H=4, P=64, G=2, N=100, init="all", state_dtype="bf16"),
 }
@@ -135,3 +137,12 @@ def test_sizes_noalloc_equals_workspace_entry():
     torch.cuda.synchronize()
     assert torch.equal(d1["y"].view(torch.int16), d2["y"].view(torch.int16))
     assert torch.equal(d1["pool"].view(torch.int32), d2["pool"].view(torch.int32))
+
+
+def test_many_tiny_sequences():
+    """3000 sequences of 0..8 tokens (the token recurrence, the short kernel
+    and empty sequences) in one call, every one against the oracle."""
+    lens = list(np.random.default_rng(9).integers(0, 9, 3000))
+    prob = small_problem(lens, H=4, P=64, G=2, N=64, seed=491, max_slots=3100, init="bernoulli")
+    wy, wf = full_check(prob)
+    print(f"3000 tiny sequences: y worst/bound {wy:.3f}  final rel {wf:.2e}", flush=True)
