@@ -541,7 +541,20 @@ class Runner:
         return out
 
 
-def config_line(prob, m, alg):
+def counted_traffic(workload, kernels, args):
+    """HBM bytes per launch of each kernel from the committed counter runs,
+    where they apply (they were taken with the default routing, fp32 states
+    and the in-place entry point), and their sum for the whole call."""
+    if args.short_max != SHORT_MAX or args.state_dtype != "f32" or args.entry != "inplace":
+        per = {k: None for k in kernels}
+    else:
+        per = {k: traffic_for(k, workload) for k in kernels}
+    vals = list(per.values())
+    per["whole"] = sum(vals) if vals and all(v is not None for v in vals) else None
+    return per
+
+
+def config_line(prob, m, alg, traffic):
     """The per-workload summary: µs per call, tokens/s, the whole call and
     the longest kernel against their rooflines."""
     kern = m["kern_us"]
@@ -549,8 +562,8 @@ def config_line(prob, m, alg):
     return {"tokens": prob["total_len"], "batch": prob["batch"], "us_per_call": m["us_per_call"],
             "tokens_per_s": round(prob["total_len"] / (m["ms"] * 1e-3), 1),
             "kernels_us": {n: round(v, 2) for n, v in kern.items()},
-            "roofline_whole_call": roofline_entry("whole", alg, m["ms"] * 1e3),
-            "roofline_dominant_kernel": roofline_entry(dom, alg, kern[dom])}
+            "roofline_whole_call": roofline_entry("whole", alg, m["ms"] * 1e3, traffic["whole"]),
+            "roofline_dominant_kernel": roofline_entry(dom, alg, kern[dom], traffic[dom])}
 
 
 def main():
@@ -597,9 +610,9 @@ def main():
 
     alg = algorithmic(prob, args.short_max)
     dom = max(kern_us, key=kern_us.get)
-    roof = roofline_entry(dom, alg, kern_us[dom],
-                          traffic_for(dom, args.workload) if args.short_max == SHORT_MAX and args.state_dtype == "f32" else None)
-    whole = roofline_entry("whole", alg, ms * 1e3)
+    traffic = counted_traffic(args.workload, run.knames_run, args)
+    roof = roofline_entry(dom, alg, kern_us[dom], traffic[dom])
+    whole = roofline_entry("whole", alg, ms * 1e3, traffic["whole"])
     per_kernel_roof = {n: roofline_entry(n, alg, kern_us[n]) for n in run.knames_run if alg[n]["bytes"] or alg[n]["flops"]}
 
     out = {
@@ -642,7 +655,8 @@ def main():
                 pm = r.measure(args.config_steps, 2, flush, warm=False)
                 del r
                 torch.cuda.empty_cache()
-            per[name] = config_line(p, pm, algorithmic(p, args.short_max))
+            per[name] = config_line(p, pm, algorithmic(p, args.short_max),
+                                    counted_traffic(name, list(pm["kern_us"]), args))
         out["per_config"] = per
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(prob, args.cpu_seconds, args.entry)

@@ -203,3 +203,22 @@ def test_short_path_launch_rule():
     assert not f(prob([129], 64), -1) and f(prob([128], 64), -1)
     assert not f(prob([200], 128), 100) and f(prob([100], 128), 100)
     assert f(prob([300, 300], 128), -1) and f(prob([0], 64), -1)
+
+
+def test_counted_traffic_sums_the_call(monkeypatch):
+    """The whole call's counted traffic is the sum over its kernels, and
+    nothing is reported where the counters do not apply (another routing,
+    bf16 states, the separate-states entry) or a kernel has none."""
+    import types
+    table = {"w": {"ssd_chunk_state": 10, "ssd_state_passing": 20, "ssd_chunk_scan": 30}}
+    monkeypatch.setattr(bench, "traffic_for", lambda k, w: table.get(w, {}).get(k))
+    args = types.SimpleNamespace(short_max=bench.SHORT_MAX, state_dtype="f32", entry="inplace")
+    ks = ["ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan"]
+    t = bench.counted_traffic("w", ks, args)
+    assert t["whole"] == 60 and t["ssd_chunk_scan"] == 30
+    assert bench.counted_traffic("w", ks + ["ssd_short"], args)["whole"] is None
+    assert bench.counted_traffic("other", ks, args)["whole"] is None
+    for kw in (dict(short_max=0), dict(state_dtype="bf16"), dict(entry="separate")):
+        a = types.SimpleNamespace(**dict(vars(args), **kw))
+        t = bench.counted_traffic("w", ks, a)
+        assert all(v is None for v in t.values()), kw
