@@ -220,6 +220,86 @@ def test_short_path_extremes():
     full_check(prob)
 
 
+def check_block_scaled(prob, short_max, rel=1e-2):
+    """y against the oracle relative to its local magnitude: in every
+    32-token block of a sequence (the kernels' row blocks) and head, the
+    largest error is at most rel * the block's largest |y_ref|, and the
+    block's error norm at most rel * its norm; final states and untouched
+    slots as in full_check.  Returns the worst error / block max."""
+    d = torch_io.upload(prob, "cuda")
+    torch_io.run(d, short_path_max=short_max)
+    torch.cuda.synchronize()
+    ref = oracle.recurrence(prob, want_pool=False)
+    y = y_host(d)
+    assert np.all(np.isfinite(y))
+    qsl = prob["query_start_loc"]
+    worst = 0.0
+    for b in range(len(qsl) - 1):
+        for t0 in range(int(qsl[b]), int(qsl[b + 1]), 32):
+            t1 = min(t0 + 32, int(qsl[b + 1]))
+            for h in range(prob["nheads"]):
+                r, g = ref["y"][t0:t1, h], y[t0:t1, h]
+                s = np.abs(r).max()
+                if s == 0:
+                    assert np.all(g == 0)
+                    continue
+                e = np.abs(g - r).max() / s
+                worst = max(worst, e)
+                assert e <= rel, f"seq {b} tokens {t0}..{t1} head {h}: error {e:.2e} of the block's max |y|"
+                assert np.linalg.norm(g - r) <= rel * np.linalg.norm(r)
+    ci = prob["cache_indices"]
+    fin = d["pool"].index_select(0, torch.from_numpy(ci.astype(np.int64)).cuda()).float().cpu().numpy()
+    for b in range(len(ci)):
+        assert_final(fin[b], ref["final"][b], f"seq {b}")
+    return worst
+
+
+@pytest.mark.parametrize("route", ["default", "chunked"])
+@pytest.mark.parametrize("N,case", [(128, "positive_A"), (256, "positive_A"), (128, "negative_dts"),
+                                    (64, "negative_dts")])
+def test_growing_states(N, case, route):
+    """A * dts > 0, where the state grows instead of decaying: a positive A
+    (the recurrence of "mamba2_ssd_scan" takes A as given), or negative dts
+    (dt + dt_bias < 0 without softplus).  |y| then grows by orders of
+    magnitude along a sequence; the kernels' fp16 operands keep the error
+    relative to the local magnitude (checked per 32-token block and head),
+    while the elementwise bound's absolute floor of 2e-2 assumes |y| of
+    order 10 (see test_scaled_inputs)."""
+    prob = small_problem([700, 300, 40, 5, 0], H=4, P=64, G=2, N=N, seed=7 * len(case) + N, init="all")
+    rng = np.random.default_rng(N + len(case))
+    H, T = 4, prob["total_len"]
+    if case == "positive_A":
+        # the drawn dts are at most about 0.3: A * dts up to 0.015 per token, e^10.5 over 700
+        prob["A"] = rng.uniform(0.01, 0.05, H).astype(np.float32)
+    else:
+        prob["dt_softplus"] = False
+        prob["dt"] = rng.uniform(-0.2, 0.05, (T, H)).astype(np.float32).reshape(prob["dt"].shape)
+        prob["dt_bias"] = np.zeros(H, np.float32)
+        prob["A"] = -rng.uniform(0.05, 0.1, H).astype(np.float32)  # A * dts in (-0.005, 0.02)
+    w = check_block_scaled(prob, DEFAULT if route == "default" else CHUNKED)
+    print(f"{case} N={N} ({route}): worst error / block max |y| {w:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("scale", [100.0, 1000.0])
+def test_scaled_inputs(scale):
+    """y is linear in x and the initial states together: scaling both by k
+    scales y by k, and the elementwise bound scales with it,
+    |dy| <= 2e-2 (k + |y_ref|) (the bound of the problem divided by k)."""
+    prob = small_problem([700, 300, 60], H=4, P=64, G=2, N=128, seed=95, init="all")
+    prob["x"] = bf16(bf16_to_f64(prob["x"]) * scale)
+    prob["pool"] = (prob["pool"] * np.float32(scale)).astype(np.float32)
+    d, _ = gpu_run(prob)
+    ref = oracle.recurrence(prob, want_pool=False)
+    y = y_host(d)
+    ratio = np.abs(y - ref["y"]) / (Y_RTOL * (scale + np.abs(ref["y"])))
+    assert ratio.max() <= 1.0, f"error {ratio.max():.3f} x the scaled bound"
+    ci = prob["cache_indices"]
+    fin = d["pool"].cpu().numpy()[ci.astype(np.int64)]
+    for b in range(len(ci)):
+        assert_final(fin[b], ref["final"][b], f"seq {b}")
+    print(f"x and states x{scale:.0f}: worst / scaled bound {ratio.max():.3f}", flush=True)
+
+
 def test_short_nan_slot_not_read():
     """A short sequence without an initial state must not read its slot."""
     prob = small_problem([50, 7, 120], H=4, P=64, G=1, N=64, max_slots=5, seed=98, init=[0, 1, 0])
