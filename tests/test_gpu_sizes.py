@@ -146,3 +146,23 @@ def test_many_tiny_sequences():
     prob = small_problem(lens, H=4, P=64, G=2, N=64, seed=491, max_slots=3100, init="bernoulli")
     wy, wf = full_check(prob)
     print(f"3000 tiny sequences: y worst/bound {wy:.3f}  final rel {wf:.2e}", flush=True)
+
+
+def test_sizes_profiled_entry():
+    """The entry point with per-kernel events (the one bench.py times) takes
+    the same mapping: results bitwise those of the plain entry point, and the
+    events span the call."""
+    import bench
+    spec = dict(SIZES["n64_p96"])
+    lens = spec.pop("seqlens")
+    prob = small_problem(lens, seed=493, max_slots=len(lens) + 2, **spec)
+    hip = bench.Hip()
+    run = bench.Runner(torch, binding.load_library(), hip, torch.device("cuda:0"), prob, bench.SHORT_MAX)
+    events = [hip.event() for _ in range(run.nk + 1)]
+    run.call(events)
+    d = torch_io.upload(prob, "cuda")
+    torch_io.run(d)
+    torch.cuda.synchronize()
+    assert torch.equal(run.d["y"].view(torch.int16), d["y"].view(torch.int16))
+    assert torch.equal(run.d["pool"].view(torch.int32), d["pool"].view(torch.int32))
+    assert hip.elapsed_ms(events[0], events[run.nk]) > 0.0
