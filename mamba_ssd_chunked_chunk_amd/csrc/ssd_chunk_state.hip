@@ -448,6 +448,9 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_state_kernel(Params p) {
     // it); consumers store head j-2 and multiply head j-1.
     if (producer) {
         const int pw = wave - kConsumers;  // producer wavefront 0 .. 7
+        // at dstate <= 128 the producers issue ahead of the consumers (a higher
+        // wave priority): measured faster there, and slower at dstate 256
+        if constexpr (N <= 128) __builtin_amdgcn_s_setprio(1);
         prologue([] {}, [] {});
 
         // ---- heads
