@@ -78,3 +78,33 @@ def frob_rel(a, b) -> float:
     nb = np.linalg.norm(b)
     nd = np.linalg.norm(a - b)
     return float(nd if nb == 0 else nd / nb)
+
+
+def pad_by_hand(prob):
+    """The same problem at the kernels' sizes, built on the host: head_dim
+    rounded up to 64 m and split into m heads of 64 per head (dt, A, D,
+    dt_bias repeated), dstate rounded up to 64 / 128 / 256; zeros in every
+    added channel and column (x, B, C and the pool)."""
+    H, P, G, N = prob["nheads"], prob["head_dim"], prob["ngroups"], prob["dstate"]
+    T = int(prob["query_start_loc"][-1])
+    m = (P + 63) // 64
+    Np = 64 if N <= 64 else 128 if N <= 128 else 256
+    q = dict(prob)
+    x = np.zeros((T, H, 64 * m), np.uint16)
+    x[:, :, :P] = prob["x"].reshape(T, H, P)
+    q["x"] = x.reshape(T, H * m, 64)
+    q["dt"] = np.repeat(prob["dt"].reshape(T, H), m, axis=1)
+    for k in ("A", "D", "dt_bias"):
+        if prob.get(k) is not None:
+            q[k] = np.repeat(prob[k], m)
+    for k in ("B", "C"):
+        a = np.zeros((T, G, Np), np.uint16)
+        a[:, :, :N] = prob[k].reshape(T, G, N)
+        q[k] = a
+    pool = prob["pool"]
+    S = pool.shape[0]
+    pp = np.zeros((S, H, 64 * m, Np), pool.dtype)
+    pp[:, :, :P, :N] = pool
+    q["pool"] = pp.reshape(S, H * m, 64, Np)
+    q.update(nheads=H * m, head_dim=64, dstate=Np)
+    return q

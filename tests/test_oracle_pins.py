@@ -19,7 +19,7 @@ import pytest
 
 import oracle
 from oracle.chunked import chunked_scan, softplus
-from ssd_testlib import bf16, bf16_to_f64, clone, frob_rel, max_rel, small_problem, sub_batch
+from ssd_testlib import bf16, bf16_to_f64, clone, frob_rel, max_rel, pad_by_hand, small_problem, sub_batch
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -96,6 +96,46 @@ def test_chunked_equals_recurrence(chunk, dt_softplus):
     ch = chunked_scan(prob, chunk)
     assert max_rel(ch["y"], rec["y"]) <= 1e-10
     assert max_rel(ch["final"], rec["final"]) <= 1e-10
+
+
+@pytest.mark.parametrize("chunk", [1, 16, 256])
+@pytest.mark.parametrize("case", ["positive_A", "negative_dts"])
+def test_chunked_equals_recurrence_when_states_grow(chunk, case):
+    """A * dts > 0 (a positive A, or negative dts without softplus): the state
+    grows, and the chunked form still equals the recurrence (the segment-sum
+    reformulation holds for any sign of the exponent)."""
+    prob = small_problem(MIXED_LENS, H=4, P=4, G=2, N=8, seed=12, init="all")
+    rng = np.random.default_rng(12)
+    if case == "positive_A":
+        prob["A"] = rng.uniform(0.01, 0.05, 4).astype(np.float32)
+    else:
+        prob["dt_softplus"] = False
+        prob["dt"] = rng.uniform(-0.2, 0.05, prob["dt"].shape).astype(np.float32)
+        prob["dt_bias"] = np.zeros(4, np.float32)
+    rec = oracle.recurrence(prob)
+    assert np.abs(rec["final"]).max() > 2.0 * np.abs(prob["pool"]).max()  # the states did grow
+    ch = chunked_scan(prob, chunk)
+    assert max_rel(ch["y"], rec["y"]) <= 1e-10
+    assert max_rel(ch["final"], rec["final"]) <= 1e-10
+
+
+@pytest.mark.parametrize("P,N", [(4, 5), (96, 100), (128, 8), (70, 3)])
+def test_padding_changes_no_value(P, N):
+    """What the size adapter relies on: zero columns of B and C, zero
+    channels of x and zero state entries change no value of the others, and
+    each 64-channel block of a head behaves as a head of its own with the
+    head's dt, A, D and dt_bias.  The oracle on the hand-padded problem,
+    cropped, equals the oracle on the problem itself, bit for bit."""
+    prob = small_problem([50, 0, 7, 130], H=2, P=P, G=1, N=N, seed=13, init="bernoulli")
+    q = pad_by_hand(prob)
+    a = oracle.recurrence(prob)
+    b = oracle.recurrence(q)
+    T, H = prob["total_len"], prob["nheads"]
+    m = q["nheads"] // H
+    yb = b["y"].reshape(T, H, 64 * m)[:, :, :P]
+    assert np.array_equal(a["y"].reshape(T, H, P), yb)
+    fb = b["final"].reshape(-1, H, 64 * m, q["dstate"])[:, :, :P, :N]
+    assert np.array_equal(a["final"].reshape(-1, H, P, N), fb)
 
 
 # ------------------------------------------- A = 0: masked linear attention
