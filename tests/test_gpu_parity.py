@@ -451,6 +451,39 @@ def test_deterministic_bitwise():
     assert torch.equal(d1["y"], d2["y"]) and torch.equal(d1["pool"], d2["pool"])
 
 
+def test_concurrent_streams_bitwise():
+    """The library keeps no state between calls: four problems of different
+    sizes and routes (dstate 64, 128 and 256, short, chunked and decode
+    sequences, a non-default short-path limit), each with its own workspace,
+    launched alternately on two streams with nothing between the launches,
+    give bitwise the results of the same calls made one at a time, and every
+    sequence matches the oracle."""
+    cases = [
+        (small_problem([700, 3, 90, 257], H=4, P=64, G=2, N=128, seed=611, max_slots=7, init="bernoulli"), DEFAULT),
+        (small_problem([1000, 40], H=2, P=64, G=1, N=256, seed=612, max_slots=4, init="all"), DEFAULT),
+        (small_problem([5, 1, 128, 60, 0, 2], H=4, P=64, G=4, N=64, seed=613, max_slots=8, init="all"), DEFAULT),
+        (small_problem([300, 33, 129], H=2, P=64, G=1, N=128, seed=614, max_slots=5, init="half"), 40),
+    ]
+    alone = [gpu_run(prob, sm)[0] for prob, sm in cases]
+    ds = [torch_io.upload(prob, "cuda") for prob, _ in cases]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    keep = []  # workspaces, alive until the streams are done
+    for i, (d, (_, sm)) in enumerate(zip(ds, cases)):
+        with torch.cuda.stream(streams[i % 2]):
+            keep.append(torch_io.run(d, short_path_max=sm))
+    torch.cuda.synchronize()
+    for i, ((prob, _), a, d) in enumerate(zip(cases, alone, ds)):
+        assert torch.equal(a["y"].view(torch.int16), d["y"].view(torch.int16)), f"problem {i}: y"
+        assert torch.equal(a["pool"].view(torch.int32), d["pool"].view(torch.int32)), f"problem {i}: pool"
+        ref = oracle.recurrence(prob)
+        assert_y(y_host(d), ref["y"], f"problem {i}")
+        fin = d["pool"].cpu().numpy()
+        for b, slot in enumerate(prob["cache_indices"]):
+            assert_final(fin[int(slot)], ref["final"][b], f"problem {i} seq {b}")
+
+
 def test_nan_sentinel_slots_not_read():
     prob = small_problem([200, 0, 333], H=4, P=64, G=1, N=64, max_slots=6, seed=43, init=[0, 0, 1])
     ci = prob["cache_indices"]
