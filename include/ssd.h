@@ -60,7 +60,7 @@ extern "C" {
 
 #define SSD_ABI_VERSION 18
 #define SSD_MAX_DSTATE 256  /* largest dstate, as in "mamba2_ssd_scan", comptime MAX_DSTATE */
-#define SSD_MAX_HEAD_DIM 1024  /* largest head_dim this build takes (the pages fix none) */
+#define SSD_MAX_HEAD_DIM 1024  /* largest head_dim the library takes (the pages fix none) */
 #define SSD_SHORT_PATH_LIMIT 128  /* longest sequence the short path can take */
 #define SSD_RECUR_LIMIT 4         /* of those, the longest the token recurrence takes */
 /* element types of the state tensors (ssd_problem.state_dtype) */
@@ -71,7 +71,7 @@ typedef enum ssd_status {
     SSD_OK = 0,
     SSD_ERR_NULL_ARG = 1,     /* a required pointer is NULL                     */
     SSD_ERR_BAD_SHAPE = 2,    /* negative/zero sizes, nheads % ngroups != 0 ...  */
-    SSD_ERR_UNSUPPORTED = 3,  /* a size beyond this build's limits              */
+    SSD_ERR_UNSUPPORTED = 3,  /* a size beyond the library's limits             */
     SSD_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than required         */
     SSD_ERR_BAD_INPUT = 5,    /* ssd_validate_inputs found a violated precondition */
     SSD_ERR_HIP = 6,          /* a HIP runtime call or kernel launch failed       */
@@ -99,7 +99,7 @@ typedef struct ssd_problem {
     int32_t ngroups;     /* G                                                 */
     int32_t dstate;      /* N; 1 .. SSD_MAX_DSTATE (see "Sizes" below)        */
     int32_t max_slots;   /* leading dimension of ssm_pool; >= 1               */
-    int32_t chunk_size;  /* 0 selects 256; this build supports 256 only       */
+    int32_t chunk_size;  /* 0 selects 256; only 256 is supported             */
     int32_t dt_softplus; /* nonzero: dts = softplus(dt + dt_bias); zero: dt + dt_bias */
     int32_t state_dtype; /* SSD_STATE_F32 or SSD_STATE_BF16: storage type of the states
                           * ("Mamba2SSDChunkScanVarlenFwdInplace": execute's state_dtype

@@ -177,7 +177,7 @@ const char *ssd_status_string(int s) {
     case SSD_OK: return "SSD_OK";
     case SSD_ERR_NULL_ARG: return "SSD_ERR_NULL_ARG: a required pointer is NULL";
     case SSD_ERR_BAD_SHAPE: return "SSD_ERR_BAD_SHAPE: malformed problem sizes";
-    case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED: sizes not supported by this build";
+    case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED: sizes beyond the library's limits";
     case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE: workspace missing, misaligned or too small";
     case SSD_ERR_BAD_INPUT: return "SSD_ERR_BAD_INPUT: query_start_loc or cache_indices violate a precondition";
     case SSD_ERR_HIP: return "SSD_ERR_HIP: a HIP runtime call failed";

@@ -20,7 +20,7 @@
 namespace ssd {
 
 constexpr int kChunk = 256;      // chunk length (tokens)
-constexpr int kHeadDim = 64;     // P supported by this build
+constexpr int kHeadDim = 64;     // P the kernels take
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kShortMax = 128;   // longest sequence the short-path kernel takes
